@@ -1,0 +1,289 @@
+"""Benchmark of the MAPL boundary hot path on one MI355X.
+
+One step = one pass of the whole hot path over one micro-batch at the 150M
+boundary shape (B=8, T=2048 -> N=16384 tokens, d=1024, r=128, V=32000, bf16):
+
+  pack A,P -> compress -> rvq encode -> stream sync -> rvq decode ->
+  reconstruct -> reconstruct backward -> compress backward -> spel_step
+
+The residual VQ runs on Z (r=128) as G=4 groups of width 32, K=256, R=2;
+spel_step runs on the fp32 1024 x 128 projector with alpha=1e-3, beta=0.9 and
+8 Newton-Schulz iterations.  Inputs are seeded synthetic tensors resident in
+HBM; before each step a 1 GiB write evicts the caches (L2 and the 256 MB
+Infinity Cache), outside the timed region.
+
+`value` is boundary tokens per second of the whole step (N / ms_per_step).
+The compress+reconstruct pair alone, the per-kernel times and the roofline of
+the dominant codec kernel are reported beside it, each timed with HIP events
+on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # dense bf16 matrix
+F32_PEAK_TFLOPS = 157.3      # fp32 matrix
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=2048, help="token sample of the CPU-oracle baseline")
+    return p.parse_args()
+
+
+class Shape:
+    B, T, d, r, V = 8, 2048, 1024, 128, 32000
+    G, K, R = 4, 256, 2
+    N = B * T
+    seed = 2
+    alpha, beta, ns = 1e-3, 0.9, 8
+
+
+def make_inputs(dev):
+    import synth
+    S = Shape
+    inp = synth.codec_inputs(S.seed, S.N, S.d, S.r, S.V, "bf16")
+    w = S.r // S.G
+    C = synth.rvq_codebooks(S.seed, 1, S.G, S.K, w, 1.0 / 32.0)
+    sender = C + torch.from_numpy(synth.gaussian(synth.stream(S.seed, 9), C.shape, 1e-4).astype(np.float32))
+    packets = [synth.stream_packets(S.seed, i, sender) for i in range(8)]
+    sp = synth.spel_inputs(S.seed, S.d, S.r, 1e-3)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    g["C"] = C.to(dev)
+    g["packets"] = [(i.to(dev), v.to(dev)) for i, v in packets]
+    g["A32"] = sp["A"].to(dev)
+    g["m"] = sp["m"].to(dev)
+    return inp, g
+
+
+def alloc(g, lac):
+    S = Shape
+    dev = g["X"].device
+    bufs = dict(
+        pk=torch.empty(lac.mapl_pack_bytes(S.d, S.r), dtype=torch.uint8, device=dev),
+        Z=torch.empty((S.N, S.r), dtype=torch.bfloat16, device=dev),
+        Zq=torch.empty((S.N, S.r), dtype=torch.bfloat16, device=dev),
+        codes=torch.empty((S.N, S.R, S.G), dtype=torch.uint8, device=dev),
+        Xh=torch.empty((S.N, S.d), dtype=torch.bfloat16, device=dev),
+        gZ=torch.empty((S.N, S.r), dtype=torch.bfloat16, device=dev),
+        gX=torch.empty((S.N, S.d), dtype=torch.bfloat16, device=dev),
+        gA=torch.empty((S.d, S.r), dtype=torch.float32, device=dev),
+        ws=torch.empty(lac.mapl_bwd_workspace_bytes(S.B, S.T, S.d, S.r), dtype=torch.uint8, device=dev),
+        sws=torch.empty(lac.spel_workspace_bytes(S.d, S.r), dtype=torch.uint8, device=dev),
+    )
+    return bufs
+
+
+def step(lac, g, b, it, ev=None):
+    """One pass of the hot path.  ev: optional dict name -> (start, end) events."""
+    S = Shape
+
+    def mark(name, i):
+        if ev is not None:
+            ev[name][i].record()
+
+    mark("pack", 0)
+    lac.mapl_pack(g["P"], g["A"], pk=b["pk"])
+    mark("pack", 1)
+    mark("compress", 0)
+    lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"], Z=b["Z"], pk=b["pk"], pk_ready=True)
+    mark("compress", 1)
+    mark("rvq_encode", 0)
+    lac.rvq_encode(b["Z"], g["C"], S.G, S.K, S.R, codes=b["codes"])
+    mark("rvq_encode", 1)
+    idx, vals = g["packets"][it % len(g["packets"])]
+    lac.rvq_stream_apply(g["C"], idx, vals)
+    mark("rvq_decode", 0)
+    lac.rvq_decode(b["codes"], g["C"], S.G, S.K, S.R, S.r, Zq=b["Zq"])
+    mark("rvq_decode", 1)
+    mark("reconstruct", 0)
+    lac.mapl_reconstruct(b["Zq"], g["tids"], g["E"], g["P"], g["A"], Xhat=b["Xh"], pk=b["pk"], pk_ready=True)
+    mark("reconstruct", 1)
+    mark("reconstruct_bwd", 0)
+    lac.mapl_reconstruct_bwd(g["gXhat"], b["Zq"], g["A"], gZ=b["gZ"], gA=b["gA"], accumulate=False, pk=b["pk"],
+                             pk_ready=True, ws=b["ws"])
+    mark("reconstruct_bwd", 1)
+    mark("compress_bwd", 0)
+    lac.mapl_compress_bwd(b["gZ"], g["X"], g["tids"], g["E"], g["P"], g["A"], gX=b["gX"], gA=b["gA"],
+                          accumulate=True, ws=b["ws"])
+    mark("compress_bwd", 1)
+    mark("spel_step", 0)
+    lac.spel_step(g["A32"], b["gA"], g["m"], S.alpha, S.beta, S.ns, ws=b["sws"])
+    mark("spel_step", 1)
+
+
+def pair(lac, g, b):
+    lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"], Z=b["Z"], pk=b["pk"], pk_ready=True)
+    lac.mapl_reconstruct(b["Z"], g["tids"], g["E"], g["P"], g["A"], Xhat=b["Xh"], pk=b["pk"], pk_ready=True)
+
+
+PHASES = ["pack", "compress", "rvq_encode", "rvq_decode", "reconstruct", "reconstruct_bwd", "compress_bwd",
+          "spel_step"]
+
+
+def algorithmic(inp):
+    """Algorithmic bytes and flops per launch of the codec kernels at this shape."""
+    S = Shape
+    n_distinct = int(np.unique(inp["tids"].numpy()).size)
+    e_rows = n_distinct * 2 * S.r
+    per_tok = 2 * S.d + 4 + 2 * S.r             # X or Xhat (bf16) + tid + Z (bf16)
+    comp_bytes = S.N * per_tok + e_rows + 2 * S.d * S.r + 2 * S.r * S.r   # + At + Qn
+    reco_bytes = S.N * per_tok + e_rows + 2 * S.d * S.r * 2               # + A + Pt
+    comp_flops = S.N * (2 * S.d * S.r + 2 * S.r * S.r)                    # executed: X A + E[t] (P A)
+    reco_flops = S.N * 4 * S.d * S.r
+    return dict(n_distinct=n_distinct, compress_bytes=comp_bytes, reconstruct_bytes=reco_bytes,
+                compress_flops=comp_flops, reconstruct_flops=reco_flops)
+
+
+def cpu_baseline(inp, n_tok):
+    """The fp64 oracle of the same step on a token sample (host cores)."""
+    from oracle import codec, rvq, spel
+    import synth
+    S = Shape
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    sl = slice(0, n_tok)
+    X = inp["X"][sl].double().numpy()
+    t = inp["tids"][sl].numpy()
+    E, P, A = inp["E"].double().numpy(), inp["P"].double().numpy(), inp["A"].double().numpy()
+    gXh = inp["gXhat"][sl].double().numpy()
+    w = S.r // S.G
+    C = synth.rvq_codebooks(S.seed, 1, S.G, S.K, w, 1.0 / 32.0).double().numpy()
+    sp = synth.spel_inputs(S.seed, S.d, S.r, 1e-3)
+    t0 = time.perf_counter()
+    Z = codec.compress(X, t, E, P, A)
+    enc = rvq.encode(Z, C, S.G, S.K, S.R)
+    Zq = rvq.decode(enc["codes"], C, S.G, S.K, S.R)
+    Xh = codec.reconstruct(Zq, t, E, P, A)
+    gZ, gA1 = codec.reconstruct_bwd(gXh, Zq, A)
+    gX, gA2 = codec.compress_bwd(gZ, X, t, E, P, A)
+    spel.spel_step(sp["A"].double().numpy(), gA1 + gA2, sp["m"].double().numpy(), S.alpha, S.beta, S.ns)
+    dt = time.perf_counter() - t0
+    del Xh, gX
+    return {"value": n_tok / dt, "unit": "boundary tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one full step of the fp64 oracle (codec fwd+bwd, RVQ encode/decode, one spel_step on "
+                      f"1024x128) on the first {n_tok} of {S.N} tokens: {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import learned_activation_compression_amd as lac
+    lac.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S = Shape
+    inp, g = make_inputs(dev)
+    b = alloc(g, lac)
+    flush = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    stream = torch.cuda.current_stream()
+
+    for i in range(args.warmup):
+        step(lac, g, b, i)
+    torch.cuda.synchronize()
+
+    ev = {p: [torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for p in PHASES}
+    step_ms, phase_ms = [], {p: [] for p in PHASES}
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        step(lac, g, b, args.warmup + i, ev)
+        s1.record(stream)
+        torch.cuda.synchronize()
+        step_ms.append(s0.elapsed_time(s1))
+        for p in PHASES:
+            phase_ms[p].append(ev[p][0].elapsed_time(ev[p][1]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+
+    # compress+reconstruct pair, cold (flushed) and warm
+    pair_cold, pair_warm = [], []
+    for i in range(args.steps):
+        if flush is not None:
+            flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pair(lac, g, b)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pair_cold.append(e0.elapsed_time(e1))
+    for i in range(args.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        pair(lac, g, b)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pair_warm.append(e0.elapsed_time(e1))
+
+    ms = float(np.mean(step_ms))
+    med = {p: float(np.median(v)) for p, v in phase_ms.items()}
+    alg = algorithmic(inp)
+    # dominant codec kernel: the larger of compress / reconstruct by time
+    dom = "reconstruct" if med["reconstruct"] >= med["compress"] else "compress"
+    dom_bytes = alg[f"{dom}_bytes"]
+    dom_s = med[dom] * 1e-3
+    achieved = dom_bytes / dom_s / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+                "algorithmic_bytes": dom_bytes, "ms": round(med[dom], 5)}
+    pc = float(np.median(pair_cold))
+    pw = float(np.median(pair_warm))
+    pair_bytes = alg["compress_bytes"] + alg["reconstruct_bytes"]
+    pair_flops = alg["compress_flops"] + alg["reconstruct_flops"]
+
+    out = {
+        "metric": "boundary tokens/s compress+reconstruct (d=1024,r=128) and % HBM/MFMA roofline",
+        "value": round(S.N / (ms * 1e-3), 1),
+        "unit": "boundary tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "150M-shaped boundary, whole hot path per step (codec fwd+bwd, RVQ G=4xw32 K=256 "
+                               "R=2, stream sync, spel_step 1024x128 NS8)",
+                   "B": S.B, "T": S.T, "N": S.N, "d": S.d, "r": S.r, "V": S.V, "flush_between_steps": flush is not None},
+        "roofline": roofline,
+        "pair": {"tokens_per_s": round(S.N / (pc * 1e-3), 1), "ms": round(pc, 5), "ms_warm": round(pw, 5),
+                 "hbm_frac": round(pair_bytes / (pc * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "mfma_frac": round(pair_flops / (pc * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "algorithmic_bytes": pair_bytes, "flops": pair_flops},
+        "phase_ms": {p: round(v, 5) for p, v in med.items()},
+        "wall_s_timed_loop": round(wall, 3),
+        "distinct_tids": alg["n_distinct"],
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

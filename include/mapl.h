@@ -1,0 +1,201 @@
+/*
+ * mapl.h -- C ABI of the MAPL pipeline-boundary activation codec for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The method is that of "Learned Subspace Compression for Communication-
+ * Efficient Pipeline Parallelism" (MAPL).  A boundary activation X (B x T x d,
+ * flattened to N = B*T rows) is compressed on the sending stage to
+ * Z = (X - E_small[tids] P) A  (Section 3.2, Eq. (1)) and rebuilt on the
+ * receiving stage as Xhat = Z A^T + E_small'[tids] P'  (Eq. (2)), with
+ * A in St(d, r) (A^T A = I_r), E_small in R^{V x r} trainable and
+ * P in R^{r x d} a frozen random orthonormal matrix (Eq. (3)).  The projector
+ * is updated once per optimizer step by SPEL (Section 3.3, Eq. (4)-(7),
+ * Algorithm 1), and Z may further be vector-quantised over G groups and R
+ * residual rounds (Section 3.5) with streamed codebook sync (Appendix F).
+ *
+ * Conventions shared by every entry point
+ *  - Every tensor argument is a caller-owned, contiguous, row-major DEVICE
+ *    pointer.  The library never allocates, frees or keeps a pointer.
+ *  - Work is enqueued on `stream` (NULL = the default stream) and the call
+ *    returns without synchronising; outputs are valid once the stream is.
+ *  - Outputs must not alias inputs, except where an argument is documented as
+ *    updated in place.
+ *  - Each call returns MAPL_OK (0) or a negative status.  Arguments are
+ *    validated on the host before anything is enqueued; on a validation error
+ *    nothing is enqueued and no output is touched.  A failed launch is
+ *    reported as MAPL_ERR_HIP (no synchronisation is done to detect it).
+ *  - `dt` selects the storage type of every floating-point tensor of a codec
+ *    call (X, Xhat, Z, gZ, gX, gXhat, E_small, P, A): MAPL_BF16 (bf16 storage,
+ *    fp32 accumulation, one round-to-nearest-even on output) or MAPL_F32.
+ *    gA is always fp32.
+ *  - Token ids are int32.  A token id outside [0, V) is a caller error; the
+ *    kernels never read out of bounds for it (its anchor row is taken as
+ *    zero), and mapl_check_tids counts such ids on the device.
+ *  - Shape limits of the bf16 codec path: d % 64 == 0, r % 32 == 0,
+ *    32 <= r <= 512, r <= d.  The fp32 path needs only 1 <= r <= d.
+ *  - The library holds no state between calls and is reentrant; calls on
+ *    different streams may overlap when their outputs and workspaces differ.
+ */
+#ifndef MAPL_H
+#define MAPL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MAPL_F32 = 0, MAPL_BF16 = 1 } mapl_dtype;
+
+enum {
+  MAPL_OK = 0,
+  MAPL_ERR_NULL = -1,      /* a required pointer is NULL                       */
+  MAPL_ERR_SHAPE = -2,     /* a size is out of range or breaks an alignment    */
+  MAPL_ERR_DTYPE = -3,     /* unsupported dtype                                */
+  MAPL_ERR_ARG = -4,       /* a scalar argument is out of range                */
+  MAPL_ERR_WORKSPACE = -5, /* workspace or pack buffer too small               */
+  MAPL_ERR_HIP = -6        /* the HIP runtime reported an error on launch      */
+};
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* mapl_status_string(int status);
+
+/* Library version string (static storage). */
+const char* mapl_version(void);
+
+/* ------------------------------------------------------------------------
+ * Packed weights.
+ *
+ * The bf16 codec kernels read A and P through a packed copy laid out for the
+ * matrix cores:  section At = A^T (r x d), section Pt = P^T (d x r) and
+ * section Qn = -(P A)^T (r x r, formed in fp32 and rounded once), all bf16.
+ * In training A changes once per optimizer step (SPEL) and P never, so one
+ * pack serves every micro-batch of a step.  Every codec entry point takes
+ * (pk, pk_bytes, pk_ready): with pk_ready == 0 the call first (re)builds the
+ * sections it needs from its own P and A arguments; with pk_ready == 1 the
+ * caller guarantees that pk already holds mapl_pack(P, A) of exactly these
+ * matrices.  For dt == MAPL_F32 no pack is used (pk may be NULL and
+ * mapl_pack_bytes returns 0).
+ * ---------------------------------------------------------------------- */
+size_t mapl_pack_bytes(int64_t d, int64_t r, mapl_dtype dt);
+
+/* Build all sections of the pack from P [r][d] and A [d][r]. */
+int mapl_pack(const void* P, const void* A, void* pk, size_t pk_bytes,
+              int64_t d, int64_t r, mapl_dtype dt, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Forward codec (Section 3.2, Eq. (1)-(3); Algorithm 1 steps 1 and 3).
+ * ---------------------------------------------------------------------- */
+
+/* Eq. (1): Z[N][r] = (X[N][d] - E_small[tids] P) A,  N = B*T.
+ * X [N][d], tids [N], E_small [V][r], P [r][d], A [d][r] -> Z [N][r].
+ * The bf16 path evaluates the exact re-association X A - E_small[tids] (P A). */
+int mapl_compress(const void* X, const int32_t* tids, const void* E_small,
+                  const void* P, const void* A, void* Z,
+                  int64_t B, int64_t T, int64_t d, int64_t r, int64_t V,
+                  mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready,
+                  hipStream_t stream);
+
+/* Eq. (2): Xhat[N][d] = Z A^T + E_small[tids] P.  Pass the RECEIVING stage's
+ * anchor (E_{p+1}, P_{p+1}) and the sender's projector A. */
+int mapl_reconstruct(const void* Z, const int32_t* tids, const void* E_small,
+                     const void* P, const void* A, void* Xhat,
+                     int64_t B, int64_t T, int64_t d, int64_t r, int64_t V,
+                     mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready,
+                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Backward of both maps (Section 3.1 "Setup": the backward pass sends the
+ * gradient across the same boundary; Section 3.2: it is routed through the
+ * same projector).  gA is fp32 [d][r]; accumulate == 0 overwrites it,
+ * accumulate == 1 adds into it (to sum both maps' terms and micro-batches).
+ * The reduction over tokens is deterministic (fixed split and order, no
+ * floating-point atomics); it uses `ws` of mapl_bwd_workspace_bytes().
+ * ---------------------------------------------------------------------- */
+size_t mapl_bwd_workspace_bytes(int64_t B, int64_t T, int64_t d, int64_t r, mapl_dtype dt);
+
+/* Receiver side, given gXhat = dL/dXhat [N][d]:
+ *   gZ[N][r] = gXhat A ;   gA (+)= gXhat^T Z.
+ * Uses the At section of the pack (built from A when pk_ready == 0). */
+int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A,
+                         void* gZ, float* gA, int accumulate,
+                         int64_t B, int64_t T, int64_t d, int64_t r,
+                         mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Sender side, given gZ = dL/dZ [N][r]:
+ *   gX[N][d] = gZ A^T ;   gA (+)= (X - E_small[tids] P)^T gZ.
+ * The bf16 path evaluates the exact re-association
+ *   X^T gZ - P^T (E_small[tids]^T gZ). */
+int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids,
+                      const void* E_small, const void* P, const void* A,
+                      void* gX, float* gA, int accumulate,
+                      int64_t B, int64_t T, int64_t d, int64_t r, int64_t V,
+                      mapl_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Count token ids outside [0, V) into *bad_count (device int32, overwritten). */
+int mapl_check_tids(const int32_t* tids, int64_t N, int64_t V, int32_t* bad_count,
+                    hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Residual multi-codebook VQ of Z (Section 3.5; Appendix E.4, Appendix F).
+ *
+ * Z [N][r] is split into G groups of width w = r/G (group g = columns
+ * [g w, (g+1) w)).  Codebooks are fp32; codeword k of group g used in round
+ * rho starts at C + rho*C_round_stride + (g*K + k)*w.  C_round_stride = 0
+ * shares one codebook across all rounds (the paper's single per-stage C_p);
+ * C_round_stride >= r*K gives each round its own.  Codes are uint8
+ * [N][R][G] at codes[(n*R + rho)*G + g], so K <= 256.
+ * Limits: w % 4 == 0, w <= 64, K % 32 == 0, 32 <= K <= 256, R >= 1.
+ * ---------------------------------------------------------------------- */
+
+/* Encode: for rho = 0..R-1 and each group, code = argmin_k ||res - c_k||^2
+ * (squared Euclidean, evaluated as ||c_k||^2 - 2<res, c_k> in fp32 on the
+ * matrix cores; exact ties go to the lowest k; a NaN distance never wins), then
+ * res -= c_code.  res starts as Z (z_dt: MAPL_BF16 or MAPL_F32). */
+int rvq_encode(const void* Z, mapl_dtype z_dt, const float* C, int64_t C_round_stride,
+               uint8_t* codes, int64_t N, int64_t r, int64_t G, int64_t K, int64_t R,
+               hipStream_t stream);
+
+/* Decode: Zq[n][g*w + j] = sum over rho (in order) of codeword codes[n][rho][g]
+ * of round rho, accumulated in fp32 and stored as out_dt. */
+int rvq_decode(const uint8_t* codes, const float* C, int64_t C_round_stride,
+               void* Zq, mapl_dtype out_dt, int64_t N, int64_t r, int64_t G,
+               int64_t K, int64_t R, hipStream_t stream);
+
+/* Streaming codebook sync on the receiver (Section 3.5 "Codebook
+ * Synchronization", Appendix F): overwrite n whole codewords.  idx [n] holds
+ * flat codeword indices q in [0, R_c*G*K) where codeword q starts at C + q*w;
+ * vals [n][w] holds the sender's values, copied bit-exactly.  Out-of-range
+ * indices are skipped.  Duplicate indices in one call: the last one wins. */
+int rvq_stream_apply(float* C, const int32_t* idx, const float* vals, int64_t n,
+                     int64_t r, int64_t G, int64_t K, int64_t R_c, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * SPEL projector update (Section 3.3, Eq. (4)-(7), Algorithm 1 step 4).
+ *
+ * On fp32 A [d][r] (updated in place) and momentum m [d][r] (updated in
+ * place), given the Euclidean gradient g [d][r]:
+ *   g_R = g - A sym(A^T g),  sym(M) = (M + M^T)/2          (Eq. 4)
+ *   m   = beta m + (1 - beta) g_R                            (Eq. 5)
+ *   D   = NS(m / ||m||_F)   (D = 0 when m == 0)              (Eq. 6)
+ *   A   = NS(A - alpha D)   (input not rescaled)             (Eq. 7)
+ * with NS the cubic Newton-Schulz polar iteration X <- 1.5 X - 0.5 X (X^T X)
+ * run ns_iters times (8 in this build's specification).  If D_out is not
+ * NULL the direction D [d][r] is also written there.
+ * Limits: r % 32 == 0, d % 32 == 0, r <= d, r <= 1024, 0 <= beta < 1,
+ * 0 <= alpha <= 0.7, 1 <= ns_iters <= 64.
+ * ---------------------------------------------------------------------- */
+size_t spel_workspace_bytes(int64_t d, int64_t r);
+
+int spel_step(float* A, const float* g, float* m, float alpha, float beta, int ns_iters,
+              float* D_out, int64_t d, int64_t r, void* ws, size_t ws_bytes,
+              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAPL_H */

@@ -1,0 +1,314 @@
+// C ABI of the MAPL codec library: host-side validation, then launches.
+// The operations and their sources are documented in include/mapl.h.
+#include <cmath>
+
+#include "../../include/mapl.h"
+#include "internal.h"
+
+using namespace mapl;
+
+namespace {
+
+constexpr const char* kVersion = "mapl-gfx950 0.1.0";
+
+// Launch status: clears any error left by an earlier call before enqueueing
+// and reports the launch error (if any) afterwards.
+struct LaunchScope {
+  LaunchScope() { (void)hipGetLastError(); }
+  int done() const { return hipGetLastError() == hipSuccess ? MAPL_OK : MAPL_ERR_HIP; }
+};
+
+inline bool dtype_ok(mapl_dtype dt) { return dt == MAPL_F32 || dt == MAPL_BF16; }
+
+// Shared shape rules of the codec entry points.
+int check_codec_shape(int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, mapl_dtype dt, bool needV) {
+  if (!dtype_ok(dt)) return MAPL_ERR_DTYPE;
+  if (B < 0 || T < 0) return MAPL_ERR_SHAPE;
+  if (B > 0 && T > INT32_MAX / B) return MAPL_ERR_SHAPE;
+  if (d < 1 || r < 1 || r > d || d > (1 << 20)) return MAPL_ERR_SHAPE;
+  if (needV && (V < 1 || V > INT32_MAX)) return MAPL_ERR_SHAPE;
+  if (dt == MAPL_BF16) {
+    if (d % 64 != 0 || r % 32 != 0 || r < 32 || r > 512) return MAPL_ERR_SHAPE;
+  } else {
+    if (d > 4096) return MAPL_ERR_SHAPE;
+  }
+  const int64_t N = B * T;
+  if (N * d > (int64_t(1) << 40)) return MAPL_ERR_SHAPE;
+  return MAPL_OK;
+}
+
+int check_pack(void* pk, size_t pk_bytes, int64_t d, int64_t r, mapl_dtype dt) {
+  if (dt != MAPL_BF16) return MAPL_OK;
+  if (pk == nullptr) return MAPL_ERR_NULL;
+  if (pk_bytes < pack_bytes_bf16(d, r)) return MAPL_ERR_WORKSPACE;
+  return MAPL_OK;
+}
+
+size_t bwd_ws_bytes(int64_t N, int64_t d, int64_t r, mapl_dtype dt) {
+  if (dt == MAPL_F32) return size_t(N) * d * sizeof(float);
+  const int S = gram_splits_bf16(int(N));
+  return (size_t(S) * d * r + size_t(S) * r * r + size_t(r) * r) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mapl_status_string(int status) {
+  switch (status) {
+    case MAPL_OK: return "ok";
+    case MAPL_ERR_NULL: return "a required pointer is NULL";
+    case MAPL_ERR_SHAPE: return "a size is out of range or breaks an alignment rule";
+    case MAPL_ERR_DTYPE: return "unsupported dtype";
+    case MAPL_ERR_ARG: return "a scalar argument is out of range";
+    case MAPL_ERR_WORKSPACE: return "workspace or pack buffer too small";
+    case MAPL_ERR_HIP: return "the HIP runtime reported a launch error";
+    default: return "unknown status";
+  }
+}
+
+const char* mapl_version(void) { return kVersion; }
+
+size_t mapl_pack_bytes(int64_t d, int64_t r, mapl_dtype dt) {
+  if (dt != MAPL_BF16 || d < 1 || r < 1) return 0;
+  return pack_bytes_bf16(d, r);
+}
+
+int mapl_pack(const void* P, const void* A, void* pk, size_t pk_bytes, int64_t d, int64_t r, mapl_dtype dt,
+              hipStream_t stream) {
+  int st = check_codec_shape(1, 1, d, r, 1, dt, false);
+  if (st) return st;
+  if (dt == MAPL_F32) return MAPL_OK;
+  if (!P || !A) return MAPL_ERR_NULL;
+  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
+  LaunchScope ls;
+  PackView v = pack_view(pk, d, r);
+  const uint16_t* A16 = static_cast<const uint16_t*>(A);
+  const uint16_t* P16 = static_cast<const uint16_t*>(P);
+  launch_pack_At(A16, v.At, int(d), int(r), stream);
+  launch_pack_Pt(P16, v.Pt, int(d), int(r), stream);
+  launch_pack_Qn(P16, A16, v.Qn, int(d), int(r), stream);
+  return ls.done();
+}
+
+int mapl_compress(const void* X, const int32_t* tids, const void* E_small, const void* P, const void* A, void* Z,
+                  int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, mapl_dtype dt, void* pk, size_t pk_bytes,
+                  int pk_ready, hipStream_t stream) {
+  int st = check_codec_shape(B, T, d, r, V, dt, true);
+  if (st) return st;
+  if (pk_ready != 0 && pk_ready != 1) return MAPL_ERR_ARG;
+  const int N = int(B * T);
+  if (N == 0) return MAPL_OK;  // nothing to do; outputs untouched
+  if (!X || !tids || !E_small || !P || !A || !Z) return MAPL_ERR_NULL;
+  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
+  LaunchScope ls;
+  if (dt == MAPL_F32) {
+    launch_compress_f32(static_cast<const float*>(X), tids, static_cast<const float*>(E_small),
+                        static_cast<const float*>(P), static_cast<const float*>(A), static_cast<float*>(Z), N, int(d),
+                        int(r), int(V), stream);
+    return ls.done();
+  }
+  PackView v = pack_view(pk, d, r);
+  if (!pk_ready) {
+    launch_pack_At(static_cast<const uint16_t*>(A), v.At, int(d), int(r), stream);
+    launch_pack_Qn(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v.Qn, int(d), int(r), stream);
+  }
+  launch_tok_reduce_bf16(static_cast<const uint16_t*>(X), v.At, tids, static_cast<const uint16_t*>(E_small), v.Qn,
+                         static_cast<uint16_t*>(Z), N, int(d), int(r), int(V), stream);
+  return ls.done();
+}
+
+int mapl_reconstruct(const void* Z, const int32_t* tids, const void* E_small, const void* P, const void* A,
+                     void* Xhat, int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, mapl_dtype dt, void* pk,
+                     size_t pk_bytes, int pk_ready, hipStream_t stream) {
+  int st = check_codec_shape(B, T, d, r, V, dt, true);
+  if (st) return st;
+  if (pk_ready != 0 && pk_ready != 1) return MAPL_ERR_ARG;
+  const int N = int(B * T);
+  if (N == 0) return MAPL_OK;  // nothing to do; outputs untouched
+  if (!Z || !tids || !E_small || !P || !A || !Xhat) return MAPL_ERR_NULL;
+  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
+  LaunchScope ls;
+  if (dt == MAPL_F32) {
+    launch_reconstruct_f32(static_cast<const float*>(Z), tids, static_cast<const float*>(E_small),
+                           static_cast<const float*>(P), static_cast<const float*>(A), static_cast<float*>(Xhat), N,
+                           int(d), int(r), int(V), stream);
+    return ls.done();
+  }
+  PackView v = pack_view(pk, d, r);
+  if (!pk_ready) launch_pack_Pt(static_cast<const uint16_t*>(P), v.Pt, int(d), int(r), stream);
+  launch_tok_expand_bf16(static_cast<const uint16_t*>(Z), static_cast<const uint16_t*>(A), tids,
+                         static_cast<const uint16_t*>(E_small), v.Pt, static_cast<uint16_t*>(Xhat), N, int(d), int(r),
+                         int(V), stream);
+  return ls.done();
+}
+
+size_t mapl_bwd_workspace_bytes(int64_t B, int64_t T, int64_t d, int64_t r, mapl_dtype dt) {
+  if (check_codec_shape(B, T, d, r, 1, dt, false)) return 0;
+  return bwd_ws_bytes(B * T, d, r, dt);
+}
+
+int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A, void* gZ, float* gA, int accumulate,
+                         int64_t B, int64_t T, int64_t d, int64_t r, mapl_dtype dt, void* pk, size_t pk_bytes,
+                         int pk_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_codec_shape(B, T, d, r, 1, dt, false);
+  if (st) return st;
+  if ((accumulate != 0 && accumulate != 1) || (pk_ready != 0 && pk_ready != 1)) return MAPL_ERR_ARG;
+  const int64_t N = B * T;
+  if (!gA) return MAPL_ERR_NULL;
+  if (N == 0) {  // empty batch: gA = 0 (or unchanged when accumulating)
+    LaunchScope ls0;
+    if (!accumulate) launch_fill_f32(gA, d * r, 0.f, stream);
+    return ls0.done();
+  }
+  if (!gXhat || !Z || !A || !gZ) return MAPL_ERR_NULL;
+  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
+  const size_t need = bwd_ws_bytes(N, d, r, dt);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return ws == nullptr ? MAPL_ERR_NULL : MAPL_ERR_WORKSPACE;
+  LaunchScope ls;
+  if (dt == MAPL_F32) {
+    if (N > 0)
+      launch_rowmap_f32(static_cast<const float*>(gXhat), static_cast<const float*>(A), static_cast<float*>(gZ),
+                        int(N), int(d), int(r), 0, stream);
+    launch_outer_f32(static_cast<const float*>(gXhat), static_cast<const float*>(Z), gA, int(N), int(d), int(r),
+                     accumulate, stream);
+    return ls.done();
+  }
+  PackView v = pack_view(pk, d, r);
+  if (!pk_ready) launch_pack_At(static_cast<const uint16_t*>(A), v.At, int(d), int(r), stream);
+  const int S = gram_splits_bf16(int(N));
+  float* part = static_cast<float*>(ws);
+  if (N > 0) {
+    launch_tok_reduce_bf16(static_cast<const uint16_t*>(gXhat), v.At, nullptr, nullptr, nullptr,
+                           static_cast<uint16_t*>(gZ), int(N), int(d), int(r), 1, stream);
+    launch_gram_bf16(static_cast<const uint16_t*>(gXhat), nullptr, 1, static_cast<const uint16_t*>(Z), part, int(N),
+                     int(d), int(r), S, stream);
+    launch_reduce_partials(part, S, gA, d * r, accumulate, stream);
+  }
+  return ls.done();
+}
+
+int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const void* E_small, const void* P,
+                      const void* A, void* gX, float* gA, int accumulate, int64_t B, int64_t T, int64_t d, int64_t r,
+                      int64_t V, mapl_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_codec_shape(B, T, d, r, V, dt, true);
+  if (st) return st;
+  if (accumulate != 0 && accumulate != 1) return MAPL_ERR_ARG;
+  const int64_t N = B * T;
+  if (!gA) return MAPL_ERR_NULL;
+  if (N == 0) {  // empty batch: gA = 0 (or unchanged when accumulating)
+    LaunchScope ls0;
+    if (!accumulate) launch_fill_f32(gA, d * r, 0.f, stream);
+    return ls0.done();
+  }
+  if (!gZ || !X || !tids || !E_small || !P || !A || !gX) return MAPL_ERR_NULL;
+  const size_t need = bwd_ws_bytes(N, d, r, dt);
+  if (need > 0 && (ws == nullptr || ws_bytes < need)) return ws == nullptr ? MAPL_ERR_NULL : MAPL_ERR_WORKSPACE;
+  LaunchScope ls;
+  if (dt == MAPL_F32) {
+    float* R = static_cast<float*>(ws);
+    if (N > 0) {
+      launch_rowmap_f32(static_cast<const float*>(gZ), static_cast<const float*>(A), static_cast<float*>(gX), int(N),
+                        int(d), int(r), 1, stream);
+      launch_residual_f32(static_cast<const float*>(X), tids, static_cast<const float*>(E_small),
+                          static_cast<const float*>(P), R, int(N), int(d), int(r), int(V), stream);
+    }
+    launch_outer_f32(R, static_cast<const float*>(gZ), gA, int(N), int(d), int(r), accumulate, stream);
+    return ls.done();
+  }
+  const int S = gram_splits_bf16(int(N));
+  float* part1 = static_cast<float*>(ws);
+  float* part2 = part1 + size_t(S) * d * r;
+  float* M = part2 + size_t(S) * r * r;
+  const uint16_t* gZ16 = static_cast<const uint16_t*>(gZ);
+  // gX = gZ A^T
+  launch_tok_expand_bf16(gZ16, static_cast<const uint16_t*>(A), nullptr, nullptr, nullptr,
+                         static_cast<uint16_t*>(gX), int(N), int(d), int(r), 1, stream);
+  // gA (+)= X^T gZ - P^T (E[t]^T gZ)
+  launch_gram_bf16(static_cast<const uint16_t*>(X), nullptr, 1, gZ16, part1, int(N), int(d), int(r), S, stream);
+  launch_gram_bf16(static_cast<const uint16_t*>(E_small), tids, int(V), gZ16, part2, int(N), int(r), int(r), S,
+                   stream);
+  launch_reduce_partials(part1, S, gA, d * r, accumulate, stream);
+  launch_reduce_partials(part2, S, M, r * r, 0, stream);
+  // gA[i][j] -= sum_k P[k][i] M[k][j]
+  launch_small_gemm(int(d), int(r), int(r), P, 1, /*sai*/ 1, /*sak*/ d, M, 0, r, 1, gA, 0, r, 1, -1.f, 1.f, stream);
+  return ls.done();
+}
+
+int mapl_check_tids(const int32_t* tids, int64_t N, int64_t V, int32_t* bad_count, hipStream_t stream) {
+  if (!bad_count || (N > 0 && !tids)) return MAPL_ERR_NULL;
+  if (N < 0 || N > INT32_MAX || V < 1 || V > INT32_MAX) return MAPL_ERR_SHAPE;
+  LaunchScope ls;
+  launch_check_tids(tids, int(N), int(V), bad_count, stream);
+  return ls.done();
+}
+
+// ------------------------------------------------------------------ RVQ --
+static int check_rvq_shape(int64_t N, int64_t r, int64_t G, int64_t K, int64_t R, int64_t stride) {
+  if (N < 0 || N > INT32_MAX || r < 1 || G < 1 || K < 1 || R < 1 || R > 64) return MAPL_ERR_SHAPE;
+  if (r % G != 0 || K > 256) return MAPL_ERR_SHAPE;
+  if (N * r > (int64_t(1) << 40)) return MAPL_ERR_SHAPE;
+  if (stride != 0 && stride < r * K) return MAPL_ERR_ARG;
+  return MAPL_OK;
+}
+
+int rvq_encode(const void* Z, mapl_dtype z_dt, const float* C, int64_t C_round_stride, uint8_t* codes, int64_t N,
+               int64_t r, int64_t G, int64_t K, int64_t R, hipStream_t stream) {
+  int st = check_rvq_shape(N, r, G, K, R, C_round_stride);
+  if (st) return st;
+  if (!dtype_ok(z_dt)) return MAPL_ERR_DTYPE;
+  if (!Z || !C || !codes) return MAPL_ERR_NULL;
+  const int64_t w = r / G;
+  if (!(w == 2 || w == 4 || w == 8 || w == 16 || w == 32 || w == 64)) return MAPL_ERR_SHAPE;
+  if (K % 32 != 0 || K < 32) return MAPL_ERR_SHAPE;
+  if ((w * K + K) * int64_t(sizeof(float)) > 65536) return MAPL_ERR_SHAPE;
+  if (N == 0) return MAPL_OK;
+  LaunchScope ls;
+  launch_rvq_encode(Z, z_dt == MAPL_BF16, C, C_round_stride, codes, int(N), int(r), int(G), int(K), int(R), stream);
+  return ls.done();
+}
+
+int rvq_decode(const uint8_t* codes, const float* C, int64_t C_round_stride, void* Zq, mapl_dtype out_dt, int64_t N,
+               int64_t r, int64_t G, int64_t K, int64_t R, hipStream_t stream) {
+  int st = check_rvq_shape(N, r, G, K, R, C_round_stride);
+  if (st) return st;
+  if (!dtype_ok(out_dt)) return MAPL_ERR_DTYPE;
+  if (!codes || !C || !Zq) return MAPL_ERR_NULL;
+  if (N == 0) return MAPL_OK;
+  LaunchScope ls;
+  launch_rvq_decode(codes, C, C_round_stride, Zq, out_dt == MAPL_BF16, int(N), int(r), int(G), int(K), int(R),
+                    stream);
+  return ls.done();
+}
+
+int rvq_stream_apply(float* C, const int32_t* idx, const float* vals, int64_t n, int64_t r, int64_t G, int64_t K,
+                     int64_t R_c, hipStream_t stream) {
+  if (n < 0 || n > INT32_MAX || r < 1 || G < 1 || K < 1 || R_c < 1 || r % G != 0) return MAPL_ERR_SHAPE;
+  if (!C || (n > 0 && (!idx || !vals))) return MAPL_ERR_NULL;
+  if (n == 0) return MAPL_OK;
+  LaunchScope ls;
+  launch_rvq_stream(C, idx, vals, int(n), int(r / G), R_c * G * K, stream);
+  return ls.done();
+}
+
+// ----------------------------------------------------------------- SPEL --
+size_t spel_workspace_bytes(int64_t d, int64_t r) {
+  if (d < 1 || r < 1 || r > d || r > 1024 || d % 32 || r % 32 || d > (1 << 24)) return 0;
+  return spel_ws_bytes(d, r);
+}
+
+int spel_step(float* A, const float* g, float* m, float alpha, float beta, int ns_iters, float* D_out, int64_t d,
+              int64_t r, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (d < 1 || r < 1 || r > d || r > 1024 || d % 32 || r % 32 || d > (1 << 24)) return MAPL_ERR_SHAPE;
+  if (!A || !g || !m) return MAPL_ERR_NULL;
+  if (!(beta >= 0.f && beta < 1.f) || !(alpha >= 0.f && alpha <= 0.7f) || ns_iters < 1 || ns_iters > 64)
+    return MAPL_ERR_ARG;
+  const size_t need = spel_ws_bytes(d, r);
+  if (!ws) return MAPL_ERR_NULL;
+  if (ws_bytes < need) return MAPL_ERR_WORKSPACE;
+  LaunchScope ls;
+  launch_spel(A, g, m, alpha, beta, ns_iters, D_out, int(d), int(r), ws, stream);
+  return ls.done();
+}
+
+}  // extern "C"

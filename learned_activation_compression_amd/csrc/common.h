@@ -1,0 +1,69 @@
+// Device-side helpers shared by the MAPL kernels (gfx950 only).
+//
+// Matrix-core conventions used throughout (wave64):
+//   v_mfma_f32_32x32x16_bf16  A: lane l supplies row  (l & 31), 8 consecutive k (k = 8*(l>>5) + i)
+//                             B: lane l supplies col  (l & 31), the same 8 k
+//                             D: lane l, register v holds row 8*(v>>2) + 4*(l>>5) + (v&3), col (l & 31)
+//   v_mfma_f32_32x32x2_f32    A: lane l supplies row (l & 31), k = (l >> 5)
+//                             B: lane l supplies col (l & 31), k = (l >> 5)
+//                             D: same layout as above.
+// The pairing of k slots between A and B is symmetric, so any consistent
+// assignment of contraction indices to k slots gives the same sum.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mapl {
+
+typedef uint16_t bf16_t;  // bf16 storage (raw bits)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf2f(bf16_t v) { return __uint_as_float(static_cast<uint32_t>(v) << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f)); }
+
+__device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
+  return static_cast<uint32_t>(f2bf(lo)) | (static_cast<uint32_t>(f2bf(hi)) << 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f2bf(v); }
+
+// 16-byte global load of 8 bf16 as an MFMA operand.
+__device__ __forceinline__ bf16x8 ld_bf16x8(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() { return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u}); }
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32_32x32x2(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Row index (within a 32x32 tile) held by register v of a lane in the upper
+// (hi = 1) or lower half-wave, for the 32x32 MFMA output layout.
+__device__ __forceinline__ int mfma32_row(int v, int hi) { return 8 * (v >> 2) + 4 * hi + (v & 3); }
+
+// Spread consecutive workgroup ids over the 8 XCDs so that each XCD receives a
+// contiguous range of tiles (tiles that share operands then share an L2).
+__device__ __forceinline__ int xcd_swizzle(int bid, int total) {
+  if ((total & 7) != 0) return bid;
+  return (bid & 7) * (total >> 3) + (bid >> 3);
+}
+
+}  // namespace mapl

@@ -1,0 +1,76 @@
+// Host-side launchers of the MAPL kernels.  Each launcher assumes its
+// arguments were validated by the C ABI layer and only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mapl {
+
+// ---- packed weights (bf16): At = A^T [r][d], Pt = P^T [d][r], Qn = -(P A)^T [r][r]
+struct PackView {
+  uint16_t* At;
+  uint16_t* Pt;
+  uint16_t* Qn;
+};
+size_t pack_bytes_bf16(int64_t d, int64_t r);
+PackView pack_view(void* pk, int64_t d, int64_t r);
+void launch_pack_At(const uint16_t* A, uint16_t* At, int d, int r, hipStream_t s);
+void launch_pack_Pt(const uint16_t* P, uint16_t* Pt, int d, int r, hipStream_t s);
+void launch_pack_Qn(const uint16_t* P, const uint16_t* A, uint16_t* Qn, int d, int r, hipStream_t s);
+
+// generic small fp32-accumulating GEMM with arbitrary strides:
+//   C(i,j) = alpha * sum_k A(i,k) B(k,j) + beta * C(i,j)
+// type codes: 0 = fp32, 1 = bf16
+void launch_small_gemm(int M, int N, int K, const void* A, int a_ty, int64_t sai, int64_t sak,
+                       const void* B, int b_ty, int64_t sbk, int64_t sbj, void* C, int c_ty,
+                       int64_t sci, int64_t scj, float alpha, float beta, hipStream_t s);
+
+// ---- bf16 codec
+// out[N][r] = in[N][d] A  (- E[tids] (P A)) via At and Qn; E == nullptr drops the anchor term
+void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* At, const int32_t* tids,
+                            const uint16_t* E, const uint16_t* Qn, uint16_t* out,
+                            int N, int d, int r, int V, hipStream_t s);
+// out[N][d] = in[N][r] A^T (+ E[tids] P) via A and Pt; E == nullptr drops the anchor term
+void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* A, const int32_t* tids,
+                            const uint16_t* E, const uint16_t* Pt, uint16_t* out,
+                            int N, int d, int r, int V, hipStream_t s);
+// token-split partial Gram: part[s][i][j] = sum_{n in split s} L[n][i] R[n][j],
+// L = in_l [N][Ld] or, when tids != nullptr, L[n] = E[tids[n]] ([V][Ld]).
+int gram_splits_bf16(int N);
+void launch_gram_bf16(const uint16_t* L, const int32_t* tids, int V, const uint16_t* R,
+                      float* part, int N, int Ld, int r, int splits, hipStream_t s);
+// out[e] = (accumulate ? out[e] : 0) + sum_s part[s][e], e < count (fixed order)
+void launch_reduce_partials(const float* part, int splits, float* out, int64_t count,
+                            int accumulate, hipStream_t s);
+
+// ---- fp32 codec (small problems, plain fp32 arithmetic)
+void launch_compress_f32(const float* X, const int32_t* tids, const float* E, const float* P,
+                         const float* A, float* Z, int N, int d, int r, int V, hipStream_t s);
+void launch_residual_f32(const float* X, const int32_t* tids, const float* E, const float* P,
+                         float* R, int N, int d, int r, int V, hipStream_t s);
+void launch_reconstruct_f32(const float* Z, const int32_t* tids, const float* E, const float* P,
+                            const float* A, float* Xh, int N, int d, int r, int V, hipStream_t s);
+void launch_rowmap_f32(const float* in, const float* A, float* out, int N, int d, int r,
+                       int transposeA, hipStream_t s);
+void launch_outer_f32(const float* L, const float* R, float* gA, int N, int d, int r,
+                      int accumulate, hipStream_t s);
+
+void launch_fill_f32(float* p, int64_t count, float value, hipStream_t s);
+void launch_check_tids(const int32_t* tids, int N, int V, int32_t* bad, hipStream_t s);
+
+// ---- residual VQ
+void launch_rvq_encode(const void* Z, int z_bf16, const float* C, int64_t stride,
+                       uint8_t* codes, int N, int r, int G, int K, int R, hipStream_t s);
+void launch_rvq_decode(const uint8_t* codes, const float* C, int64_t stride, void* Zq, int out_bf16,
+                       int N, int r, int G, int K, int R, hipStream_t s);
+void launch_rvq_stream(float* C, const int32_t* idx, const float* vals, int n, int w,
+                       int64_t total_codewords, hipStream_t s);
+
+// ---- SPEL
+size_t spel_ws_bytes(int64_t d, int64_t r);
+void launch_spel(float* A, const float* g, float* m, float alpha, float beta, int ns_iters,
+                 float* D_out, int d, int r, void* ws, hipStream_t s);
+
+}  // namespace mapl

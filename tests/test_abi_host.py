@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol that
+include/mapl.h declares, and its host validation returns the documented status
+codes before anything is enqueued.  No call here reaches a kernel launch, so
+these run without a GPU."""
+import ctypes
+
+import pytest
+
+import learned_activation_compression_amd as lac
+
+OK, ENULL, ESHAPE, EDTYPE, EARG, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6
+F32, BF16 = lac.MAPL_F32, lac.MAPL_BF16
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lac.load()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = lac.exported_symbols()
+    assert len(names) == 15, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(lac._SIGS), set(names) ^ set(lac._SIGS)
+
+
+def test_status_strings_and_version(lib):
+    for s in (OK, ENULL, ESHAPE, EDTYPE, EARG, EWS, EHIP):
+        assert lib.mapl_status_string(s)
+    assert lib.mapl_status_string(-99) == b"unknown status"
+    assert lib.mapl_version().startswith(b"mapl-gfx950")
+
+
+def test_pack_and_workspace_sizes(lib):
+    d, r = 1024, 128
+    want = 2 * r * d + 2 * d * r + 2 * r * r
+    got = lib.mapl_pack_bytes(d, r, BF16)
+    assert want <= got <= want + 3 * 256
+    assert lib.mapl_pack_bytes(d, r, F32) == 0
+    assert lib.mapl_bwd_workspace_bytes(8, 2048, d, r, BF16) > 0
+    assert lib.mapl_bwd_workspace_bytes(1, 128, 256, 32, F32) == 128 * 256 * 4
+    assert lib.mapl_bwd_workspace_bytes(1, 128, 1000, 32, BF16) == 0     # d % 64 != 0
+    assert lib.spel_workspace_bytes(2048, 256) >= 3 * 2048 * 256 * 4
+    assert lib.spel_workspace_bytes(2048, 250) == 0                      # r % 32 != 0
+
+
+def _compress(lib, **kw):
+    a = dict(X=FAKE, tids=FAKE, E=FAKE, P=FAKE, A=FAKE, Z=FAKE, B=8, T=2048, d=1024, r=128, V=32000, dt=BF16,
+             pk=FAKE, pk_bytes=10 ** 7, pk_ready=1, s=None)
+    a.update(kw)
+    return lib.mapl_compress(a["X"], a["tids"], a["E"], a["P"], a["A"], a["Z"], a["B"], a["T"], a["d"], a["r"],
+                             a["V"], a["dt"], a["pk"], a["pk_bytes"], a["pk_ready"], a["s"])
+
+
+def test_compress_validation(lib):
+    assert _compress(lib, X=None) == ENULL
+    assert _compress(lib, tids=None) == ENULL
+    assert _compress(lib, pk=None) == ENULL
+    assert _compress(lib, pk_bytes=100) == EWS
+    assert _compress(lib, d=1000) == ESHAPE          # bf16 needs d % 64 == 0
+    assert _compress(lib, r=100) == ESHAPE           # bf16 needs r % 32 == 0
+    assert _compress(lib, r=2048) == ESHAPE          # r > d
+    assert _compress(lib, r=1024, d=1024) == ESHAPE  # bf16 r <= 512
+    assert _compress(lib, V=0) == ESHAPE
+    assert _compress(lib, B=-1) == ESHAPE
+    assert _compress(lib, dt=7) == EDTYPE
+    assert _compress(lib, pk_ready=2) == EARG
+    assert _compress(lib, dt=F32, d=8192, r=64, pk=None, pk_bytes=0) == ESHAPE  # fp32 d <= 4096
+
+
+def test_empty_batch_is_a_no_op(lib):
+    # N = 0 passes validation and returns before any launch
+    assert _compress(lib, B=0) == OK
+    assert lib.mapl_reconstruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2048, 1024, 128, 32000, BF16, FAKE, 10 ** 7,
+                                1, None) == OK
+    assert lib.rvq_encode(FAKE, BF16, FAKE, 0, FAKE, 0, 256, 8, 256, 2, None) == OK
+    assert lib.rvq_decode(FAKE, FAKE, 0, FAKE, F32, 0, 256, 8, 256, 2, None) == OK
+    assert lib.rvq_stream_apply(FAKE, FAKE, FAKE, 0, 256, 8, 256, 1, None) == OK
+
+
+def test_backward_validation(lib):
+    ws = lib.mapl_bwd_workspace_bytes(8, 2048, 1024, 128, BF16)
+    f = lib.mapl_reconstruct_bwd
+    assert f(None, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, BF16, FAKE, 10 ** 7, 1, FAKE, ws, None) == ENULL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, BF16, FAKE, 10 ** 7, 1, FAKE, ws - 4, None) == EWS
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, BF16, FAKE, 10 ** 7, 1, None, ws, None) == ENULL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2048, 1024, 128, BF16, FAKE, 10 ** 7, 1, FAKE, ws, None) == EARG
+    g = lib.mapl_compress_bwd
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 8, 2048, 1024, 128, 32000, BF16, FAKE, ws,
+             None) == ENULL
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, 32000, BF16, FAKE, 16,
+             None) == EWS
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1000, 128, 32000, BF16, FAKE, ws,
+             None) == ESHAPE
+
+
+def test_rvq_validation(lib):
+    e = lib.rvq_encode
+    assert e(None, BF16, FAKE, 0, FAKE, 16384, 256, 8, 256, 2, None) == ENULL
+    assert e(FAKE, BF16, FAKE, 0, FAKE, 16384, 256, 7, 256, 2, None) == ESHAPE   # r % G
+    assert e(FAKE, BF16, FAKE, 0, FAKE, 16384, 256, 8, 512, 2, None) == ESHAPE   # K > 256 (uint8 codes)
+    assert e(FAKE, BF16, FAKE, 0, FAKE, 16384, 256, 8, 100, 2, None) == ESHAPE   # K % 32
+    assert e(FAKE, BF16, FAKE, 0, FAKE, 16384, 384, 3, 256, 2, None) == ESHAPE   # w = 128 unsupported
+    assert e(FAKE, BF16, FAKE, 0, FAKE, 16384, 256, 8, 256, 0, None) == ESHAPE   # R >= 1
+    assert e(FAKE, BF16, FAKE, 100, FAKE, 16384, 256, 8, 256, 2, None) == EARG   # 0 < stride < r*K
+    assert e(FAKE, 5, FAKE, 0, FAKE, 16384, 256, 8, 256, 2, None) == EDTYPE
+    d = lib.rvq_decode
+    assert d(FAKE, FAKE, 0, None, F32, 16384, 256, 8, 256, 2, None) == ENULL
+    assert d(FAKE, FAKE, 0, FAKE, 9, 16384, 256, 8, 256, 2, None) == EDTYPE
+    s = lib.rvq_stream_apply
+    assert s(None, FAKE, FAKE, 8, 256, 8, 256, 1, None) == ENULL
+    assert s(FAKE, FAKE, FAKE, 8, 250, 8, 256, 1, None) == ESHAPE
+
+
+def test_spel_validation(lib):
+    ws = lib.spel_workspace_bytes(2048, 256)
+    f = lib.spel_step
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 256, FAKE, ws - 1, None) == EWS
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 256, None, ws, None) == ENULL
+    assert f(None, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 256, FAKE, ws, None) == ENULL
+    assert f(FAKE, FAKE, FAKE, 1e-3, 1.0, 8, None, 2048, 256, FAKE, ws, None) == EARG     # beta < 1
+    assert f(FAKE, FAKE, FAKE, 0.9, 0.9, 8, None, 2048, 256, FAKE, ws, None) == EARG      # alpha <= 0.7
+    assert f(FAKE, FAKE, FAKE, float("nan"), 0.9, 8, None, 2048, 256, FAKE, ws, None) == EARG
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 0, None, 2048, 256, FAKE, ws, None) == EARG     # ns_iters >= 1
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 250, FAKE, ws, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, 256, 512, FAKE, ws, None) == ESHAPE    # r > d
+
+
+def test_check_tids_validation(lib):
+    assert lib.mapl_check_tids(FAKE, 10, 0, FAKE, None) == ESHAPE
+    assert lib.mapl_check_tids(FAKE, 10, 5, None, None) == ENULL
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    X = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(lac.MaplError):
+        lac.mapl_compress(X, torch.zeros(4, dtype=torch.int32), torch.zeros(8, 32, dtype=torch.bfloat16),
+                          torch.zeros(32, 64, dtype=torch.bfloat16), torch.zeros(64, 32, dtype=torch.bfloat16))
