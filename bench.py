@@ -121,7 +121,7 @@ def step(lac, g, b, it, ev=None):
     mark("reconstruct_bwd", 1)
     mark("compress_bwd", 0)
     lac.mapl_compress_bwd(b["gZ"], g["X"], g["tids"], g["E"], g["P"], g["A"], gX=b["gX"], gA=b["gA"],
-                          accumulate=True, ws=b["ws"])
+                          accumulate=True, pk=b["pk"], pk_ready=True, ws=b["ws"])
     mark("compress_bwd", 1)
     mark("spel_step", 0)
     lac.spel_step(g["A32"], b["gA"], g["m"], S.alpha, S.beta, S.ns, ws=b["sws"])

@@ -31,8 +31,8 @@
  *  - Token ids are int32.  A token id outside [0, V) is a caller error; the
  *    kernels never read out of bounds for it (its anchor row is taken as
  *    zero), and mapl_check_tids counts such ids on the device.
- *  - Shape limits of the bf16 codec path: d % 64 == 0, r % 32 == 0,
- *    32 <= r <= 512, r <= d.  The fp32 path needs only 1 <= r <= d.
+ *  - Shape limits of the bf16 codec path: d % 128 == 0, r a power of two
+ *    with 32 <= r <= 512, r <= d.  The fp32 path needs 1 <= r <= d <= 4096.
  *  - The library holds no state between calls and is reentrant; calls on
  *    different streams may overlap when their outputs and workspaces differ.
  */
@@ -69,19 +69,22 @@ const char* mapl_version(void);
  * Packed weights.
  *
  * The bf16 codec kernels read A and P through a packed copy laid out for the
- * matrix cores:  section At = A^T (r x d), section Pt = P^T (d x r) and
- * section Qn = -(P A)^T (r x r, formed in fp32 and rounded once), all bf16.
- * In training A changes once per optimizer step (SPEL) and P never, so one
- * pack serves every micro-batch of a step.  Every codec entry point takes
- * (pk, pk_bytes, pk_ready): with pk_ready == 0 the call first (re)builds the
- * sections it needs from its own P and A arguments; with pk_ready == 1 the
- * caller guarantees that pk already holds mapl_pack(P, A) of exactly these
- * matrices.  For dt == MAPL_F32 no pack is used (pk may be NULL and
- * mapl_pack_bytes returns 0).
+ * matrix cores: the operands A^T (r x d), A (d x r), P^T (d x r) and
+ * -(P A)^T (r x r, formed with fp32 accumulation and rounded once), all bf16
+ * and stored in fragment order, i.e. as the 64-lane x 16-byte pieces one
+ * v_mfma_f32_32x32x16_bf16 consumes, so that every weight load of a wave is
+ * one contiguous kilobyte.  In training A changes once per optimizer step
+ * (SPEL) and P never, so one pack serves every micro-batch of a step.
+ * Every bf16 codec entry point takes (pk, pk_bytes, pk_ready): with
+ * pk_ready == 0 the call first rebuilds the pack from its own P and A
+ * arguments (mapl_reconstruct_bwd, which has no P, rebuilds only the A^T
+ * part); with pk_ready == 1 the caller guarantees that pk holds
+ * mapl_pack(P, A) of exactly these matrices.  For dt == MAPL_F32 no pack is
+ * used (pk may be NULL and mapl_pack_bytes returns 0).
  * ---------------------------------------------------------------------- */
 size_t mapl_pack_bytes(int64_t d, int64_t r, mapl_dtype dt);
 
-/* Build all sections of the pack from P [r][d] and A [d][r]. */
+/* Build the whole pack from P [r][d] and A [d][r] (bf16). */
 int mapl_pack(const void* P, const void* A, void* pk, size_t pk_bytes,
               int64_t d, int64_t r, mapl_dtype dt, hipStream_t stream);
 
@@ -118,7 +121,7 @@ size_t mapl_bwd_workspace_bytes(int64_t B, int64_t T, int64_t d, int64_t r, mapl
 
 /* Receiver side, given gXhat = dL/dXhat [N][d]:
  *   gZ[N][r] = gXhat A ;   gA (+)= gXhat^T Z.
- * Uses the At section of the pack (built from A when pk_ready == 0). */
+ * Uses the A^T part of the pack (rebuilt from A when pk_ready == 0). */
 int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A,
                          void* gZ, float* gA, int accumulate,
                          int64_t B, int64_t T, int64_t d, int64_t r,
@@ -133,7 +136,8 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids,
                       const void* E_small, const void* P, const void* A,
                       void* gX, float* gA, int accumulate,
                       int64_t B, int64_t T, int64_t d, int64_t r, int64_t V,
-                      mapl_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+                      mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Count token ids outside [0, V) into *bad_count (device int32, overwritten). */
 int mapl_check_tids(const int32_t* tids, int64_t N, int64_t V, int32_t* bad_count,

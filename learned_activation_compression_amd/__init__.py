@@ -49,7 +49,7 @@ _SIGS = {
     "mapl_reconstruct_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32,
                                     _vp, _sz, _vp]),
     "mapl_compress_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
-                                 _vp, _sz, _vp]),
+                                 _vp, _sz, _i32, _vp, _sz, _vp]),
     "mapl_check_tids": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "rvq_encode": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
     "rvq_decode": (_i32, [_vp, _vp, _i64, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _vp]),
@@ -241,7 +241,8 @@ def mapl_reconstruct_bwd(gXhat, Z, A, gZ=None, gA=None, accumulate=False, pk=Non
     return gZ, gA
 
 
-def mapl_compress_bwd(gZ, X, tids, E_small, P, A, gX=None, gA=None, accumulate=False, ws=None, stream=None):
+def mapl_compress_bwd(gZ, X, tids, E_small, P, A, gX=None, gA=None, accumulate=False, pk=None, pk_ready=False,
+                      ws=None, stream=None):
     """gX = gZ A^T ;  gA (+)= (X - E_small[tids] P)^T gZ.  Returns (gX, gA)."""
     d, r = A.shape
     B, T = _tokens(gZ, r, "gZ")
@@ -252,11 +253,13 @@ def mapl_compress_bwd(gZ, X, tids, E_small, P, A, gX=None, gA=None, accumulate=F
     if gA is None:
         gA = torch.zeros((d, r), dtype=torch.float32, device=gZ.device) if accumulate else \
             _empty((d, r), torch.float32, gZ)
+    pk, nb = _pk(pk, d, r, dt, gZ)
     ws, wb = _ws(ws, int(load().mapl_bwd_workspace_bytes(B, T, d, r, dt)), gZ)
     _check(load().mapl_compress_bwd(_dev(gZ, "gZ"), _dev(X, "X", gZ.dtype), _dev(tids, "tids", torch.int32),
                                     _dev(E_small, "E_small", gZ.dtype), _dev(P, "P", gZ.dtype),
                                     _dev(A, "A", gZ.dtype), _dev(gX, "gX", gZ.dtype), _dev(gA, "gA", torch.float32),
                                     int(bool(accumulate)), B, T, d, r, V, dt,
+                                    pk.data_ptr() if pk is not None else None, nb, int(bool(pk_ready)),
                                     ws.data_ptr() if ws is not None else None, wb, _stream(stream)),
            "mapl_compress_bwd")
     return gX, gA

@@ -28,7 +28,9 @@ int check_codec_shape(int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, map
   if (d < 1 || r < 1 || r > d || d > (1 << 20)) return MAPL_ERR_SHAPE;
   if (needV && (V < 1 || V > INT32_MAX)) return MAPL_ERR_SHAPE;
   if (dt == MAPL_BF16) {
-    if (d % 64 != 0 || r % 32 != 0 || r < 32 || r > 512) return MAPL_ERR_SHAPE;
+    // r a power of two in [32, 512]; d a multiple of 128 (the compression kernel
+    // splits d into four 32-column-aligned quarters)
+    if (d % 128 != 0 || r < 32 || r > 512 || (r & (r - 1)) != 0) return MAPL_ERR_SHAPE;
   } else {
     if (d > 4096) return MAPL_ERR_SHAPE;
   }
@@ -85,9 +87,7 @@ int mapl_pack(const void* P, const void* A, void* pk, size_t pk_bytes, int64_t d
   PackView v = pack_view(pk, d, r);
   const uint16_t* A16 = static_cast<const uint16_t*>(A);
   const uint16_t* P16 = static_cast<const uint16_t*>(P);
-  launch_pack_At(A16, v.At, int(d), int(r), stream);
-  launch_pack_Pt(P16, v.Pt, int(d), int(r), stream);
-  launch_pack_Qn(P16, A16, v.Qn, int(d), int(r), stream);
+  launch_pack_all(P16, A16, v, int(d), int(r), stream);
   return ls.done();
 }
 
@@ -109,11 +109,8 @@ int mapl_compress(const void* X, const int32_t* tids, const void* E_small, const
     return ls.done();
   }
   PackView v = pack_view(pk, d, r);
-  if (!pk_ready) {
-    launch_pack_At(static_cast<const uint16_t*>(A), v.At, int(d), int(r), stream);
-    launch_pack_Qn(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v.Qn, int(d), int(r), stream);
-  }
-  launch_tok_reduce_bf16(static_cast<const uint16_t*>(X), v.At, tids, static_cast<const uint16_t*>(E_small), v.Qn,
+  if (!pk_ready) launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), stream);
+  launch_tok_reduce_bf16(static_cast<const uint16_t*>(X), v.AtF, tids, static_cast<const uint16_t*>(E_small), v.QnF,
                          static_cast<uint16_t*>(Z), N, int(d), int(r), int(V), stream);
   return ls.done();
 }
@@ -136,10 +133,9 @@ int mapl_reconstruct(const void* Z, const int32_t* tids, const void* E_small, co
     return ls.done();
   }
   PackView v = pack_view(pk, d, r);
-  if (!pk_ready) launch_pack_Pt(static_cast<const uint16_t*>(P), v.Pt, int(d), int(r), stream);
-  launch_tok_expand_bf16(static_cast<const uint16_t*>(Z), static_cast<const uint16_t*>(A), tids,
-                         static_cast<const uint16_t*>(E_small), v.Pt, static_cast<uint16_t*>(Xhat), N, int(d), int(r),
-                         int(V), stream);
+  if (!pk_ready) launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), stream);
+  launch_tok_expand_bf16(static_cast<const uint16_t*>(Z), v.AF, tids, static_cast<const uint16_t*>(E_small), v.PtF,
+                         static_cast<uint16_t*>(Xhat), N, int(d), int(r), int(V), stream);
   return ls.done();
 }
 
@@ -175,11 +171,11 @@ int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A, void* 
     return ls.done();
   }
   PackView v = pack_view(pk, d, r);
-  if (!pk_ready) launch_pack_At(static_cast<const uint16_t*>(A), v.At, int(d), int(r), stream);
+  if (!pk_ready) launch_pack_AtF(static_cast<const uint16_t*>(A), v.AtF, int(d), int(r), stream);
   const int S = gram_splits_bf16(int(N));
   float* part = static_cast<float*>(ws);
   if (N > 0) {
-    launch_tok_reduce_bf16(static_cast<const uint16_t*>(gXhat), v.At, nullptr, nullptr, nullptr,
+    launch_tok_reduce_bf16(static_cast<const uint16_t*>(gXhat), v.AtF, nullptr, nullptr, nullptr,
                            static_cast<uint16_t*>(gZ), int(N), int(d), int(r), 1, stream);
     launch_gram_bf16(static_cast<const uint16_t*>(gXhat), nullptr, 1, static_cast<const uint16_t*>(Z), part, int(N),
                      int(d), int(r), S, stream);
@@ -190,10 +186,11 @@ int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A, void* 
 
 int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const void* E_small, const void* P,
                       const void* A, void* gX, float* gA, int accumulate, int64_t B, int64_t T, int64_t d, int64_t r,
-                      int64_t V, mapl_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+                      int64_t V, mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
   int st = check_codec_shape(B, T, d, r, V, dt, true);
   if (st) return st;
-  if (accumulate != 0 && accumulate != 1) return MAPL_ERR_ARG;
+  if ((accumulate != 0 && accumulate != 1) || (pk_ready != 0 && pk_ready != 1)) return MAPL_ERR_ARG;
   const int64_t N = B * T;
   if (!gA) return MAPL_ERR_NULL;
   if (N == 0) {  // empty batch: gA = 0 (or unchanged when accumulating)
@@ -202,6 +199,7 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const 
     return ls0.done();
   }
   if (!gZ || !X || !tids || !E_small || !P || !A || !gX) return MAPL_ERR_NULL;
+  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
   const size_t need = bwd_ws_bytes(N, d, r, dt);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return ws == nullptr ? MAPL_ERR_NULL : MAPL_ERR_WORKSPACE;
   LaunchScope ls;
@@ -221,9 +219,11 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const 
   float* part2 = part1 + size_t(S) * d * r;
   float* M = part2 + size_t(S) * r * r;
   const uint16_t* gZ16 = static_cast<const uint16_t*>(gZ);
+  PackView v = pack_view(pk, d, r);
+  if (!pk_ready) launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), stream);
   // gX = gZ A^T
-  launch_tok_expand_bf16(gZ16, static_cast<const uint16_t*>(A), nullptr, nullptr, nullptr,
-                         static_cast<uint16_t*>(gX), int(N), int(d), int(r), 1, stream);
+  launch_tok_expand_bf16(gZ16, v.AF, nullptr, nullptr, nullptr, static_cast<uint16_t*>(gX), int(N), int(d), int(r), 1,
+                         stream);
   // gA (+)= X^T gZ - P^T (E[t]^T gZ)
   launch_gram_bf16(static_cast<const uint16_t*>(X), nullptr, 1, gZ16, part1, int(N), int(d), int(r), S, stream);
   launch_gram_bf16(static_cast<const uint16_t*>(E_small), tids, int(V), gZ16, part2, int(N), int(r), int(r), S,

@@ -19,17 +19,23 @@
 namespace mapl {
 
 // ---------------------------------------------------------------- reduce --
-// One block: 64 tokens x RB*32 output columns.  The contraction (d steps of
-// the X A term, then r steps of the anchor term) is split over the 4 waves;
+// One block: 64 tokens x RB*32 output columns.  The contraction (d/16 steps of
+// the X A term, then r/16 steps of the anchor term) is split over the 4 waves;
 // each wave accumulates the whole 64 x RB*32 tile for its share of k, and the
-// four partial tiles are summed in LDS in a fixed order.
-template <int RB>
-__global__ __launch_bounds__(256) void k_tok_reduce(const bf16_t* __restrict__ X, const bf16_t* __restrict__ At,
+// four partial tiles are summed through LDS in a fixed order.
+//
+// Operands stream through a P-stage register ring: the loads of step s+P are
+// issued right after step s is consumed, unconditionally (token rows and
+// token ids are clamped to valid rows; a token past N only feeds an output
+// column that is never stored, an invalid id is zeroed by a select), so the
+// compiler can keep P steps of loads in flight.
+template <int RB, int P>
+__global__ __launch_bounds__(256) void k_tok_reduce(const bf16_t* __restrict__ X, const bf16_t* __restrict__ AtF,
                                                     const int32_t* __restrict__ tids, const bf16_t* __restrict__ E,
-                                                    const bf16_t* __restrict__ Qn, bf16_t* __restrict__ Z, int N,
+                                                    const bf16_t* __restrict__ QnF, bf16_t* __restrict__ Z, int N,
                                                     int d, int r, int V) {
-  __shared__ float red[2][RB][2][16][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) float redbuf[4 * RB * 64 * 16];
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int hi = lane >> 5, l32 = lane & 31;
   const int tok0 = blockIdx.x * 64;
   const int rbase = blockIdx.y * (RB * 32);
@@ -44,229 +50,300 @@ __global__ __launch_bounds__(256) void k_tok_reduce(const bf16_t* __restrict__ X
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  const int n0 = tok0 + l32, n1 = tok0 + 32 + l32;
-  const bool v0 = n0 < N, v1 = n1 < N;
-
-  // ---- X A part: steps [sb, min(se, Sd))
-  {
-    const bf16_t* x0 = X + size_t(v0 ? n0 : 0) * d + 8 * hi;
-    const bf16_t* x1 = X + size_t(v1 ? n1 : 0) * d + 8 * hi;
-    const bf16_t* a0 = At + size_t(rbase + l32) * d + 8 * hi;
-    const int s_end = se < Sd ? se : Sd;
-    int s = sb;
-    if (s < s_end) {
-      bf16x8 b0 = v0 ? ld_bf16x8(x0 + s * 16) : zero_bf16x8();
-      bf16x8 b1 = v1 ? ld_bf16x8(x1 + s * 16) : zero_bf16x8();
-      bf16x8 a[RB];
-#pragma unroll
-      for (int i = 0; i < RB; ++i) a[i] = ld_bf16x8(a0 + size_t(i) * 32 * d + s * 16);
-      for (; s < s_end; ++s) {
-        bf16x8 nb0 = b0, nb1 = b1, na[RB];
-#pragma unroll
-        for (int i = 0; i < RB; ++i) na[i] = a[i];
-        if (s + 1 < s_end) {
-          const int k = (s + 1) * 16;
-          nb0 = v0 ? ld_bf16x8(x0 + k) : zero_bf16x8();
-          nb1 = v1 ? ld_bf16x8(x1 + k) : zero_bf16x8();
-#pragma unroll
-          for (int i = 0; i < RB; ++i) na[i] = ld_bf16x8(a0 + size_t(i) * 32 * d + k);
-        }
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          acc[i][0] = mfma_bf16_32x32x16(a[i], b0, acc[i][0]);
-          acc[i][1] = mfma_bf16_32x32x16(a[i], b1, acc[i][1]);
-        }
-        b0 = nb0;
-        b1 = nb1;
-#pragma unroll
-        for (int i = 0; i < RB; ++i) a[i] = na[i];
-      }
-    }
-  }
-  // ---- anchor part  - E[t] (P A) = E[t] Qn^T: steps [max(sb, Sd), se)
-  if (Se > 0 && se > Sd) {
-    const int t0 = v0 ? tids[n0] : -1;
-    const int t1 = v1 ? tids[n1] : -1;
+  const int n0 = min(tok0 + l32, N - 1), n1 = min(tok0 + 32 + l32, N - 1);
+  const bf16_t* x0 = X + size_t(n0) * d + 8 * hi;
+  const bf16_t* x1 = X + size_t(n1) * d + 8 * hi;
+  // weight fragments of this block's row blocks: unit (s * MB + rbase/32 + i) * 64 + lane
+  const int MB = r >> 5;
+  const bf16_t* a0 = AtF + (size_t(rbase >> 5) * 64 + lane) * 8;
+  // anchor operands (rows of E picked by token id; an invalid id reads row 0 and is zeroed)
+  uint32_t m0 = ~0u, m1 = ~0u;  // anchor-operand masks (0 for an invalid id)
+  const bf16_t* er0 = x0;
+  const bf16_t* er1 = x1;
+  const bf16_t* q0 = a0;
+  if (Se > 0) {
+    const int t0 = tids[n0], t1 = tids[n1];
     const bool e0 = (t0 >= 0 && t0 < V), e1 = (t1 >= 0 && t1 < V);
-    const bf16_t* er0 = E + size_t(e0 ? t0 : 0) * r + 8 * hi;
-    const bf16_t* er1 = E + size_t(e1 ? t1 : 0) * r + 8 * hi;
-    const bf16_t* q0 = Qn + size_t(rbase + l32) * r + 8 * hi;
-    for (int s = (sb > Sd ? sb : Sd); s < se; ++s) {
-      const int k = (s - Sd) * 16;
-      bf16x8 b0 = e0 ? ld_bf16x8(er0 + k) : zero_bf16x8();
-      bf16x8 b1 = e1 ? ld_bf16x8(er1 + k) : zero_bf16x8();
+    m0 = e0 ? ~0u : 0u;
+    m1 = e1 ? ~0u : 0u;
+    er0 = E + size_t(e0 ? t0 : 0) * r + 8 * hi;
+    er1 = E + size_t(e1 ? t1 : 0) * r + 8 * hi;
+    q0 = QnF + (size_t(rbase >> 5) * 64 + lane) * 8;
+  }
+
+  bf16x8 ba[P][RB], bb[P][2];
+  auto issue = [&](int st, int s) {
+    s = s < se ? s : se - 1;  // past the end: reload the last step (never consumed)
+    const bool xs = s < Sd;
+    const int sl = xs ? s : s - Sd;
+    const int k = sl * 16;
+    const bf16_t* pb0 = xs ? x0 + k : er0 + k;
+    const bf16_t* pb1 = xs ? x1 + k : er1 + k;
+    const bf16_t* pa = (xs ? a0 : q0) + size_t(sl) * MB * 512;
+    constexpr size_t astr = 512;  // next row block of the same K-step
+    bb[st][0] = ld_bf16x8(pb0);
+    bb[st][1] = ld_bf16x8(pb1);
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        bf16x8 a = ld_bf16x8(q0 + size_t(i) * 32 * r + k);
-        acc[i][0] = mfma_bf16_32x32x16(a, b0, acc[i][0]);
-        acc[i][1] = mfma_bf16_32x32x16(a, b1, acc[i][1]);
+    for (int i = 0; i < RB; ++i) ba[st][i] = ld_bf16x8(pa + i * astr);
+  };
+
+  if (sb < se) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) issue(u, sb + u);
+    for (int s0 = sb; s0 < se; s0 += P) {
+#pragma unroll
+      for (int u = 0; u < P; ++u) {
+        const int s = s0 + u;
+        if (s < se) {
+          const bool as = s >= Sd;
+          const bf16x8 b0 = mask_bf16x8(bb[u][0], as ? m0 : ~0u);
+          const bf16x8 b1 = mask_bf16x8(bb[u][1], as ? m1 : ~0u);
+#pragma unroll
+          for (int i = 0; i < RB; ++i) {
+            acc[i][0] = mfma_bf16_32x32x16(ba[u][i], b0, acc[i][0]);
+            acc[i][1] = mfma_bf16_32x32x16(ba[u][i], b1, acc[i][1]);
+          }
+        }
+        issue(u, s + P);  // unconditional: keeps the in-flight count fixed
       }
     }
   }
 
-  // ---- fixed-order sum of the four wave tiles: (w0 + w2) + (w1 + w3)
-  if (wave >= 2) {
+  // ---- fixed-order sum of the four wave tiles, (w0 + w1) + (w2 + w3), in two
+  // rounds (token block j = 0, then 1).  Each wave writes its 32 x 32 tiles of
+  // the round to LDS as [wave][r-block][lane][4 x 16 bytes], the 16-byte chunk
+  // q stored at position q ^ ((lane >> 1) & 3) so that 8 consecutive lanes hit
+  // 8 different bank groups; then wave w sums r-block w of the round (RB == 4)
+  // or its share of them and stores straight from registers: lane (token
+  // l&31) holds 4 consecutive output columns per register group.
+  float* red = &redbuf[0];
+  const int sw = (lane >> 1) & 3;
 #pragma unroll
-    for (int i = 0; i < RB; ++i)
+  for (int j = 0; j < 2; ++j) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < RB; ++i) {
+      f32x4* dst = reinterpret_cast<f32x4*>(red + ((wave * RB + i) * 64 + lane) * 16);
 #pragma unroll
-        for (int v = 0; v < 16; ++v) red[wave - 2][i][j][v][lane] = acc[i][j][v];
-  }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] += red[wave][i][j][v][lane];
-  }
-  __syncthreads();
-  if (wave < 2) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) red[wave][i][j][v][lane] = acc[i][j][v];
-  }
-  __syncthreads();
-
-  // ---- store: thread -> (token n, RB*8 consecutive output columns)
-  const int n = threadIdx.x >> 2, c = threadIdx.x & 3;
-  const int gn = tok0 + n;
-  if (gn < N) {
-    const int cb = n >> 5, ln = n & 31;
-    uint32_t w[RB * 4];
-#pragma unroll
-    for (int e = 0; e < RB * 8; e += 2) {
-      float f[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int m = c * RB * 8 + e + u;
-        const int rb = m >> 5, mm = m & 31;
-        const int v = 4 * (mm >> 3) + (mm & 3), h = (mm >> 2) & 1;
-        const int ll = h * 32 + ln;
-        f[u] = red[0][rb][cb][v][ll] + red[1][rb][cb][v][ll];
-      }
-      w[e >> 1] = pack2bf(f[0], f[1]);
+      for (int q = 0; q < 4; ++q)
+        dst[q ^ sw] = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     }
-    u32x4* dst = reinterpret_cast<u32x4*>(Z + size_t(gn) * r + rbase + c * RB * 8);
+    __syncthreads();
+    const int n = tok0 + j * 32 + l32;
 #pragma unroll
-    for (int q = 0; q < RB; ++q) dst[q] = u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+    for (int i = 0; i < RB; ++i) {
+      if ((i & 3) != wave) continue;  // r-block i is summed and stored by wave i % 4
+      f32x4 sum[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int qs = q ^ sw;
+        f32x4 t0 = reinterpret_cast<const f32x4*>(red + ((0 * RB + i) * 64 + lane) * 16)[qs];
+        f32x4 t1 = reinterpret_cast<const f32x4*>(red + ((1 * RB + i) * 64 + lane) * 16)[qs];
+        f32x4 t2 = reinterpret_cast<const f32x4*>(red + ((2 * RB + i) * 64 + lane) * 16)[qs];
+        f32x4 t3 = reinterpret_cast<const f32x4*>(red + ((3 * RB + i) * 64 + lane) * 16)[qs];
+        sum[q] = (t0 + t1) + (t2 + t3);
+      }
+      if (n < N) {
+        bf16_t* row = Z + size_t(n) * r + rbase + i * 32 + 4 * hi;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<u32x2*>(row + 8 * q) = u32x2{pack2bf(sum[q][0], sum[q][1]), pack2bf(sum[q][2], sum[q][3])};
+      }
+    }
+    __syncthreads();
   }
 }
 
-void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* At, const int32_t* tids, const uint16_t* E,
-                            const uint16_t* Qn, uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
+void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32_t* tids, const uint16_t* E,
+                            const uint16_t* QnF, uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
   const int nb = r / 32;
   const int RB = (nb % 4 == 0) ? 4 : (nb % 2 == 0) ? 2 : 1;
   dim3 grid((N + 63) / 64, r / (RB * 32));
   if (RB == 4)
-    hipLaunchKernelGGL(k_tok_reduce<4>, grid, dim3(256), 0, s, in, At, tids, E, Qn, out, N, d, r, V);
+    hipLaunchKernelGGL((k_tok_reduce<4, 4>), grid, dim3(256), 0, s, in, AtF, tids, E, QnF, out, N, d, r, V);
   else if (RB == 2)
-    hipLaunchKernelGGL(k_tok_reduce<2>, grid, dim3(256), 0, s, in, At, tids, E, Qn, out, N, d, r, V);
+    hipLaunchKernelGGL((k_tok_reduce<2, 6>), grid, dim3(256), 0, s, in, AtF, tids, E, QnF, out, N, d, r, V);
   else
-    hipLaunchKernelGGL(k_tok_reduce<1>, grid, dim3(256), 0, s, in, At, tids, E, Qn, out, N, d, r, V);
+    hipLaunchKernelGGL((k_tok_reduce<1, 8>), grid, dim3(256), 0, s, in, AtF, tids, E, QnF, out, N, d, r, V);
 }
 
 // ---------------------------------------------------------------- expand --
-// One block: TB*32 tokens x 4*CB*32 output channels; wave w owns channels
-// [w*CB*32, (w+1)*CB*32) of the block and all its tokens.  K = r (Z A^T)
-// followed by r (E[t] P via Pt) accumulate into the same fp32 registers.
-template <int CB, int TB>
-__global__ __launch_bounds__(256) void k_tok_expand(const bf16_t* __restrict__ in, const bf16_t* __restrict__ A,
+// out[N][d] = in[N][r] A^T (+ E[t] P).  One block: TB*32 tokens x 256 output
+// channels; wave w owns channels [64w, 64w+64) (two 32-row matrix-core blocks)
+// and all tokens of the block.
+//
+// 1. The block's token operand rows [in[n] | E[t_n]] (S K-steps of 16, i.e.
+//    2S 16-byte units per row) are loaded once with coalesced 16-byte loads
+//    into LDS, unit u of row t at t*UR + (u ^ (t & 7)) so that the matrix-core
+//    reads below (32 rows, one unit each) hit distinct bank groups.  All four
+//    waves share them.
+// 2. Each K-step: the two weight fragments of the wave come from the
+//    fragment-ordered AF / PtF pack through a P-stage register ring; the TB
+//    token fragments are read from LDS one step ahead.
+// 3. The 256-channel output rows go back through the same LDS (8-byte chunk
+//    c of row t at chunk position c ^ 2*(t & 7)) and out with 16-byte stores,
+//    each row segment written by 32 consecutive lanes.
+// Invalid token ids read row 0 of E and their anchor units are zeroed.
+// Two blocks fit on a CU (<= 256 registers per lane, 64 KB LDS), so one
+// block's loads overlap the other's matrix-core work.
+template <int TB, int PER, int P>
+__global__ __launch_bounds__(256, 2) void k_tok_expand(const bf16_t* __restrict__ in, const bf16_t* __restrict__ AF,
                                                     const int32_t* __restrict__ tids, const bf16_t* __restrict__ E,
-                                                    const bf16_t* __restrict__ Pt, bf16_t* __restrict__ out, int N,
-                                                    int d, int r, int V, int nx, int ny) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+                                                    const bf16_t* __restrict__ PtF, bf16_t* __restrict__ out, int N,
+                                                    int d, int r, int V, int nx, int ny, int ur_log2) {
+  constexpr int TT = TB * 32;
+  extern __shared__ __attribute__((aligned(16))) u32x4 lds[];
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int hi = lane >> 5, l32 = lane & 31;
   const int bid = xcd_swizzle(blockIdx.x, nx * ny);
   const int bx = bid % nx, by = bid / nx;
-  const int ch0 = bx * (4 * CB * 32) + wave * (CB * 32);
-  const int tok0 = by * (TB * 32);
-  if (ch0 >= d) return;  // whole wave outside d (d % 32 == 0 keeps blocks whole)
+  const int chb = bx * 256;              // first channel of the block
+  const int ch0 = chb + wave * 64;       // first channel of this wave
+  const int tok0 = by * TT;
+  const bool wave_on = ch0 < d;          // d % 64 == 0
+  const int UR = 1 << ur_log2;           // 16-byte units per token row
+  const int Sz = r >> 4;
+  const int S = (E != nullptr) ? 2 * Sz : Sz;
+  const int uz = 2 * Sz;                 // units of the `in` part
+  const int msk = UR >= 8 ? 7 : UR - 1;
 
-  f32x16 acc[CB][TB];
+  // ---- 1. stage token rows: every thread first loads the token ids of its
+  // PER units (PER = TT * UR / 256, a compile-time constant so that the loops
+  // below carry no branches), then issues all of its row loads, then writes
+  // them to LDS -- two memory round trips in total.
+  int tk[PER];
 #pragma unroll
-  for (int i = 0; i < CB; ++i)
+  for (int k = 0; k < PER; ++k) {
+    const int t = (threadIdx.x + 256 * k) >> ur_log2;
+    tk[k] = (E != nullptr) ? tids[min(tok0 + t, N - 1)] : 0;
+  }
+  u32x4 v[PER];
+  uint32_t mk[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int q = threadIdx.x + 256 * k;
+    const int t = q >> ur_log2, u = q & (UR - 1);
+    const int n = min(tok0 + t, N - 1);
+    const bool zpart = u < uz;
+    const bool ok = zpart | (unsigned(tk[k]) < unsigned(V));
+    const bf16_t* zsrc = in + size_t(n) * r + u * 8;
+    const bf16_t* esrc = E + size_t(ok ? tk[k] : 0) * r + (u - uz) * 8;
+    v[k] = *reinterpret_cast<const u32x4*>(zpart ? zsrc : esrc);
+    mk[k] = ok ? ~0u : 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int q = threadIdx.x + 256 * k;
+    const int t = q >> ur_log2, u = q & (UR - 1);
+    lds[t * UR + (u ^ (t & msk))] = v[k] & u32x4{mk[k], mk[k], mk[k], mk[k]};
+  }
+  __syncthreads();
+
+  f32x16 acc[2][TB];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < TB; ++j) acc[i][j] = f32x16{};
 
-  bool cv[CB];
+  if (wave_on) {
+    const int MBd = d >> 5;
+    const bf16_t* af = AF + (size_t(ch0 >> 5) * 64 + lane) * 8;
+    const bf16_t* pf = (E != nullptr) ? PtF + (size_t(ch0 >> 5) * 64 + lane) * 8 : af;
+    bf16x8 ba[P][2];
+    auto issue = [&](int st, int s) {
+      s = s < S ? s : S - 1;
+      const bool zs = s < Sz;
+      const bf16_t* pa = (zs ? af : pf) + size_t(zs ? s : s - Sz) * MBd * 512;
+      ba[st][0] = ld_bf16x8(pa);
+      ba[st][1] = ld_bf16x8(pa + 512);
+    };
+    auto ldsb = [&](int s, int j) {
+      const int t = j * 32 + l32;
+      const int u = 2 * s + hi;
+      return __builtin_bit_cast(bf16x8, lds[t * UR + (u ^ (t & msk))]);
+    };
 #pragma unroll
-  for (int i = 0; i < CB; ++i) cv[i] = (ch0 + i * 32) < d;
-
-  int tok[TB];
-  bool tv[TB];
+    for (int u = 0; u < P; ++u) issue(u, u);
+    bf16x8 bnext[TB];
 #pragma unroll
-  for (int j = 0; j < TB; ++j) {
-    tok[j] = tok0 + j * 32 + l32;
-    tv[j] = tok[j] < N;
-  }
-
-  const int Sz = r >> 4;
-  // Z A^T
-  for (int s = 0; s < Sz; ++s) {
-    const int k = s * 16 + 8 * hi;
-    bf16x8 a[CB], b[TB];
+    for (int j = 0; j < TB; ++j) bnext[j] = ldsb(0, j);
+    for (int s0 = 0; s0 < S; s0 += P) {
 #pragma unroll
-    for (int i = 0; i < CB; ++i) a[i] = cv[i] ? ld_bf16x8(A + size_t(ch0 + i * 32 + l32) * r + k) : zero_bf16x8();
+      for (int u = 0; u < P; ++u) {
+        const int s = s0 + u;
+        if (s < S) {
+          bf16x8 b[TB];
 #pragma unroll
-    for (int j = 0; j < TB; ++j) b[j] = tv[j] ? ld_bf16x8(in + size_t(tok[j]) * r + k) : zero_bf16x8();
+          for (int j = 0; j < TB; ++j) b[j] = bnext[j];
+          const int sn = s + 1 < S ? s + 1 : s;
 #pragma unroll
-    for (int i = 0; i < CB; ++i)
+          for (int j = 0; j < TB; ++j) bnext[j] = ldsb(sn, j);
 #pragma unroll
-      for (int j = 0; j < TB; ++j) acc[i][j] = mfma_bf16_32x32x16(a[i], b[j], acc[i][j]);
-  }
-  // + E[t] P
-  if (E != nullptr) {
-    int trow[TB];
-    bool ev[TB];
+          for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < TB; ++j) {
-      const int t = tv[j] ? tids[tok[j]] : -1;
-      ev[j] = (t >= 0 && t < V);
-      trow[j] = ev[j] ? t : 0;
-    }
-    for (int s = 0; s < Sz; ++s) {
-      const int k = s * 16 + 8 * hi;
-      bf16x8 a[CB], b[TB];
-#pragma unroll
-      for (int i = 0; i < CB; ++i) a[i] = cv[i] ? ld_bf16x8(Pt + size_t(ch0 + i * 32 + l32) * r + k) : zero_bf16x8();
-#pragma unroll
-      for (int j = 0; j < TB; ++j) b[j] = ev[j] ? ld_bf16x8(E + size_t(trow[j]) * r + k) : zero_bf16x8();
-#pragma unroll
-      for (int i = 0; i < CB; ++i)
-#pragma unroll
-        for (int j = 0; j < TB; ++j) acc[i][j] = mfma_bf16_32x32x16(a[i], b[j], acc[i][j]);
-    }
-  }
-  // store 4 consecutive channels (8 bytes) per register group
-#pragma unroll
-  for (int i = 0; i < CB; ++i) {
-    if (!cv[i]) continue;
-#pragma unroll
-    for (int j = 0; j < TB; ++j) {
-      if (!tv[j]) continue;
-      bf16_t* row = out + size_t(tok[j]) * d + ch0 + i * 32 + 4 * hi;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        u32x2 w = {pack2bf(acc[i][j][4 * g], acc[i][j][4 * g + 1]), pack2bf(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3])};
-        *reinterpret_cast<u32x2*>(row + 8 * g) = w;
+            for (int j = 0; j < TB; ++j) acc[i][j] = mfma_bf16_32x32x16(ba[u][i], b[j], acc[i][j]);
+        }
+        issue(u, s + P);
       }
+    }
+  }
+  __syncthreads();  // token rows no longer needed: reuse LDS for the output tile
+
+  // ---- 3. output tile [TT][256] bf16 through LDS: 8-byte chunk c of row t at c ^ 2*(t & 7)
+  uint32_t* o32 = reinterpret_cast<uint32_t*>(lds);
+  if (wave_on) {
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int t = j * 32 + l32;
+      const int sw = 2 * (t & 7);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c = (wave * 64 + i * 32 + 8 * g + 4 * hi) >> 2;  // 8-byte chunk within the row (0..63)
+          uint32_t* dst = o32 + t * 128 + (c ^ sw) * 2;
+          dst[0] = pack2bf(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
+          dst[1] = pack2bf(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        }
+    }
+  }
+  __syncthreads();
+  const int units = min(256, d - chb) >> 3;  // 16-byte units of a row inside d: 32, or 8*k at the edge
+#pragma unroll
+  for (int pass = 0; pass < TT / 8; ++pass) {
+    const int t = pass * 8 + (threadIdx.x >> 5);
+    const int c16 = threadIdx.x & 31;  // 16-byte unit = 8-byte chunks 2*c16, 2*c16+1
+    const int n = tok0 + t;
+    if (n < N && c16 < units) {
+      const u32x4 v = lds[t * 32 + (c16 ^ (t & 7))];
+      *reinterpret_cast<u32x4*>(out + size_t(n) * d + chb + c16 * 8) = v;
     }
   }
 }
 
-void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* A, const int32_t* tids, const uint16_t* E,
-                            const uint16_t* Pt, uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
-  constexpr int CB = 2, TB = 4;
-  const int nx = (d + 4 * CB * 32 - 1) / (4 * CB * 32);
-  const int ny = (N + TB * 32 - 1) / (TB * 32);
-  hipLaunchKernelGGL((k_tok_expand<CB, TB>), dim3(nx * ny), dim3(256), 0, s, in, A, tids, E, Pt, out, N, d, r, V,
-                     nx, ny);
+void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_t* tids, const uint16_t* E,
+                            const uint16_t* PtF, uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
+  const int S = (E != nullptr) ? r / 8 : r / 16;  // K-steps
+  const int UR = 2 * S;                            // 16-byte units per token row (a power of two)
+  int ur_log2 = 0;
+  while ((1 << ur_log2) < UR) ++ur_log2;
+  // token tile: the staged rows (TT * UR * 16 B) and the output tile (TT * 512 B) share <= 64 KB
+  const int TB = (UR <= 32) ? 4 : (UR <= 64) ? 2 : 1;
+  const int TT = TB * 32;
+  const size_t lds = size_t(TT) * (UR * 16 > 512 ? UR * 16 : 512);
+  const int nx = (d + 255) / 256;
+  const int ny = (N + TT - 1) / TT;
+  const int per = TT * UR / 256;  // 2, 4, 8 or 16
+  constexpr int P = 4;
+#define MAPL_EXPAND(TBv, PERv)                                                                                \
+  hipLaunchKernelGGL((k_tok_expand<TBv, PERv, P>), dim3(nx * ny), dim3(256), lds, s, in, AF, tids, E, PtF, out, N, \
+                     d, r, V, nx, ny, ur_log2)
+  if (TB == 4 && per == 16) MAPL_EXPAND(4, 16);
+  else if (TB == 4 && per == 8) MAPL_EXPAND(4, 8);
+  else if (TB == 4 && per == 4) MAPL_EXPAND(4, 4);
+  else if (TB == 4 && per == 2) MAPL_EXPAND(4, 2);
+  else if (TB == 2) MAPL_EXPAND(2, 16);
+  else MAPL_EXPAND(1, 16);
+#undef MAPL_EXPAND
 }
 
 // ------------------------------------------------------------------ gram --
@@ -283,7 +360,7 @@ __global__ __launch_bounds__(256) void k_gram(const bf16_t* __restrict__ L, cons
                                               int r, int tok_per_split) {
   __shared__ __attribute__((aligned(16))) bf16_t Ls[128][kGramPitch];
   __shared__ __attribute__((aligned(16))) bf16_t Rs[JB * 32][kGramPitch];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int hi = lane >> 5, l32 = lane & 31;
   const int i0 = blockIdx.x * 128, j0 = blockIdx.y * (JB * 32);
   const int sidx = blockIdx.z;

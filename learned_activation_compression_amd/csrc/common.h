@@ -55,6 +55,17 @@ __device__ __forceinline__ f32x16 mfma_f32_32x32x2(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// Wave index within the block as a scalar (wave-uniform) value, so that
+// control flow that depends on it compiles to scalar branches.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Keep an MFMA operand (mask = ~0u) or zero it (mask = 0) without a branch.
+__device__ __forceinline__ bf16x8 mask_bf16x8(bf16x8 v, uint32_t m) {
+  u32x4 u = __builtin_bit_cast(u32x4, v);
+  u &= u32x4{m, m, m, m};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
 // Row index (within a 32x32 tile) held by register v of a lane in the upper
 // (hi = 1) or lower half-wave, for the 32x32 MFMA output layout.
 __device__ __forceinline__ int mfma32_row(int v, int hi) { return 8 * (v >> 2) + 4 * hi + (v & 3); }

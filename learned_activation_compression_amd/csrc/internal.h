@@ -8,17 +8,21 @@
 
 namespace mapl {
 
-// ---- packed weights (bf16): At = A^T [r][d], Pt = P^T [d][r], Qn = -(P A)^T [r][r]
+// ---- packed weights (bf16, fragment order; see pack.hip):
+//   AtF = A^T (r x d), AF = A (d x r), PtF = P^T (d x r), QnF = -(P A)^T (r x r)
 struct PackView {
-  uint16_t* At;
-  uint16_t* Pt;
-  uint16_t* Qn;
+  uint16_t* AtF;
+  uint16_t* AF;
+  uint16_t* PtF;
+  uint16_t* QnF;
 };
 size_t pack_bytes_bf16(int64_t d, int64_t r);
 PackView pack_view(void* pk, int64_t d, int64_t r);
-void launch_pack_At(const uint16_t* A, uint16_t* At, int d, int r, hipStream_t s);
-void launch_pack_Pt(const uint16_t* P, uint16_t* Pt, int d, int r, hipStream_t s);
-void launch_pack_Qn(const uint16_t* P, const uint16_t* A, uint16_t* Qn, int d, int r, hipStream_t s);
+void launch_pack_AtF(const uint16_t* A, uint16_t* AtF, int d, int r, hipStream_t s);
+void launch_pack_AF(const uint16_t* A, uint16_t* AF, int d, int r, hipStream_t s);
+void launch_pack_PtF(const uint16_t* P, uint16_t* PtF, int d, int r, hipStream_t s);
+// all four sections
+void launch_pack_all(const uint16_t* P, const uint16_t* A, PackView v, int d, int r, hipStream_t s);
 
 // generic small fp32-accumulating GEMM with arbitrary strides:
 //   C(i,j) = alpha * sum_k A(i,k) B(k,j) + beta * C(i,j)
@@ -28,13 +32,13 @@ void launch_small_gemm(int M, int N, int K, const void* A, int a_ty, int64_t sai
                        int64_t sci, int64_t scj, float alpha, float beta, hipStream_t s);
 
 // ---- bf16 codec
-// out[N][r] = in[N][d] A  (- E[tids] (P A)) via At and Qn; E == nullptr drops the anchor term
-void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* At, const int32_t* tids,
-                            const uint16_t* E, const uint16_t* Qn, uint16_t* out,
+// out[N][r] = in[N][d] A  (- E[tids] (P A)) via AtF and QnF; E == nullptr drops the anchor term
+void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32_t* tids,
+                            const uint16_t* E, const uint16_t* QnF, uint16_t* out,
                             int N, int d, int r, int V, hipStream_t s);
-// out[N][d] = in[N][r] A^T (+ E[tids] P) via A and Pt; E == nullptr drops the anchor term
-void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* A, const int32_t* tids,
-                            const uint16_t* E, const uint16_t* Pt, uint16_t* out,
+// out[N][d] = in[N][r] A^T (+ E[tids] P) via AF and PtF; E == nullptr drops the anchor term
+void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_t* tids,
+                            const uint16_t* E, const uint16_t* PtF, uint16_t* out,
                             int N, int d, int r, int V, hipStream_t s);
 // token-split partial Gram: part[s][i][j] = sum_{n in split s} L[n][i] R[n][j],
 // L = in_l [N][Ld] or, when tids != nullptr, L[n] = E[tids[n]] ([V][Ld]).

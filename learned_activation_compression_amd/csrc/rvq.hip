@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void k_rvq_encode(const ZT* __restrict__ Z, co
   extern __shared__ float sh[];
   float* cbT = sh;           // [W][K]
   float* nrm = sh + W * K;   // [K]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
   const int g = blockIdx.x;
   const int tok_base = blockIdx.y * (4 * kRvqTilesPerWave * 32) + wave * (kRvqTilesPerWave * 32);

@@ -35,7 +35,7 @@ __device__ __forceinline__ float inv_norm_from_parts(const float* parts, int n) 
 __global__ __launch_bounds__(256) void k_spel_gram(const float* __restrict__ Xl, const float* __restrict__ Xr,
                                                    const float* __restrict__ sparts, int nsp, float* __restrict__ part,
                                                    int d, int r, int rows_per_split) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
   const int i0 = blockIdx.x * 64 + (wave >> 1) * 32;
   const int j0 = blockIdx.y * 64 + (wave & 1) * 32;
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
                                                  float* __restrict__ Y0) {
   __shared__ float red[2][16][64];
   __shared__ float wsum[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
   const int jb = wave & 1, kh = wave >> 1;
   const int i0 = blockIdx.x * 32;

@@ -35,7 +35,7 @@ def test_status_strings_and_version(lib):
 
 def test_pack_and_workspace_sizes(lib):
     d, r = 1024, 128
-    want = 2 * r * d + 2 * d * r + 2 * r * r
+    want = 3 * 2 * r * d + 2 * r * r
     got = lib.mapl_pack_bytes(d, r, BF16)
     assert want <= got <= want + 3 * 256
     assert lib.mapl_pack_bytes(d, r, F32) == 0
@@ -59,7 +59,9 @@ def test_compress_validation(lib):
     assert _compress(lib, tids=None) == ENULL
     assert _compress(lib, pk=None) == ENULL
     assert _compress(lib, pk_bytes=100) == EWS
-    assert _compress(lib, d=1000) == ESHAPE          # bf16 needs d % 64 == 0
+    assert _compress(lib, d=1000) == ESHAPE          # bf16 needs d % 128 == 0
+    assert _compress(lib, d=320) == ESHAPE
+    assert _compress(lib, r=96) == ESHAPE            # bf16 needs r a power of two
     assert _compress(lib, r=100) == ESHAPE           # bf16 needs r % 32 == 0
     assert _compress(lib, r=2048) == ESHAPE          # r > d
     assert _compress(lib, r=1024, d=1024) == ESHAPE  # bf16 r <= 512
@@ -88,12 +90,15 @@ def test_backward_validation(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, BF16, FAKE, 10 ** 7, 1, None, ws, None) == ENULL
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2048, 1024, 128, BF16, FAKE, 10 ** 7, 1, FAKE, ws, None) == EARG
     g = lib.mapl_compress_bwd
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 8, 2048, 1024, 128, 32000, BF16, FAKE, ws,
-             None) == ENULL
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, 32000, BF16, FAKE, 16,
-             None) == EWS
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1000, 128, 32000, BF16, FAKE, ws,
-             None) == ESHAPE
+    pk = 10 ** 7
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 8, 2048, 1024, 128, 32000, BF16, FAKE, pk, 1, FAKE,
+             ws, None) == ENULL
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, 32000, BF16, FAKE, pk, 1, FAKE,
+             16, None) == EWS
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, 32000, BF16, None, pk, 1, FAKE,
+             ws, None) == ENULL
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1000, 128, 32000, BF16, FAKE, pk, 1, FAKE,
+             ws, None) == ESHAPE
 
 
 def test_rvq_validation(lib):

@@ -94,11 +94,11 @@ def test_fp32_round_trip_in_span():
 SMALL_BF16 = [  # (N, d, r): several tiles plus a ragged tail in tokens and channels
     (1000, 1024, 128),
     (777, 2048, 256),
-    (130, 320, 64),
+    (130, 384, 64),      # d not a multiple of the 256-channel tile
     (300, 1024, 512),
     (65, 512, 32),
-    (200, 1024, 96),
-    (1, 64, 32),
+    (200, 640, 32),
+    (1, 128, 32),
 ]
 
 
