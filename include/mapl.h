@@ -187,8 +187,11 @@ int rvq_stream_apply(float* C, const int32_t* idx, const float* vals, int64_t n,
  *   D   = NS(m / ||m||_F)   (D = 0 when m == 0)              (Eq. 6)
  *   A   = NS(A - alpha D)   (input not rescaled)             (Eq. 7)
  * with NS the cubic Newton-Schulz polar iteration X <- 1.5 X - 0.5 X (X^T X)
- * run ns_iters times (8 in this build's specification).  If D_out is not
- * NULL the direction D [d][r] is also written there.
+ * run ns_iters times (the method uses 8).  If D_out is not NULL the
+ * direction D [d][r] is also written there.  A, g, m, D_out and ws must be
+ * 16-byte aligned (MAPL_ERR_ARG otherwise) and no buffer may overlap another.
+ * The workspace needs no initial contents; consecutive calls on one stream
+ * may share it, calls that overlap in time may not.
  * Limits: r % 32 == 0, d % 32 == 0, r <= d, r <= 1024, 0 <= beta < 1,
  * 0 <= alpha <= 0.7, 1 <= ns_iters <= 64.
  * ---------------------------------------------------------------------- */

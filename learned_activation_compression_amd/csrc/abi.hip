@@ -306,6 +306,10 @@ int spel_step(float* A, const float* g, float* m, float alpha, float beta, int n
   const size_t need = spel_ws_bytes(d, r);
   if (!ws) return MAPL_ERR_NULL;
   if (ws_bytes < need) return MAPL_ERR_WORKSPACE;
+  // the kernels move rows of every operand as 16-byte vectors
+  if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(g) | reinterpret_cast<uintptr_t>(m) |
+       reinterpret_cast<uintptr_t>(D_out) | reinterpret_cast<uintptr_t>(ws)) & 15)
+    return MAPL_ERR_ARG;
   LaunchScope ls;
   launch_spel(A, g, m, alpha, beta, ns_iters, D_out, int(d), int(r), ws, stream);
   return ls.done();

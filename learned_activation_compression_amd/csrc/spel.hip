@@ -8,12 +8,25 @@
 // times; the LMO input is m / ||m||_F (zero when m == 0) and the retraction
 // input is not rescaled.
 //
-// Every product is one of two shapes, both on v_mfma_f32_32x32x2_f32:
-//   gram  part[s] = Xl[rows of s]^T Xr[rows of s]   (r x r, split over d rows)
-//   xm    out = X M                                  (d x r, K = r)
-// The r x r reduction over splits runs in a fixed order (deterministic).
-// Scale factors 1/||m||_F are recomputed by each consumer from fixed-order
-// partial sums written by the momentum epilogue.
+// The problem is small (a few MB) and the iteration is a chain of dependent
+// products, so every kernel is built for latency: all operand loads of a wave
+// are in flight before its first matrix-core instruction, and no launch
+// exists only to reduce.
+//
+//   gram  part[q] = sum over row group q of Xl^T Xr (r x r, both triangles).
+//         One block per (upper-triangle pair of 32 x 32 column blocks, row
+//         group); its 4 waves sum in LDS.  For Eq. (4) the block stores
+//         sym(.) of its piece (sym is linear, so the pieces add up to
+//         sym(A^T g)).
+//   xm    out = s X M  d x r with M = f(sum_q part[q]) formed while loading:
+//         f = identity for Eq. (4), 1.5 I - 0.5 s^2 (.) for a Newton-Schulz
+//         step.  One block per 32 x 32 output tile; the 4 waves split K = r
+//         and sum in LDS; the epilogue applies Eq. (4)-(5), a plain
+//         Newton-Schulz step, or the last step of Eq. (6) / Eq. (7).
+//
+// All sums run in a fixed order, so a step is bitwise repeatable.  The scale
+// s = 1/||m||_F comes from per-block partial sums of squares written by the
+// momentum epilogue, added up in a fixed order by the one launch that uses it.
 #include "common.h"
 #include "internal.h"
 
@@ -22,212 +35,273 @@ namespace mapl {
 namespace {
 
 enum { XM_TANGENT = 0, XM_NS = 1, XM_NS_LAST_LMO = 2, XM_NS_LAST_RET = 3 };
-enum { RED_SYM = 0, RED_NS = 1 };
 
-__device__ __forceinline__ float inv_norm_from_parts(const float* parts, int n) {
-  if (parts == nullptr) return 1.f;
-  float s = 0.f;
-  for (int i = 0; i < n; ++i) s += parts[i];
-  return s > 0.f ? 1.f / sqrtf(s) : 0.f;
+constexpr int kChunk = 32;  // rows per wave per Gram chunk (16 matrix-core K-steps)
+
+// Position of element (i, j) of a 32 x 32 tile in the accumulator fragment
+// order [v][lane] of v_mfma_f32_32x32x2_f32 (lane = 32 h + j holds row
+// 8 (v >> 2) + 4 h + (v & 3)).
+__device__ __forceinline__ int frag_index(int i, int j) {
+  return (((i >> 3) << 2 | (i & 3)) << 6) + (((i >> 2) & 1) << 5) + j;
 }
 
-// part[s][i][j] = sc^2 * sum_{k in split s} Xl[k][i] Xr[k][j]  (sc = 1 unless scale parts are given)
+__device__ __forceinline__ void store_frag(float* dst, const f32x16& acc, int lane) {
+#pragma unroll
+  for (int v = 0; v < 16; ++v) dst[v * 64 + lane] = acc[v];
+}
+
+__device__ __forceinline__ f32x4 ld4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void st4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+// Upper-triangle pair index -> (bi, bj), bi <= bj, row-major.
+__device__ __forceinline__ void pair_of(int p, int nb, int& bi, int& bj) {
+  bi = 0;
+  int rem = p;
+  while (rem >= nb - bi) {
+    rem -= nb - bi;
+    ++bi;
+  }
+  bj = bi + rem;
+}
+
+// TWO = 1 (Eq. (4)): piece = sym(A^T g) over the group's rows, from
+// acc1 = A_bi^T g_bj and acc2 = A_bj^T g_bi.  TWO = 0: piece = X_bi^T X_bj.
+// Tile (bi, bj) of part[grp] gets the piece, tile (bj, bi) its transpose.
+template <int TWO>
 __global__ __launch_bounds__(256) void k_spel_gram(const float* __restrict__ Xl, const float* __restrict__ Xr,
-                                                   const float* __restrict__ sparts, int nsp, float* __restrict__ part,
-                                                   int d, int r, int rows_per_split) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+                                                   float* __restrict__ part, int d, int r, int groups) {
+  __shared__ float red[(1 + TWO) * 4 * 1024];
+  __shared__ float tile[32 * 33];
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
-  const int i0 = blockIdx.x * 64 + (wave >> 1) * 32;
-  const int j0 = blockIdx.y * 64 + (wave & 1) * 32;
-  if (i0 >= r || j0 >= r) return;
-  const int s = blockIdx.z;
-  const int kb = s * rows_per_split;
-  const int ke = min(d, kb + rows_per_split);
-  f32x16 acc = f32x16{};
-  const float* pl = Xl + size_t(kb + h) * r + i0 + l32;
-  const float* pr = Xr + size_t(kb + h) * r + j0 + l32;
-  int k = kb;
-  for (; k + 8 <= ke; k += 8) {
-    float a[4], b[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      a[u] = pl[size_t(k - kb + 2 * u) * r];
-      b[u] = pr[size_t(k - kb + 2 * u) * r];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc = mfma_f32_32x32x2(a[u], b[u], acc);
-  }
-  for (; k < ke; k += 2) {
-    const bool ok = (k + h) < ke;
-    const float a = ok ? pl[size_t(k - kb) * r] : 0.f;
-    const float b = ok ? pr[size_t(k - kb) * r] : 0.f;
-    acc = mfma_f32_32x32x2(a, b, acc);
-  }
-  const float sc = inv_norm_from_parts(sparts, nsp);
-  const float sc2 = sc * sc;
-  float* dst = part + size_t(s) * r * r;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) dst[size_t(i0 + mfma32_row(v, h)) * r + j0 + l32] = acc[v] * sc2;
-}
+  const int p = blockIdx.x / groups, grp = blockIdx.x % groups;
+  int bi, bj;
+  pair_of(p, r >> 5, bi, bj);
+  const bool two = TWO && bi != bj;
 
-// mode RED_SYM: M = (G + G^T)/2 ; mode RED_NS: M = 1.5 I - 0.5 G ; G = sum_s part[s]
-__global__ __launch_bounds__(256) void k_spel_reduce(const float* __restrict__ part, int S, float* __restrict__ M,
-                                                     int r, int mode) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= r * r) return;
-  const int i = e / r, j = e % r;
-  float gsum = 0.f;
-  for (int s = 0; s < S; ++s) gsum += part[size_t(s) * r * r + e];
-  if (mode == RED_SYM) {
-    float gt = 0.f;
-    for (int s = 0; s < S; ++s) gt += part[size_t(s) * r * r + size_t(j) * r + i];
-    M[e] = 0.5f * (gsum + gt);
-  } else {
-    M[e] = (i == j ? 1.5f : 0.f) - 0.5f * gsum;
-  }
-}
-
-// out[i][j] = sx * sum_k X[i][k] M[k][j] with the epilogue of `mode`.
-// Block: 32 rows x 64 columns; wave = (column half jb, k half kh).
-__global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, const float* __restrict__ sparts, int nsp,
-                                                 const float* __restrict__ M, float* __restrict__ out, int d, int r,
-                                                 int mode, const float* __restrict__ g, float* __restrict__ m,
-                                                 float beta, float* __restrict__ norm_parts,
-                                                 const float* __restrict__ Acur, float alpha, float* __restrict__ Dout,
-                                                 float* __restrict__ Y0) {
-  __shared__ float red[2][16][64];
-  __shared__ float wsum[4];
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int h = lane >> 5, l32 = lane & 31;
-  const int jb = wave & 1, kh = wave >> 1;
-  const int i0 = blockIdx.x * 32;
-  const int j0 = blockIdx.y * 64 + jb * 32;
-  const bool active = j0 < r;
-  const int half = r >> 1;
-  const int kb = kh * half, ke = kb + half;
-  f32x16 acc = f32x16{};
-  if (active) {
-    const float* px = X + size_t(i0 + l32) * r + h;
-    const float* pm = M + size_t(h) * r + j0 + l32;
-    int k = kb;
-    for (; k + 8 <= ke; k += 8) {
-      float a[4], b[4];
+  f32x16 acc1 = f32x16{}, acc2 = f32x16{};
+  for (int c = grp * 4 + w; c * kChunk < d; c += groups * 4) {
+    const int k0 = c * kChunk;
+    float a[kChunk / 2], b[kChunk / 2], a2[kChunk / 2], b2[kChunk / 2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = px[k + 2 * u];
-        b[u] = pm[size_t(k + 2 * u) * r];
+    for (int t = 0; t < kChunk / 2; ++t) {
+      const size_t row = size_t(k0 + 2 * t + h) * r;
+      a[t] = Xl[row + bi * 32 + l32];
+      b[t] = Xr[row + bj * 32 + l32];
+      if (two) {
+        a2[t] = Xl[row + bj * 32 + l32];
+        b2[t] = Xr[row + bi * 32 + l32];
       }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) acc = mfma_f32_32x32x2(a[u], b[u], acc);
     }
-    for (; k < ke; k += 2) {
-      const bool ok = (k + h) < ke;
-      acc = mfma_f32_32x32x2(ok ? px[k] : 0.f, ok ? pm[size_t(k) * r] : 0.f, acc);
+    __builtin_amdgcn_sched_barrier(0);  // keep every load ahead of the first multiply
+#pragma unroll
+    for (int t = 0; t < kChunk / 2; ++t) acc1 = mfma_f32_32x32x2(a[t], b[t], acc1);
+    if (two) {
+#pragma unroll
+      for (int t = 0; t < kChunk / 2; ++t) acc2 = mfma_f32_32x32x2(a2[t], b2[t], acc2);
     }
   }
-  if (kh == 1 && active) {
+
+  // the block's 4 waves in a fixed order
+  store_frag(red + w * 1024, acc1, lane);
+  if (TWO) store_frag(red + 4096 + w * 1024, acc2, lane);
+  __syncthreads();
+  const int i = threadIdx.x >> 3, j = (threadIdx.x & 7) * 4;
+  const int fi = frag_index(i, j);
+  f32x4 s1 = (ld4(red + fi) + ld4(red + 1024 + fi)) + (ld4(red + 2048 + fi) + ld4(red + 3072 + fi));
+  if (TWO) {
+    // sym: (G1_ij + G2_ji) / 2 off the diagonal, (G1_ij + G1_ji) / 2 on it
+    const f32x4 s2 = (ld4(red + 4096 + fi) + ld4(red + 5120 + fi)) + (ld4(red + 6144 + fi) + ld4(red + 7168 + fi));
+    const f32x4 tt = (bi != bj) ? s2 : s1;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) red[jb][v][lane] = acc[v];
+    for (int q = 0; q < 4; ++q) tile[i * 33 + j + q] = tt[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s1[q] = 0.5f * (s1[q] + tile[(j + q) * 33 + i]);
+  }
+  float* dst = part + size_t(grp) * r * r;
+  st4(dst + size_t(bi * 32 + i) * r + bj * 32 + j, s1);
+  if (bi != bj) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[size_t(bj * 32 + j + q) * r + bi * 32 + i] = s1[q];
+  }
+}
+
+// acc += X[row][kc .. kc+CH) * M[kc .. kc+CH)[col] on the 32x32x2 matrix core,
+// M = f(sum over G pieces).  At step t lane half h takes k = kc + (CH/2) h + t,
+// so each lane reads CH/2 consecutive floats of its X row as 16-byte loads;
+// all loads are issued before the first multiply.
+template <int CH, int G, bool NS>
+__device__ __forceinline__ void xm_chunk(const float* __restrict__ xr, const float* __restrict__ part, size_t rr,
+                                         int kc, int r, int col, int h, float sc2, f32x16& acc) {
+  constexpr int HK = CH / 2;
+  f32x4 xa[HK / 4];
+  float mb[G][HK];
+  const float* xk = xr + kc + HK * h;
+#pragma unroll
+  for (int q = 0; q < HK / 4; ++q) xa[q] = ld4(xk + 4 * q);
+#pragma unroll
+  for (int gq = 0; gq < G; ++gq)
+#pragma unroll
+    for (int t = 0; t < HK; ++t) mb[gq][t] = part[gq * rr + size_t(kc + HK * h + t) * r + col];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < HK; ++t) {
+    float sum = mb[0][t];
+#pragma unroll
+    for (int gq = 1; gq < G; ++gq) sum += mb[gq][t];
+    const float mv = NS ? ((kc + HK * h + t == col) ? 1.5f : 0.f) - 0.5f * (sc2 * sum) : sum;
+    acc = mfma_f32_32x32x2(xa[t >> 2][t & 3], mv, acc);
+  }
+}
+
+// 1/||m||_F from n per-block partial sums, added in a fixed order by wave 0
+// and broadcast through LDS (0 when m == 0).
+__device__ float block_inv_norm(const float* nparts, int n, float* slot) {
+  if (wave_id() == 0) {
+    const int lane = threadIdx.x & 63;
+    float s = 0.f;
+    for (int b0 = 0; b0 < n; b0 += 64) s += (b0 + lane < n) ? nparts[b0 + lane] : 0.f;
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) *slot = s > 0.f ? 1.f / sqrtf(s) : 0.f;
   }
   __syncthreads();
-  float local = 0.f;
-  if (kh == 0 && active) {
-    const float sx = inv_norm_from_parts(sparts, nsp);
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int i = i0 + mfma32_row(v, h), j = j0 + l32;
-      const size_t o = size_t(i) * r + j;
-      const float val = (acc[v] + red[jb][v][lane]) * sx;
-      if (mode == XM_TANGENT) {
-        const float gR = g[o] - val;
-        const float mn = beta * m[o] + (1.f - beta) * gR;
-        m[o] = mn;
-        local = fmaf(mn, mn, local);
-      } else if (mode == XM_NS || mode == XM_NS_LAST_RET) {
-        out[o] = val;
-      } else {  // XM_NS_LAST_LMO
-        out[o] = val;
-        if (Dout) Dout[o] = val;
-        Y0[o] = Acur[o] - alpha * val;
-      }
+  return *slot;
+}
+
+// out = s X M for one 32 x 32 tile (block (row tile, col tile)); wave w takes
+// K range [w r/4, (w+1) r/4) (r % 32 == 0, so each range is a multiple of 8).
+template <int G, bool NS>
+__global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, const float* __restrict__ nparts_in,
+                                                 const float* __restrict__ part, float* __restrict__ out, int d, int r,
+                                                 int mode, const float* __restrict__ g, float* __restrict__ m,
+                                                 float beta, float* __restrict__ nparts_out,
+                                                 const float* __restrict__ Acur, float alpha, float* __restrict__ Dout,
+                                                 float* __restrict__ Y0) {
+  __shared__ float red[4 * 1024];
+  __shared__ float wsum[4];
+  __shared__ float scs;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int h = lane >> 5, l32 = lane & 31;
+  const int i0 = blockIdx.x * 32, j0 = blockIdx.y * 32;
+  const float sx = nparts_in ? block_inv_norm(nparts_in, (d >> 5) * (r >> 5), &scs) : 1.f;
+  const float sc2 = sx * sx;
+  const size_t rr = size_t(r) * r;
+
+  f32x16 acc = f32x16{};
+  {
+    const float* xr = X + size_t(i0 + l32) * r;
+    const int kq = r >> 2;
+    int kc = w * kq;
+    const int ke = kc + kq;
+    constexpr int CB = (G >= 4) ? 32 : 64;  // at most 64 pending scalar loads per lane
+    for (; kc + CB <= ke; kc += CB) xm_chunk<CB, G, NS>(xr, part, rr, kc, r, j0 + l32, h, sc2, acc);
+    if (CB == 64 && kc + 32 <= ke) {
+      xm_chunk<32, G, NS>(xr, part, rr, kc, r, j0 + l32, h, sc2, acc);
+      kc += 32;
     }
+    if (kc + 16 <= ke) {
+      xm_chunk<16, G, NS>(xr, part, rr, kc, r, j0 + l32, h, sc2, acc);
+      kc += 16;
+    }
+    if (kc + 8 <= ke) xm_chunk<8, G, NS>(xr, part, rr, kc, r, j0 + l32, h, sc2, acc);
   }
+  store_frag(red + w * 1024, acc, lane);
+  __syncthreads();
+  const int i = threadIdx.x >> 3, j = (threadIdx.x & 7) * 4;
+  const int fi = frag_index(i, j);
+  const f32x4 v = (ld4(red + fi) + ld4(red + 1024 + fi)) + (ld4(red + 2048 + fi) + ld4(red + 3072 + fi));
+  const size_t o = size_t(i0 + i) * r + j0 + j;
+
   if (mode == XM_TANGENT) {
-    // fixed-order block sum: lanes by xor-butterfly, then waves 0 and 1 in order
+    // Eq. (4)-(5): g_R = g - A sym(A^T g) ; m = beta m + (1 - beta) g_R
+    const f32x4 gv = ld4(g + o), mv = ld4(m + o);
+    f32x4 mn;
+    float local = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      mn[q] = beta * mv[q] + (1.f - beta) * (gv[q] - v[q]);
+      local = fmaf(mn[q], mn[q], local);
+    }
+    st4(m + o, mn);
+    // this block's share of ||m||_F^2: xor-butterfly within the wave, waves in order
     for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
-    if (lane == 0) wsum[wave] = local;
+    if (lane == 0) wsum[w] = local;
     __syncthreads();
-    if (threadIdx.x == 0) norm_parts[blockIdx.y * gridDim.x + blockIdx.x] = wsum[0] + wsum[1];
+    if (threadIdx.x == 0)
+      nparts_out[blockIdx.y * gridDim.x + blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    return;
+  }
+  const f32x4 val = v * sx;
+  if (mode == XM_NS || mode == XM_NS_LAST_RET) {
+    st4(out + o, val);
+  } else {  // XM_NS_LAST_LMO: D = val ; Y0 = A - alpha D
+    if (Dout) st4(Dout + o, val);
+    st4(Y0 + o, ld4(Acur + o) - alpha * val);
   }
 }
 
-int spel_splits(int d, int r) {
-  const int tiles = ((r + 63) / 64) * ((r + 63) / 64);
-  int s = (256 + tiles - 1) / tiles;
-  const int max_s = d / 64 > 0 ? d / 64 : 1;
-  if (s > max_s) s = max_s;
-  if (s < 1) s = 1;
-  return s;
+// row groups of the Gram pieces: 1, 2 or 4, about 256 rows each
+int spel_groups(int64_t d) { return d >= 1024 ? 4 : d >= 512 ? 2 : 1; }
+
+template <bool NS>
+void launch_xm(int G, dim3 grid, hipStream_t s, const float* X, const float* nparts_in, const float* part, float* out,
+               int d, int r, int mode, const float* g, float* m, float beta, float* nparts_out, const float* Acur,
+               float alpha, float* Dout, float* Y0) {
+  auto k = G == 4 ? k_spel_xm<4, NS> : G == 2 ? k_spel_xm<2, NS> : k_spel_xm<1, NS>;
+  hipLaunchKernelGGL(k, grid, dim3(256), 0, s, X, nparts_in, part, out, d, r, mode, g, m, beta, nparts_out, Acur,
+                     alpha, Dout, Y0);
 }
 
 }  // namespace
 
+// workspace: Xa | Xb | Xc [d][r] | part [groups][r][r] | nparts [(d/32)(r/32)]
 size_t spel_ws_bytes(int64_t d, int64_t r) {
-  const int S = spel_splits(int(d), int(r));
-  const int64_t nparts = (d / 32) * ((r + 63) / 64);
-  return (size_t(3) * d * r + size_t(S) * r * r + size_t(r) * r + size_t(nparts) + 64) * sizeof(float);
+  const size_t floats = 3 * size_t(d) * r + size_t(spel_groups(d)) * r * r + size_t(d / 32) * (r / 32);
+  return (floats + 64) * sizeof(float);
 }
 
 void launch_spel(float* A, const float* g, float* m, float alpha, float beta, int ns_iters, float* D_out, int d, int r,
                  void* ws, hipStream_t s) {
-  const int S = spel_splits(d, r);
-  int rps = (d + S - 1) / S;
-  rps = (rps + 1) & ~1;
-  float* base = static_cast<float*>(ws);
-  float* Xa = base;
+  const int G = spel_groups(d);
+  float* Xa = static_cast<float*>(ws);
   float* Xb = Xa + size_t(d) * r;
   float* Xc = Xb + size_t(d) * r;
-  float* parts = Xc + size_t(d) * r;
-  float* M = parts + size_t(S) * r * r;
-  float* nparts = M + size_t(r) * r;
-  const int nsp = (d / 32) * ((r + 63) / 64);
+  float* part = Xc + size_t(d) * r;
+  float* nparts = part + size_t(G) * r * r;
 
-  const dim3 ggrid((r + 63) / 64, (r + 63) / 64, S);
-  const dim3 rgrid((r * r + 255) / 256);
-  const dim3 xgrid(d / 32, (r + 63) / 64);
+  const int nb = r / 32;
+  const dim3 blk(256);
+  const dim3 ggrid(nb * (nb + 1) / 2 * G);
+  const dim3 xgrid(d / 32, r / 32);
 
-  // Eq. (4)-(5): S = A^T g ; m = beta m + (1 - beta)(g - A sym(S))
-  hipLaunchKernelGGL(k_spel_gram, ggrid, dim3(256), 0, s, A, g, nullptr, 0, parts, d, r, rps);
-  hipLaunchKernelGGL(k_spel_reduce, rgrid, dim3(256), 0, s, parts, S, M, r, int(RED_SYM));
-  hipLaunchKernelGGL(k_spel_xm, xgrid, dim3(256), 0, s, A, nullptr, 0, M, nullptr, d, r, int(XM_TANGENT), g, m, beta,
-                     nparts, nullptr, 0.f, nullptr, nullptr);
+  // Eq. (4)-(5): M = sym(A^T g) ; m = beta m + (1 - beta)(g - A M) ; per-block sums of m^2
+  hipLaunchKernelGGL(k_spel_gram<1>, ggrid, blk, 0, s, A, g, part, d, r, G);
+  launch_xm<false>(G, xgrid, s, A, nullptr, part, nullptr, d, r, int(XM_TANGENT), g, m, beta, nparts, nullptr, 0.f,
+                   nullptr, nullptr);
 
-  // Eq. (6): D = NS(m / ||m||_F); the last iteration also forms Y0 = A - alpha D in Xc
+  // Eq. (6): D = NS(s m), s = 1/||m||_F; the last step forms Y0 = A - alpha D in Xc
   const float* cur = m;
-  const float* cur_sc = nparts;
-  int cur_nsp = nsp;
+  const float* cur_np = nparts;
   float* bufs[2] = {Xa, Xb};
   for (int it = 0; it < ns_iters; ++it) {
     float* nxt = bufs[it & 1];
-    hipLaunchKernelGGL(k_spel_gram, ggrid, dim3(256), 0, s, cur, cur, cur_sc, cur_nsp, parts, d, r, rps);
-    hipLaunchKernelGGL(k_spel_reduce, rgrid, dim3(256), 0, s, parts, S, M, r, int(RED_NS));
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G);
     const int mode = (it == ns_iters - 1) ? int(XM_NS_LAST_LMO) : int(XM_NS);
-    hipLaunchKernelGGL(k_spel_xm, xgrid, dim3(256), 0, s, cur, cur_sc, cur_nsp, M, nxt, d, r, mode, nullptr, nullptr,
-                       0.f, nullptr, A, alpha, D_out, Xc);
+    launch_xm<true>(G, xgrid, s, cur, cur_np, part, nxt, d, r, mode, nullptr, nullptr, 0.f, nullptr, A, alpha, D_out,
+                    Xc);
     cur = nxt;
-    cur_sc = nullptr;
-    cur_nsp = 0;
+    cur_np = nullptr;
   }
 
-  // Eq. (7): A = NS(A - alpha D), input unscaled; the last iteration writes A
+  // Eq. (7): A = NS(A - alpha D), input unscaled; the last step writes A
   cur = Xc;
   for (int it = 0; it < ns_iters; ++it) {
     float* nxt = (it == ns_iters - 1) ? A : bufs[it & 1];
-    hipLaunchKernelGGL(k_spel_gram, ggrid, dim3(256), 0, s, cur, cur, nullptr, 0, parts, d, r, rps);
-    hipLaunchKernelGGL(k_spel_reduce, rgrid, dim3(256), 0, s, parts, S, M, r, int(RED_NS));
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G);
     const int mode = (it == ns_iters - 1) ? int(XM_NS_LAST_RET) : int(XM_NS);
-    hipLaunchKernelGGL(k_spel_xm, xgrid, dim3(256), 0, s, cur, nullptr, 0, M, nxt, d, r, mode, nullptr, nullptr, 0.f,
-                       nullptr, nullptr, 0.f, nullptr, nullptr);
+    launch_xm<true>(G, xgrid, s, cur, nullptr, part, nxt, d, r, mode, nullptr, nullptr, 0.f, nullptr, nullptr, 0.f,
+                    nullptr, nullptr);
     cur = nxt;
   }
 }

@@ -6,8 +6,8 @@ sym(M) = (M + M^T)/2, Eq. (5) heavy-ball momentum, Eq. (6) spectral LMO
 direction d = Polar(m), Eq. (7) retraction A <- Polar(A - alpha d), in the
 order of Algorithm 1, step 4.
 
-The pages name Polar Express for Polar(.) but print no coefficients.  This
-build fixes the polar map to the cubic Newton-Schulz iteration
+The pages name Polar Express for Polar(.) but print no coefficients.  Here
+the polar map is fixed to the cubic Newton-Schulz iteration
 X <- 1.5 X - 0.5 X (X^T X), 8 iterations, with the Gram matrix X^T X formed
 first.  Readings taken where the pages are silent:
   * the LMO input is scaled by its Frobenius norm (all singular values <= 1,

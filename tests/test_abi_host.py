@@ -131,6 +131,9 @@ def test_spel_validation(lib):
     assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 0, None, 2048, 256, FAKE, ws, None) == EARG     # ns_iters >= 1
     assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 250, FAKE, ws, None) == ESHAPE
     assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, 256, 512, FAKE, ws, None) == ESHAPE    # r > d
+    odd = ctypes.c_void_p(0x1004)
+    assert f(odd, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 256, FAKE, ws, None) == EARG      # A not 16-B aligned
+    assert f(FAKE, FAKE, odd, 1e-3, 0.9, 8, None, 2048, 256, FAKE, ws, None) == EARG      # m not 16-B aligned
 
 
 def test_check_tids_validation(lib):

@@ -43,7 +43,8 @@ def test_spel_1b_config():
 
 @pytest.mark.parametrize("d,r,alpha,beta,iters", [(256, 32, 0.05, 0.9, 8), (1024, 128, 1e-3, 0.9, 8),
                                                   (512, 64, 0.3, 0.5, 5), (96, 96, 0.1, 0.0, 8),
-                                                  (2048, 512, 2e-3, 0.95, 8)])
+                                                  (2048, 512, 2e-3, 0.95, 8),
+                                                  (1056, 160, 0.02, 0.9, 8)])
 def test_spel_shapes_with_nonzero_momentum(d, r, alpha, beta, iters):
     inp = synth.spel_inputs(100 + d + r, d, r, 1e-3)
     m0 = torch.from_numpy(synth.gaussian(synth.stream(7, d, r), (d, r), 1e-4).astype(np.float32))
