@@ -43,7 +43,12 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-tokens", type=int, default=2048, help="token sample of the CPU-oracle baseline")
+    p.add_argument("--cpu-tokens", type=int, default=16384, help="token sample of the CPU-oracle baseline")
+    p.add_argument("--cpu-reps", type=int, default=5, help="repetitions of the CPU-oracle sample")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run one plain 256 MiB device copy first (a known-size reference for HBM byte counters)")
+    p.add_argument("--cases", metavar="FILE", default=None,
+                   help="also time every workload of the measurement table and write them to FILE (JSON)")
     return p.parse_args()
 
 
@@ -151,8 +156,26 @@ def algorithmic(inp):
                 compress_flops=comp_flops, reconstruct_flops=reco_flops)
 
 
-def cpu_baseline(inp, n_tok):
-    """The fp64 oracle of the same step on a token sample (host cores)."""
+def counter_traffic():
+    """HBM traffic per compress launch from the committed rocprofv3 counter
+    summary, or None once the kernel source differs from the one measured."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "compress_150m_hbm_counters.txt")
+    src = os.path.join(ROOT, "learned_activation_compression_amd", "csrc", "codec_bf16.hip")
+    try:
+        lines = open(path).read().splitlines()
+        traffic = int([l for l in lines if l.startswith("traffic_bytes_per_launch:")][0].split(":")[1])
+        sha = [l for l in lines if l.startswith("source_sha256")][0].split(":")[1].strip()
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != sha:
+            return None
+        return traffic
+    except (OSError, IndexError, ValueError):
+        return None
+
+
+def cpu_baseline(inp, n_tok, reps):
+    """The fp64 oracle of the same step on a token sample (host cores), run
+    `reps` times; the rate is the sample's tokens over the mean time."""
     from oracle import codec, rvq, spel
     import synth
     S = Shape
@@ -170,25 +193,142 @@ def cpu_baseline(inp, n_tok):
     C = synth.rvq_codebooks(S.seed, 1, S.G, S.K, w, 1.0 / 32.0).double().numpy()
     sp = synth.spel_inputs(S.seed, S.d, S.r, 1e-3)
     t0 = time.perf_counter()
-    Z = codec.compress(X, t, E, P, A)
-    enc = rvq.encode(Z, C, S.G, S.K, S.R)
-    Zq = rvq.decode(enc["codes"], C, S.G, S.K, S.R)
-    Xh = codec.reconstruct(Zq, t, E, P, A)
-    gZ, gA1 = codec.reconstruct_bwd(gXh, Zq, A)
-    gX, gA2 = codec.compress_bwd(gZ, X, t, E, P, A)
-    spel.spel_step(sp["A"].double().numpy(), gA1 + gA2, sp["m"].double().numpy(), S.alpha, S.beta, S.ns)
-    dt = time.perf_counter() - t0
-    del Xh, gX
+    for _ in range(reps):
+        Z = codec.compress(X, t, E, P, A)
+        enc = rvq.encode(Z, C, S.G, S.K, S.R)
+        Zq = rvq.decode(enc["codes"], C, S.G, S.K, S.R)
+        Xh = codec.reconstruct(Zq, t, E, P, A)
+        gZ, gA1 = codec.reconstruct_bwd(gXh, Zq, A)
+        gX, gA2 = codec.compress_bwd(gZ, X, t, E, P, A)
+        spel.spel_step(sp["A"].double().numpy(), gA1 + gA2, sp["m"].double().numpy(), S.alpha, S.beta, S.ns)
+        del Xh, gX
+    dt = (time.perf_counter() - t0) / reps
     return {"value": n_tok / dt, "unit": "boundary tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"one full step of the fp64 oracle (codec fwd+bwd, RVQ encode/decode, one spel_step on "
-                      f"1024x128) on the first {n_tok} of {S.N} tokens: {dt:.2f} s"}
+                      f"1024x128) on {n_tok} of the {S.N} tokens, {reps} runs, mean {dt:.2f} s per run"}
+
+
+def _timed(fn, flush, iters=20, warm=3):
+    """Median / p10 / p90 (ms) of fn() bracketed by HIP events on the current
+    stream, each run after a cache-evicting write (outside the events)."""
+    stream = torch.cuda.current_stream()
+    for _ in range(warm):
+        fn()
+    out = []
+    for _ in range(iters):
+        if flush is not None:
+            flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1))
+    a = np.array(out)
+    return {"ms": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5)}
+
+
+def _codec_counts(N, d, r, n_distinct):
+    """Algorithmic bytes and executed flops of each codec map (whole batch)."""
+    e = n_distinct * 2 * r
+    c = dict(
+        compress=(N * (2 * d + 4 + 2 * r) + e + 2 * d * r + 2 * r * r, N * (2 * d * r + 2 * r * r)),
+        reconstruct=(N * (2 * r + 4 + 2 * d) + e + 2 * 2 * d * r, N * 4 * d * r),
+        reconstruct_bwd=(N * (2 * d + 2 * r + 2 * r) + 2 * d * r + 4 * d * r, N * 4 * d * r),
+        compress_bwd=(N * (2 * r + 2 * d + 4 + 2 * d) + e + 2 * 2 * d * r + 2 * 4 * d * r,
+                      N * (4 * d * r + 2 * r * r) + 2 * d * r * r),
+    )
+    c["pair"] = (c["compress"][0] + c["reconstruct"][0], c["compress"][1] + c["reconstruct"][1])
+    return c
+
+
+def run_cases(lac, dev, flush):
+    """Every workload of the measurement table, each timed cold (flushed)."""
+    import synth
+    res = {"hbm_peak_GBs": HBM_PEAK_GBS, "bf16_peak_TFLOPs": BF16_PEAK_TFLOPS, "f32_peak_TFLOPs": F32_PEAK_TFLOPS,
+           "cases": []}
+
+    def add(name, t, nbytes, flops, bound, tokens=None, peak_tf=BF16_PEAK_TFLOPS):
+        s = t["ms"] * 1e-3
+        row = dict(case=name, **t, bytes=int(nbytes), flops=int(flops), bound=bound,
+                   GBs=round(nbytes / s / 1e9, 1), hbm_frac=round(nbytes / s / 1e9 / HBM_PEAK_GBS, 4),
+                   TFLOPs=round(flops / s / 1e12, 2), mfma_frac=round(flops / s / 1e12 / peak_tf, 4))
+        if tokens:
+            row["tokens_per_s"] = round(tokens / s, 1)
+        res["cases"].append(row)
+        print(f"# {name:34s} {t['ms']*1e3:9.1f} us  {row['GBs']:8.1f} GB/s ({row['hbm_frac']:.3f})  "
+              f"{row['TFLOPs']:8.2f} TF/s ({row['mfma_frac']:.3f})", file=sys.stderr, flush=True)
+
+    def codec_case(tag, c, r, x_kind="gauss"):
+        N, d = c["B"] * c["T"], c["d"]
+        inp = synth.codec_inputs(c["seed"], N, d, r, c["V"], "bf16", x_kind=x_kind)
+        g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        nd = int(np.unique(inp["tids"].numpy()).size)
+        cnt = _codec_counts(N, d, r, nd)
+        pk = lac.mapl_pack(g["P"], g["A"])
+        Z = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+        Xh = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+        gZ = torch.empty_like(Z)
+        gX = torch.empty_like(Xh)
+        gA = torch.empty((d, r), dtype=torch.float32, device=dev)
+        ws = torch.empty(lac.mapl_bwd_workspace_bytes(c["B"], c["T"], d, r), dtype=torch.uint8, device=dev)
+        comp = lambda: lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"], Z=Z, pk=pk, pk_ready=True)
+        reco = lambda: lac.mapl_reconstruct(Z, g["tids"], g["E"], g["P"], g["A"], Xhat=Xh, pk=pk, pk_ready=True)
+        rbwd = lambda: lac.mapl_reconstruct_bwd(g["gXhat"], Z, g["A"], gZ=gZ, gA=gA, accumulate=False, pk=pk,
+                                                pk_ready=True, ws=ws)
+        cbwd = lambda: lac.mapl_compress_bwd(gZ, g["X"], g["tids"], g["E"], g["P"], g["A"], gX=gX, gA=gA,
+                                             accumulate=True, pk=pk, pk_ready=True, ws=ws)
+        bound = "hbm" if r <= 128 else "mfma"
+        add(f"{tag} pair", _timed(lambda: (comp(), reco()), flush), *cnt["pair"], bound, tokens=N)
+        add(f"{tag} compress", _timed(comp, flush), *cnt["compress"], bound, tokens=N)
+        add(f"{tag} reconstruct", _timed(reco, flush), *cnt["reconstruct"], bound, tokens=N)
+        add(f"{tag} reconstruct_bwd", _timed(rbwd, flush), *cnt["reconstruct_bwd"], bound, tokens=N)
+        add(f"{tag} compress_bwd", _timed(cbwd, flush), *cnt["compress_bwd"], bound, tokens=N)
+        del g, pk, Z, Xh, gZ, gX, gA, ws
+        return inp
+
+    C = synth.CONFIGS
+    codec_case("150m d1024 r128", C["150m"], 128)
+    for r in C["sweep"]["ranks"]:
+        codec_case(f"sweep d1024 r{r}", C["sweep"], r, x_kind="lowrank")
+    codec_case("1b d2048 r256", C["1b"], 256)
+
+    # residual VQ at r=256, G=8 x w=32, K=256, R=2 on Z from the codec
+    c = C["rvq"]
+    N, d, r, G, K, R = c["B"] * c["T"], c["d"], c["r"], c["G"], c["K"], c["R"]
+    inp = synth.codec_inputs(c["seed"], N, d, r, c["V"], "bf16", with_grad=False)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    Z = lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"])
+    Cb = synth.rvq_codebooks(c["seed"], 1, G, K, r // G, c["codebook_var"]).to(dev)
+    codes = torch.empty((N, R, G), dtype=torch.uint8, device=dev)
+    Zq = torch.empty((N, r), dtype=torch.float32, device=dev)
+    enc = lambda: lac.rvq_encode(Z, Cb, G, K, R, codes=codes)
+    dec = lambda: lac.rvq_decode(codes, Cb, G, K, R, r, Zq=Zq)
+    add("rvq r256 G8 K256 R2 encode", _timed(enc, flush), N * (2 * r + R * G) + Cb.numel() * 4,
+        N * 2 * r * K * R, "mfma", tokens=N, peak_tf=F32_PEAK_TFLOPS)
+    add("rvq r256 G8 K256 R2 decode (fp32)", _timed(dec, flush), N * (R * G + 4 * r) + Cb.numel() * 4,
+        N * r * R, "hbm", tokens=N, peak_tf=F32_PEAK_TFLOPS)
+    del g, Z, Cb, codes, Zq
+
+    # one spel_step on the fp32 2048 x 256 projector
+    c = C["1b"]
+    d, r, sp = c["d"], c["r"], c["spel"]
+    si = synth.spel_inputs(c["seed"], d, r, sp["g_var"])
+    A, gg, m = si["A"].to(dev), si["g"].to(dev), si["m"].to(dev)
+    sws = torch.empty(lac.spel_workspace_bytes(d, r), dtype=torch.uint8, device=dev)
+    # repeated steps from the same gradient: A stays on the manifold, m keeps accumulating
+    spel_fn = lambda: lac.spel_step(A, gg, m, sp["alpha"], sp["beta"], sp["ns_iters"], ws=sws)
+    flops = 4 * d * r * r * (1 + 2 * sp["ns_iters"])
+    add("spel_step d2048 r256 NS8", _timed(spel_fn, flush), 4 * 4 * d * r, flops, "mfma", peak_tf=F32_PEAK_TFLOPS)
+    return res
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only: the boundary codec has no multi-GPU path here "
+              f"(got --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -203,6 +343,13 @@ def main():
     flush = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
     stream = torch.cuda.current_stream()
 
+    if args.copy_calibration:
+        src = torch.ones(1 << 26, dtype=torch.float32, device=dev)  # 256 MiB read, 256 MiB written
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(lac, g, b, i)
     torch.cuda.synchronize()
@@ -247,14 +394,14 @@ def main():
     ms = float(np.mean(step_ms))
     med = {p: float(np.median(v)) for p, v in phase_ms.items()}
     alg = algorithmic(inp)
-    # dominant codec kernel: the larger of compress / reconstruct by time
-    dom = "reconstruct" if med["reconstruct"] >= med["compress"] else "compress"
-    dom_bytes = alg[f"{dom}_bytes"]
-    dom_s = med[dom] * 1e-3
+    # the metric's dominant kernel: compress (Eq. 1), one launch per step, timed cold by the step's events
+    dom_bytes = alg["compress_bytes"]
+    dom_s = med["compress"] * 1e-3
     achieved = dom_bytes / dom_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
-                "algorithmic_bytes": dom_bytes, "ms": round(med[dom], 5)}
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
+                "kernel": "compress (k_tok_reduce<4, 4, true>)", "algorithmic_bytes": dom_bytes,
+                "ms": round(med["compress"], 5)}
     pc = float(np.median(pair_cold))
     pw = float(np.median(pair_warm))
     pair_bytes = alg["compress_bytes"] + alg["reconstruct_bytes"]
@@ -281,7 +428,11 @@ def main():
         "distinct_tids": alg["n_distinct"],
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_tokens, S.N), max(1, args.cpu_reps))
+    if args.cases:
+        res = run_cases(lac, dev, flush)
+        with open(args.cases, "w") as f:
+            json.dump(res, f, indent=1)
     print(json.dumps(out), flush=True)
 
 

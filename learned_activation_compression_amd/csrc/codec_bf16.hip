@@ -29,7 +29,7 @@ namespace mapl {
 // token ids are clamped to valid rows; a token past N only feeds an output
 // column that is never stored, an invalid id is zeroed by a select), so the
 // compiler can keep P steps of loads in flight.
-template <int RB, int P>
+template <int RB, int P, bool ANCHOR>
 __global__ __launch_bounds__(256) void k_tok_reduce(const bf16_t* __restrict__ X, const bf16_t* __restrict__ AtF,
                                                     const int32_t* __restrict__ tids, const bf16_t* __restrict__ E,
                                                     const bf16_t* __restrict__ QnF, bf16_t* __restrict__ Z, int N,
@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void k_tok_reduce(const bf16_t* __restrict__ X
   const int tok0 = blockIdx.x * 64;
   const int rbase = blockIdx.y * (RB * 32);
   const int Sd = d >> 4;
-  const int Se = (E != nullptr) ? (r >> 4) : 0;
+  const int Se = ANCHOR ? (r >> 4) : 0;
   const int S = Sd + Se;
   const int sb = (S * wave) >> 2, se = (S * (wave + 1)) >> 2;
 
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void k_tok_reduce(const bf16_t* __restrict__ X
   const bf16_t* er0 = x0;
   const bf16_t* er1 = x1;
   const bf16_t* q0 = a0;
-  if (Se > 0) {
+  if (ANCHOR) {
     const int t0 = tids[n0], t1 = tids[n1];
     const bool e0 = (t0 >= 0 && t0 < V), e1 = (t1 >= 0 && t1 < V);
     m0 = e0 ? ~0u : 0u;
@@ -158,12 +158,12 @@ void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32
   const int nb = r / 32;
   const int RB = (nb % 4 == 0) ? 4 : (nb % 2 == 0) ? 2 : 1;
   dim3 grid((N + 63) / 64, r / (RB * 32));
-  if (RB == 4)
-    hipLaunchKernelGGL((k_tok_reduce<4, 4>), grid, dim3(256), 0, s, in, AtF, tids, E, QnF, out, N, d, r, V);
-  else if (RB == 2)
-    hipLaunchKernelGGL((k_tok_reduce<2, 6>), grid, dim3(256), 0, s, in, AtF, tids, E, QnF, out, N, d, r, V);
-  else
-    hipLaunchKernelGGL((k_tok_reduce<1, 8>), grid, dim3(256), 0, s, in, AtF, tids, E, QnF, out, N, d, r, V);
+  // ANCHOR = true is the compress map of Eq. (1); false is the plain product (gZ = gXhat A)
+  auto k = (E != nullptr) ? (RB == 4 ? k_tok_reduce<4, 4, true> : RB == 2 ? k_tok_reduce<2, 6, true>
+                                                                         : k_tok_reduce<1, 8, true>)
+                          : (RB == 4 ? k_tok_reduce<4, 4, false> : RB == 2 ? k_tok_reduce<2, 6, false>
+                                                                          : k_tok_reduce<1, 8, false>);
+  hipLaunchKernelGGL(k, grid, dim3(256), 0, s, in, AtF, tids, E, QnF, out, N, d, r, V);
 }
 
 // ---------------------------------------------------------------- expand --
