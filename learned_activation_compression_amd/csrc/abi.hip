@@ -39,6 +39,9 @@ int check_codec_shape(int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, map
   return MAPL_OK;
 }
 
+// one split count for both backward maps (the larger Gram decides)
+int bwd_splits(int64_t N, int64_t d, int64_t r) { return gram_splits_bf16(int(N), int(d + r), int(r)); }
+
 int check_pack(void* pk, size_t pk_bytes, int64_t d, int64_t r, mapl_dtype dt) {
   if (dt != MAPL_BF16) return MAPL_OK;
   if (pk == nullptr) return MAPL_ERR_NULL;
@@ -46,10 +49,12 @@ int check_pack(void* pk, size_t pk_bytes, int64_t d, int64_t r, mapl_dtype dt) {
   return MAPL_OK;
 }
 
+// bf16: the Gram partials [S][d + r][r] of compress_bwd (reconstruct_bwd uses
+// the first S d r of them) and M [r][r]
 size_t bwd_ws_bytes(int64_t N, int64_t d, int64_t r, mapl_dtype dt) {
   if (dt == MAPL_F32) return size_t(N) * d * sizeof(float);
-  const int S = gram_splits_bf16(int(N));
-  return (size_t(S) * d * r + size_t(S) * r * r + size_t(r) * r) * sizeof(float);
+  const int S = bwd_splits(N, d, r);
+  return (size_t(S) * (d + r) * r + size_t(r) * r) * sizeof(float);
 }
 
 }  // namespace
@@ -172,14 +177,15 @@ int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A, void* 
   }
   PackView v = pack_view(pk, d, r);
   if (!pk_ready) launch_pack_AtF(static_cast<const uint16_t*>(A), v.AtF, int(d), int(r), stream);
-  const int S = gram_splits_bf16(int(N));
+  const int S = bwd_splits(N, d, r);  // same split count as compress_bwd: the workspace fits both
   float* part = static_cast<float*>(ws);
   if (N > 0) {
     launch_tok_reduce_bf16(static_cast<const uint16_t*>(gXhat), v.AtF, nullptr, nullptr, nullptr,
                            static_cast<uint16_t*>(gZ), int(N), int(d), int(r), 1, stream);
-    launch_gram_bf16(static_cast<const uint16_t*>(gXhat), nullptr, 1, static_cast<const uint16_t*>(Z), part, int(N),
-                     int(d), int(r), S, stream);
-    launch_reduce_partials(part, S, gA, d * r, accumulate, stream);
+    // gA (+)= gXhat^T Z
+    launch_gram_bf16(static_cast<const uint16_t*>(gXhat), d, false, int(d), nullptr, 1, nullptr, 0,
+                     static_cast<const uint16_t*>(Z), int(r), part, int(N), S, stream);
+    launch_reduce_partials(part, S, d * r, gA, d * r, accumulate, nullptr, 0, stream);
   }
   return ls.done();
 }
@@ -214,24 +220,21 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const 
     launch_outer_f32(R, static_cast<const float*>(gZ), gA, int(N), int(d), int(r), accumulate, stream);
     return ls.done();
   }
-  const int S = gram_splits_bf16(int(N));
-  float* part1 = static_cast<float*>(ws);
-  float* part2 = part1 + size_t(S) * d * r;
-  float* M = part2 + size_t(S) * r * r;
+  const int S = bwd_splits(N, d, r);
+  float* part = static_cast<float*>(ws);           // [S][d + r][r]
+  float* M = part + size_t(S) * (d + r) * r;       // [r][r]
   const uint16_t* gZ16 = static_cast<const uint16_t*>(gZ);
   PackView v = pack_view(pk, d, r);
   if (!pk_ready) launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), stream);
   // gX = gZ A^T
   launch_tok_expand_bf16(gZ16, v.AF, nullptr, nullptr, nullptr, static_cast<uint16_t*>(gX), int(N), int(d), int(r), 1,
                          stream);
-  // gA (+)= X^T gZ - P^T (E[t]^T gZ)
-  launch_gram_bf16(static_cast<const uint16_t*>(X), nullptr, 1, gZ16, part1, int(N), int(d), int(r), S, stream);
-  launch_gram_bf16(static_cast<const uint16_t*>(E_small), tids, int(V), gZ16, part2, int(N), int(r), int(r), S,
-                   stream);
-  launch_reduce_partials(part1, S, gA, d * r, accumulate, stream);
-  launch_reduce_partials(part2, S, M, r * r, 0, stream);
-  // gA[i][j] -= sum_k P[k][i] M[k][j]
-  launch_small_gemm(int(d), int(r), int(r), P, 1, /*sai*/ 1, /*sak*/ d, M, 0, r, 1, gA, 0, r, 1, -1.f, 1.f, stream);
+  // gA (+)= X^T gZ - P^T (E[t]^T gZ): one Gram over the rows of [X | E[t]], then
+  // the split sums (rows < d into gA, rows >= d into M) and gA -= P^T M
+  launch_gram_bf16(static_cast<const uint16_t*>(X), d, false, int(d), tids, int(V),
+                   static_cast<const uint16_t*>(E_small), int(r), gZ16, int(r), part, int(N), S, stream);
+  launch_reduce_partials(part, S, (d + r) * r, gA, d * r, accumulate, M, r * r, stream);
+  launch_sub_ptm(static_cast<const uint16_t*>(P), M, gA, int(d), int(r), stream);
   return ls.done();
 }
 

@@ -153,16 +153,231 @@ __global__ __launch_bounds__(256) void k_tok_reduce(const bf16_t* __restrict__ X
   }
 }
 
+// ------------------------------------------------------ reduce, streamed --
+// For r >= 128.  One block: 64 tokens x all r output columns; wave w owns the
+// r-blocks [w RBW, (w+1) RBW) over the whole contraction, so no partial tiles
+// are summed.  The contraction runs in chunks of 64 channels: d/64 chunks of
+// the token rows against AtF, then (ANCHOR) r/64 chunks of the anchor rows
+// E[t] against QnF.  Each chunk -- 64 token rows of 128 bytes and the chunk's
+// weight fragments of every wave -- is copied by global_load_lds straight into
+// slot c % S of an LDS ring, S - 1 chunks ahead of the one being multiplied,
+// without passing through registers.
+//   Token row t of a slot holds its eight 16-byte units at positions
+//   u ^ (t & 7): the copy picks, per lane, the source unit that belongs at its
+//   (fixed) destination, and the matrix-core reads (32 rows, one unit each)
+//   then hit 8 different bank groups.
+//   Synchronisation per chunk: each wave waits until its own copies of chunk
+//   c are done (vmcnt counts the copies of the S - 2 younger chunks still in
+//   flight), a barrier makes every wave's copies visible and guarantees that
+//   all waves are done with chunk c - 1, whose slot then receives chunk
+//   c + S - 1.  Copies past the last chunk repeat it into a slot never read.
+constexpr int kRedKC = 64;  // channels per chunk
+
+// Lane l copies 16 bytes from g to LDS byte address (l_base + 16 l); l_base is
+// uniform over the wave.  Written as inline assembly: the compiler would
+// otherwise treat every such copy as a possible write to any LDS the later
+// copies and reads touch and wait for all of them, and the ring's order is
+// kept here by explicit vmcnt waits and barriers instead.  The "memory"
+// clobber keeps every LDS access of the program on its side of the copy.
+__device__ __forceinline__ void copy16_to_lds(const void* g, const void* l_base) {
+  const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(l_base)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(la) : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+template <int RBW, int S>
+struct RedRing {
+  static constexpr int XU = 64 * kRedKC * 2 / 16;  // 16-byte units of token rows per slot
+  static constexpr int WU = 4 * 4 * RBW * 64;      // 4 waves x 4 K-steps x RBW fragments x 64 lanes
+  static constexpr int SLOT = XU + WU;
+  static constexpr int PER = 2 + 4 * RBW;          // copies per wave per chunk
+  static constexpr size_t BYTES = size_t(S) * SLOT * 16;
+};
+
+template <int RBW, int S, int G, bool ANCHOR>
+__global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __restrict__ X,
+                                                            const bf16_t* __restrict__ AtF,
+                                                            const int32_t* __restrict__ tids,
+                                                            const bf16_t* __restrict__ E,
+                                                            const bf16_t* __restrict__ QnF, bf16_t* __restrict__ Z,
+                                                            int N, int d, int r, int V) {
+  using RR = RedRing<RBW, S>;
+  static_assert(S % G == 0 && S / G >= 2, "each wave group needs its own slots");
+  extern __shared__ __attribute__((aligned(16))) u32x4 ring[];
+  const int lane = threadIdx.x & 63, wv = wave_id();
+  const int grp = wv >> 2, w = wv & 3;  // group grp multiplies the chunks c with c % G == grp
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int tok0 = blockIdx.x * 64;
+  const int MB = r >> 5;
+  const int cx = d / kRedKC, nch = cx + (ANCHOR ? r / kRedKC : 0);
+
+  // copy role: this lane copies unit (lane & 7) of rows 16 w + 8 q + (lane >> 3), q = 0, 1;
+  // the row's low 3 bits are lane >> 3, so the source unit is (lane & 7) ^ (lane >> 3)
+  const int cu = (lane & 7) ^ (lane >> 3);
+  // element offsets of the two copied rows: in X (token rows) and in E (anchor rows)
+  size_t xoff[2], eoff[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int tk = min(tok0 + 16 * w + 8 * q + (lane >> 3), N - 1);
+    xoff[q] = size_t(tk) * d + 8 * cu;
+    eoff[q] = 8 * cu;
+    if (ANCHOR) {
+      const int t = tids[tk];
+      eoff[q] += size_t((t >= 0 && t < V) ? t : 0) * r;
+    }
+  }
+  // matrix-core operand masks: token tb*32 + l32 with an invalid id reads a zero anchor row
+  uint32_t bm[2] = {~0u, ~0u};
+  if (ANCHOR) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int t = tids[min(tok0 + tb * 32 + l32, N - 1)];
+      bm[tb] = (t >= 0 && t < V) ? ~0u : 0u;
+    }
+    asm volatile("" : : "v"(bm[0]), "v"(bm[1]));  // resolve the ids before the first copy is queued
+  }
+
+  // chunk c into slot c % S; past the last chunk the last one is copied again into that
+  // (free) slot, which is never read
+  auto issue = [&](int c) {
+    u32x4* slot = ring + (c % S) * RR::SLOT;
+    c = min(c, nch - 1);
+    const bool xs = c < cx;
+    const int ch = (xs ? c : c - cx) * kRedKC;
+    copy16_to_lds((xs ? X + xoff[0] : E + eoff[0]) + ch, slot + (16 * w) * 8);
+    copy16_to_lds((xs ? X + xoff[1] : E + eoff[1]) + ch, slot + (16 * w + 8) * 8);
+    const bf16_t* wb = (xs ? AtF : QnF) + size_t(4 * (xs ? c : c - cx)) * MB * 512;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int i = 0; i < RBW; ++i)
+        copy16_to_lds(wb + (size_t(ks * MB + w * RBW + i) * 64 + lane) * 8,
+                      slot + RR::XU + ((w * 4 + ks) * RBW + i) * 64);
+  };
+
+  f32x16 acc[2][RBW];
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) acc[tb][i] = f32x16{};
+
+#pragma unroll
+  for (int u = 0; u < S / G - 1; ++u) issue(grp + G * u);
+  for (int c0 = 0; c0 < nch; c0 += G) {
+    const int c = c0 + grp;
+    wait_vmcnt<(S / G - 2) * RR::PER>();  // this wave's copies of chunk c are done
+    __syncthreads();                       // everyone's are; chunk c - G is free
+    issue(c + S - G);
+    if (c < nch) {
+      const u32x4* slot = ring + (c % S) * RR::SLOT;
+      const bool anchor = ANCHOR && c >= cx;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int pu = (2 * ks + hi) ^ (l32 & 7);
+        bf16x8 b[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          b[tb] = __builtin_bit_cast(bf16x8, slot[(tb * 32 + l32) * 8 + pu]);
+          if (ANCHOR) b[tb] = mask_bf16x8(b[tb], anchor ? bm[tb] : ~0u);
+        }
+#pragma unroll
+        for (int i = 0; i < RBW; ++i) {
+          const bf16x8 a = __builtin_bit_cast(bf16x8, slot[RR::XU + ((w * 4 + ks) * RBW + i) * 64 + lane]);
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) acc[tb][i] = mfma_bf16_32x32x16(a, b[tb], acc[tb][i]);
+        }
+      }
+    }
+  }
+  wait_vmcnt<0>();  // no copy may still be writing the ring
+  if (G > 1) {
+    // group 1 hands its partial tiles to group 0 through the ring, added in a fixed order
+    __syncthreads();
+    f32x4* red = reinterpret_cast<f32x4*>(ring) + size_t(w) * (2 * RBW * 4 * 64);
+    if (grp == 1) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int i = 0; i < RBW; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            red[((tb * RBW + i) * 4 + q) * 64 + lane] =
+                f32x4{acc[tb][i][4 * q], acc[tb][i][4 * q + 1], acc[tb][i][4 * q + 2], acc[tb][i][4 * q + 3]};
+    }
+    __syncthreads();
+    if (grp == 1) return;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int i = 0; i < RBW; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 o = red[((tb * RBW + i) * 4 + q) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[tb][i][4 * q + e] += o[e];
+        }
+  }
+
+  // lane holds, for token tb*32 + l32, 4 consecutive output columns per register group
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int n = tok0 + tb * 32 + l32;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+      bf16_t* row = Z + size_t(n) * r + (w * RBW + i) * 32 + 4 * hi;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x2*>(row + 8 * q) =
+            u32x2{pack2bf(acc[tb][i][4 * q], acc[tb][i][4 * q + 1]), pack2bf(acc[tb][i][4 * q + 2], acc[tb][i][4 * q + 3])};
+    }
+  }
+}
+
+template <int RBW, int S, int G, bool ANCHOR>
+static void launch_reduce_dma(const uint16_t* in, const uint16_t* AtF, const int32_t* tids, const uint16_t* E,
+                              const uint16_t* QnF, uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
+  auto k = k_tok_reduce_dma<RBW, S, G, ANCHOR>;
+  const size_t lds = RedRing<RBW, S>::BYTES;
+  static bool attr = false;  // once per process: allow more than 64 KB of dynamic LDS
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+    attr = true;
+  }
+  hipLaunchKernelGGL(k, dim3((N + 63) / 64), dim3(256 * G), lds, s, in, AtF, tids, E, QnF, out, N, d, r, V);
+}
+
 void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32_t* tids, const uint16_t* E,
                             const uint16_t* QnF, uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
+  // ANCHOR = true is the compress map of Eq. (1); false is the plain product (gZ = gXhat A)
+  const bool anc = E != nullptr;
+  if (r == 128) {
+    if (anc) launch_reduce_dma<1, 6, 2, true>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
+    else launch_reduce_dma<1, 6, 2, false>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
+    return;
+  }
+  if (r == 256) {
+    if (anc) launch_reduce_dma<2, 3, 1, true>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
+    else launch_reduce_dma<2, 3, 1, false>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
+    return;
+  }
+  if (r == 512) {
+    if (anc) launch_reduce_dma<4, 2, 1, true>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
+    else launch_reduce_dma<4, 2, 1, false>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
+    return;
+  }
   const int nb = r / 32;
   const int RB = (nb % 4 == 0) ? 4 : (nb % 2 == 0) ? 2 : 1;
   dim3 grid((N + 63) / 64, r / (RB * 32));
-  // ANCHOR = true is the compress map of Eq. (1); false is the plain product (gZ = gXhat A)
-  auto k = (E != nullptr) ? (RB == 4 ? k_tok_reduce<4, 4, true> : RB == 2 ? k_tok_reduce<2, 6, true>
-                                                                         : k_tok_reduce<1, 8, true>)
-                          : (RB == 4 ? k_tok_reduce<4, 4, false> : RB == 2 ? k_tok_reduce<2, 6, false>
-                                                                          : k_tok_reduce<1, 8, false>);
+  auto k = anc ? (RB == 4 ? k_tok_reduce<4, 4, true> : RB == 2 ? k_tok_reduce<2, 6, true> : k_tok_reduce<1, 8, true>)
+               : (RB == 4 ? k_tok_reduce<4, 4, false> : RB == 2 ? k_tok_reduce<2, 6, false>
+                                                               : k_tok_reduce<1, 8, false>);
   hipLaunchKernelGGL(k, grid, dim3(256), 0, s, in, AtF, tids, E, QnF, out, N, d, r, V);
 }
 
@@ -347,126 +562,296 @@ void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_
 }
 
 // ------------------------------------------------------------------ gram --
-// part[s][i][j] = sum over tokens n of split s of L[n][i] R[n][j].
-// Block: 128 rows i (4 waves x 32) x JB*32 columns j, one token split.
-// Token chunks of 64 are staged into LDS transposed ([row][token]) so that
-// each lane reads 8 consecutive tokens as one 16-byte operand.
-constexpr int kGramChunk = 64;
-constexpr int kGramPitch = kGramChunk + 8;
+// part[s][i][j] = sum over the tokens n of split s of L[n][i] R[n][j] for
+// i < Ld + Le, j < Rd.  Row i < Ld of L is in[n][i] (LT = false, in is
+// [N][ldin]) or in[i][n] (LT = true, in is L^T = [Ld][ldin], as P is for
+// P A); row Ld + q is E[tids[n]][q] (zero for an id outside [0, V)).
+//
+// Block: 128 rows x TJ columns of one token split; the 4 waves tile it as
+// WI x WJ (64 x 64 each for TJ = 128).  Tokens stream in chunks of 64 through
+// two LDS buffers holding the chunk transposed, [row][token]: row t of a
+// buffer is 8 units of 16 bytes (8 tokens each), unit c stored at position
+// c ^ (t & 7), so that the matrix-core reads (32 rows, one unit each) and the
+// staging writes (8 lanes, 8 different units) both spread over the banks.
+// Staging: thread (tg, g) loads the 8 x 8 block of tokens 8 tg..+7 and rows
+// 8 g..+7 as eight 16-byte row segments (each wave instruction reads eight
+// full 128-byte lines), transposes it in registers with byte permutes and
+// writes eight units.  The loads of the next three chunks are in flight while
+// the current chunk is multiplied.
+constexpr int kGramTok = 64;     // tokens per chunk (4 matrix-core K-steps)
+constexpr int kGramRound = 512;  // tokens per fully unrolled round of chunks
 
-template <int JB>
-__global__ __launch_bounds__(256) void k_gram(const bf16_t* __restrict__ L, const int32_t* __restrict__ tids, int V,
-                                              const bf16_t* __restrict__ R, float* __restrict__ part, int N, int Ld,
-                                              int r, int tok_per_split) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ls[128][kGramPitch];
-  __shared__ __attribute__((aligned(16))) bf16_t Rs[JB * 32][kGramPitch];
-  const int lane = threadIdx.x & 63, wave = wave_id();
-  const int hi = lane >> 5, l32 = lane & 31;
-  const int i0 = blockIdx.x * 128, j0 = blockIdx.y * (JB * 32);
-  const int sidx = blockIdx.z;
-  const int nb = sidx * tok_per_split;
-  const int ne = min(N, nb + tok_per_split);
-
-  f32x16 acc[JB];
+__device__ __forceinline__ void transpose8x8_b16(const u32x4 (&v)[8], u32x4 (&o)[8]) {
+  // o[q] word k = (element q of v[2k], element q of v[2k+1]) as (low, high)
 #pragma unroll
-  for (int j = 0; j < JB; ++j) acc[j] = f32x16{};
-
-  for (int c0 = nb; c0 < ne; c0 += kGramChunk) {
-    // stage L: 64 tokens x 128 rows, 16 chunks of 8 per token
-    for (int q = threadIdx.x; q < kGramChunk * 16; q += 256) {
-      const int t = q & (kGramChunk - 1), ic = (q >> 6) * 8;
-      const int n = c0 + t;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (n < ne && i0 + ic < Ld) {
-        const bf16_t* row = nullptr;
-        if (tids != nullptr) {
-          const int tk = tids[n];
-          if (tk >= 0 && tk < V) row = L + size_t(tk) * Ld;
-        } else {
-          row = L + size_t(n) * Ld;
-        }
-        if (row) v = *reinterpret_cast<const u32x4*>(row + i0 + ic);
-      }
+  for (int q = 0; q < 8; ++q) {
+    const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Ls[ic + 2 * e][t] = bf16_t(v[e] & 0xffffu);
-        Ls[ic + 2 * e + 1][t] = bf16_t(v[e] >> 16);
-      }
-    }
-    // stage R: 64 tokens x JB*32 columns
-    for (int q = threadIdx.x; q < kGramChunk * JB * 4; q += 256) {
-      const int t = q & (kGramChunk - 1), jc = (q >> 6) * 8;
-      const int n = c0 + t;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (n < ne) v = *reinterpret_cast<const u32x4*>(R + size_t(n) * r + j0 + jc);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Rs[jc + 2 * e][t] = bf16_t(v[e] & 0xffffu);
-        Rs[jc + 2 * e + 1][t] = bf16_t(v[e] >> 16);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < kGramChunk / 16; ++ks) {
-      const int k = ks * 16 + 8 * hi;
-      const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&Ls[wave * 32 + l32][k]));
-#pragma unroll
-      for (int j = 0; j < JB; ++j) {
-        const bf16x8 b = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&Rs[j * 32 + l32][k]));
-        acc[j] = mfma_bf16_32x32x16(a, b, acc[j]);
-      }
-    }
-    __syncthreads();
-  }
-  float* dst = part + size_t(sidx) * Ld * r;
-#pragma unroll
-  for (int j = 0; j < JB; ++j) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int i = i0 + wave * 32 + mfma32_row(v, hi);
-      if (i < Ld) dst[size_t(i) * r + j0 + j * 32 + l32] = acc[j][v];
-    }
+    for (int k = 0; k < 4; ++k) o[q][k] = __builtin_amdgcn_perm(v[2 * k + 1][q >> 1], v[2 * k][q >> 1], sel);
   }
 }
 
-int gram_splits_bf16(int N) {
-  int s = N / 512;
+template <int TJ, bool LT>
+__global__ __launch_bounds__(256) void k_gram2(const bf16_t* __restrict__ in, int64_t ldin, int Ld,
+                                               const int32_t* __restrict__ tids, int V,
+                                               const bf16_t* __restrict__ E, int Le, const bf16_t* __restrict__ R,
+                                               int Rd, float* __restrict__ part, int N, int tps, int ntile_i,
+                                               int ntile_j) {
+  constexpr int WJ = (TJ == 128) ? 2 : 1;
+  constexpr int WI = 4 / WJ;
+  constexpr int MI = 128 / WI / 32, MJ = TJ / WJ / 32;
+  constexpr int BUF = (128 + TJ) * 8;  // units per buffer
+  __shared__ u32x4 sm[2 * BUF];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int wi = wave / WJ, wj = wave % WJ;
+  const int bid = xcd_swizzle(blockIdx.x, int(gridDim.x));
+  const int ti = bid % ntile_i, tj = (bid / ntile_i) % ntile_j, sp = bid / (ntile_i * ntile_j);
+  const int i0 = ti * 128, j0 = tj * TJ;
+  const int rows = Ld + Le;
+  const int nb = sp * tps, ne = min(N, nb + tps);
+
+  // staging role of this thread
+  const int tid = threadIdx.x;
+  const bool isL = tid < 128, isR = tid >= 128 && tid < 128 + TJ;
+  const int tg = tid & 7, g = (isL ? tid : tid - 128) >> 3;
+  const int srow = isL ? i0 + 8 * g : j0 + 8 * g;  // first row (L) or column (R) of the 8 x 8 block
+  constexpr int D = 3;  // chunks whose loads are in flight while one is multiplied
+  u32x4 v[D][8];
+  uint32_t mk[D];  // bit e: element e of v[u] is real data (else it is zeroed when staged)
+  int tq[D][8];    // anchor rows: token ids of the chunk D ahead of the one in v[u]
+  // an anchor-row tile (rows >= Ld come from E[tids]); uniform over the block
+  const bool tileE = __builtin_amdgcn_readfirstlane(int(!LT && Le > 0 && i0 >= Ld)) != 0;
+  const bool roleL = wave < 2;             // waves 0-1 stage L, waves 2-3 stage R (uniform per wave)
+  const bool active = roleL || isR;        // lanes of waves 2-3 past the TJ columns stage nothing
+  const bool insideE = srow < rows;
+  // element e of a load is row idx_e of `base` (stride `stride`)
+  const bf16_t* base;
+  int64_t stride;
+  if (roleL && LT) {
+    base = in;
+    stride = ldin;
+  } else if (roleL && tileE) {
+    base = E + (insideE ? srow - Ld : 0);
+    stride = Le;
+  } else if (roleL) {
+    base = in + srow;
+    stride = ldin;
+  } else {
+    base = R + (isR ? srow : 0);
+    stride = Rd;
+  }
+
+  // Loads are unconditional from clamped addresses; what falls outside is
+  // zeroed only when staged, so that no select waits on a load and the loads
+  // of D chunks stay in flight.  Anchor rows need their token ids first: those
+  // of chunk c + D are loaded right after the rows of chunk c, so waiting for
+  // them never waits for a later chunk.
+  auto load_tids = [&](int (&t)[8], int rb, int c) {
+    const int n0 = rb + c * kGramTok + 8 * tg;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = tids[min(n0 + e, ne - 1)];
+  };
+  auto load = [&](u32x4 (&w)[8], uint32_t& m, int (&t)[8], int rb, int c) {
+    const int n0 = rb + c * kGramTok + 8 * tg;
+    m = 0u;
+    if (roleL && LT) {  // the 8 tokens are the columns of rows srow..srow+7
+      const int nn = min(n0, ne - 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        w[e] = *reinterpret_cast<const u32x4*>(base + size_t(min(srow + e, Ld - 1)) * stride + nn);
+        m |= uint32_t((srow + e < Ld) && (n0 < ne)) << e;
+      }
+    } else if (roleL && tileE) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const bool ok = insideE && (n0 + e < ne) && t[e] >= 0 && t[e] < V;
+        w[e] = *reinterpret_cast<const u32x4*>(base + size_t(ok ? t[e] : 0) * stride);
+        m |= uint32_t(ok) << e;
+      }
+      load_tids(t, rb, c + D);
+    } else {  // token rows of X or R
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        w[e] = *reinterpret_cast<const u32x4*>(base + size_t(min(n0 + e, ne - 1)) * stride);
+        m |= uint32_t(active && (n0 + e < ne)) << e;
+      }
+    }
+  };
+  auto stage = [&](const u32x4 (&w)[8], uint32_t m, int b) {
+    if (!active) return;
+    u32x4 x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = ((m >> e) & 1u) ? w[e] : u32x4{0u, 0u, 0u, 0u};
+    u32x4* dst = sm + b * BUF + (roleL ? 0 : 128 * 8) + 8 * g * 8;  // row 8 g of the L or R part
+    if (roleL && LT) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) dst[q * 8 + (tg ^ q)] = x[q];
+    } else {
+      u32x4 o[8];
+      transpose8x8_b16(x, o);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) dst[q * 8 + (tg ^ q)] = o[q];
+    }
+  };
+
+  f32x16 acc[MI][MJ];
+#pragma unroll
+  for (int a = 0; a < MI; ++a)
+#pragma unroll
+    for (int b = 0; b < MJ; ++b) acc[a][b] = f32x16{};
+
+  // Rounds of NR chunks, each a straight line of code (so that the compiler
+  // counts the loads in flight exactly): register set u holds the chunks
+  // c with c % D == u.  Chunks past the block's tokens load clamped rows and
+  // are staged as zeros.
+  constexpr int NR = kGramRound / kGramTok;
+  for (int rb = nb; rb < ne; rb += kGramRound) {
+    if (tileE) {
+#pragma unroll
+      for (int u = 0; u < D; ++u) load_tids(tq[u], rb, u);
+    }
+#pragma unroll
+    for (int u = 0; u < D; ++u) load(v[u], mk[u], tq[u], rb, u);
+    stage(v[0], mk[0], 0);
+    load(v[0], mk[0], tq[0], rb, D);
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NR; ++c) {
+      const u32x4* Ls = sm + (c & 1) * BUF;
+      const u32x4* Rs = Ls + 128 * 8;
+#pragma unroll
+      for (int ks = 0; ks < kGramTok / 16; ++ks) {
+        const int un = (2 * ks + hi) ^ (l32 & 7);
+        bf16x8 a[MI], b[MJ];
+#pragma unroll
+        for (int m = 0; m < MI; ++m) a[m] = __builtin_bit_cast(bf16x8, Ls[(wi * MI * 32 + m * 32 + l32) * 8 + un]);
+#pragma unroll
+        for (int m = 0; m < MJ; ++m) b[m] = __builtin_bit_cast(bf16x8, Rs[(wj * MJ * 32 + m * 32 + l32) * 8 + un]);
+#pragma unroll
+        for (int x = 0; x < MI; ++x)
+#pragma unroll
+          for (int y = 0; y < MJ; ++y) acc[x][y] = mfma_bf16_32x32x16(a[x], b[y], acc[x][y]);
+      }
+      const int u1 = (c + 1) % D;
+      if (c + 1 < NR) stage(v[u1], mk[u1], (c + 1) & 1);
+      if (c + 1 + D < NR) load(v[u1], mk[u1], tq[u1], rb, c + 1 + D);
+      __syncthreads();
+    }
+  }
+
+  float* dst = part + size_t(sp) * rows * Rd;
+#pragma unroll
+  for (int x = 0; x < MI; ++x)
+#pragma unroll
+    for (int y = 0; y < MJ; ++y)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int i = i0 + wi * MI * 32 + x * 32 + mfma32_row(q, hi);
+        if (i < rows) dst[size_t(i) * Rd + j0 + wj * MJ * 32 + y * 32 + l32] = acc[x][y][q];
+      }
+}
+
+int gram_splits_bf16(int N, int rows, int Rd) {
+  (void)rows;
+  (void)Rd;
+  int s = (N + kGramRound - 1) / kGramRound;  // one round of 512 tokens per block where possible
+  if (s > 64) s = 64;                          // bounds the partials: at most 64 d x r pieces
   if (s < 1) s = 1;
-  if (s > 64) s = 64;
   return s;
 }
 
-void launch_gram_bf16(const uint16_t* L, const int32_t* tids, int V, const uint16_t* R, float* part, int N, int Ld,
-                      int r, int splits, hipStream_t s) {
+void launch_gram_bf16(const uint16_t* in, int64_t ldin, bool LT, int Ld, const int32_t* tids, int V,
+                      const uint16_t* E, int Le, const uint16_t* R, int Rd, float* part, int N, int splits,
+                      hipStream_t s) {
   int tps = (N + splits - 1) / splits;
-  tps = (tps + kGramChunk - 1) / kGramChunk * kGramChunk;
-  const int nb = r / 32;
-  const int JB = (nb % 4 == 0) ? 4 : (nb % 2 == 0) ? 2 : 1;
-  dim3 grid((Ld + 127) / 128, r / (JB * 32), splits);
-  if (JB == 4)
-    hipLaunchKernelGGL(k_gram<4>, grid, dim3(256), 0, s, L, tids, V, R, part, N, Ld, r, tps);
-  else if (JB == 2)
-    hipLaunchKernelGGL(k_gram<2>, grid, dim3(256), 0, s, L, tids, V, R, part, N, Ld, r, tps);
-  else
-    hipLaunchKernelGGL(k_gram<1>, grid, dim3(256), 0, s, L, tids, V, R, part, N, Ld, r, tps);
+  tps = (tps + kGramRound - 1) / kGramRound * kGramRound;
+  const int TJ = Rd >= 128 ? 128 : Rd;
+  const int ti = (Ld + Le + 127) / 128, tj = Rd / TJ;
+  const dim3 grid(unsigned(ti * tj * splits));
+#define MAPL_GRAM(TJv, LTv)                                                                                      \
+  hipLaunchKernelGGL((k_gram2<TJv, LTv>), grid, dim3(256), 0, s, in, ldin, Ld, tids, V, E, Le, R, Rd, part, N, tps, \
+                     ti, tj)
+  if (LT) {
+    if (TJ == 128) MAPL_GRAM(128, true);
+    else if (TJ == 64) MAPL_GRAM(64, true);
+    else MAPL_GRAM(32, true);
+  } else {
+    if (TJ == 128) MAPL_GRAM(128, false);
+    else if (TJ == 64) MAPL_GRAM(64, false);
+    else MAPL_GRAM(32, false);
+  }
+#undef MAPL_GRAM
 }
 
 // ------------------------------------------------------ partial reduction --
-__global__ __launch_bounds__(256) void k_reduce_partials(const float* __restrict__ part, int splits,
-                                                         float* __restrict__ out, int64_t count4, int64_t count,
-                                                         int accumulate) {
+// Element e < n0 + n1 of the split sums sum_s part[s * stride + e] goes to
+// out0[e] (added to it when acc0) for e < n0, else to out1[e - n0]; the
+// splits are added in order, eight loads in flight at a time.
+__global__ __launch_bounds__(256) void k_reduce_partials(const float* __restrict__ part, int splits, int64_t stride4,
+                                                         float* __restrict__ out0, int64_t n0_4, int acc0,
+                                                         float* __restrict__ out1, int64_t n1_4) {
   const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= count4) return;
-  f32x4 s = accumulate ? reinterpret_cast<const f32x4*>(out)[e] : f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < splits; ++k) s += reinterpret_cast<const f32x4*>(part + size_t(k) * count)[e];
-  reinterpret_cast<f32x4*>(out)[e] = s;
+  if (e >= n0_4 + n1_4) return;
+  const f32x4* p = reinterpret_cast<const f32x4*>(part) + e;
+  f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < splits; k0 += 8) {
+    f32x4 t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = (k0 + u < splits) ? p[size_t(k0 + u) * stride4] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += t[u];
+  }
+  if (e < n0_4) {
+    f32x4* o = reinterpret_cast<f32x4*>(out0) + e;
+    *o = acc0 ? *o + s : s;
+  } else {
+    reinterpret_cast<f32x4*>(out1)[e - n0_4] = s;
+  }
 }
 
-void launch_reduce_partials(const float* part, int splits, float* out, int64_t count, int accumulate,
-                            hipStream_t s) {
-  const int64_t c4 = count / 4;
-  hipLaunchKernelGGL(k_reduce_partials, dim3(unsigned((c4 + 255) / 256)), dim3(256), 0, s, part, splits, out, c4,
-                     count, accumulate);
+void launch_reduce_partials(const float* part, int splits, int64_t stride, float* out0, int64_t n0, int acc0,
+                            float* out1, int64_t n1, hipStream_t s) {
+  const int64_t c4 = (n0 + n1) / 4;
+  hipLaunchKernelGGL(k_reduce_partials, dim3(unsigned((c4 + 255) / 256)), dim3(256), 0, s, part, splits, stride / 4,
+                     out0, n0 / 4, acc0, out1, n1 / 4);
+}
+
+// ------------------------------------------------- anchor-term correction --
+// gA[i][j] -= sum_k P[k][i] M[k][j]  (P bf16 [r][d], M fp32 [r][r], gA fp32 [d][r]).
+// One block per 32 x 32 tile of gA; the 4 waves split k and add in LDS.
+__global__ __launch_bounds__(256) void k_sub_ptm(const bf16_t* __restrict__ P, const float* __restrict__ M,
+                                                 float* __restrict__ gA, int d, int r) {
+  __shared__ float red[4 * 1024];
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int i0 = blockIdx.x * 32, j0 = blockIdx.y * 32;
+  const int kq = r >> 2;  // r % 32 == 0: a multiple of 8
+  f32x16 acc = f32x16{};
+  for (int kc = wave * kq; kc < (wave + 1) * kq; kc += 8) {
+    float a[4], b[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int k = kc + 2 * t + hi;
+      a[t] = bf2f(P[size_t(k) * d + i0 + l32]);
+      b[t] = M[size_t(k) * r + j0 + l32];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc = mfma_f32_32x32x2(a[t], b[t], acc);
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) red[wave * 1024 + v * 64 + lane] = acc[v];
+  __syncthreads();
+  const int i = threadIdx.x >> 3, j = (threadIdx.x & 7) * 4;
+  const int fi = ((((i >> 3) << 2) | (i & 3)) << 6) + (((i >> 2) & 1) << 5) + j;
+  const f32x4* r4 = reinterpret_cast<const f32x4*>(red);
+  const f32x4 sum = (r4[fi / 4] + r4[(1024 + fi) / 4]) + (r4[(2048 + fi) / 4] + r4[(3072 + fi) / 4]);
+  f32x4* o = reinterpret_cast<f32x4*>(gA + size_t(i0 + i) * r + j0 + j);
+  *o = *o - sum;
+}
+
+void launch_sub_ptm(const uint16_t* P, const float* M, float* gA, int d, int r, hipStream_t s) {
+  hipLaunchKernelGGL(k_sub_ptm, dim3(d / 32, r / 32), dim3(256), 0, s, P, M, gA, d, r);
 }
 
 }  // namespace mapl

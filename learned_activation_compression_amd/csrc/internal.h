@@ -24,13 +24,6 @@ void launch_pack_PtF(const uint16_t* P, uint16_t* PtF, int d, int r, hipStream_t
 // all four sections
 void launch_pack_all(const uint16_t* P, const uint16_t* A, PackView v, int d, int r, hipStream_t s);
 
-// generic small fp32-accumulating GEMM with arbitrary strides:
-//   C(i,j) = alpha * sum_k A(i,k) B(k,j) + beta * C(i,j)
-// type codes: 0 = fp32, 1 = bf16
-void launch_small_gemm(int M, int N, int K, const void* A, int a_ty, int64_t sai, int64_t sak,
-                       const void* B, int b_ty, int64_t sbk, int64_t sbj, void* C, int c_ty,
-                       int64_t sci, int64_t scj, float alpha, float beta, hipStream_t s);
-
 // ---- bf16 codec
 // out[N][r] = in[N][d] A  (- E[tids] (P A)) via AtF and QnF; E == nullptr drops the anchor term
 void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32_t* tids,
@@ -40,14 +33,20 @@ void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32
 void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_t* tids,
                             const uint16_t* E, const uint16_t* PtF, uint16_t* out,
                             int N, int d, int r, int V, hipStream_t s);
-// token-split partial Gram: part[s][i][j] = sum_{n in split s} L[n][i] R[n][j],
-// L = in_l [N][Ld] or, when tids != nullptr, L[n] = E[tids[n]] ([V][Ld]).
-int gram_splits_bf16(int N);
-void launch_gram_bf16(const uint16_t* L, const int32_t* tids, int V, const uint16_t* R,
-                      float* part, int N, int Ld, int r, int splits, hipStream_t s);
-// out[e] = (accumulate ? out[e] : 0) + sum_s part[s][e], e < count (fixed order)
-void launch_reduce_partials(const float* part, int splits, float* out, int64_t count,
-                            int accumulate, hipStream_t s);
+// token-split partial Gram: part[s][i][j] = sum_{n in split s} L[n][i] R[n][j] for
+// i < Ld + Le, j < Rd.  Row i < Ld of L is in[n][i] (LT false, in [N][ldin]) or
+// in[i][n] (LT true, in [Ld][ldin]); row Ld + q is E[tids[n]][q] (zero for an
+// invalid id).  R is [N][Rd].  part is [splits][Ld + Le][Rd] fp32.
+int gram_splits_bf16(int N, int rows, int Rd);
+void launch_gram_bf16(const uint16_t* in, int64_t ldin, bool LT, int Ld, const int32_t* tids, int V,
+                      const uint16_t* E, int Le, const uint16_t* R, int Rd, float* part, int N, int splits,
+                      hipStream_t s);
+// fixed-order split sums: e < n0 -> out0[e] (+= when acc0), else out1[e - n0];
+// split k of element e at part[k * stride + e]; n0, n1, stride multiples of 4
+void launch_reduce_partials(const float* part, int splits, int64_t stride, float* out0, int64_t n0, int acc0,
+                            float* out1, int64_t n1, hipStream_t s);
+// gA[i][j] -= sum_k P[k][i] M[k][j]  (P bf16 [r][d], M fp32 [r][r], gA fp32 [d][r])
+void launch_sub_ptm(const uint16_t* P, const float* M, float* gA, int d, int r, hipStream_t s);
 
 // ---- fp32 codec (small problems, plain fp32 arithmetic)
 void launch_compress_f32(const float* X, const int32_t* tids, const float* E, const float* P,
