@@ -152,7 +152,8 @@ int mapl_check_tids(const int32_t* tids, int64_t N, int64_t V, int32_t* bad_coun
  * shares one codebook across all rounds (the paper's single per-stage C_p);
  * C_round_stride >= r*K gives each round its own.  Codes are uint8
  * [N][R][G] at codes[(n*R + rho)*G + g], so K <= 256.
- * Limits: w % 4 == 0, w <= 64, K % 32 == 0, 32 <= K <= 256, R >= 1.
+ * Limits: w in {2, 4, 8, 16, 32, 64}, K % 32 == 0, 32 <= K <= 256, R >= 1, and
+ * (w (K + 2) + K) * 4 <= 65536 (one group's codebook fits in LDS).
  * ---------------------------------------------------------------------- */
 
 /* Encode: for rho = 0..R-1 and each group, code = argmin_k ||res - c_k||^2

@@ -264,7 +264,7 @@ int rvq_encode(const void* Z, mapl_dtype z_dt, const float* C, int64_t C_round_s
   const int64_t w = r / G;
   if (!(w == 2 || w == 4 || w == 8 || w == 16 || w == 32 || w == 64)) return MAPL_ERR_SHAPE;
   if (K % 32 != 0 || K < 32) return MAPL_ERR_SHAPE;
-  if ((w * K + K) * int64_t(sizeof(float)) > 65536) return MAPL_ERR_SHAPE;
+  if ((w * (K + 2) + K) * int64_t(sizeof(float)) > 65536) return MAPL_ERR_SHAPE;  // encode's LDS codebook
   if (N == 0) return MAPL_OK;
   LaunchScope ls;
   launch_rvq_encode(Z, z_dt == MAPL_BF16, C, C_round_stride, codes, int(N), int(r), int(G), int(K), int(R), stream);

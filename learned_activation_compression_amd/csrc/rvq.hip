@@ -6,11 +6,13 @@
 // Appendix F (streamed codebook sync: the receiver overwrites the codewords
 // the sender streams).
 //
-// Encode: one block owns one group g and a range of tokens.  The round's
-// codebook for g sits in LDS transposed ([dim][codeword]) with its squared
-// norms.  Each wave keeps NT tiles of 32 tokens' residuals in registers (lane
-// half h holds dims [h*W/2, (h+1)*W/2) of token l&31) and scores 32 codewords
-// at a time with v_mfma_f32_32x32x2_f32: score_k = ||c_k||^2 - 2 <res, c_k>.
+// Encode: one block owns one group g and 256 tokens, one 32-token tile per
+// wave (8 waves, two per SIMD, so that one wave's argmin overlaps the other's
+// matrix-core work).  The round's codebook for g sits in LDS transposed
+// ([dim][codeword]) with its squared norms.  Lane half h holds dims
+// [h W/2, (h+1) W/2) of token l & 31, pre-scaled by -2, and 32 codewords at a
+// time are scored with v_mfma_f32_32x32x2_f32 on an accumulator that starts
+// at the codewords' squared norms: score_k = ||c_k||^2 - 2 <res, c_k>.
 // Candidates are visited in increasing k within a lane and merged with the
 // partner half-wave preferring the lower index, so exact ties resolve to the
 // lowest codeword index; NaN scores never compare smaller.
@@ -19,90 +21,161 @@
 
 namespace mapl {
 
-constexpr int kRvqTilesPerWave = 2;
+constexpr int kRvqWaves = 8;  // 32-token tiles per block, one per wave
 
 template <int W, typename ZT>
-__global__ __launch_bounds__(256) void k_rvq_encode(const ZT* __restrict__ Z, const float* __restrict__ C,
-                                                    int64_t stride, uint8_t* __restrict__ codes, int N, int r, int G,
-                                                    int K, int R) {
+__global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode(const ZT* __restrict__ Z, const float* __restrict__ C,
+                                                               int64_t stride, uint8_t* __restrict__ codes, int N,
+                                                               int r, int G, int K, int R) {
   constexpr int H = W / 2;  // dims per lane (k steps of the 32x32x2 MFMA)
-  extern __shared__ float sh[];
-  float* cbT = sh;           // [W][K]
-  float* nrm = sh + W * K;   // [K]
+  extern __shared__ __attribute__((aligned(16))) float sh[];
+  const int P = K + 2;       // row pitch: the two lane halves read rows H apart in other banks
+  float* cbT = sh;           // [W][P]
+  float* nrm = sh + W * P;   // [K]
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
   const int g = blockIdx.x;
-  const int tok_base = blockIdx.y * (4 * kRvqTilesPerWave * 32) + wave * (kRvqTilesPerWave * 32);
+  const int n = blockIdx.y * (kRvqWaves * 32) + wave * 32 + l32;
 
-  float res[kRvqTilesPerWave][H];
+  float res[H];
+  {
+    const ZT* zr = Z + size_t(min(n, N - 1)) * r + g * W + h * H;
+    if (sizeof(ZT) == 2 && H % 8 == 0) {  // bf16: 16-byte loads of 8 values
 #pragma unroll
-  for (int t = 0; t < kRvqTilesPerWave; ++t) {
-    const int n = tok_base + t * 32 + l32;
+      for (int s = 0; s < H; s += 8) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(zr + s);
 #pragma unroll
-    for (int s = 0; s < H; ++s)
-      res[t][s] = (n < N) ? to_f32<ZT>(Z[size_t(n) * r + g * W + h * H + s]) : 0.f;
+        for (int e = 0; e < 4; ++e) {
+          res[s + 2 * e] = __uint_as_float(u[e] << 16);
+          res[s + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        }
+      }
+    } else if (sizeof(ZT) == 4 && H % 4 == 0) {  // fp32: 16-byte loads of 4 values
+#pragma unroll
+      for (int s = 0; s < H; s += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(zr + s);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[s + e] = v[e];
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < H; ++s) res[s] = to_f32<ZT>(zr[s]);
+    }
+    if (n >= N) {
+#pragma unroll
+      for (int s = 0; s < H; ++s) res[s] = 0.f;
+    }
   }
 
   for (int rho = 0; rho < R; ++rho) {
     if (rho == 0 || stride != 0) {
       __syncthreads();
       const float* book = C + rho * stride + size_t(g) * K * W;
-      for (int e = threadIdx.x; e < K * W; e += 256) {
-        const int k = e / W, j = e % W;
-        cbT[j * K + k] = book[e];
-      }
-      __syncthreads();
-      for (int k = threadIdx.x; k < K; k += 256) {
-        float s2 = 0.f;
-        for (int j = 0; j < W; ++j) s2 = fmaf(cbT[j * K + k], cbT[j * K + k], s2);
-        nrm[k] = s2;
-      }
-      __syncthreads();
-    }
+      // coalesced reads of codeword k, written transposed
+      if (W % 4 == 0 && W <= 64) {
+        // 16 bytes (dims j0..j0+3) per thread; the W/4 threads of a codeword are
+        // consecutive lanes, whose partial squared norms are added by a
+        // fixed-order butterfly
+        for (int e = threadIdx.x; e < K * W / 4; e += 64 * kRvqWaves) {
+          const int k = e / (W / 4), j0 = 4 * (e % (W / 4));
+          const f32x4 v = *reinterpret_cast<const f32x4*>(book + size_t(k) * W + j0);
+          float s2 = 0.f;
 #pragma unroll
-    for (int t = 0; t < kRvqTilesPerWave; ++t) {
-      float best = __builtin_inff();
-      int bk = 0;
-      for (int kb = 0; kb < K; kb += 32) {
-        f32x16 acc = f32x16{};
-#pragma unroll
-        for (int s = 0; s < H; ++s) acc = mfma_f32_32x32x2(cbT[(h * H + s) * K + kb + l32], res[t][s], acc);
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int k = kb + mfma32_row(v, h);
-          const float sc = nrm[k] - 2.f * acc[v];
-          if (sc < best) {
-            best = sc;
-            bk = k;
+          for (int q = 0; q < 4; ++q) {
+            cbT[(j0 + q) * P + k] = v[q];
+            s2 = fmaf(v[q], v[q], s2);
           }
+#pragma unroll
+          for (int off = 1; off < W / 4; off <<= 1) s2 += __shfl_xor(s2, off);
+          if (j0 == 0) nrm[k] = s2;
+        }
+        __syncthreads();
+      } else {
+        for (int e = threadIdx.x; e < K * W; e += 64 * kRvqWaves) cbT[(e % W) * P + e / W] = book[e];
+        __syncthreads();
+        for (int k = threadIdx.x; k < K; k += 64 * kRvqWaves) {
+          float s2 = 0.f;
+#pragma unroll
+          for (int j = 0; j < W; ++j) s2 = fmaf(cbT[j * P + k], cbT[j * P + k], s2);
+          nrm[k] = s2;
+        }
+        __syncthreads();
+      }
+    }
+    float b[H];
+#pragma unroll
+    for (int s = 0; s < H; ++s) b[s] = -2.f * res[s];
+    float best = __builtin_inff();
+    int bk = 0;
+    // accumulator row 8 q + 4 h + e (e < 4) starts at that codeword's squared norm
+    auto init = [&](int kb) {
+      f32x16 acc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 nv = *reinterpret_cast<const f32x4*>(nrm + kb + 8 * q + 4 * h);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * q + e] = nv[e];
+      }
+      return acc;
+    };
+    auto pick = [&](const f32x16& acc, int kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        if (acc[v] < best) {
+          best = acc[v];
+          bk = kb + mfma32_row(v, h);
         }
       }
-      const float ob = __shfl_xor(best, 32);
-      const int ok = __shfl_xor(bk, 32);
-      if (ob < best || (ob == best && ok < bk)) {
-        best = ob;
-        bk = ok;
-      }
-      const int n = tok_base + t * 32 + l32;
-      if (h == 0 && n < N) codes[(size_t(n) * R + rho) * G + g] = uint8_t(bk);
+    };
+    int kb = 0;
+    // two blocks of 32 codewords at a time: two independent accumulator chains
+    for (; kb + 64 <= K; kb += 64) {
+      f32x16 acc0 = init(kb), acc1 = init(kb + 32);
+      float a0[H], a1[H];
 #pragma unroll
-      for (int s = 0; s < H; ++s) res[t][s] -= cbT[(h * H + s) * K + bk];
+      for (int s = 0; s < H; ++s) {
+        a0[s] = cbT[(h * H + s) * P + kb + l32];
+        a1[s] = cbT[(h * H + s) * P + kb + 32 + l32];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // every operand read ahead of the first multiply
+#pragma unroll
+      for (int s = 0; s < H; ++s) {
+        acc0 = mfma_f32_32x32x2(a0[s], b[s], acc0);
+        acc1 = mfma_f32_32x32x2(a1[s], b[s], acc1);
+      }
+      pick(acc0, kb);
+      pick(acc1, kb + 32);
     }
+    if (kb < K) {  // K % 64 == 32: the last 32 codewords
+      f32x16 acc = init(kb);
+#pragma unroll
+      for (int s = 0; s < H; ++s) acc = mfma_f32_32x32x2(cbT[(h * H + s) * P + kb + l32], b[s], acc);
+      pick(acc, kb);
+    }
+    const float ob = __shfl_xor(best, 32);
+    const int ok = __shfl_xor(bk, 32);
+    if (ob < best || (ob == best && ok < bk)) {
+      best = ob;
+      bk = ok;
+    }
+    if (h == 0 && n < N) codes[(size_t(n) * R + rho) * G + g] = uint8_t(bk);
+#pragma unroll
+    for (int s = 0; s < H; ++s) res[s] -= cbT[(h * H + s) * P + bk];
   }
 }
 
 template <int W>
 static void rvq_encode_w(const void* Z, int z_bf16, const float* C, int64_t stride, uint8_t* codes, int N, int r,
                          int G, int K, int R, hipStream_t s) {
-  const int tpb = 4 * kRvqTilesPerWave * 32;
+  const int tpb = kRvqWaves * 32;
   dim3 grid(G, (N + tpb - 1) / tpb);
-  const size_t lds = (size_t(W) * K + K) * sizeof(float);
+  const size_t lds = (size_t(W) * (K + 2) + K) * sizeof(float);
   if (z_bf16)
-    hipLaunchKernelGGL((k_rvq_encode<W, bf16_t>), grid, dim3(256), lds, s, static_cast<const bf16_t*>(Z), C, stride,
-                       codes, N, r, G, K, R);
+    hipLaunchKernelGGL((k_rvq_encode<W, bf16_t>), grid, dim3(64 * kRvqWaves), lds, s, static_cast<const bf16_t*>(Z),
+                       C, stride, codes, N, r, G, K, R);
   else
-    hipLaunchKernelGGL((k_rvq_encode<W, float>), grid, dim3(256), lds, s, static_cast<const float*>(Z), C, stride,
-                       codes, N, r, G, K, R);
+    hipLaunchKernelGGL((k_rvq_encode<W, float>), grid, dim3(64 * kRvqWaves), lds, s, static_cast<const float*>(Z), C,
+                       stride, codes, N, r, G, K, R);
 }
 
 void launch_rvq_encode(const void* Z, int z_bf16, const float* C, int64_t stride, uint8_t* codes, int N, int r, int G,
@@ -118,34 +191,64 @@ void launch_rvq_encode(const void* Z, int z_bf16, const float* C, int64_t stride
   }
 }
 
-// Decode: Zq[n][g*W + j] = sum_rho C[rho*stride + (g*K + code)*W + j], rounds in order.
-template <typename OT>
+// Decode: Zq[n][g*W + j] = sum_rho C[rho*stride + (g*K + code)*W + j], rounds in
+// order.  A thread owns CH consecutive outputs of one (token, group): it reads
+// the R codes once and moves its codeword slices as 16-byte vectors.
+template <typename OT, int CH>
 __global__ __launch_bounds__(256) void k_rvq_decode(const uint8_t* __restrict__ codes, const float* __restrict__ C,
                                                     int64_t stride, OT* __restrict__ Zq, int N, int r, int G, int K,
                                                     int R) {
-  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= int64_t(N) * r) return;
-  const int n = int(e / r), col = int(e % r);
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;  // chunk index
+  const int per_tok = r / CH;
+  if (e >= int64_t(N) * per_tok) return;
+  const int n = int(e / per_tok), col = int(e % per_tok) * CH;
   const int W = r / G;
   const int g = col / W, j = col % W;
-  float acc = 0.f;
+  float acc[CH];
+#pragma unroll
+  for (int q = 0; q < CH; ++q) acc[q] = 0.f;
   for (int rho = 0; rho < R; ++rho) {
     const int k = codes[(size_t(n) * R + rho) * G + g];
-    if (k < K) acc += C[rho * stride + (size_t(g) * K + k) * W + j];  // a code >= K (corrupt input) adds nothing
+    if (k >= K) continue;  // a code >= K (corrupt input) adds nothing
+    const float* cw = C + rho * stride + (size_t(g) * K + k) * W + j;
+    if (CH >= 4) {
+#pragma unroll
+      for (int q = 0; q < CH; q += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(cw + q);
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) acc[q + e2] += v[e2];
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < CH; ++q) acc[q] += cw[q];
+    }
   }
-  Zq[e] = from_f32<OT>(acc);
+  OT* o = Zq + size_t(n) * r + col;
+#pragma unroll
+  for (int q = 0; q < CH; ++q) o[q] = from_f32<OT>(acc[q]);
 }
 
 void launch_rvq_decode(const uint8_t* codes, const float* C, int64_t stride, void* Zq, int out_bf16, int N, int r,
                        int G, int K, int R, hipStream_t s) {
-  const int64_t tot = int64_t(N) * r;
+  const int W = r / G;
+  const int CH = (W % 8 == 0) ? 8 : (W % 4 == 0) ? 4 : (W % 2 == 0) ? 2 : 1;
+  const int64_t tot = int64_t(N) * r / CH;
   dim3 grid(unsigned((tot + 255) / 256));
-  if (out_bf16)
-    hipLaunchKernelGGL(k_rvq_decode<bf16_t>, grid, dim3(256), 0, s, codes, C, stride, static_cast<bf16_t*>(Zq), N, r,
-                       G, K, R);
-  else
-    hipLaunchKernelGGL(k_rvq_decode<float>, grid, dim3(256), 0, s, codes, C, stride, static_cast<float*>(Zq), N, r, G,
-                       K, R);
+#define MAPL_DEC(OTv, CHv)                                                                                         \
+  hipLaunchKernelGGL((k_rvq_decode<OTv, CHv>), grid, dim3(256), 0, s, codes, C, stride, static_cast<OTv*>(Zq), N, r, \
+                     G, K, R)
+  if (out_bf16) {
+    if (CH == 8) MAPL_DEC(bf16_t, 8);
+    else if (CH == 4) MAPL_DEC(bf16_t, 4);
+    else if (CH == 2) MAPL_DEC(bf16_t, 2);
+    else MAPL_DEC(bf16_t, 1);
+  } else {
+    if (CH == 8) MAPL_DEC(float, 8);
+    else if (CH == 4) MAPL_DEC(float, 4);
+    else if (CH == 2) MAPL_DEC(float, 2);
+    else MAPL_DEC(float, 1);
+  }
+#undef MAPL_DEC
 }
 
 // Stream apply: C[idx[q]*W + j] = vals[q*W + j]; a later duplicate of idx[q]
