@@ -173,24 +173,6 @@ __global__ __launch_bounds__(256) void k_tok_reduce(const bf16_t* __restrict__ X
 //   c + S - 1.  Copies past the last chunk repeat it into a slot never read.
 constexpr int kRedKC = 64;  // channels per chunk
 
-// Lane l copies 16 bytes from g to LDS byte address (l_base + 16 l); l_base is
-// uniform over the wave.  Written as inline assembly: the compiler would
-// otherwise treat every such copy as a possible write to any LDS the later
-// copies and reads touch and wait for all of them, and the ring's order is
-// kept here by explicit vmcnt waits and barriers instead.  The "memory"
-// clobber keeps every LDS access of the program on its side of the copy.
-__device__ __forceinline__ void copy16_to_lds(const void* g, const void* l_base) {
-  const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(l_base)));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(la) : "memory", "m0");
-}
-
-// s_waitcnt with only the vector-memory counter limited (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
 template <int RBW, int S>
 struct RedRing {
   static constexpr int XU = 64 * kRedKC * 2 / 16;  // 16-byte units of token rows per slot
@@ -357,6 +339,7 @@ void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32
                             const uint16_t* QnF, uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
   // ANCHOR = true is the compress map of Eq. (1); false is the plain product (gZ = gXhat A)
   const bool anc = E != nullptr;
+  if (r >= 512 && launch_tok_gemm_bf16(in, d, tids, V, E, anc ? r : 0, AtF, QnF, out, N, r, s)) return;
   if (r == 128) {
     if (anc) launch_reduce_dma<1, 6, 2, true>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
     else launch_reduce_dma<1, 6, 2, false>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
@@ -537,6 +520,7 @@ __global__ __launch_bounds__(256, 2) void k_tok_expand(const bf16_t* __restrict_
 
 void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_t* tids, const uint16_t* E,
                             const uint16_t* PtF, uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
+  if (r >= 256 && launch_tok_gemm_bf16(in, r, tids, V, E, E != nullptr ? r : 0, AF, PtF, out, N, d, s)) return;
   const int S = (E != nullptr) ? r / 8 : r / 16;  // K-steps
   const int UR = 2 * S;                            // 16-byte units per token row (a power of two)
   int ur_log2 = 0;

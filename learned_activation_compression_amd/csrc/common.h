@@ -77,4 +77,23 @@ __device__ __forceinline__ int xcd_swizzle(int bid, int total) {
   return (bid & 7) * (total >> 3) + (bid >> 3);
 }
 
+// Lane l copies 16 bytes from g to LDS byte address (l_base + 16 l); l_base is
+// uniform over the wave.  Written as inline assembly: the compiler would
+// otherwise treat every such copy as a possible write to any LDS the later
+// copies and reads touch and wait for all of them, and the ring's order is
+// kept here by explicit vmcnt waits and barriers instead.  The "memory"
+// clobber keeps every LDS access of the program on its side of the copy.
+__device__ __forceinline__ void copy16_to_lds(const void* g, const void* l_base) {
+  const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)(l_base)));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(la) : "memory", "m0");
+}
+
+// s_waitcnt with only the vector-memory counter limited (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+
 }  // namespace mapl

@@ -48,6 +48,12 @@ void launch_reduce_partials(const float* part, int splits, int64_t stride, float
 // gA[i][j] -= sum_k P[k][i] M[k][j]  (P bf16 [r][d], M fp32 [r][r], gA fp32 [d][r])
 void launch_sub_ptm(const uint16_t* P, const float* M, float* gA, int d, int r, hipStream_t s);
 
+// token GEMM out[N][C] = [src | E[t]] W with W from the packs F1 (k < K1) and F2
+// (anchor rows, K2 of them; E == nullptr or K2 == 0 drops them).  Returns false,
+// launching nothing, for shapes it does not cover (K1, K2 % 64, C % 128).
+bool launch_tok_gemm_bf16(const uint16_t* src, int K1, const int32_t* tids, int V, const uint16_t* E, int K2,
+                          const uint16_t* F1, const uint16_t* F2, uint16_t* out, int N, int C, hipStream_t s);
+
 // ---- fp32 codec (small problems, plain fp32 arithmetic)
 void launch_compress_f32(const float* X, const int32_t* tids, const float* E, const float* P,
                          const float* A, float* Z, int N, int d, int r, int V, hipStream_t s);
