@@ -183,7 +183,7 @@ int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A, void* 
     launch_tok_reduce_bf16(static_cast<const uint16_t*>(gXhat), v.AtF, nullptr, nullptr, nullptr,
                            static_cast<uint16_t*>(gZ), int(N), int(d), int(r), 1, stream);
     // gA (+)= gXhat^T Z
-    launch_gram_bf16(static_cast<const uint16_t*>(gXhat), d, false, int(d), nullptr, 1, nullptr, 0,
+    launch_gram_bf16(static_cast<const uint16_t*>(gXhat), d, int(d), nullptr, 1, nullptr, 0,
                      static_cast<const uint16_t*>(Z), int(r), part, int(N), S, stream);
     launch_reduce_partials(part, S, d * r, gA, d * r, accumulate, nullptr, 0, stream);
   }
@@ -231,7 +231,7 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const 
                          stream);
   // gA (+)= X^T gZ - P^T (E[t]^T gZ): one Gram over the rows of [X | E[t]], then
   // the split sums (rows < d into gA, rows >= d into M) and gA -= P^T M
-  launch_gram_bf16(static_cast<const uint16_t*>(X), d, false, int(d), tids, int(V),
+  launch_gram_bf16(static_cast<const uint16_t*>(X), d, int(d), tids, int(V),
                    static_cast<const uint16_t*>(E_small), int(r), gZ16, int(r), part, int(N), S, stream);
   launch_reduce_partials(part, S, (d + r) * r, gA, d * r, accumulate, M, r * r, stream);
   launch_sub_ptm(static_cast<const uint16_t*>(P), M, gA, int(d), int(r), stream);

@@ -547,9 +547,8 @@ void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_
 
 // ------------------------------------------------------------------ gram --
 // part[s][i][j] = sum over the tokens n of split s of L[n][i] R[n][j] for
-// i < Ld + Le, j < Rd.  Row i < Ld of L is in[n][i] (LT = false, in is
-// [N][ldin]) or in[i][n] (LT = true, in is L^T = [Ld][ldin], as P is for
-// P A); row Ld + q is E[tids[n]][q] (zero for an id outside [0, V)).
+// i < Ld + Le, j < Rd.  Row i < Ld of L is in[n][i] (in is [N][ldin]); row
+// Ld + q is E[tids[n]][q] (zero for an id outside [0, V)).
 //
 // Block: 128 rows x TJ columns of one token split; the 4 waves tile it as
 // WI x WJ (64 x 64 each for TJ = 128).  Tokens stream in chunks of 64 through
@@ -575,7 +574,7 @@ __device__ __forceinline__ void transpose8x8_b16(const u32x4 (&v)[8], u32x4 (&o)
   }
 }
 
-template <int TJ, bool LT>
+template <int TJ>
 __global__ __launch_bounds__(256) void k_gram2(const bf16_t* __restrict__ in, int64_t ldin, int Ld,
                                                const int32_t* __restrict__ tids, int V,
                                                const bf16_t* __restrict__ E, int Le, const bf16_t* __restrict__ R,
@@ -605,17 +604,14 @@ __global__ __launch_bounds__(256) void k_gram2(const bf16_t* __restrict__ in, in
   uint32_t mk[D];  // bit e: element e of v[u] is real data (else it is zeroed when staged)
   int tq[D][8];    // anchor rows: token ids of the chunk D ahead of the one in v[u]
   // an anchor-row tile (rows >= Ld come from E[tids]); uniform over the block
-  const bool tileE = __builtin_amdgcn_readfirstlane(int(!LT && Le > 0 && i0 >= Ld)) != 0;
+  const bool tileE = __builtin_amdgcn_readfirstlane(int(Le > 0 && i0 >= Ld)) != 0;
   const bool roleL = wave < 2;             // waves 0-1 stage L, waves 2-3 stage R (uniform per wave)
   const bool active = roleL || isR;        // lanes of waves 2-3 past the TJ columns stage nothing
   const bool insideE = srow < rows;
   // element e of a load is row idx_e of `base` (stride `stride`)
   const bf16_t* base;
   int64_t stride;
-  if (roleL && LT) {
-    base = in;
-    stride = ldin;
-  } else if (roleL && tileE) {
+  if (roleL && tileE) {
     base = E + (insideE ? srow - Ld : 0);
     stride = Le;
   } else if (roleL) {
@@ -639,14 +635,7 @@ __global__ __launch_bounds__(256) void k_gram2(const bf16_t* __restrict__ in, in
   auto load = [&](u32x4 (&w)[8], uint32_t& m, int (&t)[8], int rb, int c) {
     const int n0 = rb + c * kGramTok + 8 * tg;
     m = 0u;
-    if (roleL && LT) {  // the 8 tokens are the columns of rows srow..srow+7
-      const int nn = min(n0, ne - 8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        w[e] = *reinterpret_cast<const u32x4*>(base + size_t(min(srow + e, Ld - 1)) * stride + nn);
-        m |= uint32_t((srow + e < Ld) && (n0 < ne)) << e;
-      }
-    } else if (roleL && tileE) {
+    if (roleL && tileE) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const bool ok = insideE && (n0 + e < ne) && t[e] >= 0 && t[e] < V;
@@ -668,15 +657,10 @@ __global__ __launch_bounds__(256) void k_gram2(const bf16_t* __restrict__ in, in
 #pragma unroll
     for (int e = 0; e < 8; ++e) x[e] = ((m >> e) & 1u) ? w[e] : u32x4{0u, 0u, 0u, 0u};
     u32x4* dst = sm + b * BUF + (roleL ? 0 : 128 * 8) + 8 * g * 8;  // row 8 g of the L or R part
-    if (roleL && LT) {
+    u32x4 o[8];
+    transpose8x8_b16(x, o);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) dst[q * 8 + (tg ^ q)] = x[q];
-    } else {
-      u32x4 o[8];
-      transpose8x8_b16(x, o);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) dst[q * 8 + (tg ^ q)] = o[q];
-    }
+    for (int q = 0; q < 8; ++q) dst[q * 8 + (tg ^ q)] = o[q];
   };
 
   f32x16 acc[MI][MJ];
@@ -745,26 +729,19 @@ int gram_splits_bf16(int N, int rows, int Rd) {
   return s;
 }
 
-void launch_gram_bf16(const uint16_t* in, int64_t ldin, bool LT, int Ld, const int32_t* tids, int V,
-                      const uint16_t* E, int Le, const uint16_t* R, int Rd, float* part, int N, int splits,
-                      hipStream_t s) {
+void launch_gram_bf16(const uint16_t* in, int64_t ldin, int Ld, const int32_t* tids, int V, const uint16_t* E,
+                      int Le, const uint16_t* R, int Rd, float* part, int N, int splits, hipStream_t s) {
   int tps = (N + splits - 1) / splits;
   tps = (tps + kGramRound - 1) / kGramRound * kGramRound;
   const int TJ = Rd >= 128 ? 128 : Rd;
   const int ti = (Ld + Le + 127) / 128, tj = Rd / TJ;
   const dim3 grid(unsigned(ti * tj * splits));
-#define MAPL_GRAM(TJv, LTv)                                                                                      \
-  hipLaunchKernelGGL((k_gram2<TJv, LTv>), grid, dim3(256), 0, s, in, ldin, Ld, tids, V, E, Le, R, Rd, part, N, tps, \
-                     ti, tj)
-  if (LT) {
-    if (TJ == 128) MAPL_GRAM(128, true);
-    else if (TJ == 64) MAPL_GRAM(64, true);
-    else MAPL_GRAM(32, true);
-  } else {
-    if (TJ == 128) MAPL_GRAM(128, false);
-    else if (TJ == 64) MAPL_GRAM(64, false);
-    else MAPL_GRAM(32, false);
-  }
+#define MAPL_GRAM(TJv)                                                                                      \
+  hipLaunchKernelGGL((k_gram2<TJv>), grid, dim3(256), 0, s, in, ldin, Ld, tids, V, E, Le, R, Rd, part, N, tps, ti, \
+                     tj)
+  if (TJ == 128) MAPL_GRAM(128);
+  else if (TJ == 64) MAPL_GRAM(64);
+  else MAPL_GRAM(32);
 #undef MAPL_GRAM
 }
 

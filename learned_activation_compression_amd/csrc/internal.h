@@ -34,13 +34,11 @@ void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_
                             const uint16_t* E, const uint16_t* PtF, uint16_t* out,
                             int N, int d, int r, int V, hipStream_t s);
 // token-split partial Gram: part[s][i][j] = sum_{n in split s} L[n][i] R[n][j] for
-// i < Ld + Le, j < Rd.  Row i < Ld of L is in[n][i] (LT false, in [N][ldin]) or
-// in[i][n] (LT true, in [Ld][ldin]); row Ld + q is E[tids[n]][q] (zero for an
-// invalid id).  R is [N][Rd].  part is [splits][Ld + Le][Rd] fp32.
+// i < Ld + Le, j < Rd.  Row i < Ld of L is in[n][i] (in [N][ldin]); row Ld + q is
+// E[tids[n]][q] (zero for an invalid id).  R is [N][Rd].  part is [splits][Ld + Le][Rd].
 int gram_splits_bf16(int N, int rows, int Rd);
-void launch_gram_bf16(const uint16_t* in, int64_t ldin, bool LT, int Ld, const int32_t* tids, int V,
-                      const uint16_t* E, int Le, const uint16_t* R, int Rd, float* part, int N, int splits,
-                      hipStream_t s);
+void launch_gram_bf16(const uint16_t* in, int64_t ldin, int Ld, const int32_t* tids, int V, const uint16_t* E,
+                      int Le, const uint16_t* R, int Rd, float* part, int N, int splits, hipStream_t s);
 // fixed-order split sums: e < n0 -> out0[e] (+= when acc0), else out1[e - n0];
 // split k of element e at part[k * stride + e]; n0, n1, stride multiples of 4
 void launch_reduce_partials(const float* part, int splits, int64_t stride, float* out0, int64_t n0, int acc0,

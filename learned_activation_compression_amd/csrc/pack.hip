@@ -78,46 +78,94 @@ void launch_pack_PtF(const uint16_t* P, uint16_t* PtF, int d, int r, hipStream_t
   frag_pack(P, /*sm*/ 1, /*sk*/ d, d, r, PtF, s);  // W(m, k) = P[k][m]
 }
 
-// QnF from the split partials of P A: W(j, k) = -(P A)[k][j] = -sum_s part[s][k][j],
-// rounded once to bf16, written in fragment order (M = K = r).
-__global__ __launch_bounds__(256) void k_qn_finalize(const float* __restrict__ part, int S, bf16_t* __restrict__ QnF,
-                                                     int r) {
-  const int u = blockIdx.x * 256 + threadIdx.x;
-  const int MB = r / 32;
-  if (u >= (r / 16) * MB * 64) return;
-  const int l = u & 63, frag = u >> 6;
-  const int sidx = frag / MB, mb = frag % MB;
-  const int j = mb * 32 + (l & 31);
-  const int k0 = sidx * 16 + 8 * (l >> 5);
+// The three A / P sections in one launch: unit u of the concatenation
+// [AtF | AF | PtF] (section boundaries at multiples of 64 units).
+__global__ __launch_bounds__(256) void k_frag_pack3(const bf16_t* __restrict__ A, const bf16_t* __restrict__ P,
+                                                    bf16_t* __restrict__ AtF, bf16_t* __restrict__ AF,
+                                                    bf16_t* __restrict__ PtF, int d, int r) {
+  const int64_t u0 = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t n1 = int64_t(d / 16) * (r / 32) * 64, n2 = int64_t(r / 16) * (d / 32) * 64;
+  const bf16_t* src;
+  int64_t sm, sk, u;
+  int M;
+  bf16_t* dst;
+  if (u0 < n1) {
+    src = A, sm = 1, sk = r, M = r, dst = AtF, u = u0;  // W(m, k) = A[k][m]
+  } else if (u0 < n1 + n2) {
+    src = A, sm = r, sk = 1, M = d, dst = AF, u = u0 - n1;  // W(m, k) = A[m][k]
+  } else if (u0 < n1 + 2 * n2) {
+    src = P, sm = 1, sk = d, M = d, dst = PtF, u = u0 - n1 - n2;  // W(m, k) = P[k][m]
+  } else {
+    return;
+  }
+  const int MB = M / 32;
+  const int l = int(u & 63);
+  const int64_t frag = u >> 6;
+  const int st = int(frag / MB), mb = int(frag % MB);
+  const int m = mb * 32 + (l & 31);
+  const int k0 = st * 16 + 8 * (l >> 5);
   uint32_t w[4];
 #pragma unroll
-  for (int e = 0; e < 8; e += 2) {
-    float v[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      float acc = 0.f;
-      for (int s = 0; s < S; ++s) acc += part[size_t(s) * r * r + size_t(k0 + e + q) * r + j];
-      v[q] = -acc;
-    }
-    w[e >> 1] = pack2bf(v[0], v[1]);
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t lo = src[m * sm + int64_t(k0 + 2 * e) * sk];
+    const uint32_t hi = src[m * sm + int64_t(k0 + 2 * e + 1) * sk];
+    w[e] = lo | (hi << 16);
   }
-  reinterpret_cast<u32x4*>(QnF)[u] = u32x4{w[0], w[1], w[2], w[3]};
+  reinterpret_cast<u32x4*>(dst)[u] = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// Full pack.  P A is formed by the split-row bf16 Gram with L = P^T read in
-// place (P is L^T) and R = A, contracting over the d columns of P; its fp32
-// partials live in the AtF section, which is written afterwards.
+// QnF = fragments of W = -(P A)^T (M = K = r), rounded once to bf16.  One block
+// per 32 x 32 tile (i, j) of P A; the 4 waves split the d-long contraction:
+// the matrix-core A operand is 16 bytes of a row of P, the B operand the AtF
+// fragment of the same K-step, and the four partial tiles are added in LDS in
+// a fixed order.
+__global__ __launch_bounds__(256) void k_qn_direct(const bf16_t* __restrict__ P, const bf16_t* __restrict__ AtF,
+                                                   bf16_t* __restrict__ QnF, int d, int r) {
+  __shared__ float red[4 * 1024];
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int hi = lane >> 5, l32 = lane & 31;
+  const int i0 = blockIdx.x * 32, mbj = blockIdx.y;  // rows i0.. of P A, column block mbj
+  const int MB = r / 32;
+  const int S = d / 16, sb = S * w / 4, se = S * (w + 1) / 4;
+  const bf16_t* prow = P + size_t(i0 + l32) * d + 8 * hi;
+  f32x16 acc = f32x16{};
+  for (int s0 = sb; s0 < se; s0 += 8) {
+    bf16x8 a[8], b[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int st = min(s0 + t, se - 1);
+      a[t] = ld_bf16x8(prow + 16 * st);
+      b[t] = ld_bf16x8(AtF + ((size_t(st) * MB + mbj) * 64 + lane) * 8);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+      if (s0 + t < se) acc = mfma_bf16_32x32x16(a[t], b[t], acc);
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) red[w * 1024 + v * 64 + lane] = acc[v];
+  __syncthreads();
+  if (w != 0) return;
+  // lane (column j = mbj*32 + l32) holds rows i = i0 + 8 q + 4 hi + t of P A (t < 4),
+  // which in W = -(P A)^T are elements 4 hi + t of unit ((i >> 4) MB + mbj) 64 + l32 + 32 (q & 1)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int o = (4 * q + t) * 64 + lane;
+      v[t] = -((red[o] + red[1024 + o]) + (red[2048 + o] + red[3072 + o]));
+    }
+    const size_t unit = (size_t((i0 >> 4) + (q >> 1)) * MB + mbj) * 64 + l32 + 32 * (q & 1);
+    *reinterpret_cast<u32x2*>(QnF + unit * 8 + 4 * hi) = u32x2{pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
+  }
+}
+
+// Full pack: the three A / P sections, then QnF from P and the fresh AtF.
 void launch_pack_all(const uint16_t* P, const uint16_t* A, PackView v, int d, int r, hipStream_t s) {
-  int S = gram_splits_bf16(d, r, r);
-  if (S > d / (2 * r)) S = d / (2 * r);  // partials must fit in the AtF section (2 r d bytes)
-  if (S < 1) S = 1;
-  float* part = reinterpret_cast<float*>(v.AtF);
-  launch_gram_bf16(P, d, /*LT*/ true, r, nullptr, 1, nullptr, 0, A, r, part, d, S, s);
-  const int units = (r / 16) * (r / 32) * 64;
-  hipLaunchKernelGGL(k_qn_finalize, dim3((units + 255) / 256), dim3(256), 0, s, part, S, v.QnF, r);
-  launch_pack_AtF(A, v.AtF, d, r, s);
-  launch_pack_AF(A, v.AF, d, r, s);
-  launch_pack_PtF(P, v.PtF, d, r, s);
+  const int64_t units = int64_t(d / 16) * (r / 32) * 64 + 2 * int64_t(r / 16) * (d / 32) * 64;
+  hipLaunchKernelGGL(k_frag_pack3, dim3(unsigned((units + 255) / 256)), dim3(256), 0, s, A, P, v.AtF, v.AF, v.PtF,
+                     d, r);
+  hipLaunchKernelGGL(k_qn_direct, dim3(r / 32, r / 32), dim3(256), 0, s, P, v.AtF, v.QnF, d, r);
 }
 
 }  // namespace mapl
