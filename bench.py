@@ -161,12 +161,15 @@ def counter_traffic():
     summary, or None once the kernel source differs from the one measured."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "compress_150m_hbm_counters.txt")
-    src = os.path.join(ROOT, "learned_activation_compression_amd", "csrc", "codec_bf16.hip")
+    csrc = os.path.join(ROOT, "learned_activation_compression_amd", "csrc")
     try:
         lines = open(path).read().splitlines()
         traffic = int([l for l in lines if l.startswith("traffic_bytes_per_launch:")][0].split(":")[1])
         sha = [l for l in lines if l.startswith("source_sha256")][0].split(":")[1].strip()
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != sha:
+        h = hashlib.sha256()
+        for f in ("codec_bf16.hip", "common.h"):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+        if h.hexdigest() != sha:
             return None
         return traffic
     except (OSError, IndexError, ValueError):
@@ -400,7 +403,7 @@ def main():
     achieved = dom_bytes / dom_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
-                "kernel": "compress (k_tok_reduce<4, 4, true>)", "algorithmic_bytes": dom_bytes,
+                "kernel": "compress (k_tok_reduce_dma<1, 6, 2, true>)", "algorithmic_bytes": dom_bytes,
                 "ms": round(med["compress"], 5)}
     pc = float(np.median(pair_cold))
     pw = float(np.median(pair_warm))
