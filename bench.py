@@ -288,7 +288,14 @@ def run_cases(lac, dev, flush):
         add(f"{tag} reconstruct", _timed(reco, flush), *cnt["reconstruct"], bound, tokens=N)
         add(f"{tag} reconstruct_bwd", _timed(rbwd, flush), *cnt["reconstruct_bwd"], bound, tokens=N)
         add(f"{tag} compress_bwd", _timed(cbwd, flush), *cnt["compress_bwd"], bound, tokens=N)
-        del g, pk, Z, Xh, gZ, gX, gA, ws
+        # sender's anchor-table gradient from gX (Y read once, P, tids, the whole [V][r] table written)
+        V = c["V"]
+        gE = torch.empty((V, r), dtype=torch.float32, device=dev)
+        aws = torch.empty(lac.mapl_anchor_grad_workspace_bytes(c["B"], c["T"], r, V), dtype=torch.uint8, device=dev)
+        agrad = lambda: lac.mapl_anchor_grad(gX, g["tids"], g["P"], V, -1.0, gE=gE, ws=aws)
+        add(f"{tag} anchor_grad", _timed(agrad, flush), 2 * N * d + 4 * N + 2 * r * d + 4 * V * r, 2 * N * d * r,
+            "hbm", tokens=N)
+        del g, pk, Z, Xh, gZ, gX, gA, ws, gE, aws
         return inp
 
     C = synth.CONFIGS

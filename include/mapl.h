@@ -139,6 +139,29 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids,
                       mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Anchor-table gradient (Section 3.2 and Eq. (3): E_small is trainable; its
+ * row t_n enters Eq. (1) as -E[t_n] P A and Eq. (2) as +E'[t_n] P').  For a
+ * d-wide token gradient Y [N][d]:
+ *   gE[v] (+)= alpha * sum over the tokens n with tids[n] == v of Y[n] P^T
+ * - receiver's table (Eq. (2)): Y = gXhat, alpha = +1, P = the receiver's P;
+ * - sender's table (Eq. (1)):   Y = gX = gZ A^T (the gX output of
+ *   mapl_compress_bwd), alpha = -1, since gZ (P A)^T = (gZ A^T) P^T;
+ * - a table shared by both sides: two calls, the second with accumulate = 1.
+ * Y and P use `dt`; gE is fp32 [V][r] (accumulate == 0 overwrites all V rows,
+ * 1 adds).  Tokens whose id is outside [0, V) contribute nothing.  The sums
+ * are exact 64-bit fixed-point accumulations at one power-of-two scale chosen
+ * from max |alpha Y[n] P^T| (every sum fits; each term is rounded once, by
+ * at most N 2^-61 times that maximum), so the result does not depend on the
+ * order of the additions: it is bitwise repeatable.  Inputs must be
+ * finite (alpha non-finite: MAPL_ERR_ARG).  Uses a 16-byte aligned `ws` of
+ * mapl_anchor_grad_workspace_bytes() (MAPL_ERR_ARG if misaligned): N*r fp32
+ * projected rows and a V*r 64-bit accumulator.  Shapes follow the codec
+ * rules (bf16: d % 128 == 0, r a power of two in [32, 512]); V*r <= 2^36, N*r <= 2^38. */
+size_t mapl_anchor_grad_workspace_bytes(int64_t B, int64_t T, int64_t r, int64_t V);
+int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* gE, float alpha,
+                     int accumulate, int64_t B, int64_t T, int64_t d, int64_t r, int64_t V,
+                     mapl_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* Count token ids outside [0, V) into *bad_count (device int32, overwritten). */
 int mapl_check_tids(const int32_t* tids, int64_t N, int64_t V, int32_t* bad_count,
                     hipStream_t stream);

@@ -23,7 +23,8 @@ import torch
 __all__ = [
     "MaplError", "LIB_PATH", "load", "exported_symbols",
     "mapl_pack_bytes", "mapl_pack", "mapl_compress", "mapl_reconstruct",
-    "mapl_bwd_workspace_bytes", "mapl_reconstruct_bwd", "mapl_compress_bwd", "mapl_check_tids",
+    "mapl_bwd_workspace_bytes", "mapl_reconstruct_bwd", "mapl_compress_bwd",
+    "mapl_anchor_grad_workspace_bytes", "mapl_anchor_grad", "mapl_check_tids",
     "rvq_encode", "rvq_decode", "rvq_stream_apply", "spel_workspace_bytes", "spel_step",
     "MAPL_F32", "MAPL_BF16",
 ]
@@ -50,6 +51,8 @@ _SIGS = {
                                     _vp, _sz, _vp]),
     "mapl_compress_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
                                  _vp, _sz, _i32, _vp, _sz, _vp]),
+    "mapl_anchor_grad_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "mapl_anchor_grad": (_i32, [_vp, _vp, _vp, _vp, _f32, _i32, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
     "mapl_check_tids": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "rvq_encode": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
     "rvq_decode": (_i32, [_vp, _vp, _i64, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _vp]),
@@ -263,6 +266,29 @@ def mapl_compress_bwd(gZ, X, tids, E_small, P, A, gX=None, gA=None, accumulate=F
                                     ws.data_ptr() if ws is not None else None, wb, _stream(stream)),
            "mapl_compress_bwd")
     return gX, gA
+
+
+def mapl_anchor_grad_workspace_bytes(B: int, T: int, r: int, V: int) -> int:
+    return int(load().mapl_anchor_grad_workspace_bytes(B, T, r, V))
+
+
+def mapl_anchor_grad(Y, tids, P, V: int, alpha: float = 1.0, gE=None, accumulate=False, ws=None, stream=None):
+    """gE [V, r] fp32 (+)= alpha * scatter-sum over tids of Y P^T.
+
+    Receiver's anchor table: Y = gXhat, alpha = +1.  Sender's: Y = gX (the
+    gX output of mapl_compress_bwd), alpha = -1."""
+    r, d = P.shape
+    B, T = _tokens(Y, d, "Y")
+    dt = _dt(Y)
+    if gE is None:
+        gE = torch.zeros((V, r), dtype=torch.float32, device=Y.device) if accumulate else \
+            _empty((V, r), torch.float32, Y)
+    ws, wb = _ws(ws, int(load().mapl_anchor_grad_workspace_bytes(B, T, r, V)), Y)
+    _check(load().mapl_anchor_grad(_dev(Y, "Y"), _dev(tids, "tids", torch.int32), _dev(P, "P", Y.dtype),
+                                   _dev(gE, "gE", torch.float32), float(alpha), int(bool(accumulate)), B, T, d, r, V,
+                                   dt, ws.data_ptr() if ws is not None else None, wb, _stream(stream)),
+           "mapl_anchor_grad")
+    return gE
 
 
 def mapl_check_tids(tids, V: int, bad=None, stream=None) -> torch.Tensor:

@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmapl.so")
 ARCH = "gfx950"
 
-SOURCES = ["abi.hip", "pack.hip", "codec_bf16.hip", "codec_gemm.hip", "codec_f32.hip", "rvq.hip", "spel.hip"]
+SOURCES = ["abi.hip", "pack.hip", "codec_bf16.hip", "codec_gemm.hip", "codec_f32.hip", "rvq.hip", "spel.hip", "anchor_grad.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops.
 COMMON_FLAGS = [

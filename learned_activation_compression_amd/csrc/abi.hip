@@ -238,6 +238,36 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const 
   return ls.done();
 }
 
+size_t mapl_anchor_grad_workspace_bytes(int64_t B, int64_t T, int64_t r, int64_t V) {
+  if (B < 0 || T < 0 || r < 1 || V < 1 || V > INT32_MAX) return 0;
+  if (B > 0 && T > INT32_MAX / B) return 0;
+  return anchor_grad_ws_bytes(B * T, r, V);
+}
+
+int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* gE, float alpha, int accumulate,
+                     int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, mapl_dtype dt, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  int st = check_codec_shape(B, T, d, r, V, dt, true);
+  if (st) return st;
+  if ((accumulate != 0 && accumulate != 1) || !std::isfinite(alpha)) return MAPL_ERR_ARG;
+  const int64_t N = B * T;
+  if (V * r > (int64_t(1) << 36) || N * r > (int64_t(1) << 38)) return MAPL_ERR_SHAPE;  // 1-D grids
+  if (!gE) return MAPL_ERR_NULL;
+  if (N == 0) {  // empty batch: gE = 0 (or unchanged when accumulating)
+    if (accumulate) return MAPL_OK;
+    LaunchScope ls0;
+    launch_fill_f32(gE, V * r, 0.f, stream);
+    return ls0.done();
+  }
+  if (!Y || !tids || !P) return MAPL_ERR_NULL;
+  if (!ws) return MAPL_ERR_NULL;
+  if (ws_bytes < anchor_grad_ws_bytes(N, r, V)) return MAPL_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) & 15) return MAPL_ERR_ARG;
+  LaunchScope ls;
+  launch_anchor_grad(Y, dt == MAPL_BF16, tids, P, gE, alpha, accumulate, int(N), int(d), int(r), int(V), ws, stream);
+  return ls.done();
+}
+
 int mapl_check_tids(const int32_t* tids, int64_t N, int64_t V, int32_t* bad_count, hipStream_t stream) {
   if (!bad_count || (N > 0 && !tids)) return MAPL_ERR_NULL;
   if (N < 0 || N > INT32_MAX || V < 1 || V > INT32_MAX) return MAPL_ERR_SHAPE;

@@ -67,6 +67,12 @@ void launch_outer_f32(const float* L, const float* R, float* gA, int N, int d, i
 void launch_fill_f32(float* p, int64_t count, float value, hipStream_t s);
 void launch_check_tids(const int32_t* tids, int N, int V, int32_t* bad, hipStream_t s);
 
+// anchor-table gradient: workspace (projected rows, 64-bit accumulator, max
+// cell) and the four launches (zero, project, scatter, finish)
+size_t anchor_grad_ws_bytes(int64_t N, int64_t r, int64_t V);
+void launch_anchor_grad(const void* Y, int y_bf16, const int32_t* tids, const void* P, float* gE, float alpha,
+                        int accumulate, int N, int d, int r, int V, void* ws, hipStream_t s);
+
 // ---- residual VQ
 void launch_rvq_encode(const void* Z, int z_bf16, const float* C, int64_t stride,
                        uint8_t* codes, int N, int r, int G, int K, int R, hipStream_t s);

@@ -20,7 +20,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = lac.exported_symbols()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lac._SIGS), set(names) ^ set(lac._SIGS)
@@ -99,6 +99,31 @@ def test_backward_validation(lib):
              ws, None) == ENULL
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1000, 128, 32000, BF16, FAKE, pk, 1, FAKE,
              ws, None) == ESHAPE
+
+
+def test_anchor_grad_validation(lib):
+    ws = lib.mapl_anchor_grad_workspace_bytes(8, 2048, 128, 32000)
+    assert ws >= 8 * 2048 * 128 * 4 + 32000 * 128 * 8
+    assert lib.mapl_anchor_grad_workspace_bytes(8, 2048, 128, 0) == 0
+    f = lib.mapl_anchor_grad
+
+    def call(Y=FAKE, tids=FAKE, P=FAKE, gE=FAKE, alpha=1.0, acc=0, B=8, T=2048, d=1024, r=128, V=32000, dt=BF16,
+             w=FAKE, wb=ws):
+        return f(Y, tids, P, gE, alpha, acc, B, T, d, r, V, dt, w, wb, None)
+
+    assert call(Y=None) == ENULL
+    assert call(tids=None) == ENULL
+    assert call(gE=None) == ENULL
+    assert call(w=None) == ENULL
+    assert call(wb=ws - 8) == EWS
+    assert call(w=ctypes.c_void_p(0x1008)) == EARG              # ws not 16-B aligned
+    assert call(acc=2) == EARG
+    assert call(alpha=float("inf")) == EARG
+    assert call(d=1000) == ESHAPE                               # bf16 d % 128
+    assert call(r=96) == ESHAPE                                 # bf16 r a power of two
+    assert call(V=0) == ESHAPE
+    assert call(dt=4) == EDTYPE
+    assert call(B=0, acc=1, Y=None, tids=None, P=None, w=None) == OK   # empty batch, accumulate: nothing to do
 
 
 def test_rvq_validation(lib):
