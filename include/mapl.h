@@ -152,11 +152,12 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids,
  * are exact 64-bit fixed-point accumulations at one power-of-two scale chosen
  * from max |alpha Y[n] P^T| (every sum fits; each term is rounded once, by
  * at most N 2^-61 times that maximum), so the result does not depend on the
- * order of the additions: it is bitwise repeatable.  Inputs must be
- * finite (alpha non-finite: MAPL_ERR_ARG).  Uses a 16-byte aligned `ws` of
+ * order of the additions: it is bitwise repeatable.  Inputs must be finite
+ * (alpha non-finite: MAPL_ERR_ARG).  Uses a 16-byte aligned `ws` of
  * mapl_anchor_grad_workspace_bytes() (MAPL_ERR_ARG if misaligned): N*r fp32
- * projected rows and a V*r 64-bit accumulator.  Shapes follow the codec
- * rules (bf16: d % 128 == 0, r a power of two in [32, 512]); V*r <= 2^36, N*r <= 2^38. */
+ * projected rows and 64 KB of partial maxima.  Shapes follow the codec rules
+ * (bf16: d % 128 == 0, r a power of two in [32, 512]); V <= 2^22,
+ * N*r <= 2^38. */
 size_t mapl_anchor_grad_workspace_bytes(int64_t B, int64_t T, int64_t r, int64_t V);
 int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* gE, float alpha,
                      int accumulate, int64_t B, int64_t T, int64_t d, int64_t r, int64_t V,

@@ -239,7 +239,7 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const 
 }
 
 size_t mapl_anchor_grad_workspace_bytes(int64_t B, int64_t T, int64_t r, int64_t V) {
-  if (B < 0 || T < 0 || r < 1 || V < 1 || V > INT32_MAX) return 0;
+  if (B < 0 || T < 0 || r < 1 || V < 1 || V > (int64_t(1) << 22)) return 0;
   if (B > 0 && T > INT32_MAX / B) return 0;
   return anchor_grad_ws_bytes(B * T, r, V);
 }
@@ -251,7 +251,7 @@ int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* g
   if (st) return st;
   if ((accumulate != 0 && accumulate != 1) || !std::isfinite(alpha)) return MAPL_ERR_ARG;
   const int64_t N = B * T;
-  if (V * r > (int64_t(1) << 36) || N * r > (int64_t(1) << 38)) return MAPL_ERR_SHAPE;  // 1-D grids
+  if (V > (int64_t(1) << 22) || N * r > (int64_t(1) << 38)) return MAPL_ERR_SHAPE;
   if (!gE) return MAPL_ERR_NULL;
   if (N == 0) {  // empty batch: gE = 0 (or unchanged when accumulating)
     if (accumulate) return MAPL_OK;

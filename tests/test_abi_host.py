@@ -103,8 +103,9 @@ def test_backward_validation(lib):
 
 def test_anchor_grad_validation(lib):
     ws = lib.mapl_anchor_grad_workspace_bytes(8, 2048, 128, 32000)
-    assert ws >= 8 * 2048 * 128 * 4 + 32000 * 128 * 8
+    assert 8 * 2048 * 128 * 4 <= ws <= 8 * 2048 * 128 * 4 + 2 ** 17   # U rows + partial maxima
     assert lib.mapl_anchor_grad_workspace_bytes(8, 2048, 128, 0) == 0
+    assert lib.mapl_anchor_grad_workspace_bytes(8, 2048, 128, 2 ** 22 + 1) == 0
     f = lib.mapl_anchor_grad
 
     def call(Y=FAKE, tids=FAKE, P=FAKE, gE=FAKE, alpha=1.0, acc=0, B=8, T=2048, d=1024, r=128, V=32000, dt=BF16,
@@ -122,6 +123,7 @@ def test_anchor_grad_validation(lib):
     assert call(d=1000) == ESHAPE                               # bf16 d % 128
     assert call(r=96) == ESHAPE                                 # bf16 r a power of two
     assert call(V=0) == ESHAPE
+    assert call(V=2 ** 22 + 1) == ESHAPE                        # owner blocks scale with V
     assert call(dt=4) == EDTYPE
     assert call(B=0, acc=1, Y=None, tids=None, P=None, w=None) == OK   # empty batch, accumulate: nothing to do
 
