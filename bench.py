@@ -211,16 +211,24 @@ def cpu_baseline(inp, n_tok, reps):
                       f"1024x128) on {n_tok} of the {S.N} tokens, {reps} runs, mean {dt:.2f} s per run"}
 
 
+def _evict(flush):
+    """Evict the inputs from L2 and the 256 MB memory-side cache by reading a
+    1 GiB buffer.  A read leaves only clean lines behind; an evicting write
+    (zero-fill) would leave the memory-side cache full of dirty lines whose
+    write-back then runs inside the next timed region."""
+    if flush is not None:
+        torch.sum(flush)
+
+
 def _timed(fn, flush, iters=20, warm=3):
     """Median / p10 / p90 (ms) of fn() bracketed by HIP events on the current
-    stream, each run after a cache-evicting write (outside the events)."""
+    stream, each run after a cache-evicting read (outside the events)."""
     stream = torch.cuda.current_stream()
     for _ in range(warm):
         fn()
     out = []
     for _ in range(iters):
-        if flush is not None:
-            flush.zero_()
+        _evict(flush)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         fn()
@@ -350,7 +358,7 @@ def main():
     S = Shape
     inp, g = make_inputs(dev)
     b = alloc(g, lac)
-    flush = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    flush = None if args.no_flush else torch.zeros(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
     stream = torch.cuda.current_stream()
 
     if args.copy_calibration:
@@ -369,8 +377,7 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.steps):
-        if flush is not None:
-            flush.zero_()
+        _evict(flush)
         s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s0.record(stream)
         step(lac, g, b, args.warmup + i, ev)
@@ -385,8 +392,7 @@ def main():
     # compress+reconstruct pair, cold (flushed) and warm
     pair_cold, pair_warm = [], []
     for i in range(args.steps):
-        if flush is not None:
-            flush.zero_()
+        _evict(flush)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         pair(lac, g, b)
