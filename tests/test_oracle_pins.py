@@ -123,6 +123,37 @@ def test_anchor_grad_equals_finite_differences():
     np.testing.assert_allclose(gE2, _central_diff(L2, m["E"]), atol=1e-9)
 
 
+def test_anchor_grad_adjoint_identity_and_loops():
+    """Eq. (1) and (2) are affine in E_small, so for any table perturbation dE
+    the pairing <gE, dE> equals the change of <gZ, Z> (sender) and of
+    <gXhat, Xhat> (receiver) exactly; and the scatter is checked against
+    explicit per-token loops, with repeated ids."""
+    m = micro_codec(6, N=9, V=4)
+    rng = np.random.default_rng(60)
+    dE = rng.standard_normal(m["E"].shape)
+    gE = codec.anchor_grad(m["gZ"], m["tids"], m["P"], m["A"], m["V"])
+    dZ = (codec.compress(m["X"], m["tids"], m["E"] + dE, m["P"], m["A"])
+          - codec.compress(m["X"], m["tids"], m["E"], m["P"], m["A"]))
+    assert abs(np.sum(gE * dE) - np.sum(m["gZ"] * dZ)) < 1e-12 * (1 + abs(np.sum(gE * dE)))
+    Zr = rng.standard_normal((m["N"], m["r"]))
+    gE2 = codec.anchor_grad(np.zeros((m["N"], m["r"])), m["tids"], m["P"], m["A"], m["V"], gXhat=m["G"],
+                            P_recv=m["P"])
+    dXh = (codec.reconstruct(Zr, m["tids"], m["E"] + dE, m["P"], m["A"])
+           - codec.reconstruct(Zr, m["tids"], m["E"], m["P"], m["A"]))
+    assert abs(np.sum(gE2 * dE) - np.sum(m["G"] * dXh)) < 1e-12 * (1 + abs(np.sum(gE2 * dE)))
+    # loops: row v collects -gZ[n] (P A)^T over the tokens with id v, plus G[n] P^T
+    both = codec.anchor_grad(m["gZ"], m["tids"], m["P"], m["A"], m["V"], gXhat=m["G"], P_recv=m["P"])
+    want = np.zeros((m["V"], m["r"]))
+    for n in range(m["N"]):
+        v = m["tids"][n]
+        for k in range(m["r"]):
+            pa = [sum(m["P"][k][i] * m["A"][i][j] for i in range(m["d"])) for j in range(m["r"])]
+            want[v][k] -= sum(m["gZ"][n][j] * pa[j] for j in range(m["r"]))
+            want[v][k] += sum(m["G"][n][i] * m["P"][k][i] for i in range(m["d"]))
+    assert len(set(m["tids"].tolist())) < m["N"]  # some id repeats
+    np.testing.assert_allclose(both, want, atol=1e-12)
+
+
 def test_stiefel_projector_inputs_and_idempotence():
     """A^T A = I (Section 3.2) for the generated projector; Z A^T A = Z."""
     inp = synth.codec_inputs(1, 64, 256, 32, 1000, "f32")
