@@ -315,7 +315,7 @@ def run_cases(lac, dev, flush):
     # residual VQ at r=256, G=8 x w=32, K=256, R=2 on Z from the codec
     c = C["rvq"]
     N, d, r, G, K, R = c["B"] * c["T"], c["d"], c["r"], c["G"], c["K"], c["R"]
-    inp = synth.codec_inputs(c["seed"], N, d, r, c["V"], "bf16", with_grad=False)
+    inp = synth.codec_inputs(c["seed"], N, d, r, c["V"], "bf16")
     g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     Z = lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"])
     Cb = synth.rvq_codebooks(c["seed"], 1, G, K, r // G, c["codebook_var"]).to(dev)
@@ -327,7 +327,19 @@ def run_cases(lac, dev, flush):
         N * 2 * r * K * R, "mfma", tokens=N, peak_tf=F32_PEAK_TFLOPS)
     add("rvq r256 G8 K256 R2 decode (fp32)", _timed(dec, flush), N * (R * G + 4 * r) + Cb.numel() * 4,
         N * r * R, "hbm", tokens=N, peak_tf=F32_PEAK_TFLOPS)
-    del g, Z, Cb, codes, Zq
+    # the backward gradient gZ = gXhat A in the paper's grouping: 128 groups of width 2, K = 256, R = 2
+    # (256 code bytes per token); the distance loop is vector-ALU work, not matrix-core work
+    gZ, _ = lac.mapl_reconstruct_bwd(g["gXhat"], Z, g["A"])
+    G2 = r // 2
+    C2 = synth.rvq_codebooks(c["seed"], 1, G2, K, 2, 1.0, sub=1).to(dev)
+    codes2 = torch.empty((N, R, G2), dtype=torch.uint8, device=dev)
+    enc2 = lambda: lac.rvq_encode(gZ, C2, G2, K, R, codes=codes2)
+    dec2 = lambda: lac.rvq_decode(codes2, C2, G2, K, R, r, Zq=Zq)
+    add("rvq gZ r256 G128 (w2) K256 R2 encode", _timed(enc2, flush), N * (2 * r + R * G2) + C2.numel() * 4,
+        N * 2 * r * K * R, "alu", tokens=N, peak_tf=F32_PEAK_TFLOPS)
+    add("rvq gZ r256 G128 (w2) K256 R2 decode", _timed(dec2, flush), N * (R * G2 + 4 * r) + C2.numel() * 4,
+        N * r * R, "hbm", tokens=N, peak_tf=F32_PEAK_TFLOPS)
+    del g, Z, Cb, codes, Zq, gZ, C2, codes2
 
     # one spel_step on the fp32 2048 x 256 projector
     c = C["1b"]

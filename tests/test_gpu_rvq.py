@@ -54,6 +54,37 @@ def test_rvq_config_full_size(R_c):
     assert e[1] <= e[0] and e[2] <= e[1]
 
 
+@pytest.mark.parametrize("G,var,step", [(8, 1.0 / 32.0, 1), (128, 1.0, 4)])
+def test_rvq_of_the_backward_gradient(G, var, step):
+    """Section 3.5 quantizes the backward gradients too: gZ = gXhat A from the
+    receiver's backward map at the RVQ workload (r = 256, K = 256, R = 2),
+    grouped as configured (G = 8 x w = 32) and as in the paper's Table 1
+    (G = 128 x w = 2, 2 rounds: 256 code bytes per token).  Codebooks match
+    the scale of gZ (unit variance per entry for w = 2).  Tokens are
+    independent, so at w = 2 the oracle checks every `step`-th token."""
+    c = synth.CONFIGS["rvq"]
+    N, r, K, R = c["B"] * c["T"], c["r"], c["K"], c["R"]
+    inp = synth.codec_inputs(c["seed"], N, c["d"], r, c["V"], "bf16")
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    Z = lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"])
+    gZ, _ = lac.mapl_reconstruct_bwd(g["gXhat"], Z, g["A"])
+    C = synth.rvq_codebooks(c["seed"], 1, G, K, r // G, var, sub=1).to(DEV)
+    codes = lac.rvq_encode(gZ, C, G, K, R)
+    Zq = lac.rvq_decode(codes, C, G, K, R, r)
+    torch.cuda.synchronize()
+    assert codes.shape == (N, R, G) and codes.dtype == torch.uint8
+    if G == 128:
+        assert codes[0].numel() == 256  # Table 1's payload per token
+    sel = np.arange(0, N, step)
+    gc = codes.cpu().numpy()[sel]
+    ora = rvq.encode(np64(gZ)[sel], np64(C), G, K, R, teacher=gc)
+    n_mis = check_codes(gc, ora, f"gZ G={G}")
+    assert n_mis <= max(4, gc.size // 100000), n_mis
+    assert_close(np64(Zq)[sel], rvq.decode(gc, np64(C), G, K, R), F32_TOL, "decode")
+    e = ora["energy"]
+    assert e[1] <= e[0] and e[2] <= e[1]
+
+
 @pytest.mark.parametrize("w,K,R,R_c,N", [(2, 256, 2, 1, 1000), (4, 64, 3, 3, 333), (8, 32, 1, 1, 70),
                                          (16, 128, 2, 2, 513), (32, 256, 2, 1, 4097), (64, 32, 4, 1, 100)])
 def test_rvq_shapes(w, K, R, R_c, N):
