@@ -228,9 +228,69 @@ __global__ __launch_bounds__(256) void k_rvq_decode(const uint8_t* __restrict__ 
   for (int q = 0; q < CH; ++q) o[q] = from_f32<OT>(acc[q]);
 }
 
+// Narrow groups (W = 2 or 4, r % 8 == 0): a thread owns 8 consecutive outputs,
+// i.e. 8 / W whole groups; per round it reads their codes with one load and
+// each codeword as one W-float vector.
+template <typename OT, int W>
+__global__ __launch_bounds__(256) void k_rvq_decode_narrow(const uint8_t* __restrict__ codes,
+                                                           const float* __restrict__ C, int64_t stride,
+                                                           OT* __restrict__ Zq, int N, int r, int G, int K, int R) {
+  constexpr int NG = 8 / W;  // groups per thread
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int per_tok = r / 8;
+  if (e >= int64_t(N) * per_tok) return;
+  const int n = int(e / per_tok), col = int(e % per_tok) * 8;
+  const int g0 = col / W;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  for (int rho = 0; rho < R; ++rho) {
+    const uint8_t* cp = codes + (size_t(n) * R + rho) * G + g0;
+    uint32_t kk;
+    if (NG == 4) kk = *reinterpret_cast<const uint32_t*>(cp);
+    else kk = *reinterpret_cast<const uint16_t*>(cp);
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int k = int((kk >> (8 * i)) & 0xffu);
+      if (k >= K) continue;  // a code >= K (corrupt input) adds nothing
+      const float* cw = C + rho * stride + (size_t(g0 + i) * K + k) * W;
+      if (W == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(cw);
+        acc[2 * i] += v.x;
+        acc[2 * i + 1] += v.y;
+      } else {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(cw);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[4 * i + q] += v[q];
+      }
+    }
+  }
+  OT* o = Zq + size_t(n) * r + col;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) o[q] = from_f32<OT>(acc[q]);
+}
+
 void launch_rvq_decode(const uint8_t* codes, const float* C, int64_t stride, void* Zq, int out_bf16, int N, int r,
                        int G, int K, int R, hipStream_t s) {
   const int W = r / G;
+  // the narrow path's vector loads need: codes at a multiple of 8 / W bytes, codewords at W * 4 bytes
+  const bool narrow_ok = (W == 2 || W == 4) && r % 8 == 0 && reinterpret_cast<uintptr_t>(codes) % (8 / W) == 0 &&
+                         reinterpret_cast<uintptr_t>(C) % (4 * W) == 0 && stride % W == 0;
+  if (narrow_ok) {
+    dim3 grid(unsigned((int64_t(N) * (r / 8) + 255) / 256));
+#define MAPL_DECN(OTv, Wv)                                                                                     \
+  hipLaunchKernelGGL((k_rvq_decode_narrow<OTv, Wv>), grid, dim3(256), 0, s, codes, C, stride,                   \
+                     static_cast<OTv*>(Zq), N, r, G, K, R)
+    if (out_bf16) {
+      if (W == 2) MAPL_DECN(bf16_t, 2);
+      else MAPL_DECN(bf16_t, 4);
+    } else {
+      if (W == 2) MAPL_DECN(float, 2);
+      else MAPL_DECN(float, 4);
+    }
+#undef MAPL_DECN
+    return;
+  }
   const int CH = (W % 8 == 0) ? 8 : (W % 4 == 0) ? 4 : (W % 2 == 0) ? 2 : 1;
   const int64_t tot = int64_t(N) * r / CH;
   dim3 grid(unsigned((tot + 255) / 256));

@@ -80,7 +80,11 @@ def test_rvq_of_the_backward_gradient(G, var, step):
     ora = rvq.encode(np64(gZ)[sel], np64(C), G, K, R, teacher=gc)
     n_mis = check_codes(gc, ora, f"gZ G={G}")
     assert n_mis <= max(4, gc.size // 100000), n_mis
-    assert_close(np64(Zq)[sel], rvq.decode(gc, np64(C), G, K, R), F32_TOL, "decode")
+    ref = rvq.decode(gc, np64(C), G, K, R)
+    assert_close(np64(Zq)[sel], ref, F32_TOL, "decode")
+    Zq16 = lac.rvq_decode(codes, C, G, K, R, r, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_close(np64(Zq16)[sel], ref, BF16_TOL, "decode bf16")
     e = ora["energy"]
     assert e[1] <= e[0] and e[2] <= e[1]
 
@@ -97,6 +101,26 @@ def test_rvq_shapes(w, K, R, R_c, N):
     Zq = lac.rvq_decode(codes, C, G, K, R, r, round_stride=stride)
     torch.cuda.synchronize()
     assert_close(np64(Zq), rvq.decode(codes.cpu().numpy(), np64(C), G, K, R), F32_TOL, "decode")
+
+
+@pytest.mark.parametrize("w", [2, 4])
+def test_rvq_decode_of_unaligned_codes(w):
+    """Codes starting at an odd byte address take the general decode path and
+    give the same values as the aligned (vector) path."""
+    G, K, R, N = 16, 64, 2, 300
+    r = G * w
+    rng = np.random.default_rng(7 + w)
+    C = torch.from_numpy(rng.standard_normal((1, G, K, w)).astype(np.float32)).to(DEV)
+    codes = torch.from_numpy(rng.integers(0, K, (N, R, G)).astype(np.uint8)).to(DEV)
+    buf = torch.zeros(N * R * G + 1, dtype=torch.uint8, device=DEV)
+    buf[1:] = codes.reshape(-1)
+    odd = buf[1:].view(N, R, G)
+    a = lac.rvq_decode(codes, C, G, K, R, r)
+    b = lac.rvq_decode(odd, C, G, K, R, r)
+    torch.cuda.synchronize()
+    assert odd.data_ptr() % 2 == 1
+    assert torch.equal(a, b)
+    assert_close(np64(a), rvq.decode(codes.cpu().numpy(), np64(C), G, K, R), F32_TOL, "decode")
 
 
 def test_rvq_codeword_inputs_come_back_exactly():
