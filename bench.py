@@ -300,7 +300,7 @@ def run_cases(lac, dev, flush):
         V = c["V"]
         gE = torch.empty((V, r), dtype=torch.float32, device=dev)
         aws = torch.empty(lac.mapl_anchor_grad_workspace_bytes(c["B"], c["T"], r, V), dtype=torch.uint8, device=dev)
-        agrad = lambda: lac.mapl_anchor_grad(gX, g["tids"], g["P"], V, -1.0, gE=gE, ws=aws)
+        agrad = lambda: lac.mapl_anchor_grad(gX, g["tids"], g["P"], V, -1.0, gE=gE, pk=pk, pk_ready=True, ws=aws)
         add(f"{tag} anchor_grad", _timed(agrad, flush), 2 * N * d + 4 * N + 2 * r * d + 4 * V * r, 2 * N * d * r,
             "hbm", tokens=N)
         del g, pk, Z, Xh, gZ, gX, gA, ws, gE, aws

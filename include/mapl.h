@@ -69,8 +69,8 @@ const char* mapl_version(void);
  * Packed weights.
  *
  * The bf16 codec kernels read A and P through a packed copy laid out for the
- * matrix cores: the operands A^T (r x d), A (d x r), P^T (d x r) and
- * -(P A)^T (r x r, formed with fp32 accumulation and rounded once), all bf16
+ * matrix cores: the operands A^T (r x d), A (d x r), P^T (d x r), P (r x d)
+ * and -(P A)^T (r x r, formed with fp32 accumulation and rounded once), all bf16
  * and stored in fragment order, i.e. as the 64-lane x 16-byte pieces one
  * v_mfma_f32_32x32x16_bf16 consumes, so that every weight load of a wave is
  * one contiguous kilobyte.  In training A changes once per optimizer step
@@ -78,7 +78,8 @@ const char* mapl_version(void);
  * Every bf16 codec entry point takes (pk, pk_bytes, pk_ready): with
  * pk_ready == 0 the call first rebuilds the pack from its own P and A
  * arguments (mapl_reconstruct_bwd, which has no P, rebuilds only the A^T
- * part); with pk_ready == 1 the caller guarantees that pk holds
+ * part; mapl_anchor_grad, which has no A, only the P part); with
+ * pk_ready == 1 the caller guarantees that pk holds
  * mapl_pack(P, A) of exactly these matrices.  For dt == MAPL_F32 no pack is
  * used (pk may be NULL and mapl_pack_bytes returns 0).
  * ---------------------------------------------------------------------- */
@@ -151,17 +152,20 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids,
  * 1 adds).  Tokens whose id is outside [0, V) contribute nothing.  The sums
  * are exact 64-bit fixed-point accumulations at one power-of-two scale chosen
  * from max |alpha Y[n] P^T| (every sum fits; each term is rounded once, by
- * at most N 2^-61 times that maximum), so the result does not depend on the
+ * at most 2^-30 times that maximum), so the result does not depend on the
  * order of the additions: it is bitwise repeatable.  Inputs must be finite
- * (alpha non-finite: MAPL_ERR_ARG).  Uses a 16-byte aligned `ws` of
- * mapl_anchor_grad_workspace_bytes() (MAPL_ERR_ARG if misaligned): N*r fp32
- * projected rows and 64 KB of partial maxima.  Shapes follow the codec rules
- * (bf16: d % 128 == 0, r a power of two in [32, 512]); V <= 2^22,
- * N*r <= 2^38. */
+ * (alpha non-finite: MAPL_ERR_ARG).  bf16 reads P through the pack (pk,
+ * pk_bytes, pk_ready as for the codec; pk_ready == 0 rebuilds only its P
+ * part from this P, so a receiver passes the pack of its own P').  Uses a
+ * 16-byte aligned `ws` of mapl_anchor_grad_workspace_bytes() (MAPL_ERR_ARG if
+ * misaligned): N*r fp32 projected rows, partial maxima and the tokens grouped
+ * by owner.  Shapes follow the codec rules (bf16: d % 128 == 0, r a power of
+ * two in [32, 512]); V <= 2^22, N*r <= 2^38. */
 size_t mapl_anchor_grad_workspace_bytes(int64_t B, int64_t T, int64_t r, int64_t V);
 int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* gE, float alpha,
                      int accumulate, int64_t B, int64_t T, int64_t d, int64_t r, int64_t V,
-                     mapl_dtype dt, void* ws, size_t ws_bytes, hipStream_t stream);
+                     mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Count token ids outside [0, V) into *bad_count (device int32, overwritten). */
 int mapl_check_tids(const int32_t* tids, int64_t N, int64_t V, int32_t* bad_count,

@@ -52,7 +52,8 @@ _SIGS = {
     "mapl_compress_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
                                  _vp, _sz, _i32, _vp, _sz, _vp]),
     "mapl_anchor_grad_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
-    "mapl_anchor_grad": (_i32, [_vp, _vp, _vp, _vp, _f32, _i32, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _vp]),
+    "mapl_anchor_grad": (_i32, [_vp, _vp, _vp, _vp, _f32, _i32, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32,
+                                _vp, _sz, _vp]),
     "mapl_check_tids": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "rvq_encode": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
     "rvq_decode": (_i32, [_vp, _vp, _i64, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _vp]),
@@ -272,7 +273,8 @@ def mapl_anchor_grad_workspace_bytes(B: int, T: int, r: int, V: int) -> int:
     return int(load().mapl_anchor_grad_workspace_bytes(B, T, r, V))
 
 
-def mapl_anchor_grad(Y, tids, P, V: int, alpha: float = 1.0, gE=None, accumulate=False, ws=None, stream=None):
+def mapl_anchor_grad(Y, tids, P, V: int, alpha: float = 1.0, gE=None, accumulate=False, pk=None, pk_ready=False,
+                     ws=None, stream=None):
     """gE [V, r] fp32 (+)= alpha * scatter-sum over tids of Y P^T.
 
     Receiver's anchor table: Y = gXhat, alpha = +1.  Sender's: Y = gX (the
@@ -283,10 +285,12 @@ def mapl_anchor_grad(Y, tids, P, V: int, alpha: float = 1.0, gE=None, accumulate
     if gE is None:
         gE = torch.zeros((V, r), dtype=torch.float32, device=Y.device) if accumulate else \
             _empty((V, r), torch.float32, Y)
+    pk, nb = _pk(pk, d, r, dt, Y)
     ws, wb = _ws(ws, int(load().mapl_anchor_grad_workspace_bytes(B, T, r, V)), Y)
     _check(load().mapl_anchor_grad(_dev(Y, "Y"), _dev(tids, "tids", torch.int32), _dev(P, "P", Y.dtype),
                                    _dev(gE, "gE", torch.float32), float(alpha), int(bool(accumulate)), B, T, d, r, V,
-                                   dt, ws.data_ptr() if ws is not None else None, wb, _stream(stream)),
+                                   dt, pk.data_ptr() if pk is not None else None, nb, int(bool(pk_ready)),
+                                   ws.data_ptr() if ws is not None else None, wb, _stream(stream)),
            "mapl_anchor_grad")
     return gE
 

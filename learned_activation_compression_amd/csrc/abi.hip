@@ -245,11 +245,12 @@ size_t mapl_anchor_grad_workspace_bytes(int64_t B, int64_t T, int64_t r, int64_t
 }
 
 int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* gE, float alpha, int accumulate,
-                     int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, mapl_dtype dt, void* ws, size_t ws_bytes,
-                     hipStream_t stream) {
+                     int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, mapl_dtype dt, void* pk, size_t pk_bytes,
+                     int pk_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
   int st = check_codec_shape(B, T, d, r, V, dt, true);
   if (st) return st;
-  if ((accumulate != 0 && accumulate != 1) || !std::isfinite(alpha)) return MAPL_ERR_ARG;
+  if ((accumulate != 0 && accumulate != 1) || (pk_ready != 0 && pk_ready != 1) || !std::isfinite(alpha))
+    return MAPL_ERR_ARG;
   const int64_t N = B * T;
   if (V > (int64_t(1) << 22) || N * r > (int64_t(1) << 38)) return MAPL_ERR_SHAPE;
   if (!gE) return MAPL_ERR_NULL;
@@ -260,11 +261,19 @@ int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* g
     return ls0.done();
   }
   if (!Y || !tids || !P) return MAPL_ERR_NULL;
+  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
   if (!ws) return MAPL_ERR_NULL;
   if (ws_bytes < anchor_grad_ws_bytes(N, r, V)) return MAPL_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) & 15) return MAPL_ERR_ARG;
   LaunchScope ls;
-  launch_anchor_grad(Y, dt == MAPL_BF16, tids, P, gE, alpha, accumulate, int(N), int(d), int(r), int(V), ws, stream);
+  const uint16_t* PF = nullptr;
+  if (dt == MAPL_BF16) {
+    PackView v = pack_view(pk, d, r);
+    if (!pk_ready) launch_pack_PF(static_cast<const uint16_t*>(P), v.PF, int(d), int(r), stream);
+    PF = v.PF;
+  }
+  launch_anchor_grad(Y, dt == MAPL_BF16, tids, P, PF, gE, alpha, accumulate, int(N), int(d), int(r), int(V), ws,
+                     stream);
   return ls.done();
 }
 

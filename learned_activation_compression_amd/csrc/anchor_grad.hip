@@ -7,18 +7,20 @@
 // pulled back through P:  gE[v] = alpha * sum_{n : t_n = v} Y[n] P^T.
 //
 // Two launches:
-//   project  U[n] = alpha Y[n] P^T (fp32 [N][r]) on the matrix cores, plus
-//            one max |U| per block (no atomics: a chain of atomics on one
-//            address serialises);
-//   own      each block owns the ids v with v % B == b (B blocks: frequent
-//            ids, which tokenizers give small numbers, land in different
-//            blocks) and one 64-column slice.  It reads every token id,
-//            queues its own tokens in LDS, adds their U rows into an LDS
-//            table of 64-bit integers at one power-of-two scale 2^e taken from
-//            the global max |U| and N, and writes its gE rows.  Integer
-//            addition is associative, so each row is the same bit pattern
-//            whatever order the tokens are added in; no row is shared between
-//            blocks, so there are no global atomics and no table in HBM.
+//   project  U[n] = alpha Y[n] P^T (fp32 [N][r]) on the matrix cores, plus a
+//            max |U| per block or output wave (no atomics: a chain of atomics
+//            on one address serialises).  bf16 at r = 128, 256 uses the
+//            codec's streaming reduction kernel with P's fragment pack.
+//   own      block b owns the ids v with v % B == b (B blocks: frequent ids,
+//            which tokenizers give small numbers, land in different blocks)
+//            and one 64-column slice.  It reads the token ids in chunks,
+//            queues its own tokens in LDS (one LDS atomic per wave and step),
+//            adds their U rows into an LDS table of 64-bit integers at one
+//            power-of-two scale 2^e taken from the global max |U| and N (runs
+//            of one id summed in registers first), and writes its gE rows.  Integer addition is associative, so each
+//            row is the same bit pattern whatever order the tokens are added
+//            in; no row is shared between blocks, so there are no global
+//            atomics and no table in HBM.
 #include <algorithm>
 
 #include "common.h"
@@ -29,10 +31,14 @@ namespace mapl {
 namespace {
 
 constexpr int kProjMaxGrid = 1024;  // project blocks along the tokens (the rest loop)
-constexpr int kOwnThreads = 1024;   // 16 waves per owner block
+constexpr int kOwnThreads = 512;    // 8 waves per owner block, two blocks per CU
 constexpr int kOwnVR = 128;         // ids per owner block (LDS table rows)
-constexpr int kOwnChunk = 8192;     // token ids scanned per round (LDS queue capacity)
+constexpr int kOwnPer = 4;          // token ids each thread loads per chunk
+constexpr int kOwnChunk = kOwnThreads * kOwnPer;  // token ids per chunk
+constexpr int kOwnQueue = 4000;     // LDS queue capacity (entries); two blocks fit in 160 KB
+static_assert(kOwnQueue >= kOwnChunk, "a chunk must fit in an empty queue");
 constexpr int kOwnBatch = 32;       // queued tokens whose U loads one wave keeps in flight
+constexpr int kOwnBatchQ = 16;      // the same in 16-byte loads (4 tokens per wave instruction)
 
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -124,95 +130,188 @@ __global__ __launch_bounds__(256) void k_ag_project_f32(const float* __restrict_
   if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
-// power-of-two scale 2^e of the fixed-point sums: with max |U| < 2^ex and at
-// most 2^lgN terms per sum, every sum stays below 2^62
-__device__ __forceinline__ int fixed_exponent(float m, int N) {
+// power-of-two scale 2^e of the fixed-point terms: with max |U| < 2^ex every
+// scaled term is below 2^30 in magnitude (an int32 after rounding), so a sum
+// of at most N < 2^31 of them stays below 2^61 in 64 bits.  Each term is
+// rounded once, by at most 2^-31 * 2^ex <= 2^-30 * max |U|.
+__device__ __forceinline__ int fixed_exponent(float m) {
   int ex;
   (void)frexpf(m, &ex);  // m < 2^ex (ex = 0 for m = 0)
-  const int lgN = (N > 1) ? 32 - __clz(N - 1) : 0;
-  return 62 - ex - lgN;
+  return 30 - ex;
+}
+
+// x * 2^e rounded to the nearest integer, as an int32 (|x| <= max |U|: exact scaling, fits)
+__device__ __forceinline__ long long fixed_term(float x, int e) {
+  return static_cast<long long>(static_cast<int>(rintf(ldexpf(x, e))));
+}
+
+// q = t / B, rem = t % B for 0 <= t < 2^24, 1 <= B < 2^16: a float estimate of
+// the quotient (off by at most one) and one correction each way, instead of
+// the integer division sequence
+__device__ __forceinline__ void divmod_small(int t, int B, float invB, int& q, int& rem) {
+  q = int(float(t) * invB);
+  rem = t - q * B;
+  if (rem < 0) q -= 1, rem += B;
+  if (rem >= B) q += 1, rem -= B;
 }
 
 // Owner block b (blockIdx.x) of B = gridDim.x holds the ids v = s B + b,
-// s < kOwnVR, and columns [64 blockIdx.y, + 64): lane = column.
-__global__ __launch_bounds__(kOwnThreads) void k_ag_own(const float* __restrict__ U, const int32_t* __restrict__ tids,
-                                                        const float* __restrict__ part, int npart,
-                                                        float* __restrict__ gE, int N, int r, int V, int accumulate) {
+// s < kOwnVR, and columns [64 blockIdx.y, + 64): lane = column.  The block
+// scans the ids chunk by chunk (the next chunk's loads in flight while the
+// current one is queued) and adds the queued rows once the scan is done or the
+// queue could overflow.  Queue entry: (slot s << 24) | token, token < 2^24.
+template <bool QUAD>
+__global__ __launch_bounds__(kOwnThreads, 2) void k_ag_own(const float* __restrict__ U,
+                                                           const int32_t* __restrict__ tids,
+                                                           const float* __restrict__ part, int npart,
+                                                           float* __restrict__ gE, int N, int r, int V, int accumulate) {
+  constexpr int NW = kOwnThreads / 64;
+  static_assert(kOwnVR <= 256, "queue entry packing");
   __shared__ unsigned long long acc[kOwnVR * 64];
-  __shared__ int q_tok[kOwnChunk];
-  __shared__ uint16_t q_slot[kOwnChunk];
-  __shared__ float red[16];
+  __shared__ uint32_t q[kOwnQueue];
+  __shared__ float red[NW];
   __shared__ int q_count;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int B = gridDim.x, b = blockIdx.x;
   const int col = blockIdx.y * 64 + lane;
   const bool colok = col < r;
+  const int ccol = min(col, r - 1);
+  const float invB = 1.0f / float(B);
+
+  // the first chunk's ids (clamped, always valid) are requested before anything else
+  int tv[kOwnPer];
+#pragma unroll
+  for (int k = 0; k < kOwnPer; ++k) tv[k] = tids[min(k * kOwnThreads + int(threadIdx.x), N - 1)];
 
   // global scale from the per-block maxima of the projection
   float m = 0.f;
   for (int i = threadIdx.x; i < npart; i += kOwnThreads) m = fmaxf(m, part[i]);
-  m = block_max<16>(m, red);
-  const int ex = fixed_exponent(m, N);
-
   for (int i = threadIdx.x; i < kOwnVR * 64; i += kOwnThreads) acc[i] = 0ull;
   if (threadIdx.x == 0) q_count = 0;
-  __syncthreads();
+  m = block_max<NW>(m, red);  // its barriers also publish the zeroed table and count
+  const int ex = fixed_exponent(m);
+
+  // QUAD (r % 4 == 0): lane = (entry g = lane >> 4, columns 4 (lane & 15) + 0..3);
+  // one 16-byte load per lane covers four entries per wave instruction, and
+  // wave w takes entries w + NW (4 j + g).  A run of one slot in a lane's own
+  // sequence of entries is summed in registers and added once.
+  auto add_queue_quad = [&](int cnt) {
+    const int g = lane >> 4, c4 = blockIdx.y * 64 + 4 * (lane & 15);
+    const bool ok4 = c4 < r;  // r % 4 == 0: all four columns or none
+    const int cc4 = min(c4, r - 4);
+    for (int i0 = w + NW * g; i0 < cnt; i0 += NW * 4 * kOwnBatchQ) {
+      f32x4 x[kOwnBatchQ];
+      int sl[kOwnBatchQ];
+#pragma unroll
+      for (int k = 0; k < kOwnBatchQ; ++k) {
+        const int i = i0 + NW * 4 * k;
+        const uint32_t e = q[min(i, cnt - 1)];  // clamped: always a queued token
+        sl[k] = (i < cnt) ? int(e >> 24) : -1;
+        x[k] = *reinterpret_cast<const f32x4*>(U + size_t(e & 0xffffffu) * r + cc4);
+      }
+#pragma unroll
+      for (int k = 0; k < kOwnBatchQ; ++k) asm volatile("" : : "v"(x[k]));
+      long long run[4] = {0, 0, 0, 0};
+      int run_slot = sl[0];
+#pragma unroll
+      for (int k = 0; k < kOwnBatchQ; ++k) {
+        if (sl[k] >= 0) {
+          if (sl[k] != run_slot) {
+            if (ok4) {
+#pragma unroll
+              for (int c = 0; c < 4; ++c)
+                atomicAdd(&acc[run_slot * 64 + (c4 & 63) + c], static_cast<unsigned long long>(run[c]));
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c) run[c] = 0;
+            run_slot = sl[k];
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) run[c] += fixed_term(x[k][c], ex);
+        }
+      }
+      if (run_slot >= 0 && ok4) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          atomicAdd(&acc[run_slot * 64 + (c4 & 63) + c], static_cast<unsigned long long>(run[c]));
+      }
+    }
+  };
+
+  // add queued rows [0, cnt): wave w takes entries w, w + NW, ...; a run of
+  // consecutive entries with one slot is summed in registers and added once
+  auto add_queue = [&](int cnt) {
+    if (QUAD) {
+      add_queue_quad(cnt);
+      return;
+    }
+    for (int i0 = w; i0 < cnt; i0 += NW * kOwnBatch) {
+      float x[kOwnBatch];
+      int sl[kOwnBatch];
+#pragma unroll
+      for (int k = 0; k < kOwnBatch; ++k) {
+        const uint32_t e = q[min(i0 + NW * k, cnt - 1)];  // clamped: always a queued token
+        sl[k] = (i0 + NW * k < cnt) ? int(e >> 24) : -1;
+        x[k] = U[size_t(e & 0xffffffu) * r + ccol];
+      }
+      // every row value is resolved here, after all loads were issued: otherwise
+      // the compiler moves each load into the branches below and waits on it there
+#pragma unroll
+      for (int k = 0; k < kOwnBatch; ++k) asm volatile("" : : "v"(x[k]));
+      long long run = 0;
+      int run_slot = sl[0];
+#pragma unroll
+      for (int k = 0; k < kOwnBatch; ++k) {
+        if (sl[k] < 0) break;  // uniform: the rest of the batch is padding
+        if (sl[k] != run_slot) {
+          if (colok) atomicAdd(&acc[run_slot * 64 + lane], static_cast<unsigned long long>(run));
+          run = 0;
+          run_slot = sl[k];
+        }
+        run += fixed_term(x[k], ex);
+      }
+      if (run_slot >= 0 && colok) atomicAdd(&acc[run_slot * 64 + lane], static_cast<unsigned long long>(run));
+    }
+  };
 
   for (int base = 0; base < N; base += kOwnChunk) {
-    // queue this block's tokens of the chunk (one LDS atomic per wave and step)
-    constexpr int PER = kOwnChunk / kOwnThreads;
-    int tv[PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) tv[k] = tids[min(base + k * kOwnThreads + int(threadIdx.x), N - 1)];
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
+    for (int k = 0; k < kOwnPer; ++k) {
       const int n = base + k * kOwnThreads + threadIdx.x;
       const int t = tv[k];
-      const bool mine = n < N && t >= 0 && t < V && (t % B) == b;
+      const bool valid = n < N && t >= 0 && t < V;
+      int tq, trem;
+      divmod_small(valid ? t : 0, B, invB, tq, trem);
+      const bool mine = valid && trem == b;
       const uint64_t mask = __ballot(mine);
       if (mask) {  // uniform per wave
         int qbase = 0;
         if (lane == 0) qbase = atomicAdd(&q_count, __popcll(mask));
         qbase = __shfl(qbase, 0);
-        if (mine) {
-          const int pos = qbase + __popcll(mask & ((1ull << lane) - 1));
-          q_tok[pos] = n;
-          q_slot[pos] = uint16_t(t / B);
-        }
+        if (mine) q[qbase + __popcll(mask & ((1ull << lane) - 1))] = (uint32_t(tq) << 24) | uint32_t(n);
       }
+    }
+    const int nb = base + kOwnChunk;
+    if (nb < N) {  // the next chunk's ids load while this one is queued and (maybe) added
+#pragma unroll
+      for (int k = 0; k < kOwnPer; ++k) tv[k] = tids[min(nb + k * kOwnThreads + int(threadIdx.x), N - 1)];
     }
     __syncthreads();
     const int cnt = q_count;
-    // add the queued rows: wave w takes entries w, w + 16, ...; kOwnBatch loads in flight
-    for (int i0 = w; i0 < cnt; i0 += 16 * kOwnBatch) {
-      float x[kOwnBatch];
-      int sl[kOwnBatch];
-#pragma unroll
-      for (int k = 0; k < kOwnBatch; ++k) {
-        // loads from clamped, always valid places; the mask is applied when adding
-        const int i = min(i0 + 16 * k, cnt - 1);
-        sl[k] = (i0 + 16 * k < cnt) ? int(q_slot[i]) : -1;
-        x[k] = U[size_t(q_tok[i]) * r + min(col, r - 1)];
-      }
-#pragma unroll
-      for (int k = 0; k < kOwnBatch; ++k)
-        if (sl[k] >= 0 && colok) {
-          // |x| <= max |U| < 2^(62 - e - lgN): the scaled value is exact and the integer fits
-          const long long qv = static_cast<long long>(rintf(ldexpf(x[k], ex)));
-          atomicAdd(&acc[sl[k] * 64 + lane], static_cast<unsigned long long>(qv));
-        }
+    if (nb >= N || cnt > kOwnQueue - kOwnChunk) {  // uniform
+      add_queue(cnt);
+      __syncthreads();  // queue consumed
+      if (threadIdx.x == 0) q_count = 0;
+      __syncthreads();
     }
-    __syncthreads();  // queue consumed
-    if (threadIdx.x == 0) q_count = 0;
-    __syncthreads();
   }
 
   // write the owned rows (every one when overwriting; rows with no token add 0)
   if (!colok) return;
-  for (int s = w; s < kOwnVR; s += 16) {
-    const int64_t v = int64_t(s) * B + b;
+  for (int sl = w; sl < kOwnVR; sl += NW) {
+    const int64_t v = int64_t(sl) * B + b;
     if (v >= V) break;
-    const float val = float(ldexp(double(static_cast<long long>(acc[s * 64 + lane])), -ex));
+    const float val = float(ldexp(double(static_cast<long long>(acc[sl * 64 + lane])), -ex));
     float* o = gE + size_t(v) * r + col;
     *o = accumulate ? *o + val : val;
   }
@@ -225,29 +324,38 @@ int proj_blocks(int N, int r, int y_bf16) {
 
 size_t a256(size_t b) { return (b + 255) & ~size_t(255); }
 
+// U [N][r] fp32 | partial maxima
+size_t part_offset(int64_t N, int64_t r) { return a256(size_t(N) * r * 4); }
+size_t npart_max(int64_t N) { return std::max<size_t>(size_t(kProjMaxGrid) * 4, size_t(4) * ((N + 63) / 64)); }
+
 }  // namespace
 
 size_t anchor_grad_ws_bytes(int64_t N, int64_t r, int64_t V) {
   (void)V;
-  return a256(size_t(N) * r * 4) + a256(size_t(kProjMaxGrid) * 16 * 4);
+  return part_offset(N, r) + a256(npart_max(N) * 4);
 }
 
-void launch_anchor_grad(const void* Y, int y_bf16, const int32_t* tids, const void* P, float* gE, float alpha,
-                        int accumulate, int N, int d, int r, int V, void* ws, hipStream_t s) {
-  char* base = static_cast<char*>(ws);
-  float* U = reinterpret_cast<float*>(base);
-  float* part = reinterpret_cast<float*>(base + a256(size_t(N) * r * 4));
-  const int npart = proj_blocks(N, r, y_bf16);
-  if (y_bf16) {
+void launch_anchor_grad(const void* Y, int y_bf16, const int32_t* tids, const void* P, const uint16_t* PF,
+                        float* gE, float alpha, int accumulate, int N, int d, int r, int V, void* ws, hipStream_t s) {
+  float* U = static_cast<float*>(ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + part_offset(N, r));
+  int npart;
+  if (y_bf16 && PF != nullptr &&
+      launch_tok_reduce_f32out(static_cast<const uint16_t*>(Y), PF, U, alpha, part, N, d, r, s)) {
+    npart = 4 * ((N + 63) / 64);
+  } else if (y_bf16) {
+    npart = proj_blocks(N, r, 1);
     const int gx = std::min((N + 31) / 32, kProjMaxGrid);
     hipLaunchKernelGGL(k_ag_project_bf16, dim3(unsigned(gx), unsigned((r + 127) / 128)), dim3(256), 0, s,
                        static_cast<const bf16_t*>(Y), static_cast<const bf16_t*>(P), U, part, alpha, N, d, r);
   } else {
+    npart = proj_blocks(N, r, 0);
     hipLaunchKernelGGL(k_ag_project_f32, dim3(unsigned(npart)), dim3(256), 0, s, static_cast<const float*>(Y),
                        static_cast<const float*>(P), U, part, alpha, N, d, r);
   }
   const int B = (V + kOwnVR - 1) / kOwnVR;
-  hipLaunchKernelGGL(k_ag_own, dim3(unsigned(B), unsigned((r + 63) / 64)), dim3(kOwnThreads), 0, s, U, tids, part,
+  auto own = (r % 4 == 0) ? k_ag_own<true> : k_ag_own<false>;
+  hipLaunchKernelGGL(own, dim3(unsigned(B), unsigned((r + 63) / 64)), dim3(kOwnThreads), 0, s, U, tids, part,
                      npart, gE, N, r, V, accumulate);
 }
 

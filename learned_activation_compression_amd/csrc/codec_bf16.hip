@@ -182,13 +182,17 @@ struct RedRing {
   static constexpr size_t BYTES = size_t(S) * SLOT * 16;
 };
 
-template <int RBW, int S, int G, bool ANCHOR>
+// OUTF: instead of bf16 Z, write fp32 rows alpha * (X A) to Uf and each output
+// wave's max |value| to part[4 * blockIdx.x + w] (the anchor-table gradient's
+// projection, X = Y and the weight pack PF).
+template <int RBW, int S, int G, bool ANCHOR, bool OUTF = false>
 __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __restrict__ X,
                                                             const bf16_t* __restrict__ AtF,
                                                             const int32_t* __restrict__ tids,
                                                             const bf16_t* __restrict__ E,
                                                             const bf16_t* __restrict__ QnF, bf16_t* __restrict__ Z,
-                                                            int N, int d, int r, int V) {
+                                                            int N, int d, int r, int V, float* __restrict__ Uf,
+                                                            float alpha, float* __restrict__ part) {
   using RR = RedRing<RBW, S>;
   static_assert(S % G == 0 && S / G >= 2, "each wave group needs its own slots");
   extern __shared__ __attribute__((aligned(16))) u32x4 ring[];
@@ -307,6 +311,31 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
   }
 
   // lane holds, for token tb*32 + l32, 4 consecutive output columns per register group
+  if (OUTF) {
+    float local = 0.f;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int n = tok0 + tb * 32 + l32;
+      if (n >= N) continue;
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) {
+        float* row = Uf + size_t(n) * r + (w * RBW + i) * 32 + 4 * hi;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = alpha * acc[tb][i][4 * q + e];
+            local = fmaxf(local, fabsf(v[e]));
+          }
+          *reinterpret_cast<f32x4*>(row + 8 * q) = v;
+        }
+      }
+    }
+    for (int off = 32; off > 0; off >>= 1) local = fmaxf(local, __shfl_xor(local, off));
+    if (lane == 0) part[4 * blockIdx.x + w] = local;
+    return;
+  }
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
     const int n = tok0 + tb * 32 + l32;
@@ -322,17 +351,32 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
   }
 }
 
-template <int RBW, int S, int G, bool ANCHOR>
+template <int RBW, int S, int G, bool ANCHOR, bool OUTF = false>
 static void launch_reduce_dma(const uint16_t* in, const uint16_t* AtF, const int32_t* tids, const uint16_t* E,
-                              const uint16_t* QnF, uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
-  auto k = k_tok_reduce_dma<RBW, S, G, ANCHOR>;
+                              const uint16_t* QnF, uint16_t* out, int N, int d, int r, int V, hipStream_t s,
+                              float* Uf = nullptr, float alpha = 1.f, float* part = nullptr) {
+  auto k = k_tok_reduce_dma<RBW, S, G, ANCHOR, OUTF>;
   const size_t lds = RedRing<RBW, S>::BYTES;
   static bool attr = false;  // once per process: allow more than 64 KB of dynamic LDS
   if (!attr) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     attr = true;
   }
-  hipLaunchKernelGGL(k, dim3((N + 63) / 64), dim3(256 * G), lds, s, in, AtF, tids, E, QnF, out, N, d, r, V);
+  hipLaunchKernelGGL(k, dim3((N + 63) / 64), dim3(256 * G), lds, s, in, AtF, tids, E, QnF, out, N, d, r, V, Uf,
+                     alpha, part);
+}
+
+bool launch_tok_reduce_f32out(const uint16_t* in, const uint16_t* F, float* U, float alpha, float* part, int N,
+                              int d, int r, hipStream_t s) {
+  if (r == 128) {
+    launch_reduce_dma<1, 6, 2, false, true>(in, F, nullptr, nullptr, nullptr, nullptr, N, d, r, 0, s, U, alpha, part);
+    return true;
+  }
+  if (r == 256) {
+    launch_reduce_dma<2, 3, 1, false, true>(in, F, nullptr, nullptr, nullptr, nullptr, N, d, r, 0, s, U, alpha, part);
+    return true;
+  }
+  return false;
 }
 
 void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32_t* tids, const uint16_t* E,

@@ -9,19 +9,22 @@
 namespace mapl {
 
 // ---- packed weights (bf16, fragment order; see pack.hip):
-//   AtF = A^T (r x d), AF = A (d x r), PtF = P^T (d x r), QnF = -(P A)^T (r x r)
+//   AtF = A^T (r x d), AF = A (d x r), PtF = P^T (d x r), QnF = -(P A)^T (r x r),
+//   PF = P (r x d)
 struct PackView {
   uint16_t* AtF;
   uint16_t* AF;
   uint16_t* PtF;
   uint16_t* QnF;
+  uint16_t* PF;
 };
 size_t pack_bytes_bf16(int64_t d, int64_t r);
 PackView pack_view(void* pk, int64_t d, int64_t r);
 void launch_pack_AtF(const uint16_t* A, uint16_t* AtF, int d, int r, hipStream_t s);
 void launch_pack_AF(const uint16_t* A, uint16_t* AF, int d, int r, hipStream_t s);
 void launch_pack_PtF(const uint16_t* P, uint16_t* PtF, int d, int r, hipStream_t s);
-// all four sections
+void launch_pack_PF(const uint16_t* P, uint16_t* PF, int d, int r, hipStream_t s);
+// all five sections
 void launch_pack_all(const uint16_t* P, const uint16_t* A, PackView v, int d, int r, hipStream_t s);
 
 // ---- bf16 codec
@@ -29,6 +32,11 @@ void launch_pack_all(const uint16_t* P, const uint16_t* A, PackView v, int d, in
 void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32_t* tids,
                             const uint16_t* E, const uint16_t* QnF, uint16_t* out,
                             int N, int d, int r, int V, hipStream_t s);
+// U[N][r] = alpha * in[N][d] W^T with W's fragments F (M = r, K = d), fp32 rows, and
+// the max |U| of each output wave in part[4 * (N / 64 block) + wave]; covers r = 128
+// and 256 (returns false, launching nothing, otherwise)
+bool launch_tok_reduce_f32out(const uint16_t* in, const uint16_t* F, float* U, float alpha, float* part, int N,
+                              int d, int r, hipStream_t s);
 // out[N][d] = in[N][r] A^T (+ E[tids] P) via AF and PtF; E == nullptr drops the anchor term
 void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_t* tids,
                             const uint16_t* E, const uint16_t* PtF, uint16_t* out,
@@ -67,11 +75,11 @@ void launch_outer_f32(const float* L, const float* R, float* gA, int N, int d, i
 void launch_fill_f32(float* p, int64_t count, float value, hipStream_t s);
 void launch_check_tids(const int32_t* tids, int N, int V, int32_t* bad, hipStream_t s);
 
-// anchor-table gradient: workspace (projected rows, 64-bit accumulator, max
-// cell) and the four launches (zero, project, scatter, finish)
+// anchor-table gradient: workspace (projected rows, partial maxima) and the two
+// launches (project, own); PF (P's fragment pack) may be nullptr
 size_t anchor_grad_ws_bytes(int64_t N, int64_t r, int64_t V);
-void launch_anchor_grad(const void* Y, int y_bf16, const int32_t* tids, const void* P, float* gE, float alpha,
-                        int accumulate, int N, int d, int r, int V, void* ws, hipStream_t s);
+void launch_anchor_grad(const void* Y, int y_bf16, const int32_t* tids, const void* P, const uint16_t* PF,
+                        float* gE, float alpha, int accumulate, int N, int d, int r, int V, void* ws, hipStream_t s);
 
 // ---- residual VQ
 void launch_rvq_encode(const void* Z, int z_bf16, const float* C, int64_t stride,

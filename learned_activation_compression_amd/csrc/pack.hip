@@ -17,6 +17,8 @@
 //   QnF: W = -(P A)^T (M = r, K = r)  anchor term of compression
 //   AF : W = A   (M = d, K = r)      reconstruction, gX = gZ A^T
 //   PtF: W = P^T (M = d, K = r)      anchor term of reconstruction
+//   PF : W = P   (M = r, K = d)      anchor-table gradient, Y P^T
+// P is also contracted over d in the anchor-table gradient (Eq. (3)).
 #include "common.h"
 #include "internal.h"
 
@@ -25,7 +27,7 @@ namespace mapl {
 static inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 size_t pack_bytes_bf16(int64_t d, int64_t r) {
-  return 3 * align256(size_t(r) * d * 2) + align256(size_t(r) * r * 2);
+  return 4 * align256(size_t(r) * d * 2) + align256(size_t(r) * r * 2);
 }
 
 PackView pack_view(void* pk, int64_t d, int64_t r) {
@@ -36,6 +38,7 @@ PackView pack_view(void* pk, int64_t d, int64_t r) {
   v.AF = reinterpret_cast<uint16_t*>(p + big);
   v.PtF = reinterpret_cast<uint16_t*>(p + 2 * big);
   v.QnF = reinterpret_cast<uint16_t*>(p + 3 * big);
+  v.PF = reinterpret_cast<uint16_t*>(p + 3 * big + align256(size_t(r) * r * 2));
   return v;
 }
 
@@ -78,11 +81,16 @@ void launch_pack_PtF(const uint16_t* P, uint16_t* PtF, int d, int r, hipStream_t
   frag_pack(P, /*sm*/ 1, /*sk*/ d, d, r, PtF, s);  // W(m, k) = P[k][m]
 }
 
-// The three A / P sections in one launch: unit u of the concatenation
-// [AtF | AF | PtF] (section boundaries at multiples of 64 units).
-__global__ __launch_bounds__(256) void k_frag_pack3(const bf16_t* __restrict__ A, const bf16_t* __restrict__ P,
+void launch_pack_PF(const uint16_t* P, uint16_t* PF, int d, int r, hipStream_t s) {
+  frag_pack(P, /*sm*/ d, /*sk*/ 1, r, d, PF, s);  // W(m, k) = P[m][k]
+}
+
+// The four A / P sections in one launch: unit u of the concatenation
+// [AtF | AF | PtF | PF] (section boundaries at multiples of 64 units).
+__global__ __launch_bounds__(256) void k_frag_pack4(const bf16_t* __restrict__ A, const bf16_t* __restrict__ P,
                                                     bf16_t* __restrict__ AtF, bf16_t* __restrict__ AF,
-                                                    bf16_t* __restrict__ PtF, int d, int r) {
+                                                    bf16_t* __restrict__ PtF, bf16_t* __restrict__ PF, int d,
+                                                    int r) {
   const int64_t u0 = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t n1 = int64_t(d / 16) * (r / 32) * 64, n2 = int64_t(r / 16) * (d / 32) * 64;
   const bf16_t* src;
@@ -95,6 +103,8 @@ __global__ __launch_bounds__(256) void k_frag_pack3(const bf16_t* __restrict__ A
     src = A, sm = r, sk = 1, M = d, dst = AF, u = u0 - n1;  // W(m, k) = A[m][k]
   } else if (u0 < n1 + 2 * n2) {
     src = P, sm = 1, sk = d, M = d, dst = PtF, u = u0 - n1 - n2;  // W(m, k) = P[k][m]
+  } else if (u0 < 2 * n1 + 2 * n2) {
+    src = P, sm = d, sk = 1, M = r, dst = PF, u = u0 - n1 - 2 * n2;  // W(m, k) = P[m][k]
   } else {
     return;
   }
@@ -160,11 +170,11 @@ __global__ __launch_bounds__(256) void k_qn_direct(const bf16_t* __restrict__ P,
   }
 }
 
-// Full pack: the three A / P sections, then QnF from P and the fresh AtF.
+// Full pack: the four A / P sections, then QnF from P and the fresh AtF.
 void launch_pack_all(const uint16_t* P, const uint16_t* A, PackView v, int d, int r, hipStream_t s) {
-  const int64_t units = int64_t(d / 16) * (r / 32) * 64 + 2 * int64_t(r / 16) * (d / 32) * 64;
-  hipLaunchKernelGGL(k_frag_pack3, dim3(unsigned((units + 255) / 256)), dim3(256), 0, s, A, P, v.AtF, v.AF, v.PtF,
-                     d, r);
+  const int64_t units = 2 * int64_t(d / 16) * (r / 32) * 64 + 2 * int64_t(r / 16) * (d / 32) * 64;
+  hipLaunchKernelGGL(k_frag_pack4, dim3(unsigned((units + 255) / 256)), dim3(256), 0, s, A, P, v.AtF, v.AF, v.PtF,
+                     v.PF, d, r);
   hipLaunchKernelGGL(k_qn_direct, dim3(r / 32, r / 32), dim3(256), 0, s, P, v.AtF, v.QnF, d, r);
 }
 

@@ -35,9 +35,9 @@ def test_status_strings_and_version(lib):
 
 def test_pack_and_workspace_sizes(lib):
     d, r = 1024, 128
-    want = 3 * 2 * r * d + 2 * r * r
+    want = 4 * 2 * r * d + 2 * r * r
     got = lib.mapl_pack_bytes(d, r, BF16)
-    assert want <= got <= want + 3 * 256
+    assert want <= got <= want + 5 * 256
     assert lib.mapl_pack_bytes(d, r, F32) == 0
     assert lib.mapl_bwd_workspace_bytes(8, 2048, d, r, BF16) > 0
     assert lib.mapl_bwd_workspace_bytes(1, 128, 256, 32, F32) == 128 * 256 * 4
@@ -103,14 +103,15 @@ def test_backward_validation(lib):
 
 def test_anchor_grad_validation(lib):
     ws = lib.mapl_anchor_grad_workspace_bytes(8, 2048, 128, 32000)
-    assert 8 * 2048 * 128 * 4 <= ws <= 8 * 2048 * 128 * 4 + 2 ** 17   # U rows + partial maxima
+    N = 8 * 2048
+    assert N * 128 * 4 <= ws <= N * 128 * 4 + 2 ** 17   # U rows + partial maxima
     assert lib.mapl_anchor_grad_workspace_bytes(8, 2048, 128, 0) == 0
     assert lib.mapl_anchor_grad_workspace_bytes(8, 2048, 128, 2 ** 22 + 1) == 0
     f = lib.mapl_anchor_grad
 
     def call(Y=FAKE, tids=FAKE, P=FAKE, gE=FAKE, alpha=1.0, acc=0, B=8, T=2048, d=1024, r=128, V=32000, dt=BF16,
-             w=FAKE, wb=ws):
-        return f(Y, tids, P, gE, alpha, acc, B, T, d, r, V, dt, w, wb, None)
+             pk=FAKE, pkb=10 ** 7, pkr=1, w=FAKE, wb=ws):
+        return f(Y, tids, P, gE, alpha, acc, B, T, d, r, V, dt, pk, pkb, pkr, w, wb, None)
 
     assert call(Y=None) == ENULL
     assert call(tids=None) == ENULL
@@ -119,6 +120,9 @@ def test_anchor_grad_validation(lib):
     assert call(wb=ws - 8) == EWS
     assert call(w=ctypes.c_void_p(0x1008)) == EARG              # ws not 16-B aligned
     assert call(acc=2) == EARG
+    assert call(pkr=3) == EARG
+    assert call(pk=None) == ENULL                               # bf16 needs the pack
+    assert call(pkb=1000) == EWS
     assert call(alpha=float("inf")) == EARG
     assert call(d=1000) == ESHAPE                               # bf16 d % 128
     assert call(r=96) == ESHAPE                                 # bf16 r a power of two

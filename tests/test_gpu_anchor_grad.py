@@ -129,6 +129,16 @@ def test_token_order_does_not_change_a_bit():
     assert torch.equal(gE1, gE3)
 
 
+def test_prepacked_weights_give_identical_bits():
+    inp = synth.codec_inputs(64, 3000, 1024, 128, 700, "bf16")
+    g = to_dev(inp)
+    pk = lac.mapl_pack(g["P"], g["A"])
+    a = lac.mapl_anchor_grad(g["gXhat"], g["tids"], g["P"], 700, 1.0)
+    b = lac.mapl_anchor_grad(g["gXhat"], g["tids"], g["P"], 700, 1.0, pk=pk, pk_ready=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 def test_zero_gradient_and_empty_batch():
     inp = synth.codec_inputs(63, 128, 256, 32, 50, "bf16")
     g = to_dev(inp)
