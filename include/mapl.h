@@ -68,9 +68,20 @@ const char* mapl_version(void);
 /* ------------------------------------------------------------------------
  * Packed weights.
  *
+ * Anchor rank.  Every codec entry point takes ra, the rank of the anchor
+ * E_small [V][ra] P [ra][d].  Eq. (3) and Table 8 use ra = r; Appendix G's
+ * Table 6 ablates the anchor: ra = 0 is "no anchor" (tids, E_small and P are
+ * then ignored and may be NULL), and ra = d with P = I is the full trainable
+ * anchor E [V][d] (also the first stage's subtraction of the token embedding,
+ * Figure 2).  For that one, pass P = NULL with ra == d: the maps then subtract
+ * or add the rows E[t] themselves (no d x d product; a dense identity P gives
+ * the same result through the general path, at the cost of that product).
+ * bf16 takes ra == 0, ra == r, or ra a multiple of 64 with r a multiple of 64;
+ * every path takes 0 <= ra <= d.
+ *
  * The bf16 codec kernels read A and P through a packed copy laid out for the
- * matrix cores: the operands A^T (r x d), A (d x r), P^T (d x r), P (r x d)
- * and -(P A)^T (r x r, formed with fp32 accumulation and rounded once), all bf16
+ * matrix cores: the operands A^T (r x d), A (d x r), P^T (d x ra), P (ra x d)
+ * and -(P A)^T (r x ra, formed with fp32 accumulation and rounded once), all bf16
  * and stored in fragment order, i.e. as the 64-lane x 16-byte pieces one
  * v_mfma_f32_32x32x16_bf16 consumes, so that every weight load of a wave is
  * one contiguous kilobyte.  In training A changes once per optimizer step
@@ -80,25 +91,25 @@ const char* mapl_version(void);
  * arguments (mapl_reconstruct_bwd, which has no P, rebuilds only the A^T
  * part; mapl_anchor_grad, which has no A, only the P part); with
  * pk_ready == 1 the caller guarantees that pk holds
- * mapl_pack(P, A) of exactly these matrices.  For dt == MAPL_F32 no pack is
- * used (pk may be NULL and mapl_pack_bytes returns 0).
+ * mapl_pack(P, A) of exactly these matrices (and this ra).  For
+ * dt == MAPL_F32 no pack is used (pk may be NULL and mapl_pack_bytes returns 0).
  * ---------------------------------------------------------------------- */
-size_t mapl_pack_bytes(int64_t d, int64_t r, mapl_dtype dt);
+size_t mapl_pack_bytes(int64_t d, int64_t r, int64_t ra, mapl_dtype dt);
 
-/* Build the whole pack from P [r][d] and A [d][r] (bf16). */
+/* Build the whole pack from P [ra][d] and A [d][r] (bf16; P unused when ra == 0). */
 int mapl_pack(const void* P, const void* A, void* pk, size_t pk_bytes,
-              int64_t d, int64_t r, mapl_dtype dt, hipStream_t stream);
+              int64_t d, int64_t r, int64_t ra, mapl_dtype dt, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Forward codec (Section 3.2, Eq. (1)-(3); Algorithm 1 steps 1 and 3).
  * ---------------------------------------------------------------------- */
 
 /* Eq. (1): Z[N][r] = (X[N][d] - E_small[tids] P) A,  N = B*T.
- * X [N][d], tids [N], E_small [V][r], P [r][d], A [d][r] -> Z [N][r].
+ * X [N][d], tids [N], E_small [V][ra], P [ra][d], A [d][r] -> Z [N][r].
  * The bf16 path evaluates the exact re-association X A - E_small[tids] (P A). */
 int mapl_compress(const void* X, const int32_t* tids, const void* E_small,
                   const void* P, const void* A, void* Z,
-                  int64_t B, int64_t T, int64_t d, int64_t r, int64_t V,
+                  int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, int64_t V,
                   mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready,
                   hipStream_t stream);
 
@@ -106,7 +117,7 @@ int mapl_compress(const void* X, const int32_t* tids, const void* E_small,
  * anchor (E_{p+1}, P_{p+1}) and the sender's projector A. */
 int mapl_reconstruct(const void* Z, const int32_t* tids, const void* E_small,
                      const void* P, const void* A, void* Xhat,
-                     int64_t B, int64_t T, int64_t d, int64_t r, int64_t V,
+                     int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, int64_t V,
                      mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready,
                      hipStream_t stream);
 
@@ -116,9 +127,10 @@ int mapl_reconstruct(const void* Z, const int32_t* tids, const void* E_small,
  * same projector).  gA is fp32 [d][r]; accumulate == 0 overwrites it,
  * accumulate == 1 adds into it (to sum both maps' terms and micro-batches).
  * The reduction over tokens is deterministic (fixed split and order, no
- * floating-point atomics); it uses `ws` of mapl_bwd_workspace_bytes().
+ * floating-point atomics); it uses `ws` of mapl_bwd_workspace_bytes(), which
+ * serves both maps.
  * ---------------------------------------------------------------------- */
-size_t mapl_bwd_workspace_bytes(int64_t B, int64_t T, int64_t d, int64_t r, mapl_dtype dt);
+size_t mapl_bwd_workspace_bytes(int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, mapl_dtype dt);
 
 /* Receiver side, given gXhat = dL/dXhat [N][d]:
  *   gZ[N][r] = gXhat A ;   gA (+)= gXhat^T Z.
@@ -136,7 +148,7 @@ int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A,
 int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids,
                       const void* E_small, const void* P, const void* A,
                       void* gX, float* gA, int accumulate,
-                      int64_t B, int64_t T, int64_t d, int64_t r, int64_t V,
+                      int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, int64_t V,
                       mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
@@ -148,8 +160,11 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids,
  * - sender's table (Eq. (1)):   Y = gX = gZ A^T (the gX output of
  *   mapl_compress_bwd), alpha = -1, since gZ (P A)^T = (gZ A^T) P^T;
  * - a table shared by both sides: two calls, the second with accumulate = 1.
- * Y and P use `dt`; gE is fp32 [V][r] (accumulate == 0 overwrites all V rows,
- * 1 adds).  Tokens whose id is outside [0, V) contribute nothing.  The sums
+ * Y and P [ra][d] use `dt`; gE is fp32 [V][ra] (accumulate == 0 overwrites all
+ * V rows, 1 adds); r is the projector's rank, on which the pack's layout
+ * depends.  P = NULL with ra == d is the full-rank anchor (P = I: the rows
+ * alpha Y[n] themselves; no pack is read).  Tokens whose id is outside
+ * [0, V) contribute nothing.  The sums
  * are exact 64-bit fixed-point accumulations at one power-of-two scale chosen
  * from max |alpha Y[n] P^T| (every sum fits; each term is rounded once, by
  * at most 2^-30 times that maximum), so the result does not depend on the
@@ -158,12 +173,12 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids,
  * pk_bytes, pk_ready as for the codec; pk_ready == 0 rebuilds only its P
  * part from this P, so a receiver passes the pack of its own P').  Uses a
  * 16-byte aligned `ws` of mapl_anchor_grad_workspace_bytes() (MAPL_ERR_ARG if
- * misaligned): N*r fp32 projected rows, partial maxima and the tokens grouped
- * by owner.  Shapes follow the codec rules (bf16: d % 128 == 0, r a power of
- * two in [32, 512]); V <= 2^22, N*r <= 2^38. */
-size_t mapl_anchor_grad_workspace_bytes(int64_t B, int64_t T, int64_t r, int64_t V);
+ * misaligned): N*ra fp32 projected rows and partial maxima.  Shapes follow
+ * the codec rules (bf16: d % 128 == 0, r a power of two in [32, 512], and the
+ * anchor-rank rules above with 1 <= ra); V <= 2^22, N*ra <= 2^38. */
+size_t mapl_anchor_grad_workspace_bytes(int64_t B, int64_t T, int64_t ra, int64_t V);
 int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* gE, float alpha,
-                     int accumulate, int64_t B, int64_t T, int64_t d, int64_t r, int64_t V,
+                     int accumulate, int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, int64_t V,
                      mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready,
                      void* ws, size_t ws_bytes, hipStream_t stream);
 

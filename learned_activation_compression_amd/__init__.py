@@ -41,19 +41,20 @@ _vp, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctyp
 _SIGS = {
     "mapl_status_string": (ctypes.c_char_p, [_i32]),
     "mapl_version": (ctypes.c_char_p, []),
-    "mapl_pack_bytes": (_sz, [_i64, _i64, _i32]),
-    "mapl_pack": (_i32, [_vp, _vp, _vp, _sz, _i64, _i64, _i32, _vp]),
-    "mapl_compress": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32, _vp]),
-    "mapl_reconstruct": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32,
-                                _vp]),
-    "mapl_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i32]),
+    "mapl_pack_bytes": (_sz, [_i64, _i64, _i64, _i32]),
+    "mapl_pack": (_i32, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32, _vp]),
+    "mapl_compress": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32,
+                             _vp]),
+    "mapl_reconstruct": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _sz,
+                                _i32, _vp]),
+    "mapl_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64, _i64, _i32]),
     "mapl_reconstruct_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32,
                                     _vp, _sz, _vp]),
-    "mapl_compress_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _i32,
-                                 _vp, _sz, _i32, _vp, _sz, _vp]),
+    "mapl_compress_bwd": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _i64,
+                                 _i32, _vp, _sz, _i32, _vp, _sz, _vp]),
     "mapl_anchor_grad_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
-    "mapl_anchor_grad": (_i32, [_vp, _vp, _vp, _vp, _f32, _i32, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32,
-                                _vp, _sz, _vp]),
+    "mapl_anchor_grad": (_i32, [_vp, _vp, _vp, _vp, _f32, _i32, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _sz,
+                                _i32, _vp, _sz, _vp]),
     "mapl_check_tids": (_i32, [_vp, _i64, _i64, _vp, _vp]),
     "rvq_encode": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
     "rvq_decode": (_i32, [_vp, _vp, _i64, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _vp]),
@@ -151,14 +152,26 @@ def _empty(shape, dtype, like):
     return torch.empty(shape, dtype=dtype, device=like.device)
 
 
+def _opt(t, name, dtype=None):
+    """Device pointer of an optional tensor (None -> NULL)."""
+    return None if t is None else _dev(t, name, dtype)
+
+
+def _ra(E_small) -> int:
+    """Anchor rank: E_small is [V, ra]; None means no anchor (ra = 0)."""
+    return 0 if E_small is None else int(E_small.shape[1])
+
+
 # ---------------------------------------------------------------- packing --
 
-def mapl_pack_bytes(d: int, r: int, dtype=torch.bfloat16) -> int:
-    return int(load().mapl_pack_bytes(d, r, MAPL_BF16 if dtype == torch.bfloat16 else MAPL_F32))
+def mapl_pack_bytes(d: int, r: int, dtype=torch.bfloat16, ra: int = None) -> int:
+    """Pack size for projector rank r and anchor rank ra (default r; 0 = no anchor)."""
+    ra = r if ra is None else ra
+    return int(load().mapl_pack_bytes(d, r, ra, MAPL_BF16 if dtype == torch.bfloat16 else MAPL_F32))
 
 
-def _pk(pk, d, r, dt, like):
-    nbytes = int(load().mapl_pack_bytes(d, r, dt))
+def _pk(pk, d, r, ra, dt, like):
+    nbytes = int(load().mapl_pack_bytes(d, r, ra, dt))
     if nbytes == 0:
         return None, 0
     if pk is None:
@@ -166,53 +179,64 @@ def _pk(pk, d, r, dt, like):
     return pk, pk.numel() * pk.element_size()
 
 
-def mapl_pack(P: torch.Tensor, A: torch.Tensor, pk: torch.Tensor = None, stream=None) -> torch.Tensor:
-    """Build the packed weights of (P [r][d], A [d][r]) into pk (allocated if None)."""
-    r, d = P.shape
+def mapl_pack(P: torch.Tensor, A: torch.Tensor, pk: torch.Tensor = None, stream=None, ra: int = None) -> torch.Tensor:
+    """Build the packed weights of (P [ra][d], A [d][r]) into pk (allocated if
+    None).  P = None packs for no anchor, or with ra = d for the full-rank
+    anchor (P = I)."""
+    d, r = A.shape
+    if P is not None:
+        ra = int(P.shape[0])
+    elif ra is None:
+        ra = 0
     dt = _dt(A)
-    pk, nb = _pk(pk, d, r, dt, A)
-    _check(load().mapl_pack(_dev(P, "P", A.dtype), _dev(A, "A"), pk.data_ptr() if pk is not None else None, nb,
-                            d, r, dt, _stream(stream)), "mapl_pack")
+    pk, nb = _pk(pk, d, r, ra, dt, A)
+    _check(load().mapl_pack(_opt(P, "P", A.dtype), _dev(A, "A"), pk.data_ptr() if pk is not None else None, nb,
+                            d, r, ra, dt, _stream(stream)), "mapl_pack")
     return pk
 
 
 # ------------------------------------------------------------------ codec --
 
 def mapl_compress(X, tids, E_small, P, A, Z=None, pk=None, pk_ready=False, stream=None) -> torch.Tensor:
-    """Eq. (1): Z = (X - E_small[tids] P) A.  X is [B,T,d] or [N,d]."""
+    """Eq. (1): Z = (X - E_small[tids] P) A.  X is [B,T,d] or [N,d]; E_small
+    [V, ra] and P [ra, d] (E_small = P = None: no anchor)."""
     d, r = A.shape
     B, T = _tokens(X, d, "X")
     dt = _dt(X)
-    V = E_small.shape[0]
+    ra = _ra(E_small)
+    V = E_small.shape[0] if E_small is not None else 0
     if Z is None:
         Z = _empty((*X.shape[:-1], r), X.dtype, X)
-    pk, nb = _pk(pk, d, r, dt, X)
-    _check(load().mapl_compress(_dev(X, "X"), _dev(tids, "tids", torch.int32), _dev(E_small, "E_small", X.dtype),
-                                _dev(P, "P", X.dtype), _dev(A, "A", X.dtype), _dev(Z, "Z", X.dtype), B, T, d, r, V,
-                                dt, pk.data_ptr() if pk is not None else None, nb, int(bool(pk_ready)),
+    pk, nb = _pk(pk, d, r, ra, dt, X)
+    _check(load().mapl_compress(_dev(X, "X"), _opt(tids, "tids", torch.int32), _opt(E_small, "E_small", X.dtype),
+                                _opt(P, "P", X.dtype), _dev(A, "A", X.dtype), _dev(Z, "Z", X.dtype), B, T, d, r, ra,
+                                V, dt, pk.data_ptr() if pk is not None else None, nb, int(bool(pk_ready)),
                                 _stream(stream)), "mapl_compress")
     return Z
 
 
 def mapl_reconstruct(Z, tids, E_small, P, A, Xhat=None, pk=None, pk_ready=False, stream=None) -> torch.Tensor:
-    """Eq. (2): Xhat = Z A^T + E_small[tids] P (receiver's E_small and P)."""
+    """Eq. (2): Xhat = Z A^T + E_small[tids] P (receiver's E_small and P; None: no anchor)."""
     d, r = A.shape
     B, T = _tokens(Z, r, "Z")
     dt = _dt(Z)
-    V = E_small.shape[0]
+    ra = _ra(E_small)
+    V = E_small.shape[0] if E_small is not None else 0
     if Xhat is None:
         Xhat = _empty((*Z.shape[:-1], d), Z.dtype, Z)
-    pk, nb = _pk(pk, d, r, dt, Z)
-    _check(load().mapl_reconstruct(_dev(Z, "Z"), _dev(tids, "tids", torch.int32),
-                                   _dev(E_small, "E_small", Z.dtype), _dev(P, "P", Z.dtype), _dev(A, "A", Z.dtype),
-                                   _dev(Xhat, "Xhat", Z.dtype), B, T, d, r, V, dt,
+    pk, nb = _pk(pk, d, r, ra, dt, Z)
+    _check(load().mapl_reconstruct(_dev(Z, "Z"), _opt(tids, "tids", torch.int32),
+                                   _opt(E_small, "E_small", Z.dtype), _opt(P, "P", Z.dtype), _dev(A, "A", Z.dtype),
+                                   _dev(Xhat, "Xhat", Z.dtype), B, T, d, r, ra, V, dt,
                                    pk.data_ptr() if pk is not None else None, nb, int(bool(pk_ready)),
                                    _stream(stream)), "mapl_reconstruct")
     return Xhat
 
 
-def mapl_bwd_workspace_bytes(B: int, T: int, d: int, r: int, dtype=torch.bfloat16) -> int:
-    return int(load().mapl_bwd_workspace_bytes(B, T, d, r, MAPL_BF16 if dtype == torch.bfloat16 else MAPL_F32))
+def mapl_bwd_workspace_bytes(B: int, T: int, d: int, r: int, dtype=torch.bfloat16, ra: int = None) -> int:
+    """Workspace of both backward maps for anchor rank ra (default r)."""
+    ra = r if ra is None else ra
+    return int(load().mapl_bwd_workspace_bytes(B, T, d, r, ra, MAPL_BF16 if dtype == torch.bfloat16 else MAPL_F32))
 
 
 def _ws(ws, nbytes, like):
@@ -234,8 +258,8 @@ def mapl_reconstruct_bwd(gXhat, Z, A, gZ=None, gA=None, accumulate=False, pk=Non
     if gA is None:
         gA = torch.zeros((d, r), dtype=torch.float32, device=gXhat.device) if accumulate else \
             _empty((d, r), torch.float32, gXhat)
-    pk, nb = _pk(pk, d, r, dt, gXhat)
-    ws, wb = _ws(ws, int(load().mapl_bwd_workspace_bytes(B, T, d, r, dt)), gXhat)
+    pk, nb = _pk(pk, d, r, 0, dt, gXhat)  # the A^T section only
+    ws, wb = _ws(ws, int(load().mapl_bwd_workspace_bytes(B, T, d, r, 0, dt)), gXhat)
     _check(load().mapl_reconstruct_bwd(_dev(gXhat, "gXhat"), _dev(Z, "Z", gXhat.dtype), _dev(A, "A", gXhat.dtype),
                                        _dev(gZ, "gZ", gXhat.dtype), _dev(gA, "gA", torch.float32),
                                        int(bool(accumulate)), B, T, d, r, dt,
@@ -247,49 +271,57 @@ def mapl_reconstruct_bwd(gXhat, Z, A, gZ=None, gA=None, accumulate=False, pk=Non
 
 def mapl_compress_bwd(gZ, X, tids, E_small, P, A, gX=None, gA=None, accumulate=False, pk=None, pk_ready=False,
                       ws=None, stream=None):
-    """gX = gZ A^T ;  gA (+)= (X - E_small[tids] P)^T gZ.  Returns (gX, gA)."""
+    """gX = gZ A^T ;  gA (+)= (X - E_small[tids] P)^T gZ.  Returns (gX, gA).
+    E_small = P = None: no anchor."""
     d, r = A.shape
     B, T = _tokens(gZ, r, "gZ")
     dt = _dt(gZ)
-    V = E_small.shape[0]
+    ra = _ra(E_small)
+    V = E_small.shape[0] if E_small is not None else 0
     if gX is None:
         gX = _empty((*gZ.shape[:-1], d), gZ.dtype, gZ)
     if gA is None:
         gA = torch.zeros((d, r), dtype=torch.float32, device=gZ.device) if accumulate else \
             _empty((d, r), torch.float32, gZ)
-    pk, nb = _pk(pk, d, r, dt, gZ)
-    ws, wb = _ws(ws, int(load().mapl_bwd_workspace_bytes(B, T, d, r, dt)), gZ)
-    _check(load().mapl_compress_bwd(_dev(gZ, "gZ"), _dev(X, "X", gZ.dtype), _dev(tids, "tids", torch.int32),
-                                    _dev(E_small, "E_small", gZ.dtype), _dev(P, "P", gZ.dtype),
+    pk, nb = _pk(pk, d, r, ra, dt, gZ)
+    ws, wb = _ws(ws, int(load().mapl_bwd_workspace_bytes(B, T, d, r, ra, dt)), gZ)
+    _check(load().mapl_compress_bwd(_dev(gZ, "gZ"), _dev(X, "X", gZ.dtype), _opt(tids, "tids", torch.int32),
+                                    _opt(E_small, "E_small", gZ.dtype), _opt(P, "P", gZ.dtype),
                                     _dev(A, "A", gZ.dtype), _dev(gX, "gX", gZ.dtype), _dev(gA, "gA", torch.float32),
-                                    int(bool(accumulate)), B, T, d, r, V, dt,
+                                    int(bool(accumulate)), B, T, d, r, ra, V, dt,
                                     pk.data_ptr() if pk is not None else None, nb, int(bool(pk_ready)),
                                     ws.data_ptr() if ws is not None else None, wb, _stream(stream)),
            "mapl_compress_bwd")
     return gX, gA
 
 
-def mapl_anchor_grad_workspace_bytes(B: int, T: int, r: int, V: int) -> int:
-    return int(load().mapl_anchor_grad_workspace_bytes(B, T, r, V))
+def mapl_anchor_grad_workspace_bytes(B: int, T: int, ra: int, V: int) -> int:
+    return int(load().mapl_anchor_grad_workspace_bytes(B, T, ra, V))
 
 
 def mapl_anchor_grad(Y, tids, P, V: int, alpha: float = 1.0, gE=None, accumulate=False, pk=None, pk_ready=False,
-                     ws=None, stream=None):
-    """gE [V, r] fp32 (+)= alpha * scatter-sum over tids of Y P^T.
+                     r: int = None, ws=None, stream=None):
+    """gE [V, ra] fp32 (+)= alpha * scatter-sum over tids of Y P^T (P [ra, d]).
 
     Receiver's anchor table: Y = gXhat, alpha = +1.  Sender's: Y = gX (the
-    gX output of mapl_compress_bwd), alpha = -1."""
-    r, d = P.shape
+    gX output of mapl_compress_bwd), alpha = -1.  r is the projector's rank,
+    on which the pack layout depends (default ra).  P = None is the full-rank
+    anchor (P = I, ra = d; no pack)."""
+    d = Y.shape[-1]
+    ra = d if P is None else int(P.shape[0])
+    if P is not None and P.shape[1] != d:
+        raise MaplError(-2, "binding", f"P is {tuple(P.shape)}, Y rows have {d} values")
+    r = ra if r is None else r
     B, T = _tokens(Y, d, "Y")
     dt = _dt(Y)
     if gE is None:
-        gE = torch.zeros((V, r), dtype=torch.float32, device=Y.device) if accumulate else \
-            _empty((V, r), torch.float32, Y)
-    pk, nb = _pk(pk, d, r, dt, Y)
-    ws, wb = _ws(ws, int(load().mapl_anchor_grad_workspace_bytes(B, T, r, V)), Y)
-    _check(load().mapl_anchor_grad(_dev(Y, "Y"), _dev(tids, "tids", torch.int32), _dev(P, "P", Y.dtype),
-                                   _dev(gE, "gE", torch.float32), float(alpha), int(bool(accumulate)), B, T, d, r, V,
-                                   dt, pk.data_ptr() if pk is not None else None, nb, int(bool(pk_ready)),
+        gE = torch.zeros((V, ra), dtype=torch.float32, device=Y.device) if accumulate else \
+            _empty((V, ra), torch.float32, Y)
+    pk, nb = _pk(pk, d, r, ra, dt, Y) if P is not None else (None, 0)
+    ws, wb = _ws(ws, int(load().mapl_anchor_grad_workspace_bytes(B, T, ra, V)), Y)
+    _check(load().mapl_anchor_grad(_dev(Y, "Y"), _dev(tids, "tids", torch.int32), _opt(P, "P", Y.dtype),
+                                   _dev(gE, "gE", torch.float32), float(alpha), int(bool(accumulate)), B, T, d, r, ra,
+                                   V, dt, pk.data_ptr() if pk is not None else None, nb, int(bool(pk_ready)),
                                    ws.data_ptr() if ws is not None else None, wb, _stream(stream)),
            "mapl_anchor_grad")
     return gE

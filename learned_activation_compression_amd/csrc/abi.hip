@@ -20,17 +20,21 @@ struct LaunchScope {
 
 inline bool dtype_ok(mapl_dtype dt) { return dt == MAPL_F32 || dt == MAPL_BF16; }
 
-// Shared shape rules of the codec entry points.
-int check_codec_shape(int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, mapl_dtype dt, bool needV) {
+// Shared shape rules of the codec entry points.  ra is the anchor rank
+// (0: no anchor); the id range V matters only when an anchor is read.
+int check_codec_shape(int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, int64_t V, mapl_dtype dt, bool needV) {
   if (!dtype_ok(dt)) return MAPL_ERR_DTYPE;
   if (B < 0 || T < 0) return MAPL_ERR_SHAPE;
   if (B > 0 && T > INT32_MAX / B) return MAPL_ERR_SHAPE;
   if (d < 1 || r < 1 || r > d || d > (1 << 20)) return MAPL_ERR_SHAPE;
-  if (needV && (V < 1 || V > INT32_MAX)) return MAPL_ERR_SHAPE;
+  if (ra < 0 || ra > d) return MAPL_ERR_SHAPE;
+  if (needV && ra > 0 && (V < 1 || V > INT32_MAX)) return MAPL_ERR_SHAPE;
   if (dt == MAPL_BF16) {
     // r a power of two in [32, 512]; d a multiple of 128 (the compression kernel
-    // splits d into four 32-column-aligned quarters)
+    // splits d into four 32-column-aligned quarters); an anchor rank other than r
+    // streams in 64-wide chunks
     if (d % 128 != 0 || r < 32 || r > 512 || (r & (r - 1)) != 0) return MAPL_ERR_SHAPE;
+    if (ra != 0 && ra != r && (ra % 64 != 0 || r % 64 != 0)) return MAPL_ERR_SHAPE;
   } else {
     if (d > 4096) return MAPL_ERR_SHAPE;
   }
@@ -39,22 +43,28 @@ int check_codec_shape(int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, map
   return MAPL_OK;
 }
 
+// the anchor pointers a map needs: none without an anchor; tids and E, and P
+// unless the anchor is the full-rank one (ra == d, P == NULL standing for I)
+bool anchor_ptrs_ok(int64_t ra, int64_t d, const void* tids, const void* E, const void* P) {
+  return ra == 0 || (tids && E && (P || ra == d));
+}
+
 // one split count for both backward maps (the larger Gram decides)
 int bwd_splits(int64_t N, int64_t d, int64_t r) { return gram_splits_bf16(int(N), int(d + r), int(r)); }
 
-int check_pack(void* pk, size_t pk_bytes, int64_t d, int64_t r, mapl_dtype dt) {
+int check_pack(void* pk, size_t pk_bytes, int64_t d, int64_t r, int64_t ra, mapl_dtype dt) {
   if (dt != MAPL_BF16) return MAPL_OK;
   if (pk == nullptr) return MAPL_ERR_NULL;
-  if (pk_bytes < pack_bytes_bf16(d, r)) return MAPL_ERR_WORKSPACE;
+  if (pk_bytes < pack_bytes_bf16(d, r, ra)) return MAPL_ERR_WORKSPACE;
   return MAPL_OK;
 }
 
-// bf16: the Gram partials [S][d + r][r] of compress_bwd (reconstruct_bwd uses
-// the first S d r of them) and M [r][r]
-size_t bwd_ws_bytes(int64_t N, int64_t d, int64_t r, mapl_dtype dt) {
+// bf16: the Gram partials [S][d + ra][r] of compress_bwd (reconstruct_bwd uses
+// the first S d r of them) and M [ra][r]; fp32: the residual [N][d]
+size_t bwd_ws_bytes(int64_t N, int64_t d, int64_t r, int64_t ra, mapl_dtype dt) {
   if (dt == MAPL_F32) return size_t(N) * d * sizeof(float);
   const int S = bwd_splits(N, d, r);
-  return (size_t(S) * (d + r) * r + size_t(r) * r) * sizeof(float);
+  return (size_t(S) * (d + ra) * r + size_t(ra) * r) * sizeof(float);
 }
 
 }  // namespace
@@ -76,95 +86,109 @@ const char* mapl_status_string(int status) {
 
 const char* mapl_version(void) { return kVersion; }
 
-size_t mapl_pack_bytes(int64_t d, int64_t r, mapl_dtype dt) {
-  if (dt != MAPL_BF16 || d < 1 || r < 1) return 0;
-  return pack_bytes_bf16(d, r);
+size_t mapl_pack_bytes(int64_t d, int64_t r, int64_t ra, mapl_dtype dt) {
+  if (dt != MAPL_BF16 || check_codec_shape(1, 1, d, r, ra, 1, dt, false)) return 0;
+  return pack_bytes_bf16(d, r, ra);
 }
 
-int mapl_pack(const void* P, const void* A, void* pk, size_t pk_bytes, int64_t d, int64_t r, mapl_dtype dt,
-              hipStream_t stream) {
-  int st = check_codec_shape(1, 1, d, r, 1, dt, false);
+int mapl_pack(const void* P, const void* A, void* pk, size_t pk_bytes, int64_t d, int64_t r, int64_t ra,
+              mapl_dtype dt, hipStream_t stream) {
+  int st = check_codec_shape(1, 1, d, r, ra, 1, dt, false);
   if (st) return st;
   if (dt == MAPL_F32) return MAPL_OK;
-  if (!P || !A) return MAPL_ERR_NULL;
-  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
+  if (!A || (ra > 0 && !P && ra != d)) return MAPL_ERR_NULL;
+  if ((st = check_pack(pk, pk_bytes, d, r, ra, dt))) return st;
   LaunchScope ls;
-  PackView v = pack_view(pk, d, r);
-  const uint16_t* A16 = static_cast<const uint16_t*>(A);
-  const uint16_t* P16 = static_cast<const uint16_t*>(P);
-  launch_pack_all(P16, A16, v, int(d), int(r), stream);
+  PackView v = pack_view(pk, d, r, ra);
+  launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), int(ra),
+                  stream);
   return ls.done();
 }
 
 int mapl_compress(const void* X, const int32_t* tids, const void* E_small, const void* P, const void* A, void* Z,
-                  int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, mapl_dtype dt, void* pk, size_t pk_bytes,
-                  int pk_ready, hipStream_t stream) {
-  int st = check_codec_shape(B, T, d, r, V, dt, true);
+                  int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, int64_t V, mapl_dtype dt, void* pk,
+                  size_t pk_bytes, int pk_ready, hipStream_t stream) {
+  int st = check_codec_shape(B, T, d, r, ra, V, dt, true);
   if (st) return st;
   if (pk_ready != 0 && pk_ready != 1) return MAPL_ERR_ARG;
   const int N = int(B * T);
   if (N == 0) return MAPL_OK;  // nothing to do; outputs untouched
-  if (!X || !tids || !E_small || !P || !A || !Z) return MAPL_ERR_NULL;
-  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
+  if (!X || !A || !Z || !anchor_ptrs_ok(ra, d, tids, E_small, P)) return MAPL_ERR_NULL;
+  if ((st = check_pack(pk, pk_bytes, d, r, ra, dt))) return st;
   LaunchScope ls;
   if (dt == MAPL_F32) {
     launch_compress_f32(static_cast<const float*>(X), tids, static_cast<const float*>(E_small),
                         static_cast<const float*>(P), static_cast<const float*>(A), static_cast<float*>(Z), N, int(d),
-                        int(r), int(V), stream);
+                        int(r), int(ra), int(V), stream);
     return ls.done();
   }
-  PackView v = pack_view(pk, d, r);
-  if (!pk_ready) launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), stream);
-  launch_tok_reduce_bf16(static_cast<const uint16_t*>(X), v.AtF, tids, static_cast<const uint16_t*>(E_small), v.QnF,
-                         static_cast<uint16_t*>(Z), N, int(d), int(r), int(V), stream);
+  PackView v = pack_view(pk, d, r, ra);
+  if (!pk_ready)
+    launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), int(ra),
+                    stream);
+  launch_tok_reduce_bf16(static_cast<const uint16_t*>(X), v.AtF, tids,
+                         ra > 0 ? static_cast<const uint16_t*>(E_small) : nullptr, v.QnF, static_cast<uint16_t*>(Z),
+                         N, int(d), int(r), int(ra), int(V), stream);
   return ls.done();
 }
 
 int mapl_reconstruct(const void* Z, const int32_t* tids, const void* E_small, const void* P, const void* A,
-                     void* Xhat, int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, mapl_dtype dt, void* pk,
-                     size_t pk_bytes, int pk_ready, hipStream_t stream) {
-  int st = check_codec_shape(B, T, d, r, V, dt, true);
+                     void* Xhat, int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, int64_t V, mapl_dtype dt,
+                     void* pk, size_t pk_bytes, int pk_ready, hipStream_t stream) {
+  int st = check_codec_shape(B, T, d, r, ra, V, dt, true);
   if (st) return st;
   if (pk_ready != 0 && pk_ready != 1) return MAPL_ERR_ARG;
   const int N = int(B * T);
   if (N == 0) return MAPL_OK;  // nothing to do; outputs untouched
-  if (!Z || !tids || !E_small || !P || !A || !Xhat) return MAPL_ERR_NULL;
-  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
+  if (!Z || !A || !Xhat || !anchor_ptrs_ok(ra, d, tids, E_small, P)) return MAPL_ERR_NULL;
+  if ((st = check_pack(pk, pk_bytes, d, r, ra, dt))) return st;
   LaunchScope ls;
   if (dt == MAPL_F32) {
     launch_reconstruct_f32(static_cast<const float*>(Z), tids, static_cast<const float*>(E_small),
                            static_cast<const float*>(P), static_cast<const float*>(A), static_cast<float*>(Xhat), N,
-                           int(d), int(r), int(V), stream);
+                           int(d), int(r), int(ra), int(V), stream);
     return ls.done();
   }
-  PackView v = pack_view(pk, d, r);
-  if (!pk_ready) launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), stream);
-  launch_tok_expand_bf16(static_cast<const uint16_t*>(Z), v.AF, tids, static_cast<const uint16_t*>(E_small), v.PtF,
-                         static_cast<uint16_t*>(Xhat), N, int(d), int(r), int(V), stream);
+  PackView v = pack_view(pk, d, r, ra);
+  if (!pk_ready)
+    launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), int(ra),
+                    stream);
+  if (ra > 0 && P == nullptr) {  // full-rank anchor: add the rows E[t] in the epilogue
+    if (!launch_tok_gemm_eadd_bf16(static_cast<const uint16_t*>(Z), int(r), tids, int(V),
+                                   static_cast<const uint16_t*>(E_small), v.AF, static_cast<uint16_t*>(Xhat), N,
+                                   int(d), stream))
+      return MAPL_ERR_SHAPE;  // not reached: ra = d != r needs r % 64 == 0
+    return ls.done();
+  }
+  if (!launch_tok_expand_bf16(static_cast<const uint16_t*>(Z), v.AF, tids,
+                              ra > 0 ? static_cast<const uint16_t*>(E_small) : nullptr, v.PtF,
+                              static_cast<uint16_t*>(Xhat), N, int(d), int(r), int(ra), int(V), stream))
+    return MAPL_ERR_SHAPE;  // not reached: check_codec_shape admits only covered shapes
   return ls.done();
 }
 
-size_t mapl_bwd_workspace_bytes(int64_t B, int64_t T, int64_t d, int64_t r, mapl_dtype dt) {
-  if (check_codec_shape(B, T, d, r, 1, dt, false)) return 0;
-  return bwd_ws_bytes(B * T, d, r, dt);
+size_t mapl_bwd_workspace_bytes(int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, mapl_dtype dt) {
+  if (check_codec_shape(B, T, d, r, ra, 1, dt, false)) return 0;
+  return bwd_ws_bytes(B * T, d, r, ra, dt);
 }
 
 int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A, void* gZ, float* gA, int accumulate,
                          int64_t B, int64_t T, int64_t d, int64_t r, mapl_dtype dt, void* pk, size_t pk_bytes,
                          int pk_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = check_codec_shape(B, T, d, r, 1, dt, false);
+  int st = check_codec_shape(B, T, d, r, 0, 1, dt, false);
   if (st) return st;
   if ((accumulate != 0 && accumulate != 1) || (pk_ready != 0 && pk_ready != 1)) return MAPL_ERR_ARG;
   const int64_t N = B * T;
   if (!gA) return MAPL_ERR_NULL;
   if (N == 0) {  // empty batch: gA = 0 (or unchanged when accumulating)
+    if (accumulate) return MAPL_OK;
     LaunchScope ls0;
-    if (!accumulate) launch_fill_f32(gA, d * r, 0.f, stream);
+    launch_fill_f32(gA, d * r, 0.f, stream);
     return ls0.done();
   }
   if (!gXhat || !Z || !A || !gZ) return MAPL_ERR_NULL;
-  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
-  const size_t need = bwd_ws_bytes(N, d, r, dt);
+  if ((st = check_pack(pk, pk_bytes, d, r, 0, dt))) return st;  // the A^T section, first in every pack
+  const size_t need = bwd_ws_bytes(N, d, r, 0, dt);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return ws == nullptr ? MAPL_ERR_NULL : MAPL_ERR_WORKSPACE;
   LaunchScope ls;
   if (dt == MAPL_F32) {
@@ -175,13 +199,13 @@ int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A, void* 
                      accumulate, stream);
     return ls.done();
   }
-  PackView v = pack_view(pk, d, r);
+  PackView v = pack_view(pk, d, r, 0);
   if (!pk_ready) launch_pack_AtF(static_cast<const uint16_t*>(A), v.AtF, int(d), int(r), stream);
   const int S = bwd_splits(N, d, r);  // same split count as compress_bwd: the workspace fits both
   float* part = static_cast<float*>(ws);
   if (N > 0) {
     launch_tok_reduce_bf16(static_cast<const uint16_t*>(gXhat), v.AtF, nullptr, nullptr, nullptr,
-                           static_cast<uint16_t*>(gZ), int(N), int(d), int(r), 1, stream);
+                           static_cast<uint16_t*>(gZ), int(N), int(d), int(r), 0, 1, stream);
     // gA (+)= gXhat^T Z
     launch_gram_bf16(static_cast<const uint16_t*>(gXhat), d, int(d), nullptr, 1, nullptr, 0,
                      static_cast<const uint16_t*>(Z), int(r), part, int(N), S, stream);
@@ -192,21 +216,22 @@ int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A, void* 
 
 int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const void* E_small, const void* P,
                       const void* A, void* gX, float* gA, int accumulate, int64_t B, int64_t T, int64_t d, int64_t r,
-                      int64_t V, mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready, void* ws, size_t ws_bytes,
-                      hipStream_t stream) {
-  int st = check_codec_shape(B, T, d, r, V, dt, true);
+                      int64_t ra, int64_t V, mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  int st = check_codec_shape(B, T, d, r, ra, V, dt, true);
   if (st) return st;
   if ((accumulate != 0 && accumulate != 1) || (pk_ready != 0 && pk_ready != 1)) return MAPL_ERR_ARG;
   const int64_t N = B * T;
   if (!gA) return MAPL_ERR_NULL;
   if (N == 0) {  // empty batch: gA = 0 (or unchanged when accumulating)
+    if (accumulate) return MAPL_OK;
     LaunchScope ls0;
-    if (!accumulate) launch_fill_f32(gA, d * r, 0.f, stream);
+    launch_fill_f32(gA, d * r, 0.f, stream);
     return ls0.done();
   }
-  if (!gZ || !X || !tids || !E_small || !P || !A || !gX) return MAPL_ERR_NULL;
-  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
-  const size_t need = bwd_ws_bytes(N, d, r, dt);
+  if (!gZ || !X || !A || !gX || !anchor_ptrs_ok(ra, d, tids, E_small, P)) return MAPL_ERR_NULL;
+  if ((st = check_pack(pk, pk_bytes, d, r, ra, dt))) return st;
+  const size_t need = bwd_ws_bytes(N, d, r, ra, dt);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return ws == nullptr ? MAPL_ERR_NULL : MAPL_ERR_WORKSPACE;
   LaunchScope ls;
   if (dt == MAPL_F32) {
@@ -215,64 +240,68 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const 
       launch_rowmap_f32(static_cast<const float*>(gZ), static_cast<const float*>(A), static_cast<float*>(gX), int(N),
                         int(d), int(r), 1, stream);
       launch_residual_f32(static_cast<const float*>(X), tids, static_cast<const float*>(E_small),
-                          static_cast<const float*>(P), R, int(N), int(d), int(r), int(V), stream);
+                          static_cast<const float*>(P), R, int(N), int(d), int(ra), int(V), stream);
     }
     launch_outer_f32(R, static_cast<const float*>(gZ), gA, int(N), int(d), int(r), accumulate, stream);
     return ls.done();
   }
   const int S = bwd_splits(N, d, r);
-  float* part = static_cast<float*>(ws);           // [S][d + r][r]
-  float* M = part + size_t(S) * (d + r) * r;       // [r][r]
+  float* part = static_cast<float*>(ws);           // [S][d + ra][r]
+  float* M = part + size_t(S) * (d + ra) * r;      // [ra][r]
   const uint16_t* gZ16 = static_cast<const uint16_t*>(gZ);
-  PackView v = pack_view(pk, d, r);
-  if (!pk_ready) launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), stream);
+  PackView v = pack_view(pk, d, r, ra);
+  if (!pk_ready)
+    launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), int(ra),
+                    stream);
   // gX = gZ A^T
-  launch_tok_expand_bf16(gZ16, v.AF, nullptr, nullptr, nullptr, static_cast<uint16_t*>(gX), int(N), int(d), int(r), 1,
-                         stream);
+  launch_tok_expand_bf16(gZ16, v.AF, nullptr, nullptr, nullptr, static_cast<uint16_t*>(gX), int(N), int(d), int(r), 0,
+                         1, stream);
   // gA (+)= X^T gZ - P^T (E[t]^T gZ): one Gram over the rows of [X | E[t]], then
   // the split sums (rows < d into gA, rows >= d into M) and gA -= P^T M
   launch_gram_bf16(static_cast<const uint16_t*>(X), d, int(d), tids, int(V),
-                   static_cast<const uint16_t*>(E_small), int(r), gZ16, int(r), part, int(N), S, stream);
-  launch_reduce_partials(part, S, (d + r) * r, gA, d * r, accumulate, M, r * r, stream);
-  launch_sub_ptm(static_cast<const uint16_t*>(P), M, gA, int(d), int(r), stream);
+                   ra > 0 ? static_cast<const uint16_t*>(E_small) : nullptr, int(ra), gZ16, int(r), part, int(N), S,
+                   stream);
+  launch_reduce_partials(part, S, (d + ra) * r, gA, d * r, accumulate, M, ra * r, stream);
+  if (ra > 0) launch_sub_ptm(static_cast<const uint16_t*>(P), M, gA, int(d), int(r), int(ra), stream);
   return ls.done();
 }
 
-size_t mapl_anchor_grad_workspace_bytes(int64_t B, int64_t T, int64_t r, int64_t V) {
-  if (B < 0 || T < 0 || r < 1 || V < 1 || V > (int64_t(1) << 22)) return 0;
+size_t mapl_anchor_grad_workspace_bytes(int64_t B, int64_t T, int64_t ra, int64_t V) {
+  if (B < 0 || T < 0 || ra < 1 || V < 1 || V > (int64_t(1) << 22)) return 0;
   if (B > 0 && T > INT32_MAX / B) return 0;
-  return anchor_grad_ws_bytes(B * T, r, V);
+  return anchor_grad_ws_bytes(B * T, ra, V);
 }
 
 int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* gE, float alpha, int accumulate,
-                     int64_t B, int64_t T, int64_t d, int64_t r, int64_t V, mapl_dtype dt, void* pk, size_t pk_bytes,
-                     int pk_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
-  int st = check_codec_shape(B, T, d, r, V, dt, true);
+                     int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, int64_t V, mapl_dtype dt, void* pk,
+                     size_t pk_bytes, int pk_ready, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int st = check_codec_shape(B, T, d, r, ra, V, dt, true);
   if (st) return st;
+  if (ra < 1) return MAPL_ERR_SHAPE;  // no anchor, no table
   if ((accumulate != 0 && accumulate != 1) || (pk_ready != 0 && pk_ready != 1) || !std::isfinite(alpha))
     return MAPL_ERR_ARG;
   const int64_t N = B * T;
-  if (V > (int64_t(1) << 22) || N * r > (int64_t(1) << 38)) return MAPL_ERR_SHAPE;
+  if (V > (int64_t(1) << 22) || N * ra > (int64_t(1) << 38)) return MAPL_ERR_SHAPE;
   if (!gE) return MAPL_ERR_NULL;
   if (N == 0) {  // empty batch: gE = 0 (or unchanged when accumulating)
     if (accumulate) return MAPL_OK;
     LaunchScope ls0;
-    launch_fill_f32(gE, V * r, 0.f, stream);
+    launch_fill_f32(gE, V * ra, 0.f, stream);
     return ls0.done();
   }
-  if (!Y || !tids || !P) return MAPL_ERR_NULL;
-  if ((st = check_pack(pk, pk_bytes, d, r, dt))) return st;
+  if (!Y || !tids || (!P && ra != d)) return MAPL_ERR_NULL;
+  if (P != nullptr && (st = check_pack(pk, pk_bytes, d, r, ra, dt))) return st;  // the identity needs no pack
   if (!ws) return MAPL_ERR_NULL;
-  if (ws_bytes < anchor_grad_ws_bytes(N, r, V)) return MAPL_ERR_WORKSPACE;
+  if (ws_bytes < anchor_grad_ws_bytes(N, ra, V)) return MAPL_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) & 15) return MAPL_ERR_ARG;
   LaunchScope ls;
   const uint16_t* PF = nullptr;
-  if (dt == MAPL_BF16) {
-    PackView v = pack_view(pk, d, r);
-    if (!pk_ready) launch_pack_PF(static_cast<const uint16_t*>(P), v.PF, int(d), int(r), stream);
+  if (dt == MAPL_BF16 && P != nullptr) {
+    PackView v = pack_view(pk, d, r, ra);
+    if (!pk_ready) launch_pack_PF(static_cast<const uint16_t*>(P), v.PF, int(d), int(ra), stream);
     PF = v.PF;
   }
-  launch_anchor_grad(Y, dt == MAPL_BF16, tids, P, PF, gE, alpha, accumulate, int(N), int(d), int(r), int(V), ws,
+  launch_anchor_grad(Y, dt == MAPL_BF16, tids, P, PF, gE, alpha, accumulate, int(N), int(d), int(ra), int(V), ws,
                      stream);
   return ls.done();
 }

@@ -130,6 +130,46 @@ __global__ __launch_bounds__(256) void k_ag_project_f32(const float* __restrict_
   if (threadIdx.x == 0) part[blockIdx.x] = m;
 }
 
+// Identity projection (the full-rank anchor, P = I, r = d): U = alpha Y.
+// bf16: 8 values per thread and step (d % 8 == 0); fp32: one value.  Grid-stride.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_ag_identity(const void* __restrict__ Yv, float* __restrict__ U,
+                                                     float* __restrict__ part, float alpha, int64_t ne) {
+  __shared__ float red[4];
+  float local = 0.f;
+  const int64_t step = int64_t(gridDim.x) * 256;
+  if (BF16) {
+    const u32x4* Y = static_cast<const u32x4*>(Yv);
+    for (int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x; u < ne / 8; u += step) {
+      const u32x4 y = Y[u];
+      f32x4 v[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t w = y[2 * h + e];
+          v[h][2 * e] = alpha * bf2f(uint16_t(w & 0xffffu));
+          v[h][2 * e + 1] = alpha * bf2f(uint16_t(w >> 16));
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) local = fmaxf(local, fabsf(v[h][e]));
+        reinterpret_cast<f32x4*>(U)[2 * u + h] = v[h];
+      }
+    }
+  } else {
+    const float* Y = static_cast<const float*>(Yv);
+    for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < ne; e += step) {
+      const float v = alpha * Y[e];
+      U[e] = v;
+      local = fmaxf(local, fabsf(v));
+    }
+  }
+  const float m = block_max<4>(local, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
+}
+
 // power-of-two scale 2^e of the fixed-point terms: with max |U| < 2^ex every
 // scaled term is below 2^30 in magnitude (an int32 after rounding), so a sum
 // of at most N < 2^31 of them stays below 2^61 in 64 bits.  Each term is
@@ -340,7 +380,14 @@ void launch_anchor_grad(const void* Y, int y_bf16, const int32_t* tids, const vo
   float* U = static_cast<float*>(ws);
   float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + part_offset(N, r));
   int npart;
-  if (y_bf16 && PF != nullptr &&
+  if (P == nullptr) {  // identity projection (r == d)
+    const int64_t ne = int64_t(N) * d;
+    npart = int(std::min<int64_t>((ne / (y_bf16 ? 8 : 1) + 255) / 256, kProjMaxGrid));
+    if (y_bf16)
+      hipLaunchKernelGGL(k_ag_identity<true>, dim3(unsigned(npart)), dim3(256), 0, s, Y, U, part, alpha, ne);
+    else
+      hipLaunchKernelGGL(k_ag_identity<false>, dim3(unsigned(npart)), dim3(256), 0, s, Y, U, part, alpha, ne);
+  } else if (y_bf16 && PF != nullptr &&
       launch_tok_reduce_f32out(static_cast<const uint16_t*>(Y), PF, U, alpha, part, N, d, r, s)) {
     npart = 4 * ((N + 63) / 64);
   } else if (y_bf16) {

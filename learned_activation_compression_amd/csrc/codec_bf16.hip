@@ -33,14 +33,14 @@ template <int RB, int P, bool ANCHOR>
 __global__ __launch_bounds__(256) void k_tok_reduce(const bf16_t* __restrict__ X, const bf16_t* __restrict__ AtF,
                                                     const int32_t* __restrict__ tids, const bf16_t* __restrict__ E,
                                                     const bf16_t* __restrict__ QnF, bf16_t* __restrict__ Z, int N,
-                                                    int d, int r, int V) {
+                                                    int d, int r, int ra, int V) {
   __shared__ __attribute__((aligned(16))) float redbuf[4 * RB * 64 * 16];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int hi = lane >> 5, l32 = lane & 31;
   const int tok0 = blockIdx.x * 64;
   const int rbase = blockIdx.y * (RB * 32);
   const int Sd = d >> 4;
-  const int Se = ANCHOR ? (r >> 4) : 0;
+  const int Se = ANCHOR ? (ra >> 4) : 0;
   const int S = Sd + Se;
   const int sb = (S * wave) >> 2, se = (S * (wave + 1)) >> 2;
 
@@ -66,8 +66,8 @@ __global__ __launch_bounds__(256) void k_tok_reduce(const bf16_t* __restrict__ X
     const bool e0 = (t0 >= 0 && t0 < V), e1 = (t1 >= 0 && t1 < V);
     m0 = e0 ? ~0u : 0u;
     m1 = e1 ? ~0u : 0u;
-    er0 = E + size_t(e0 ? t0 : 0) * r + 8 * hi;
-    er1 = E + size_t(e1 ? t1 : 0) * r + 8 * hi;
+    er0 = E + size_t(e0 ? t0 : 0) * ra + 8 * hi;
+    er1 = E + size_t(e1 ? t1 : 0) * ra + 8 * hi;
     q0 = QnF + (size_t(rbase >> 5) * 64 + lane) * 8;
   }
 
@@ -191,8 +191,9 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
                                                             const int32_t* __restrict__ tids,
                                                             const bf16_t* __restrict__ E,
                                                             const bf16_t* __restrict__ QnF, bf16_t* __restrict__ Z,
-                                                            int N, int d, int r, int V, float* __restrict__ Uf,
-                                                            float alpha, float* __restrict__ part) {
+                                                            int N, int d, int r, int ra, int V,
+                                                            float* __restrict__ Uf, float alpha,
+                                                            float* __restrict__ part) {
   using RR = RedRing<RBW, S>;
   static_assert(S % G == 0 && S / G >= 2, "each wave group needs its own slots");
   extern __shared__ __attribute__((aligned(16))) u32x4 ring[];
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
   const int hi = lane >> 5, l32 = lane & 31;
   const int tok0 = blockIdx.x * 64;
   const int MB = r >> 5;
-  const int cx = d / kRedKC, nch = cx + (ANCHOR ? r / kRedKC : 0);
+  const int cx = d / kRedKC, nch = cx + (ANCHOR ? ra / kRedKC : 0);
 
   // copy role: this lane copies unit (lane & 7) of rows 16 w + 8 q + (lane >> 3), q = 0, 1;
   // the row's low 3 bits are lane >> 3, so the source unit is (lane & 7) ^ (lane >> 3)
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
     eoff[q] = 8 * cu;
     if (ANCHOR) {
       const int t = tids[tk];
-      eoff[q] += size_t((t >= 0 && t < V) ? t : 0) * r;
+      eoff[q] += size_t((t >= 0 && t < V) ? t : 0) * ra;
     }
   }
   // matrix-core operand masks: token tb*32 + l32 with an invalid id reads a zero anchor row
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
 
 template <int RBW, int S, int G, bool ANCHOR, bool OUTF = false>
 static void launch_reduce_dma(const uint16_t* in, const uint16_t* AtF, const int32_t* tids, const uint16_t* E,
-                              const uint16_t* QnF, uint16_t* out, int N, int d, int r, int V, hipStream_t s,
+                              const uint16_t* QnF, uint16_t* out, int N, int d, int r, int ra, int V, hipStream_t s,
                               float* Uf = nullptr, float alpha = 1.f, float* part = nullptr) {
   auto k = k_tok_reduce_dma<RBW, S, G, ANCHOR, OUTF>;
   const size_t lds = RedRing<RBW, S>::BYTES;
@@ -362,41 +363,44 @@ static void launch_reduce_dma(const uint16_t* in, const uint16_t* AtF, const int
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
     attr = true;
   }
-  hipLaunchKernelGGL(k, dim3((N + 63) / 64), dim3(256 * G), lds, s, in, AtF, tids, E, QnF, out, N, d, r, V, Uf,
+  hipLaunchKernelGGL(k, dim3((N + 63) / 64), dim3(256 * G), lds, s, in, AtF, tids, E, QnF, out, N, d, r, ra, V, Uf,
                      alpha, part);
 }
 
 bool launch_tok_reduce_f32out(const uint16_t* in, const uint16_t* F, float* U, float alpha, float* part, int N,
                               int d, int r, hipStream_t s) {
   if (r == 128) {
-    launch_reduce_dma<1, 6, 2, false, true>(in, F, nullptr, nullptr, nullptr, nullptr, N, d, r, 0, s, U, alpha, part);
+    launch_reduce_dma<1, 6, 2, false, true>(in, F, nullptr, nullptr, nullptr, nullptr, N, d, r, 0, 0, s, U, alpha,
+                                            part);
     return true;
   }
   if (r == 256) {
-    launch_reduce_dma<2, 3, 1, false, true>(in, F, nullptr, nullptr, nullptr, nullptr, N, d, r, 0, s, U, alpha, part);
+    launch_reduce_dma<2, 3, 1, false, true>(in, F, nullptr, nullptr, nullptr, nullptr, N, d, r, 0, 0, s, U, alpha,
+                                            part);
     return true;
   }
   return false;
 }
 
 void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32_t* tids, const uint16_t* E,
-                            const uint16_t* QnF, uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
+                            const uint16_t* QnF, uint16_t* out, int N, int d, int r, int ra, int V, hipStream_t s) {
   // ANCHOR = true is the compress map of Eq. (1); false is the plain product (gZ = gXhat A)
-  const bool anc = E != nullptr;
-  if (r >= 512 && launch_tok_gemm_bf16(in, d, tids, V, E, anc ? r : 0, AtF, QnF, out, N, r, s)) return;
+  const bool anc = E != nullptr && ra > 0;
+  if (!anc) E = nullptr;
+  if (r >= 512 && launch_tok_gemm_bf16(in, d, tids, V, E, anc ? ra : 0, AtF, QnF, out, N, r, s)) return;
   if (r == 128) {
-    if (anc) launch_reduce_dma<1, 6, 2, true>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
-    else launch_reduce_dma<1, 6, 2, false>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
+    if (anc) launch_reduce_dma<1, 6, 2, true>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
+    else launch_reduce_dma<1, 6, 2, false>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
     return;
   }
   if (r == 256) {
-    if (anc) launch_reduce_dma<2, 3, 1, true>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
-    else launch_reduce_dma<2, 3, 1, false>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
+    if (anc) launch_reduce_dma<2, 3, 1, true>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
+    else launch_reduce_dma<2, 3, 1, false>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
     return;
   }
   if (r == 512) {
-    if (anc) launch_reduce_dma<4, 2, 1, true>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
-    else launch_reduce_dma<4, 2, 1, false>(in, AtF, tids, E, QnF, out, N, d, r, V, s);
+    if (anc) launch_reduce_dma<4, 2, 1, true>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
+    else launch_reduce_dma<4, 2, 1, false>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
     return;
   }
   const int nb = r / 32;
@@ -405,7 +409,7 @@ void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32
   auto k = anc ? (RB == 4 ? k_tok_reduce<4, 4, true> : RB == 2 ? k_tok_reduce<2, 6, true> : k_tok_reduce<1, 8, true>)
                : (RB == 4 ? k_tok_reduce<4, 4, false> : RB == 2 ? k_tok_reduce<2, 6, false>
                                                                : k_tok_reduce<1, 8, false>);
-  hipLaunchKernelGGL(k, grid, dim3(256), 0, s, in, AtF, tids, E, QnF, out, N, d, r, V);
+  hipLaunchKernelGGL(k, grid, dim3(256), 0, s, in, AtF, tids, E, QnF, out, N, d, r, ra, V);
 }
 
 // ---------------------------------------------------------------- expand --
@@ -562,9 +566,12 @@ __global__ __launch_bounds__(256, 2) void k_tok_expand(const bf16_t* __restrict_
   }
 }
 
-void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_t* tids, const uint16_t* E,
-                            const uint16_t* PtF, uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
-  if (r >= 256 && launch_tok_gemm_bf16(in, r, tids, V, E, E != nullptr ? r : 0, AF, PtF, out, N, d, s)) return;
+bool launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_t* tids, const uint16_t* E,
+                            const uint16_t* PtF, uint16_t* out, int N, int d, int r, int ra, int V, hipStream_t s) {
+  if (ra == 0) E = nullptr;
+  // the staged-row kernel takes an anchor of rank r only; other ranks use the token GEMM
+  if (r >= 256 || (E != nullptr && ra != r))
+    return launch_tok_gemm_bf16(in, r, tids, V, E, E != nullptr ? ra : 0, AF, PtF, out, N, d, s);
   const int S = (E != nullptr) ? r / 8 : r / 16;  // K-steps
   const int UR = 2 * S;                            // 16-byte units per token row (a power of two)
   int ur_log2 = 0;
@@ -587,6 +594,7 @@ void launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_
   else if (TB == 2) MAPL_EXPAND(2, 16);
   else MAPL_EXPAND(1, 16);
 #undef MAPL_EXPAND
+  return true;
 }
 
 // ------------------------------------------------------------------ gram --
@@ -823,15 +831,15 @@ void launch_reduce_partials(const float* part, int splits, int64_t stride, float
 }
 
 // ------------------------------------------------- anchor-term correction --
-// gA[i][j] -= sum_k P[k][i] M[k][j]  (P bf16 [r][d], M fp32 [r][r], gA fp32 [d][r]).
+// gA[i][j] -= sum_k P[k][i] M[k][j]  (P bf16 [ra][d], M fp32 [ra][r], gA fp32 [d][r]).
 // One block per 32 x 32 tile of gA; the 4 waves split k and add in LDS.
 __global__ __launch_bounds__(256) void k_sub_ptm(const bf16_t* __restrict__ P, const float* __restrict__ M,
-                                                 float* __restrict__ gA, int d, int r) {
+                                                 float* __restrict__ gA, int d, int r, int ra) {
   __shared__ float red[4 * 1024];
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int hi = lane >> 5, l32 = lane & 31;
   const int i0 = blockIdx.x * 32, j0 = blockIdx.y * 32;
-  const int kq = r >> 2;  // r % 32 == 0: a multiple of 8
+  const int kq = ra >> 2;  // ra % 32 == 0: a multiple of 8
   f32x16 acc = f32x16{};
   for (int kc = wave * kq; kc < (wave + 1) * kq; kc += 8) {
     float a[4], b[4];
@@ -855,8 +863,20 @@ __global__ __launch_bounds__(256) void k_sub_ptm(const bf16_t* __restrict__ P, c
   *o = *o - sum;
 }
 
-void launch_sub_ptm(const uint16_t* P, const float* M, float* gA, int d, int r, hipStream_t s) {
-  hipLaunchKernelGGL(k_sub_ptm, dim3(d / 32, r / 32), dim3(256), 0, s, P, M, gA, d, r);
+// gA -= M elementwise (the identity anchor projector), 4 values per thread
+__global__ __launch_bounds__(256) void k_sub_m(const f32x4* __restrict__ M, f32x4* __restrict__ gA, int64_t n4) {
+  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (e < n4) gA[e] = gA[e] - M[e];
+}
+
+void launch_sub_ptm(const uint16_t* P, const float* M, float* gA, int d, int r, int ra, hipStream_t s) {
+  if (P == nullptr) {
+    const int64_t n4 = int64_t(d) * r / 4;
+    hipLaunchKernelGGL(k_sub_m, dim3(unsigned((n4 + 255) / 256)), dim3(256), 0, s, reinterpret_cast<const f32x4*>(M),
+                       reinterpret_cast<f32x4*>(gA), n4);
+    return;
+  }
+  hipLaunchKernelGGL(k_sub_ptm, dim3(d / 32, r / 32), dim3(256), 0, s, P, M, gA, d, r, ra);
 }
 
 }  // namespace mapl

@@ -5,6 +5,8 @@
 // These kernels take the definitions literally (the residual X - E[t] P is
 // formed before the projection) and sum in a fixed order; they serve the fp32
 // storage type, where the bf16 matrix cores would not meet fp32 accuracy.
+// The anchor has rank ra (E [V][ra], P [ra][d]); ra == 0 is no anchor, and
+// P == nullptr with ra == d is the full-rank anchor (P = I: the row E[t] itself).
 #include "common.h"
 #include "internal.h"
 
@@ -14,24 +16,34 @@ constexpr int kTokPerBlock = 4;
 
 __device__ __forceinline__ bool tid_ok(int t, int V) { return t >= 0 && t < V; }
 
+// anchor value at column i of token id t: sum_k E[t][k] P[k][i], or E[t][i] for P = I
+__device__ __forceinline__ float anchor_at(const float* __restrict__ E, const float* __restrict__ P, int t, int ra,
+                                           int d, int i) {
+  if (P == nullptr) return E[size_t(t) * ra + i];
+  float a = 0.f;
+  for (int k = 0; k < ra; ++k) a = fmaf(E[size_t(t) * ra + k], P[size_t(k) * d + i], a);
+  return a;
+}
+
 // R[n][i] = X[n][i] - sum_k E[t_n][k] P[k][i]
 __global__ __launch_bounds__(256) void k_residual_f32(const float* __restrict__ X, const int32_t* __restrict__ tids,
                                                       const float* __restrict__ E, const float* __restrict__ P,
-                                                      float* __restrict__ R, int N, int d, int r, int V) {
+                                                      float* __restrict__ R, int N, int d, int ra, int V) {
   const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (e >= int64_t(N) * d) return;
   const int n = int(e / d), i = int(e % d);
-  const int t = tids[n];
   float a = 0.f;
-  if (tid_ok(t, V))
-    for (int k = 0; k < r; ++k) a = fmaf(E[size_t(t) * r + k], P[size_t(k) * d + i], a);
+  if (ra > 0) {
+    const int t = tids[n];
+    if (tid_ok(t, V)) a = anchor_at(E, P, t, ra, d, i);
+  }
   R[e] = X[e] - a;
 }
 
 void launch_residual_f32(const float* X, const int32_t* tids, const float* E, const float* P, float* R, int N, int d,
-                         int r, int V, hipStream_t s) {
+                         int ra, int V, hipStream_t s) {
   const int64_t tot = int64_t(N) * d;
-  hipLaunchKernelGGL(k_residual_f32, dim3(unsigned((tot + 255) / 256)), dim3(256), 0, s, X, tids, E, P, R, N, d, r,
+  hipLaunchKernelGGL(k_residual_f32, dim3(unsigned((tot + 255) / 256)), dim3(256), 0, s, X, tids, E, P, R, N, d, ra,
                      V);
 }
 
@@ -39,17 +51,18 @@ void launch_residual_f32(const float* X, const int32_t* tids, const float* E, co
 __global__ __launch_bounds__(256) void k_compress_f32(const float* __restrict__ X, const int32_t* __restrict__ tids,
                                                       const float* __restrict__ E, const float* __restrict__ P,
                                                       const float* __restrict__ A, float* __restrict__ Z, int N, int d,
-                                                      int r, int V) {
+                                                      int r, int ra, int V) {
   extern __shared__ float Rs[];  // [kTokPerBlock][d]
   const int n0 = blockIdx.x * kTokPerBlock;
   for (int e = threadIdx.x; e < kTokPerBlock * d; e += 256) {
     const int tt = e / d, i = e % d, n = n0 + tt;
     float v = 0.f;
     if (n < N) {
-      const int t = tids[n];
       float a = 0.f;
-      if (tid_ok(t, V))
-        for (int k = 0; k < r; ++k) a = fmaf(E[size_t(t) * r + k], P[size_t(k) * d + i], a);
+      if (ra > 0) {
+        const int t = tids[n];
+        if (tid_ok(t, V)) a = anchor_at(E, P, t, ra, d, i);
+      }
       v = X[size_t(n) * d + i] - a;
     }
     Rs[e] = v;
@@ -65,30 +78,32 @@ __global__ __launch_bounds__(256) void k_compress_f32(const float* __restrict__ 
 }
 
 void launch_compress_f32(const float* X, const int32_t* tids, const float* E, const float* P, const float* A,
-                         float* Z, int N, int d, int r, int V, hipStream_t s) {
+                         float* Z, int N, int d, int r, int ra, int V, hipStream_t s) {
   const size_t lds = size_t(kTokPerBlock) * d * sizeof(float);
   hipLaunchKernelGGL(k_compress_f32, dim3((N + kTokPerBlock - 1) / kTokPerBlock), dim3(256), lds, s, X, tids, E, P,
-                     A, Z, N, d, r, V);
+                     A, Z, N, d, r, ra, V);
 }
 
 // Xh[n][i] = sum_j Z[n][j] A[i][j] + sum_k E[t_n][k] P[k][i]
 __global__ __launch_bounds__(256) void k_reconstruct_f32(const float* __restrict__ Z, const int32_t* __restrict__ tids,
                                                          const float* __restrict__ E, const float* __restrict__ P,
                                                          const float* __restrict__ A, float* __restrict__ Xh, int N,
-                                                         int d, int r, int V) {
-  extern __shared__ float sh[];  // Zs [4][r], Es [4][r]
+                                                         int d, int r, int ra, int V) {
+  extern __shared__ float sh[];  // Zs [4][r], Es [4][ra]
   float* Zs = sh;
   float* Es = sh + kTokPerBlock * r;
   const int n0 = blockIdx.x * kTokPerBlock;
   for (int e = threadIdx.x; e < kTokPerBlock * r; e += 256) {
     const int tt = e / r, k = e % r, n = n0 + tt;
-    float z = 0.f, ev = 0.f;
+    Zs[e] = n < N ? Z[size_t(n) * r + k] : 0.f;
+  }
+  for (int e = threadIdx.x; e < kTokPerBlock * ra; e += 256) {
+    const int tt = e / ra, k = e % ra, n = n0 + tt;
+    float ev = 0.f;
     if (n < N) {
-      z = Z[size_t(n) * r + k];
       const int t = tids[n];
-      if (tid_ok(t, V)) ev = E[size_t(t) * r + k];
+      if (tid_ok(t, V)) ev = E[size_t(t) * ra + k];
     }
-    Zs[e] = z;
     Es[e] = ev;
   }
   __syncthreads();
@@ -98,16 +113,26 @@ __global__ __launch_bounds__(256) void k_reconstruct_f32(const float* __restrict
     float x = 0.f;
     for (int j = 0; j < r; ++j) x = fmaf(Zs[tt * r + j], A[size_t(i) * r + j], x);
     float a = 0.f;
-    for (int k = 0; k < r; ++k) a = fmaf(Es[tt * r + k], P[size_t(k) * d + i], a);
+    if (P == nullptr) {
+      if (ra > 0) a = Es[tt * ra + i];  // identity anchor: ra == d
+    } else {
+      for (int k = 0; k < ra; ++k) a = fmaf(Es[tt * ra + k], P[size_t(k) * d + i], a);
+    }
     Xh[size_t(n) * d + i] = x + a;
   }
 }
 
 void launch_reconstruct_f32(const float* Z, const int32_t* tids, const float* E, const float* P, const float* A,
-                            float* Xh, int N, int d, int r, int V, hipStream_t s) {
-  const size_t lds = size_t(2) * kTokPerBlock * r * sizeof(float);
+                            float* Xh, int N, int d, int r, int ra, int V, hipStream_t s) {
+  const size_t lds = size_t(kTokPerBlock) * (r + ra) * sizeof(float);  // <= 128 KB (r, ra <= d <= 4096)
+  static bool attr = false;  // once per process: allow more than 64 KB of dynamic LDS
+  if (!attr) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k_reconstruct_f32),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(kTokPerBlock * 2 * 4096 * sizeof(float)));
+    attr = true;
+  }
   hipLaunchKernelGGL(k_reconstruct_f32, dim3((N + kTokPerBlock - 1) / kTokPerBlock), dim3(256), lds, s, Z, tids, E,
-                     P, A, Xh, N, d, r, V);
+                     P, A, Xh, N, d, r, ra, V);
 }
 
 // transposeA == 0: out[n][j] = sum_i in[n][i] A[i][j]   (in [N][d], out [N][r])

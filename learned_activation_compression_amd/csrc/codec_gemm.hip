@@ -15,6 +15,11 @@
 //   gX            src = gZ,    K1 = r, K2 = 0, F1 = AF,            C = d
 // An id outside [0, V) gives a zero anchor row.
 //
+// The full-rank anchor (P = I, E [V][C]) adds E[t_n] to the output rows
+// instead of contracting against an identity pack: reconstruct with K2 = 0
+// and the rows E[t] added in fp32 in the epilogue (EADD), one rounding to
+// bf16 as in the contracted form.
+//
 // Block: TC output columns x TT tokens, 4 waves as 2 x 2, each wave a
 // (TC/2) x (TT/2) tile of 32 x 32 accumulators (columns = matrix-core rows,
 // tokens = matrix-core columns).  The contraction runs in chunks of 64: the
@@ -43,12 +48,14 @@ struct GemmRing {
   static constexpr int SLOT = WU + TU;
   static constexpr int PER = (WU + TU) / 64 / 4;  // copies (1 KB each) per wave per chunk
   static constexpr size_t RING = size_t(S) * SLOT * 16;
-  static constexpr size_t OUT = size_t(TC) * TT * 2;  // staged output tile
+  static constexpr size_t OUT = size_t(TC) * TT * 2;  // staged output tile (bf16)
+  static constexpr size_t OUT32 = size_t(TC) * TT * 4;  // ... fp32, for the anchor-row epilogue
   static constexpr size_t BYTES = RING > OUT ? RING : OUT;
+  static_assert(RING >= OUT32, "the fp32 output tile must fit the ring");
   static_assert((WU + TU) % 256 == 0, "copies must split evenly over the 4 waves");
 };
 
-template <int TC, int TT, int S, bool ANCHOR>
+template <int TC, int TT, int S, bool ANCHOR, bool EADD = false>
 __global__ __launch_bounds__(256) void k_tok_gemm(const bf16_t* __restrict__ src, int K1,
                                                   const int32_t* __restrict__ tids, int V,
                                                   const bf16_t* __restrict__ E, int K2,
@@ -159,6 +166,47 @@ __global__ __launch_bounds__(256) void k_tok_gemm(const bf16_t* __restrict__ src
   wait_vmcnt<0>();  // no copy may still be writing the ring
   __syncthreads();
 
+  if (EADD) {
+    // stage the tile as fp32 rows [token][TC columns] (16-byte unit u of row t at
+    // u ^ (t & 31)), then out[n] = bf16(tile[n] + E[t_n]) with 16-byte loads and stores
+    constexpr int RU4 = TC / 4;  // 16-byte fp32 units per staged row
+    f32x4* st4 = reinterpret_cast<f32x4*>(ring);
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int t = (wj * NJ + j) * 32 + l32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int u = ((wi * MI + i) * 32 + 8 * q) / 4 + hi;  // columns 4u .. 4u + 3
+          const f32x16& a = acc[i][j];
+          st4[t * RU4 + (u ^ (t & 31))] = f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+        }
+      }
+    __syncthreads();
+    constexpr int RU = TC / 8;  // 16-byte bf16 units per output row
+    for (int e = threadIdx.x; e < TT * RU; e += 256) {
+      const int t = e / RU, p = e % RU;
+      const int n = n0 + t;
+      if (n >= N) continue;
+      const int id = tids[n];
+      u32x4 ev = u32x4{0u, 0u, 0u, 0u};
+      if (id >= 0 && id < V) ev = *reinterpret_cast<const u32x4*>(E + size_t(id) * C + c0 + 8 * p);
+      const f32x4 lo = st4[t * RU4 + ((2 * p) ^ (t & 31))];
+      const f32x4 hi4 = st4[t * RU4 + ((2 * p + 1) ^ (t & 31))];
+      u32x4 o;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const f32x4 v = h ? hi4 : lo;
+        o[2 * h] = pack2bf(v[0] + bf2f(uint16_t(ev[2 * h] & 0xffffu)), v[1] + bf2f(uint16_t(ev[2 * h] >> 16)));
+        o[2 * h + 1] =
+            pack2bf(v[2] + bf2f(uint16_t(ev[2 * h + 1] & 0xffffu)), v[3] + bf2f(uint16_t(ev[2 * h + 1] >> 16)));
+      }
+      *reinterpret_cast<u32x4*>(out + size_t(n) * C + c0 + 8 * p) = o;
+    }
+    return;
+  }
+
   // stage the tile as bf16 rows [token][TC columns]: lane holds, for token
   // column l32 of block j, 4 consecutive output columns per register group
   constexpr int RU = TC / 8;  // 16-byte units per staged row
@@ -188,10 +236,10 @@ __global__ __launch_bounds__(256) void k_tok_gemm(const bf16_t* __restrict__ src
   }
 }
 
-template <int TC, int TT, int S, bool ANCHOR>
+template <int TC, int TT, int S, bool ANCHOR, bool EADD = false>
 void launch_gemm(const uint16_t* src, int K1, const int32_t* tids, int V, const uint16_t* E, int K2,
                  const uint16_t* F1, const uint16_t* F2, uint16_t* out, int N, int C, hipStream_t s) {
-  auto k = k_tok_gemm<TC, TT, S, ANCHOR>;
+  auto k = k_tok_gemm<TC, TT, S, ANCHOR, EADD>;
   const size_t lds = GemmRing<TC, TT, S>::BYTES;
   static bool attr = false;  // once per process: allow more than 64 KB of dynamic LDS
   if (!attr) {
@@ -218,6 +266,21 @@ bool launch_tok_gemm_bf16(const uint16_t* src, int K1, const int32_t* tids, int 
   if (C % 128 == 0) {
     if (anc) launch_gemm<128, 128, 4, true>(src, K1, tids, V, E, K2, F1, F2, out, N, C, s);
     else launch_gemm<128, 128, 4, false>(src, K1, tids, V, E, K2, F1, F2, out, N, C, s);
+    return true;
+  }
+  return false;
+}
+
+// out[N][C] = src[N][K1] W + E[t] (E [V][C]: the full-rank anchor rows, P = I).
+bool launch_tok_gemm_eadd_bf16(const uint16_t* src, int K1, const int32_t* tids, int V, const uint16_t* E,
+                               const uint16_t* F1, uint16_t* out, int N, int C, hipStream_t s) {
+  if (K1 % kKC != 0) return false;
+  if (C % 256 == 0) {
+    launch_gemm<256, 128, 3, false, true>(src, K1, tids, V, E, 0, F1, nullptr, out, N, C, s);
+    return true;
+  }
+  if (C % 128 == 0) {
+    launch_gemm<128, 128, 4, false, true>(src, K1, tids, V, E, 0, F1, nullptr, out, N, C, s);
     return true;
   }
   return false;

@@ -13,12 +13,16 @@
 //     lane l <- W[mb*32 + (l & 31)][s*16 + 8*(l >> 5) + 0..7]
 // at 16-byte unit (s * M/32 + mb) * 64 + l.  A wave's operand load is then one
 // contiguous kilobyte, and the row blocks of one K-step are adjacent.
-//   AtF: W = A^T (M = r, K = d)      compression, gZ = gXhat A
-//   QnF: W = -(P A)^T (M = r, K = r)  anchor term of compression
-//   AF : W = A   (M = d, K = r)      reconstruction, gX = gZ A^T
-//   PtF: W = P^T (M = d, K = r)      anchor term of reconstruction
-//   PF : W = P   (M = r, K = d)      anchor-table gradient, Y P^T
+//   AtF: W = A^T (M = r, K = d)        compression, gZ = gXhat A
+//   QnF: W = -(P A)^T (M = r, K = ra) anchor term of compression
+//   AF : W = A   (M = d, K = r)        reconstruction, gX = gZ A^T
+//   PtF: W = P^T (M = d, K = ra)       anchor term of reconstruction
+//   PF : W = P   (M = ra, K = d)       anchor-table gradient, Y P^T
+// where ra is the anchor rank (P is [ra][d]; Eq. (3) has ra = r).
 // P is also contracted over d in the anchor-table gradient (Eq. (3)).
+// The full-rank anchor (ra = d, P = I, passed as no P) needs only QnF = -A^T,
+// i.e. AtF negated; its PtF and PF sections stay unused (the maps add or
+// gather the anchor rows directly).
 #include "common.h"
 #include "internal.h"
 
@@ -26,19 +30,20 @@ namespace mapl {
 
 static inline size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
-size_t pack_bytes_bf16(int64_t d, int64_t r) {
-  return 4 * align256(size_t(r) * d * 2) + align256(size_t(r) * r * 2);
+// sections AtF, AF (r d each), PtF (d ra), QnF (r ra), PF (ra d); ra == 0: the first two only
+size_t pack_bytes_bf16(int64_t d, int64_t r, int64_t ra) {
+  return 2 * align256(size_t(r) * d * 2) + 2 * align256(size_t(ra) * d * 2) + align256(size_t(r) * ra * 2);
 }
 
-PackView pack_view(void* pk, int64_t d, int64_t r) {
+PackView pack_view(void* pk, int64_t d, int64_t r, int64_t ra) {
   char* p = static_cast<char*>(pk);
-  const size_t big = align256(size_t(r) * d * 2);
+  const size_t big = align256(size_t(r) * d * 2), anc = align256(size_t(ra) * d * 2);
   PackView v;
   v.AtF = reinterpret_cast<uint16_t*>(p);
   v.AF = reinterpret_cast<uint16_t*>(p + big);
   v.PtF = reinterpret_cast<uint16_t*>(p + 2 * big);
-  v.QnF = reinterpret_cast<uint16_t*>(p + 3 * big);
-  v.PF = reinterpret_cast<uint16_t*>(p + 3 * big + align256(size_t(r) * r * 2));
+  v.QnF = reinterpret_cast<uint16_t*>(p + 2 * big + anc);
+  v.PF = reinterpret_cast<uint16_t*>(p + 2 * big + anc + align256(size_t(r) * ra * 2));
   return v;
 }
 
@@ -77,12 +82,12 @@ void launch_pack_AF(const uint16_t* A, uint16_t* AF, int d, int r, hipStream_t s
   frag_pack(A, /*sm*/ r, /*sk*/ 1, d, r, AF, s);  // W(m, k) = A[m][k]
 }
 
-void launch_pack_PtF(const uint16_t* P, uint16_t* PtF, int d, int r, hipStream_t s) {
-  frag_pack(P, /*sm*/ 1, /*sk*/ d, d, r, PtF, s);  // W(m, k) = P[k][m]
+void launch_pack_PtF(const uint16_t* P, uint16_t* PtF, int d, int ra, hipStream_t s) {
+  frag_pack(P, /*sm*/ 1, /*sk*/ d, d, ra, PtF, s);  // W(m, k) = P[k][m]
 }
 
-void launch_pack_PF(const uint16_t* P, uint16_t* PF, int d, int r, hipStream_t s) {
-  frag_pack(P, /*sm*/ d, /*sk*/ 1, r, d, PF, s);  // W(m, k) = P[m][k]
+void launch_pack_PF(const uint16_t* P, uint16_t* PF, int d, int ra, hipStream_t s) {
+  frag_pack(P, /*sm*/ d, /*sk*/ 1, ra, d, PF, s);  // W(m, k) = P[m][k]
 }
 
 // The four A / P sections in one launch: unit u of the concatenation
@@ -90,21 +95,22 @@ void launch_pack_PF(const uint16_t* P, uint16_t* PF, int d, int r, hipStream_t s
 __global__ __launch_bounds__(256) void k_frag_pack4(const bf16_t* __restrict__ A, const bf16_t* __restrict__ P,
                                                     bf16_t* __restrict__ AtF, bf16_t* __restrict__ AF,
                                                     bf16_t* __restrict__ PtF, bf16_t* __restrict__ PF, int d,
-                                                    int r) {
+                                                    int r, int ra) {
   const int64_t u0 = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t n1 = int64_t(d / 16) * (r / 32) * 64, n2 = int64_t(r / 16) * (d / 32) * 64;
+  const int64_t n1 = int64_t(d / 16) * (r / 32) * 64;   // AtF, and AF, units
+  const int64_t n3 = int64_t(ra / 16) * (d / 32) * 64;  // PtF, and PF, units
   const bf16_t* src;
   int64_t sm, sk, u;
   int M;
   bf16_t* dst;
   if (u0 < n1) {
     src = A, sm = 1, sk = r, M = r, dst = AtF, u = u0;  // W(m, k) = A[k][m]
-  } else if (u0 < n1 + n2) {
+  } else if (u0 < 2 * n1) {
     src = A, sm = r, sk = 1, M = d, dst = AF, u = u0 - n1;  // W(m, k) = A[m][k]
-  } else if (u0 < n1 + 2 * n2) {
-    src = P, sm = 1, sk = d, M = d, dst = PtF, u = u0 - n1 - n2;  // W(m, k) = P[k][m]
-  } else if (u0 < 2 * n1 + 2 * n2) {
-    src = P, sm = d, sk = 1, M = r, dst = PF, u = u0 - n1 - 2 * n2;  // W(m, k) = P[m][k]
+  } else if (u0 < 2 * n1 + n3) {
+    src = P, sm = 1, sk = d, M = d, dst = PtF, u = u0 - 2 * n1;  // W(m, k) = P[k][m]
+  } else if (u0 < 2 * n1 + 2 * n3) {
+    src = P, sm = d, sk = 1, M = ra, dst = PF, u = u0 - 2 * n1 - n3;  // W(m, k) = P[m][k]
   } else {
     return;
   }
@@ -124,13 +130,14 @@ __global__ __launch_bounds__(256) void k_frag_pack4(const bf16_t* __restrict__ A
   reinterpret_cast<u32x4*>(dst)[u] = u32x4{w[0], w[1], w[2], w[3]};
 }
 
-// QnF = fragments of W = -(P A)^T (M = K = r), rounded once to bf16.  One block
+// QnF = fragments of W = -(P A)^T (M = r, K = ra), rounded once to bf16.  One block
 // per 32 x 32 tile (i, j) of P A; the 4 waves split the d-long contraction:
 // the matrix-core A operand is 16 bytes of a row of P, the B operand the AtF
 // fragment of the same K-step, and the four partial tiles are added in LDS in
 // a fixed order.
 __global__ __launch_bounds__(256) void k_qn_direct(const bf16_t* __restrict__ P, const bf16_t* __restrict__ AtF,
                                                    bf16_t* __restrict__ QnF, int d, int r) {
+  // grid (ra / 32, r / 32): blockIdx.x walks the ra rows of P A, blockIdx.y its r columns
   __shared__ float red[4 * 1024];
   const int lane = threadIdx.x & 63, w = wave_id();
   const int hi = lane >> 5, l32 = lane & 31;
@@ -170,12 +177,29 @@ __global__ __launch_bounds__(256) void k_qn_direct(const bf16_t* __restrict__ P,
   }
 }
 
-// Full pack: the four A / P sections, then QnF from P and the fresh AtF.
-void launch_pack_all(const uint16_t* P, const uint16_t* A, PackView v, int d, int r, hipStream_t s) {
-  const int64_t units = 2 * int64_t(d / 16) * (r / 32) * 64 + 2 * int64_t(r / 16) * (d / 32) * 64;
+// dst = -src on n 16-byte units of bf16 (a sign flip: exact)
+__global__ __launch_bounds__(256) void k_negate_units(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
+                                                      int64_t n) {
+  const int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (u < n) dst[u] = src[u] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+}
+
+// Full pack: the four A / P sections, then QnF from P and the fresh AtF
+// (ra == 0: no anchor, the A sections only; P == nullptr with ra == d: the
+// identity anchor, QnF = -AtF).
+void launch_pack_all(const uint16_t* P, const uint16_t* A, PackView v, int d, int r, int ra, hipStream_t s) {
+  const bool eye = ra > 0 && P == nullptr;
+  const int rp = eye ? 0 : ra;  // P sections to fill
+  const int64_t units = 2 * int64_t(d / 16) * (r / 32) * 64 + 2 * int64_t(rp / 16) * (d / 32) * 64;
   hipLaunchKernelGGL(k_frag_pack4, dim3(unsigned((units + 255) / 256)), dim3(256), 0, s, A, P, v.AtF, v.AF, v.PtF,
-                     v.PF, d, r);
-  hipLaunchKernelGGL(k_qn_direct, dim3(r / 32, r / 32), dim3(256), 0, s, P, v.AtF, v.QnF, d, r);
+                     v.PF, d, r, rp);
+  if (eye) {
+    const int64_t n = int64_t(d / 16) * (r / 32) * 64;  // AtF units
+    hipLaunchKernelGGL(k_negate_units, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<const u32x4*>(v.AtF), reinterpret_cast<u32x4*>(v.QnF), n);
+  } else if (ra > 0) {
+    hipLaunchKernelGGL(k_qn_direct, dim3(ra / 32, r / 32), dim3(256), 0, s, P, v.AtF, v.QnF, d, r);
+  }
 }
 
 }  // namespace mapl

@@ -7,6 +7,12 @@ P in R^{r x d}); Section 3.1 "Setup" (the backward pass transmits the gradient
 of the boundary activation) and Section 3.2 (the gradient is routed through
 the same projector A).  Tokens are flattened: N = B*T rows.
 
+Anchor variants (Table 6, the anchor-rank ablation of Appendix G, and the
+no-anchor "Subspace" rows): the anchor's rank ra may differ from the
+projector's rank r (E_small [V][ra], P [ra][d]); the full-rank anchor is the
+table E in R^{V x d}, i.e. ra = d with P = I; and "no anchor" is
+E_small = P = None, which these functions read as an anchor term of zero.
+
 Test infrastructure only: see the package docstring.
 """
 from __future__ import annotations
@@ -23,16 +29,22 @@ def anchor(tids, E_small, P) -> np.ndarray:
     return _f64(E_small)[np.asarray(tids, dtype=np.int64)] @ _f64(P)
 
 
+def _residual(X, tids, E_small, P) -> np.ndarray:
+    """X minus the anchor; without an anchor (E_small None) X itself."""
+    X = _f64(X)
+    return X if E_small is None else X - anchor(tids, E_small, P)
+
+
 def compress(X, tids, E_small, P, A) -> np.ndarray:
     """Eq. (1): Z = (X - E_small[tids] P) A, shape [N][r]."""
-    R = _f64(X) - anchor(tids, E_small, P)
-    return R @ _f64(A)
+    return _residual(X, tids, E_small, P) @ _f64(A)
 
 
 def reconstruct(Z, tids, E_small, P, A) -> np.ndarray:
     """Eq. (2): Xhat = Z A^T + E_small[tids] P, shape [N][d].  E_small and P
     are the receiving stage's anchor (E_{p+1}, P_{p+1} in Eq. (2))."""
-    return _f64(Z) @ _f64(A).T + anchor(tids, E_small, P)
+    Xh = _f64(Z) @ _f64(A).T
+    return Xh if E_small is None else Xh + anchor(tids, E_small, P)
 
 
 def reconstruct_bwd(gXhat, Z, A):
@@ -47,19 +59,19 @@ def compress_bwd(gZ, X, tids, E_small, P, A):
     """Backward of Eq. (1) with respect to X and A, given gZ = dL/dZ:
     gX = gZ A^T ([N][d]) and gA_cmp = (X - E_small[tids] P)^T gZ ([d][r])."""
     gZ = _f64(gZ)
-    R = _f64(X) - anchor(tids, E_small, P)
+    R = _residual(X, tids, E_small, P)
     return gZ @ _f64(A).T, R.T @ gZ
 
 
 def anchor_grad(gZ, tids, P, A, V, gXhat=None, P_recv=None) -> np.ndarray:
     """Gradient of the loss with respect to the trainable anchor table
-    E_small ([V][r]), Eq. (3) being trainable.  From Eq. (1): d/dE[t] of
-    -(E[t] P) A is -gZ_n (P A)^T, scatter-added to row tids[n].  If the
-    receiver's G = dL/dXhat is given, Eq. (2) adds G_n P_recv^T to row
-    tids[n] of the receiver's table (returned separately by calling this with
-    gZ = 0).  Sum over tokens in token order."""
+    E_small ([V][ra], ra = P's row count), Eq. (3) being trainable.  From
+    Eq. (1): d/dE[t] of -(E[t] P) A is -gZ_n (P A)^T, scatter-added to row
+    tids[n].  If the receiver's G = dL/dXhat is given, Eq. (2) adds
+    G_n P_recv^T to row tids[n] of the receiver's table (returned separately
+    by calling this with gZ = 0).  Sum over tokens in token order."""
     tids = np.asarray(tids, dtype=np.int64)
-    out = np.zeros((V, _f64(A).shape[1]), dtype=np.float64)
+    out = np.zeros((V, _f64(P).shape[0]), dtype=np.float64)
     rows = -(_f64(gZ) @ (_f64(P) @ _f64(A)).T)
     if gXhat is not None:
         rows = rows + _f64(gXhat) @ _f64(P_recv).T

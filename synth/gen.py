@@ -100,16 +100,28 @@ def to_dtype(x: np.ndarray, dtype: str) -> torch.Tensor:
 
 def codec_inputs(cfg_seed: int, N: int, d: int, r: int, V: int, dtype: str,
                  x_kind: str = "gauss", with_grad: bool = True,
-                 e_var: float = 0.02) -> dict:
-    """Inputs of one boundary: X [N][d], tids [N], E_small [V][r], P [r][d],
-    A [d][r] and, optionally, the upstream gradient gXhat [N][d] ~ N(0,1).
+                 e_var: float = 0.02, ra: int = None, anchor: str = "factorised") -> dict:
+    """Inputs of one boundary: X [N][d], tids [N], E_small [V][ra], P [ra][d]
+    (orthonormal rows; ra defaults to r), A [d][r] and, optionally, the
+    upstream gradient gXhat [N][d] ~ N(0,1).
+
+    anchor = "none": E and P are None (ra = 0); anchor = "full": E is [V][d]
+    and P is None, standing for the d x d identity (ra = d).
 
     Returns CPU tensors in `dtype` (tids int32) plus the fp64 pre-cast A and P
-    under 'A64' and 'P64'.
+    under 'A64' and 'P64', and the anchor rank under 'ra'.
     """
+    if anchor == "none":
+        ra = 0
+    elif anchor == "full":
+        ra = d
+    elif anchor == "factorised":
+        ra = r if ra is None else ra
+    else:
+        raise ValueError(f"unknown anchor kind {anchor!r}")
     A64 = orthonormal_columns(stream(cfg_seed, TID_A), d, r)
-    P64 = orthonormal_rows(stream(cfg_seed, TID_P), r, d)
-    E = gaussian(stream(cfg_seed, TID_E), (V, r), e_var)
+    P64 = orthonormal_rows(stream(cfg_seed, TID_P), ra, d) if anchor == "factorised" else None
+    E = gaussian(stream(cfg_seed, TID_E), (V, ra), e_var) if ra > 0 else None
     tids = zipf_tids(stream(cfg_seed, TID_TIDS), N, V)
     if x_kind == "gauss":
         X = gaussian(stream(cfg_seed, TID_X), (N, d))
@@ -118,9 +130,9 @@ def codec_inputs(cfg_seed: int, N: int, d: int, r: int, V: int, dtype: str,
     else:
         raise ValueError(f"unknown x_kind {x_kind!r}")
     out = dict(
-        X=to_dtype(X, dtype), tids=torch.from_numpy(tids), E=to_dtype(E, dtype),
-        P=to_dtype(P64, dtype), A=to_dtype(A64, dtype), A64=A64, P64=P64,
-        N=N, d=d, r=r, V=V, dtype=dtype,
+        X=to_dtype(X, dtype), tids=torch.from_numpy(tids), E=None if E is None else to_dtype(E, dtype),
+        P=None if P64 is None else to_dtype(P64, dtype), A=to_dtype(A64, dtype), A64=A64, P64=P64,
+        N=N, d=d, r=r, V=V, ra=ra, anchor=anchor, dtype=dtype,
     )
     if with_grad:
         out["gXhat"] = to_dtype(gaussian(stream(cfg_seed, TID_GXHAT), (N, d)), dtype)

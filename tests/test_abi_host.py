@@ -36,22 +36,30 @@ def test_status_strings_and_version(lib):
 def test_pack_and_workspace_sizes(lib):
     d, r = 1024, 128
     want = 4 * 2 * r * d + 2 * r * r
-    got = lib.mapl_pack_bytes(d, r, BF16)
+    got = lib.mapl_pack_bytes(d, r, r, BF16)
     assert want <= got <= want + 5 * 256
-    assert lib.mapl_pack_bytes(d, r, F32) == 0
-    assert lib.mapl_bwd_workspace_bytes(8, 2048, d, r, BF16) > 0
-    assert lib.mapl_bwd_workspace_bytes(1, 128, 256, 32, F32) == 128 * 256 * 4
-    assert lib.mapl_bwd_workspace_bytes(1, 128, 1000, 32, BF16) == 0     # d % 64 != 0
+    # no anchor: only the two A sections
+    assert 2 * 2 * r * d <= lib.mapl_pack_bytes(d, r, 0, BF16) <= 2 * 2 * r * d + 5 * 256
+    # anchor rank 256 beside r = 128: P sections d x 256, Q sections r x 256
+    want = 2 * 2 * r * d + 2 * 2 * 256 * d + 2 * r * 256
+    assert want <= lib.mapl_pack_bytes(d, r, 256, BF16) <= want + 5 * 256
+    assert lib.mapl_pack_bytes(d, r, r, F32) == 0
+    assert lib.mapl_pack_bytes(d, r, 96, BF16) == 0                      # anchor rank not a multiple of 64
+    assert lib.mapl_pack_bytes(d, r, d + 128, BF16) == 0                 # anchor rank above d
+    assert lib.mapl_bwd_workspace_bytes(8, 2048, d, r, r, BF16) > 0
+    assert lib.mapl_bwd_workspace_bytes(8, 2048, d, r, 0, BF16) < lib.mapl_bwd_workspace_bytes(8, 2048, d, r, d, BF16)
+    assert lib.mapl_bwd_workspace_bytes(1, 128, 256, 32, 32, F32) == 128 * 256 * 4
+    assert lib.mapl_bwd_workspace_bytes(1, 128, 1000, 32, 32, BF16) == 0     # d % 64 != 0
     assert lib.spel_workspace_bytes(2048, 256) >= 3 * 2048 * 256 * 4
     assert lib.spel_workspace_bytes(2048, 250) == 0                      # r % 32 != 0
 
 
 def _compress(lib, **kw):
-    a = dict(X=FAKE, tids=FAKE, E=FAKE, P=FAKE, A=FAKE, Z=FAKE, B=8, T=2048, d=1024, r=128, V=32000, dt=BF16,
-             pk=FAKE, pk_bytes=10 ** 7, pk_ready=1, s=None)
+    a = dict(X=FAKE, tids=FAKE, E=FAKE, P=FAKE, A=FAKE, Z=FAKE, B=8, T=2048, d=1024, r=128, ra=128, V=32000,
+             dt=BF16, pk=FAKE, pk_bytes=10 ** 7, pk_ready=1, s=None)
     a.update(kw)
     return lib.mapl_compress(a["X"], a["tids"], a["E"], a["P"], a["A"], a["Z"], a["B"], a["T"], a["d"], a["r"],
-                             a["V"], a["dt"], a["pk"], a["pk_bytes"], a["pk_ready"], a["s"])
+                             a["ra"], a["V"], a["dt"], a["pk"], a["pk_bytes"], a["pk_ready"], a["s"])
 
 
 def test_compress_validation(lib):
@@ -70,35 +78,49 @@ def test_compress_validation(lib):
     assert _compress(lib, dt=7) == EDTYPE
     assert _compress(lib, pk_ready=2) == EARG
     assert _compress(lib, dt=F32, d=8192, r=64, pk=None, pk_bytes=0) == ESHAPE  # fp32 d <= 4096
+    # anchor rank
+    assert _compress(lib, ra=-1) == ESHAPE
+    assert _compress(lib, ra=2048) == ESHAPE         # ra > d
+    assert _compress(lib, ra=96) == ESHAPE           # bf16: ra != r streams in 64-wide chunks
+    assert _compress(lib, r=32, ra=64) == ESHAPE     # ... and needs r % 64 == 0
+    assert _compress(lib, ra=0, tids=None, E=None, P=None, V=0, B=0) == OK    # no anchor: no table needed
+    assert _compress(lib, ra=0, X=None, tids=None, E=None, P=None, V=0) == ENULL
+    assert _compress(lib, ra=1024, B=0) == OK        # full anchor
+    assert _compress(lib, dt=F32, ra=100, pk=None, pk_bytes=0, B=0) == OK
 
 
 def test_empty_batch_is_a_no_op(lib):
     # N = 0 passes validation and returns before any launch
     assert _compress(lib, B=0) == OK
-    assert lib.mapl_reconstruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2048, 1024, 128, 32000, BF16, FAKE, 10 ** 7,
-                                1, None) == OK
+    assert lib.mapl_reconstruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 2048, 1024, 128, 128, 32000, BF16, FAKE,
+                                10 ** 7, 1, None) == OK
     assert lib.rvq_encode(FAKE, BF16, FAKE, 0, FAKE, 0, 256, 8, 256, 2, None) == OK
     assert lib.rvq_decode(FAKE, FAKE, 0, FAKE, F32, 0, 256, 8, 256, 2, None) == OK
     assert lib.rvq_stream_apply(FAKE, FAKE, FAKE, 0, 256, 8, 256, 1, None) == OK
 
 
 def test_backward_validation(lib):
-    ws = lib.mapl_bwd_workspace_bytes(8, 2048, 1024, 128, BF16)
+    ws = lib.mapl_bwd_workspace_bytes(8, 2048, 1024, 128, 0, BF16)   # the receiver's map has no anchor term
     f = lib.mapl_reconstruct_bwd
     assert f(None, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, BF16, FAKE, 10 ** 7, 1, FAKE, ws, None) == ENULL
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, BF16, FAKE, 10 ** 7, 1, FAKE, ws - 4, None) == EWS
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, BF16, FAKE, 10 ** 7, 1, None, ws, None) == ENULL
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2048, 1024, 128, BF16, FAKE, 10 ** 7, 1, FAKE, ws, None) == EARG
+    ws = lib.mapl_bwd_workspace_bytes(8, 2048, 1024, 128, 128, BF16)
     g = lib.mapl_compress_bwd
     pk = 10 ** 7
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 8, 2048, 1024, 128, 32000, BF16, FAKE, pk, 1, FAKE,
-             ws, None) == ENULL
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, 32000, BF16, FAKE, pk, 1, FAKE,
-             16, None) == EWS
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1024, 128, 32000, BF16, None, pk, 1, FAKE,
-             ws, None) == ENULL
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 2048, 1000, 128, 32000, BF16, FAKE, pk, 1, FAKE,
-             ws, None) == ESHAPE
+
+    def gc(gZ=FAKE, X=FAKE, tids=FAKE, E=FAKE, P=FAKE, A=FAKE, gX=FAKE, gA=FAKE, acc=0, B=8, T=2048, d=1024, r=128,
+           ra=128, V=32000, dt=BF16, pk=FAKE, pkb=pk, pkr=1, w=FAKE, wb=ws):
+        return g(gZ, X, tids, E, P, A, gX, gA, acc, B, T, d, r, ra, V, dt, pk, pkb, pkr, w, wb, None)
+
+    assert gc(gA=None) == ENULL
+    assert gc(wb=16) == EWS
+    assert gc(pk=None) == ENULL
+    assert gc(d=1000) == ESHAPE
+    assert gc(tids=None) == ENULL
+    assert gc(ra=256, wb=ws) == EWS                  # a wider anchor needs a larger workspace
+    assert gc(ra=0, tids=None, E=None, P=None, V=0, B=0, acc=1) == OK   # empty, accumulate: nothing to do
 
 
 def test_anchor_grad_validation(lib):
@@ -109,9 +131,9 @@ def test_anchor_grad_validation(lib):
     assert lib.mapl_anchor_grad_workspace_bytes(8, 2048, 128, 2 ** 22 + 1) == 0
     f = lib.mapl_anchor_grad
 
-    def call(Y=FAKE, tids=FAKE, P=FAKE, gE=FAKE, alpha=1.0, acc=0, B=8, T=2048, d=1024, r=128, V=32000, dt=BF16,
-             pk=FAKE, pkb=10 ** 7, pkr=1, w=FAKE, wb=ws):
-        return f(Y, tids, P, gE, alpha, acc, B, T, d, r, V, dt, pk, pkb, pkr, w, wb, None)
+    def call(Y=FAKE, tids=FAKE, P=FAKE, gE=FAKE, alpha=1.0, acc=0, B=8, T=2048, d=1024, r=128, ra=128, V=32000,
+             dt=BF16, pk=FAKE, pkb=10 ** 7, pkr=1, w=FAKE, wb=ws):
+        return f(Y, tids, P, gE, alpha, acc, B, T, d, r, ra, V, dt, pk, pkb, pkr, w, wb, None)
 
     assert call(Y=None) == ENULL
     assert call(tids=None) == ENULL
@@ -129,6 +151,9 @@ def test_anchor_grad_validation(lib):
     assert call(V=0) == ESHAPE
     assert call(V=2 ** 22 + 1) == ESHAPE                        # owner blocks scale with V
     assert call(dt=4) == EDTYPE
+    assert call(ra=0) == ESHAPE                                 # no anchor, no table
+    assert call(ra=2048) == ESHAPE
+    assert call(ra=256) == EWS                                  # the workspace holds N x ra rows
     assert call(B=0, acc=1, Y=None, tids=None, P=None, w=None) == OK   # empty batch, accumulate: nothing to do
 
 

@@ -19,20 +19,27 @@ from oracle import codec, rvq, spel
 
 # ----------------------------------------------------------------- helpers --
 
-def micro_codec(seed=0, N=7, d=8, r=3, V=5):
+def micro_codec(seed=0, N=7, d=8, r=3, V=5, ra=None):
+    """A tiny boundary; the anchor rank ra defaults to r (Eq. (3))."""
+    ra = r if ra is None else ra
     rng = np.random.default_rng(seed)
     A = synth.orthonormal_columns(rng, d, r)
-    P = synth.orthonormal_rows(rng, r, d)
-    E = rng.standard_normal((V, r)) * 0.3
+    P = synth.orthonormal_rows(rng, ra, d)
+    E = rng.standard_normal((V, ra)) * 0.3
     tids = rng.integers(0, V, size=N).astype(np.int32)
     X = rng.standard_normal((N, d))
     G = rng.standard_normal((N, d))
     gZ = rng.standard_normal((N, r))
-    return dict(A=A, P=P, E=E, tids=tids, X=X, G=G, gZ=gZ, N=N, d=d, r=r, V=V)
+    return dict(A=A, P=P, E=E, tids=tids, X=X, G=G, gZ=gZ, N=N, d=d, r=r, V=V, ra=ra)
 
 
 def loop_anchor(n, i, m):
-    return sum(m["E"][m["tids"][n]][k] * m["P"][k][i] for k in range(m["r"]))
+    return sum(m["E"][m["tids"][n]][k] * m["P"][k][i] for k in range(m["ra"]))
+
+
+# anchor ranks of the pins: Eq. (3)'s ra = r, and Appendix G's anchor rank as a
+# separate choice below and above r
+RA_CASES = [None, 2, 5]
 
 
 def loop_compress(m, X=None):
@@ -56,16 +63,18 @@ def loop_reconstruct(m, Z):
 
 # ------------------------------------------------------------ codec pins --
 
-def test_codec_forward_matches_brute_force_loops():
-    m = micro_codec(1)
+@pytest.mark.parametrize("ra", RA_CASES)
+def test_codec_forward_matches_brute_force_loops(ra):
+    m = micro_codec(1, ra=ra)
     Z = codec.compress(m["X"], m["tids"], m["E"], m["P"], m["A"])
     np.testing.assert_allclose(Z, loop_compress(m), rtol=0, atol=1e-12)
     Xh = codec.reconstruct(Z, m["tids"], m["E"], m["P"], m["A"])
     np.testing.assert_allclose(Xh, loop_reconstruct(m, Z), rtol=0, atol=1e-12)
 
 
-def test_codec_backward_matches_brute_force_loops():
-    m = micro_codec(2)
+@pytest.mark.parametrize("ra", RA_CASES)
+def test_codec_backward_matches_brute_force_loops(ra):
+    m = micro_codec(2, ra=ra)
     N, d, r = m["N"], m["d"], m["r"]
     Z = codec.compress(m["X"], m["tids"], m["E"], m["P"], m["A"])
     gZ, gA_rec = codec.reconstruct_bwd(m["G"], Z, m["A"])
@@ -109,8 +118,9 @@ def test_backward_equals_finite_differences_of_forward():
     np.testing.assert_allclose(gX, _central_diff(L_cmp_X, m["X"]), atol=1e-9)
 
 
-def test_anchor_grad_equals_finite_differences():
-    m = micro_codec(4)
+@pytest.mark.parametrize("ra", RA_CASES)
+def test_anchor_grad_equals_finite_differences(ra):
+    m = micro_codec(4, ra=ra)
     def L(E):
         Z = codec.compress(m["X"], m["tids"], E, m["P"], m["A"])
         return float(np.sum(m["gZ"] * Z))
@@ -123,12 +133,13 @@ def test_anchor_grad_equals_finite_differences():
     np.testing.assert_allclose(gE2, _central_diff(L2, m["E"]), atol=1e-9)
 
 
-def test_anchor_grad_adjoint_identity_and_loops():
+@pytest.mark.parametrize("ra", RA_CASES)
+def test_anchor_grad_adjoint_identity_and_loops(ra):
     """Eq. (1) and (2) are affine in E_small, so for any table perturbation dE
     the pairing <gE, dE> equals the change of <gZ, Z> (sender) and of
     <gXhat, Xhat> (receiver) exactly; and the scatter is checked against
     explicit per-token loops, with repeated ids."""
-    m = micro_codec(6, N=9, V=4)
+    m = micro_codec(6, N=9, V=4, ra=ra)
     rng = np.random.default_rng(60)
     dE = rng.standard_normal(m["E"].shape)
     gE = codec.anchor_grad(m["gZ"], m["tids"], m["P"], m["A"], m["V"])
@@ -143,15 +154,67 @@ def test_anchor_grad_adjoint_identity_and_loops():
     assert abs(np.sum(gE2 * dE) - np.sum(m["G"] * dXh)) < 1e-12 * (1 + abs(np.sum(gE2 * dE)))
     # loops: row v collects -gZ[n] (P A)^T over the tokens with id v, plus G[n] P^T
     both = codec.anchor_grad(m["gZ"], m["tids"], m["P"], m["A"], m["V"], gXhat=m["G"], P_recv=m["P"])
-    want = np.zeros((m["V"], m["r"]))
+    want = np.zeros((m["V"], m["ra"]))
     for n in range(m["N"]):
         v = m["tids"][n]
-        for k in range(m["r"]):
+        for k in range(m["ra"]):
             pa = [sum(m["P"][k][i] * m["A"][i][j] for i in range(m["d"])) for j in range(m["r"])]
             want[v][k] -= sum(m["gZ"][n][j] * pa[j] for j in range(m["r"]))
             want[v][k] += sum(m["G"][n][i] * m["P"][k][i] for i in range(m["d"]))
     assert len(set(m["tids"].tolist())) < m["N"]  # some id repeats
     np.testing.assert_allclose(both, want, atol=1e-12)
+
+
+def test_no_anchor_is_the_plain_projection():
+    """Table 6's "no anchor" row: without E_small and P the maps are Z = X A
+    and Xhat = Z A^T (checked by loops), the same as with an all-zero table,
+    and the backward's gA is X^T gZ."""
+    m = micro_codec(7)
+    N, d, r = m["N"], m["d"], m["r"]
+    Z = codec.compress(m["X"], None, None, None, m["A"])
+    for n in range(N):
+        for j in range(r):
+            assert abs(Z[n, j] - sum(m["X"][n][i] * m["A"][i][j] for i in range(d))) < 1e-12
+    zero = np.zeros_like(m["E"])
+    np.testing.assert_array_equal(Z, codec.compress(m["X"], m["tids"], zero, m["P"], m["A"]))
+    Xh = codec.reconstruct(Z, None, None, None, m["A"])
+    for n in range(N):
+        for i in range(d):
+            assert abs(Xh[n, i] - sum(Z[n][j] * m["A"][i][j] for j in range(r))) < 1e-12
+    gX, gA = codec.compress_bwd(m["gZ"], m["X"], None, None, None, m["A"])
+    for i in range(d):
+        for j in range(r):
+            assert abs(gA[i, j] - sum(m["X"][n][i] * m["gZ"][n][j] for n in range(N))) < 1e-12
+    np.testing.assert_allclose(gX, m["gZ"] @ m["A"].T, atol=1e-12)
+
+
+def test_full_anchor_is_a_row_gather():
+    """Table 6's fully trainable anchor: E in R^{V x d} with P = I.  The
+    anchor is then the gathered row E[t] itself, Eq. (1) subtracts it before
+    the projection, and its table gradient scatters -gZ A^T (sender) and gXhat
+    (receiver) rows by id -- each checked by explicit loops."""
+    m = micro_codec(8, N=9, V=4)
+    N, d, r, V = m["N"], m["d"], m["r"], m["V"]
+    rng = np.random.default_rng(80)
+    E = rng.standard_normal((V, d))
+    I = np.eye(d)
+    t = m["tids"]
+    np.testing.assert_array_equal(codec.anchor(t, E, I), E[t])
+    Z = codec.compress(m["X"], t, E, I, m["A"])
+    for n in range(N):
+        for j in range(r):
+            want = sum((m["X"][n][i] - E[t[n]][i]) * m["A"][i][j] for i in range(d))
+            assert abs(Z[n, j] - want) < 1e-12
+    Xh = codec.reconstruct(Z, t, E, I, m["A"])
+    for n in range(N):
+        for i in range(d):
+            assert abs(Xh[n, i] - (sum(Z[n][j] * m["A"][i][j] for j in range(r)) + E[t[n]][i])) < 1e-12
+    gE = codec.anchor_grad(m["gZ"], t, I, m["A"], V, gXhat=m["G"], P_recv=I)
+    want = np.zeros((V, d))
+    for n in range(N):
+        for i in range(d):
+            want[t[n]][i] += m["G"][n][i] - sum(m["gZ"][n][j] * m["A"][i][j] for j in range(r))
+    np.testing.assert_allclose(gE, want, atol=1e-12)
 
 
 def test_stiefel_projector_inputs_and_idempotence():
