@@ -240,15 +240,22 @@ def _timed(fn, flush, iters=20, warm=3):
             "p90": round(float(np.percentile(a, 90)), 5)}
 
 
-def _codec_counts(N, d, r, n_distinct):
-    """Algorithmic bytes and executed flops of each codec map (whole batch)."""
-    e = n_distinct * 2 * r
+def _codec_counts(N, d, r, n_distinct, ra=None, eye=False):
+    """Algorithmic bytes and executed flops of each codec map (whole batch).
+    ra is the anchor rank (default r; 0: no anchor); eye marks the full-rank
+    anchor (ra = d, P = I), whose rows are added or subtracted directly in
+    reconstruct and whose pack has no P sections."""
+    ra = r if ra is None else ra
+    t4 = 4 if ra > 0 else 0                        # token ids read
+    e = n_distinct * 2 * ra                        # distinct anchor rows read
+    pt = 0 if eye else 2 * d * ra                  # P^T pack of reconstruct
+    rflops = N * 2 * d * r + (0 if eye else N * 2 * d * ra)
     c = dict(
-        compress=(N * (2 * d + 4 + 2 * r) + e + 2 * d * r + 2 * r * r, N * (2 * d * r + 2 * r * r)),
-        reconstruct=(N * (2 * r + 4 + 2 * d) + e + 2 * 2 * d * r, N * 4 * d * r),
+        compress=(N * (2 * d + t4 + 2 * r) + e + 2 * d * r + 2 * r * ra, N * (2 * d * r + 2 * ra * r)),
+        reconstruct=(N * (2 * r + t4 + 2 * d) + e + 2 * d * r + pt, rflops),
         reconstruct_bwd=(N * (2 * d + 2 * r + 2 * r) + 2 * d * r + 4 * d * r, N * 4 * d * r),
-        compress_bwd=(N * (2 * r + 2 * d + 4 + 2 * d) + e + 2 * 2 * d * r + 2 * 4 * d * r,
-                      N * (4 * d * r + 2 * r * r) + 2 * d * r * r),
+        compress_bwd=(N * (2 * r + 2 * d + t4 + 2 * d) + e + 2 * 2 * d * r + 2 * 4 * d * r,
+                      N * (4 * d * r + 2 * ra * r) + (0 if eye else 2 * d * ra * r)),
     )
     c["pair"] = (c["compress"][0] + c["reconstruct"][0], c["compress"][1] + c["reconstruct"][1])
     return c
@@ -271,19 +278,21 @@ def run_cases(lac, dev, flush):
         print(f"# {name:34s} {t['ms']*1e3:9.1f} us  {row['GBs']:8.1f} GB/s ({row['hbm_frac']:.3f})  "
               f"{row['TFLOPs']:8.2f} TF/s ({row['mfma_frac']:.3f})", file=sys.stderr, flush=True)
 
-    def codec_case(tag, c, r, x_kind="gauss"):
+    def codec_case(tag, c, r, x_kind="gauss", ra=None, anchor="factorised"):
         N, d = c["B"] * c["T"], c["d"]
-        inp = synth.codec_inputs(c["seed"], N, d, r, c["V"], "bf16", x_kind=x_kind)
+        inp = synth.codec_inputs(c["seed"], N, d, r, c["V"], "bf16", x_kind=x_kind, ra=ra, anchor=anchor)
         g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        ra = inp["ra"]
         nd = int(np.unique(inp["tids"].numpy()).size)
-        cnt = _codec_counts(N, d, r, nd)
-        pk = lac.mapl_pack(g["P"], g["A"])
+        eye = anchor == "full"
+        cnt = _codec_counts(N, d, r, nd, ra, eye)
+        pk = lac.mapl_pack(g["P"], g["A"], ra=ra)
         Z = torch.empty((N, r), dtype=torch.bfloat16, device=dev)
         Xh = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
         gZ = torch.empty_like(Z)
         gX = torch.empty_like(Xh)
         gA = torch.empty((d, r), dtype=torch.float32, device=dev)
-        ws = torch.empty(lac.mapl_bwd_workspace_bytes(c["B"], c["T"], d, r), dtype=torch.uint8, device=dev)
+        ws = torch.empty(lac.mapl_bwd_workspace_bytes(c["B"], c["T"], d, r, ra=ra), dtype=torch.uint8, device=dev)
         comp = lambda: lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"], Z=Z, pk=pk, pk_ready=True)
         reco = lambda: lac.mapl_reconstruct(Z, g["tids"], g["E"], g["P"], g["A"], Xhat=Xh, pk=pk, pk_ready=True)
         rbwd = lambda: lac.mapl_reconstruct_bwd(g["gXhat"], Z, g["A"], gZ=gZ, gA=gA, accumulate=False, pk=pk,
@@ -296,18 +305,26 @@ def run_cases(lac, dev, flush):
         add(f"{tag} reconstruct", _timed(reco, flush), *cnt["reconstruct"], bound, tokens=N)
         add(f"{tag} reconstruct_bwd", _timed(rbwd, flush), *cnt["reconstruct_bwd"], bound, tokens=N)
         add(f"{tag} compress_bwd", _timed(cbwd, flush), *cnt["compress_bwd"], bound, tokens=N)
-        # sender's anchor-table gradient from gX (Y read once, P, tids, the whole [V][r] table written)
+        if ra == 0:
+            del g, pk, Z, Xh, gZ, gX, gA, ws
+            return inp
+        # sender's anchor-table gradient from gX (Y read once, P, tids, the whole [V][ra] table written)
         V = c["V"]
-        gE = torch.empty((V, r), dtype=torch.float32, device=dev)
-        aws = torch.empty(lac.mapl_anchor_grad_workspace_bytes(c["B"], c["T"], r, V), dtype=torch.uint8, device=dev)
-        agrad = lambda: lac.mapl_anchor_grad(gX, g["tids"], g["P"], V, -1.0, gE=gE, pk=pk, pk_ready=True, ws=aws)
-        add(f"{tag} anchor_grad", _timed(agrad, flush), 2 * N * d + 4 * N + 2 * r * d + 4 * V * r, 2 * N * d * r,
-            "hbm", tokens=N)
+        gE = torch.empty((V, ra), dtype=torch.float32, device=dev)
+        aws = torch.empty(lac.mapl_anchor_grad_workspace_bytes(c["B"], c["T"], ra, V), dtype=torch.uint8, device=dev)
+        agrad = lambda: lac.mapl_anchor_grad(gX, g["tids"], g["P"], V, -1.0, gE=gE, pk=pk, pk_ready=True, r=r,
+                                             ws=aws)
+        add(f"{tag} anchor_grad", _timed(agrad, flush), 2 * N * d + 4 * N + (0 if eye else 2 * ra * d) + 4 * V * ra,
+            0 if eye else 2 * N * d * ra, "hbm", tokens=N)
         del g, pk, Z, Xh, gZ, gX, gA, ws, gE, aws
         return inp
 
     C = synth.CONFIGS
     codec_case("150m d1024 r128", C["150m"], 128)
+    # the anchor variants of the ablation (Table 6) and a separate anchor rank
+    codec_case("150m d1024 r128 no-anchor", C["150m"], 128, anchor="none")
+    codec_case("150m d1024 r128 full-anchor", C["150m"], 128, anchor="full")
+    codec_case("150m d1024 r128 ra256", C["150m"], 128, ra=256)
     for r in C["sweep"]["ranks"]:
         codec_case(f"sweep d1024 r{r}", C["sweep"], r, x_kind="lowrank")
     codec_case("1b d2048 r256", C["1b"], 256)
@@ -428,7 +445,7 @@ def main():
     achieved = dom_bytes / dom_s / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": counter_traffic(),
-                "kernel": "compress (k_tok_reduce_dma<1, 6, 2, true>)", "algorithmic_bytes": dom_bytes,
+                "kernel": "compress (k_tok_reduce_dma<1, 6, 2, true, false>)", "algorithmic_bytes": dom_bytes,
                 "ms": round(med["compress"], 5)}
     pc = float(np.median(pair_cold))
     pw = float(np.median(pair_warm))
