@@ -1,5 +1,6 @@
 // C ABI of the MAPL codec library: host-side validation, then launches.
 // The operations and their sources are documented in include/mapl.h.
+#include <algorithm>
 #include <cmath>
 
 #include "../../include/mapl.h"
@@ -49,8 +50,9 @@ bool anchor_ptrs_ok(int64_t ra, int64_t d, const void* tids, const void* E, cons
   return ra == 0 || (tids && E && (P || ra == d));
 }
 
-// one split count for both backward maps (the larger Gram decides)
-int bwd_splits(int64_t N, int64_t d, int64_t r) { return gram_splits_bf16(int(N), int(d + r), int(r)); }
+// token splits of a backward Gram with `rows` rows (d for reconstruct_bwd,
+// d + ra for compress_bwd); the workspace holds the larger count of either
+int bwd_splits(int64_t N, int64_t rows, int64_t r) { return gram_splits_bf16(int(N), int(rows), int(r)); }
 
 int check_pack(void* pk, size_t pk_bytes, int64_t d, int64_t r, int64_t ra, mapl_dtype dt) {
   if (dt != MAPL_BF16) return MAPL_OK;
@@ -63,7 +65,7 @@ int check_pack(void* pk, size_t pk_bytes, int64_t d, int64_t r, int64_t ra, mapl
 // the first S d r of them) and M [ra][r]; fp32: the residual [N][d]
 size_t bwd_ws_bytes(int64_t N, int64_t d, int64_t r, int64_t ra, mapl_dtype dt) {
   if (dt == MAPL_F32) return size_t(N) * d * sizeof(float);
-  const int S = bwd_splits(N, d, r);
+  const int S = std::max(bwd_splits(N, d, r), bwd_splits(N, d + ra, r));
   return (size_t(S) * (d + ra) * r + size_t(ra) * r) * sizeof(float);
 }
 
@@ -201,7 +203,7 @@ int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A, void* 
   }
   PackView v = pack_view(pk, d, r, 0);
   if (!pk_ready) launch_pack_AtF(static_cast<const uint16_t*>(A), v.AtF, int(d), int(r), stream);
-  const int S = bwd_splits(N, d, r);  // same split count as compress_bwd: the workspace fits both
+  const int S = bwd_splits(N, d, r);
   float* part = static_cast<float*>(ws);
   if (N > 0) {
     launch_tok_reduce_bf16(static_cast<const uint16_t*>(gXhat), v.AtF, nullptr, nullptr, nullptr,
@@ -245,7 +247,7 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const 
     launch_outer_f32(R, static_cast<const float*>(gZ), gA, int(N), int(d), int(r), accumulate, stream);
     return ls.done();
   }
-  const int S = bwd_splits(N, d, r);
+  const int S = bwd_splits(N, d + ra, r);
   float* part = static_cast<float*>(ws);           // [S][d + ra][r]
   float* M = part + size_t(S) * (d + ra) * r;      // [ra][r]
   const uint16_t* gZ16 = static_cast<const uint16_t*>(gZ);

@@ -430,9 +430,10 @@ void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32
 //    each row segment written by 32 consecutive lanes.
 // Invalid token ids read row 0 of E and their anchor units are zeroed.
 // Two blocks fit on a CU (<= 256 registers per lane, 64 KB LDS), so one
-// block's loads overlap the other's matrix-core work.
-template <int TB, int PER, int P>
-__global__ __launch_bounds__(256, 2) void k_tok_expand(const bf16_t* __restrict__ in, const bf16_t* __restrict__ AF,
+// block's loads overlap the other's matrix-core work; with 64-token tiles
+// (32 KB) four do (MINB = 4), which measured faster for 512-byte rows.
+template <int TB, int PER, int P, int MINB = 2>
+__global__ __launch_bounds__(256, MINB) void k_tok_expand(const bf16_t* __restrict__ in, const bf16_t* __restrict__ AF,
                                                     const int32_t* __restrict__ tids, const bf16_t* __restrict__ E,
                                                     const bf16_t* __restrict__ PtF, bf16_t* __restrict__ out, int N,
                                                     int d, int r, int V, int nx, int ny, int ur_log2) {
@@ -576,8 +577,9 @@ bool launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_
   const int UR = 2 * S;                            // 16-byte units per token row (a power of two)
   int ur_log2 = 0;
   while ((1 << ur_log2) < UR) ++ur_log2;
-  // token tile: the staged rows (TT * UR * 16 B) and the output tile (TT * 512 B) share <= 64 KB
-  const int TB = (UR <= 32) ? 4 : (UR <= 64) ? 2 : 1;
+  // token tile: the staged rows (TT * UR * 16 B) and the output tile (TT * 512 B) share <= 64 KB;
+  // 512-byte rows (r = 128 with its anchor) take 64-token tiles, four blocks per CU
+  const int TB = (UR < 32) ? 4 : (UR <= 64) ? 2 : 1;
   const int TT = TB * 32;
   const size_t lds = size_t(TT) * (UR * 16 > 512 ? UR * 16 : 512);
   const int nx = (d + 255) / 256;
@@ -591,6 +593,9 @@ bool launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_
   else if (TB == 4 && per == 8) MAPL_EXPAND(4, 8);
   else if (TB == 4 && per == 4) MAPL_EXPAND(4, 4);
   else if (TB == 4 && per == 2) MAPL_EXPAND(4, 2);
+  else if (TB == 2 && per == 8)
+    hipLaunchKernelGGL((k_tok_expand<2, 8, P, 4>), dim3(nx * ny), dim3(256), lds, s, in, AF, tids, E, PtF, out, N, d,
+                       r, V, nx, ny, ur_log2);
   else if (TB == 2) MAPL_EXPAND(2, 16);
   else MAPL_EXPAND(1, 16);
 #undef MAPL_EXPAND
@@ -614,7 +619,7 @@ bool launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_
 // writes eight units.  The loads of the next three chunks are in flight while
 // the current chunk is multiplied.
 constexpr int kGramTok = 64;     // tokens per chunk (4 matrix-core K-steps)
-constexpr int kGramRound = 512;  // tokens per fully unrolled round of chunks
+constexpr int kGramRound = 512;  // tokens per block (8 chunks) unless that leaves a partial wave of blocks
 
 __device__ __forceinline__ void transpose8x8_b16(const u32x4 (&v)[8], u32x4 (&o)[8]) {
   // o[q] word k = (element q of v[2k], element q of v[2k+1]) as (low, high)
@@ -626,7 +631,7 @@ __device__ __forceinline__ void transpose8x8_b16(const u32x4 (&v)[8], u32x4 (&o)
   }
 }
 
-template <int TJ>
+template <int TJ, int NR>
 __global__ __launch_bounds__(256) void k_gram2(const bf16_t* __restrict__ in, int64_t ldin, int Ld,
                                                const int32_t* __restrict__ tids, int V,
                                                const bf16_t* __restrict__ E, int Le, const bf16_t* __restrict__ R,
@@ -725,8 +730,7 @@ __global__ __launch_bounds__(256) void k_gram2(const bf16_t* __restrict__ in, in
   // counts the loads in flight exactly): register set u holds the chunks
   // c with c % D == u.  Chunks past the block's tokens load clamped rows and
   // are staged as zeros.
-  constexpr int NR = kGramRound / kGramTok;
-  for (int rb = nb; rb < ne; rb += kGramRound) {
+  for (int rb = nb; rb < ne; rb += NR * kGramTok) {
     if (tileE) {
 #pragma unroll
       for (int u = 0; u < D; ++u) load_tids(tq[u], rb, u);
@@ -772,28 +776,63 @@ __global__ __launch_bounds__(256) void k_gram2(const bf16_t* __restrict__ in, in
       }
 }
 
+// Token splits: 512 tokens per block (one round of 8 chunks), or one round of
+// 10, 12 or 16 chunks (the fewest that do) where 512 would leave a partial
+// second wave of blocks on the chip's 256 compute units; at most 64 splits
+// (bounds the partials: at most 64 d x r pieces).
+constexpr int kGramWideRounds[3] = {10, 12, 16};
+
 int gram_splits_bf16(int N, int rows, int Rd) {
-  (void)rows;
-  (void)Rd;
-  int s = (N + kGramRound - 1) / kGramRound;  // one round of 512 tokens per block where possible
-  if (s > 64) s = 64;                          // bounds the partials: at most 64 d x r pieces
+  const int TJ = Rd >= 128 ? 128 : Rd;
+  const int tiles = ((rows + 127) / 128) * (Rd / TJ);
+  int s = (N + kGramRound - 1) / kGramRound;
+  if (tiles * s > 256) {
+    for (int nr : kGramWideRounds) {
+      const int sw = (N + nr * kGramTok - 1) / (nr * kGramTok);
+      if (tiles * sw <= 256) {
+        s = sw;
+        break;
+      }
+    }
+  }
+  if (s > 64) s = 64;
   if (s < 1) s = 1;
   return s;
 }
 
 void launch_gram_bf16(const uint16_t* in, int64_t ldin, int Ld, const int32_t* tids, int V, const uint16_t* E,
                       int Le, const uint16_t* R, int Rd, float* part, int N, int splits, hipStream_t s) {
+  // tokens per split: one round of 10, 12 or 16 chunks where that covers it, else rounds of 8
   int tps = (N + splits - 1) / splits;
-  tps = (tps + kGramRound - 1) / kGramRound * kGramRound;
+  int nr = 8;
+  if (tps > kGramRound) {
+    for (int w : kGramWideRounds)
+      if (tps <= w * kGramTok) {
+        nr = w;
+        break;
+      }
+  }
+  tps = (tps + nr * kGramTok - 1) / (nr * kGramTok) * (nr * kGramTok);
   const int TJ = Rd >= 128 ? 128 : Rd;
   const int ti = (Ld + Le + 127) / 128, tj = Rd / TJ;
   const dim3 grid(unsigned(ti * tj * splits));
-#define MAPL_GRAM(TJv)                                                                                      \
-  hipLaunchKernelGGL((k_gram2<TJv>), grid, dim3(256), 0, s, in, ldin, Ld, tids, V, E, Le, R, Rd, part, N, tps, ti, \
-                     tj)
-  if (TJ == 128) MAPL_GRAM(128);
-  else if (TJ == 64) MAPL_GRAM(64);
-  else MAPL_GRAM(32);
+#define MAPL_GRAM(TJv, NRv)                                                                                         \
+  hipLaunchKernelGGL((k_gram2<TJv, NRv>), grid, dim3(256), 0, s, in, ldin, Ld, tids, V, E, Le, R, Rd, part, N, tps, \
+                     ti, tj)
+#define MAPL_GRAM_NR(NRv)                 \
+  if (TJ == 128) MAPL_GRAM(128, NRv);     \
+  else if (TJ == 64) MAPL_GRAM(64, NRv);  \
+  else MAPL_GRAM(32, NRv);
+  if (nr == 10) {
+    MAPL_GRAM_NR(10)
+  } else if (nr == 12) {
+    MAPL_GRAM_NR(12)
+  } else if (nr == 16) {
+    MAPL_GRAM_NR(16)
+  } else {
+    MAPL_GRAM_NR(8)
+  }
+#undef MAPL_GRAM_NR
 #undef MAPL_GRAM
 }
 
