@@ -879,17 +879,21 @@ __global__ __launch_bounds__(256) void k_sub_ptm(const bf16_t* __restrict__ P, c
   const int hi = lane >> 5, l32 = lane & 31;
   const int i0 = blockIdx.x * 32, j0 = blockIdx.y * 32;
   const int kq = ra >> 2;  // ra % 32 == 0: a multiple of 8
+  const int kb = wave * kq, ke = kb + kq;
   f32x16 acc = f32x16{};
-  for (int kc = wave * kq; kc < (wave + 1) * kq; kc += 8) {
-    float a[4], b[4];
+  // 32 values of k per batch, all loads issued before the batch's multiplies
+  for (int kc = kb; kc < ke; kc += 32) {
+    float a[16], b[16];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int k = kc + 2 * t + hi;
+    for (int t = 0; t < 16; ++t) {
+      const int k = min(kc + 2 * t + hi, ke - 1);
       a[t] = bf2f(P[size_t(k) * d + i0 + l32]);
       b[t] = M[size_t(k) * r + j0 + l32];
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc = mfma_f32_32x32x2(a[t], b[t], acc);
+    for (int t = 0; t < 16; ++t)
+      if (kc + 2 * t < ke) acc = mfma_f32_32x32x2(a[t], b[t], acc);
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v) red[wave * 1024 + v * 64 + lane] = acc[v];

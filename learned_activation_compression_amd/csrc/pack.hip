@@ -131,19 +131,22 @@ __global__ __launch_bounds__(256) void k_frag_pack4(const bf16_t* __restrict__ A
 }
 
 // QnF = fragments of W = -(P A)^T (M = r, K = ra), rounded once to bf16.  One block
-// per 32 x 32 tile (i, j) of P A; the 4 waves split the d-long contraction:
-// the matrix-core A operand is 16 bytes of a row of P, the B operand the AtF
-// fragment of the same K-step, and the four partial tiles are added in LDS in
-// a fixed order.
-__global__ __launch_bounds__(256) void k_qn_direct(const bf16_t* __restrict__ P, const bf16_t* __restrict__ AtF,
-                                                   bf16_t* __restrict__ QnF, int d, int r) {
+// per 32 x 32 tile (i, j) of P A; its 16 waves split the d-long contraction
+// (the matrix-core A operand is 16 bytes of a row of P, the B operand the AtF
+// fragment of the same K-step), and the 16 partial tiles are added in LDS in
+// a fixed order, each wave summing 64 of the tile's elements.
+constexpr int kQnWaves = 16;
+
+__global__ __launch_bounds__(64 * kQnWaves) void k_qn_direct(const bf16_t* __restrict__ P,
+                                                            const bf16_t* __restrict__ AtF,
+                                                            bf16_t* __restrict__ QnF, int d, int r) {
   // grid (ra / 32, r / 32): blockIdx.x walks the ra rows of P A, blockIdx.y its r columns
-  __shared__ float red[4 * 1024];
+  __shared__ float red[kQnWaves * 1024];
   const int lane = threadIdx.x & 63, w = wave_id();
   const int hi = lane >> 5, l32 = lane & 31;
   const int i0 = blockIdx.x * 32, mbj = blockIdx.y;  // rows i0.. of P A, column block mbj
   const int MB = r / 32;
-  const int S = d / 16, sb = S * w / 4, se = S * (w + 1) / 4;
+  const int S = d / 16, sb = S * w / kQnWaves, se = S * (w + 1) / kQnWaves;
   const bf16_t* prow = P + size_t(i0 + l32) * d + 8 * hi;
   f32x16 acc = f32x16{};
   for (int s0 = sb; s0 < se; s0 += 8) {
@@ -161,6 +164,14 @@ __global__ __launch_bounds__(256) void k_qn_direct(const bf16_t* __restrict__ P,
 #pragma unroll
   for (int v = 0; v < 16; ++v) red[w * 1024 + v * 64 + lane] = acc[v];
   __syncthreads();
+  // element e = v 64 + lane of the tile (fragment order): the partials in wave order
+  const int e = w * 64 + lane;
+  float sum = red[e];
+#pragma unroll
+  for (int q = 1; q < kQnWaves; ++q) sum += red[q * 1024 + e];
+  __syncthreads();
+  red[e] = sum;
+  __syncthreads();
   if (w != 0) return;
   // lane (column j = mbj*32 + l32) holds rows i = i0 + 8 q + 4 hi + t of P A (t < 4),
   // which in W = -(P A)^T are elements 4 hi + t of unit ((i >> 4) MB + mbj) 64 + l32 + 32 (q & 1)
@@ -168,10 +179,7 @@ __global__ __launch_bounds__(256) void k_qn_direct(const bf16_t* __restrict__ P,
   for (int q = 0; q < 4; ++q) {
     float v[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int o = (4 * q + t) * 64 + lane;
-      v[t] = -((red[o] + red[1024 + o]) + (red[2048 + o] + red[3072 + o]));
-    }
+    for (int t = 0; t < 4; ++t) v[t] = -red[(4 * q + t) * 64 + lane];
     const size_t unit = (size_t((i0 >> 4) + (q >> 1)) * MB + mbj) * 64 + l32 + 32 * (q & 1);
     *reinterpret_cast<u32x2*>(QnF + unit * 8 + 4 * hi) = u32x2{pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
   }
@@ -198,7 +206,7 @@ void launch_pack_all(const uint16_t* P, const uint16_t* A, PackView v, int d, in
     hipLaunchKernelGGL(k_negate_units, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
                        reinterpret_cast<const u32x4*>(v.AtF), reinterpret_cast<u32x4*>(v.QnF), n);
   } else if (ra > 0) {
-    hipLaunchKernelGGL(k_qn_direct, dim3(ra / 32, r / 32), dim3(256), 0, s, P, v.AtF, v.QnF, d, r);
+    hipLaunchKernelGGL(k_qn_direct, dim3(ra / 32, r / 32), dim3(64 * kQnWaves), 0, s, P, v.AtF, v.QnF, d, r);
   }
 }
 
