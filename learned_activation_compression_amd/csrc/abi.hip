@@ -156,9 +156,9 @@ int mapl_reconstruct(const void* Z, const int32_t* tids, const void* E_small, co
     launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), int(ra),
                     stream);
   if (ra > 0 && P == nullptr) {  // full-rank anchor: add the rows E[t] in the epilogue
-    if (!launch_tok_gemm_eadd_bf16(static_cast<const uint16_t*>(Z), int(r), tids, int(V),
-                                   static_cast<const uint16_t*>(E_small), v.AF, static_cast<uint16_t*>(Xhat), N,
-                                   int(d), stream))
+    if (!launch_tok_expand_eadd_bf16(static_cast<const uint16_t*>(Z), v.AF, tids,
+                                     static_cast<const uint16_t*>(E_small), static_cast<uint16_t*>(Xhat), N, int(d),
+                                     int(r), int(V), stream))
       return MAPL_ERR_SHAPE;  // not reached: ra = d != r needs r % 64 == 0
     return ls.done();
   }

@@ -432,7 +432,11 @@ void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32
 // Two blocks fit on a CU (<= 256 registers per lane, 64 KB LDS), so one
 // block's loads overlap the other's matrix-core work; with 64-token tiles
 // (32 KB) four do (MINB = 4), which measured faster for 512-byte rows.
-template <int TB, int PER, int P, int MINB = 2>
+// EADD (the full-rank anchor, P = I): E is [V][d] and its rows are added to
+// the output instead of entering the contraction.  Each lane loads the
+// 8-byte pieces of E[t] that match its accumulators before the matrix-core
+// loop, and adds them in fp32 before the one rounding to bf16.
+template <int TB, int PER, int P, int MINB = 2, bool EADD = false>
 __global__ __launch_bounds__(256, MINB) void k_tok_expand(const bf16_t* __restrict__ in, const bf16_t* __restrict__ AF,
                                                     const int32_t* __restrict__ tids, const bf16_t* __restrict__ E,
                                                     const bf16_t* __restrict__ PtF, bf16_t* __restrict__ out, int N,
@@ -449,9 +453,28 @@ __global__ __launch_bounds__(256, MINB) void k_tok_expand(const bf16_t* __restri
   const bool wave_on = ch0 < d;          // d % 64 == 0
   const int UR = 1 << ur_log2;           // 16-byte units per token row
   const int Sz = r >> 4;
-  const int S = (E != nullptr) ? 2 * Sz : Sz;
+  const int S = (E != nullptr && !EADD) ? 2 * Sz : Sz;
   const int uz = 2 * Sz;                 // units of the `in` part
   const int msk = UR >= 8 ? 7 : UR - 1;
+
+  // EADD: this lane's pieces of the anchor rows (token j*32 + l32; channels
+  // ch0 + 32 i + 8 g + 4 hi .. + 3), zero for an invalid id
+  u32x2 ev[EADD ? TB : 1][2][4];
+  if (EADD) {
+#pragma unroll
+    for (int j = 0; j < TB; ++j) {
+      const int id = tids[min(tok0 + j * 32 + l32, N - 1)];
+      const bool ok = wave_on && id >= 0 && id < V;
+      const bf16_t* er = E + size_t(ok ? id : 0) * d + (wave_on ? ch0 : 0) + 4 * hi;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 x = *reinterpret_cast<const u32x2*>(er + i * 32 + 8 * g);
+          ev[j][i][g] = ok ? x : u32x2{0u, 0u};
+        }
+    }
+  }
 
   // ---- 1. stage token rows: every thread first loads the token ids of its
   // PER units (PER = TT * UR / 256, a compile-time constant so that the loops
@@ -461,7 +484,7 @@ __global__ __launch_bounds__(256, MINB) void k_tok_expand(const bf16_t* __restri
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int t = (threadIdx.x + 256 * k) >> ur_log2;
-    tk[k] = (E != nullptr) ? tids[min(tok0 + t, N - 1)] : 0;
+    tk[k] = (E != nullptr && !EADD) ? tids[min(tok0 + t, N - 1)] : 0;
   }
   u32x4 v[PER];
   uint32_t mk[PER];
@@ -548,8 +571,18 @@ __global__ __launch_bounds__(256, MINB) void k_tok_expand(const bf16_t* __restri
         for (int g = 0; g < 4; ++g) {
           const int c = (wave * 64 + i * 32 + 8 * g + 4 * hi) >> 2;  // 8-byte chunk within the row (0..63)
           uint32_t* dst = o32 + t * 128 + (c ^ sw) * 2;
-          dst[0] = pack2bf(acc[i][j][4 * g], acc[i][j][4 * g + 1]);
-          dst[1] = pack2bf(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+          float y[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = acc[i][j][4 * g + e];
+          if (EADD) {
+            const u32x2 x = ev[EADD ? j : 0][i][g];
+            y[0] += bf2f(uint16_t(x[0] & 0xffffu));
+            y[1] += bf2f(uint16_t(x[0] >> 16));
+            y[2] += bf2f(uint16_t(x[1] & 0xffffu));
+            y[3] += bf2f(uint16_t(x[1] >> 16));
+          }
+          dst[0] = pack2bf(y[0], y[1]);
+          dst[1] = pack2bf(y[2], y[3]);
         }
     }
   }
@@ -599,6 +632,27 @@ bool launch_tok_expand_bf16(const uint16_t* in, const uint16_t* AF, const int32_
   else if (TB == 2) MAPL_EXPAND(2, 16);
   else MAPL_EXPAND(1, 16);
 #undef MAPL_EXPAND
+  return true;
+}
+
+// out[N][d] = in[N][r] A^T + E[t] for the full-rank anchor (E [V][d], P = I):
+// the staged-row kernel with the anchor rows added in its epilogue for
+// r <= 128, the token GEMM's epilogue otherwise.
+bool launch_tok_expand_eadd_bf16(const uint16_t* in, const uint16_t* AF, const int32_t* tids, const uint16_t* E,
+                                 uint16_t* out, int N, int d, int r, int V, hipStream_t s) {
+  if (r > 128 || r < 64) return launch_tok_gemm_eadd_bf16(in, r, tids, V, E, AF, out, N, d, s);
+  const int UR = r / 8;  // 16-byte units of a Z row (8 or 16)
+  int ur_log2 = 0;
+  while ((1 << ur_log2) < UR) ++ur_log2;
+  constexpr int TB = 2, TT = TB * 32;
+  const size_t lds = size_t(TT) * 512;  // the output tile; the staged rows are smaller
+  const int nx = (d + 255) / 256, ny = (N + TT - 1) / TT;
+  if (UR == 16)
+    hipLaunchKernelGGL((k_tok_expand<TB, 4, 4, 2, true>), dim3(nx * ny), dim3(256), lds, s, in, AF, tids, E, nullptr,
+                       out, N, d, r, V, nx, ny, ur_log2);
+  else
+    hipLaunchKernelGGL((k_tok_expand<TB, 2, 4, 2, true>), dim3(nx * ny), dim3(256), lds, s, in, AF, tids, E, nullptr,
+                       out, N, d, r, V, nx, ny, ur_log2);
   return true;
 }
 

@@ -63,7 +63,10 @@ void launch_sub_ptm(const uint16_t* P, const float* M, float* gA, int d, int r, 
 // launching nothing, for shapes it does not cover (K1, K2 % 64, C % 128).
 bool launch_tok_gemm_bf16(const uint16_t* src, int K1, const int32_t* tids, int V, const uint16_t* E, int K2,
                           const uint16_t* F1, const uint16_t* F2, uint16_t* out, int N, int C, hipStream_t s);
-// out[N][C] = src[N][K1] W + E[t] with E [V][C] (the full-rank anchor), one rounding
+// out[N][d] = in[N][r] A^T + E[t] with E [V][d] (the full-rank anchor), one rounding; r % 64 == 0
+bool launch_tok_expand_eadd_bf16(const uint16_t* in, const uint16_t* AF, const int32_t* tids, const uint16_t* E,
+                                 uint16_t* out, int N, int d, int r, int V, hipStream_t s);
+// the token GEMM form of the same: out[N][C] = src[N][K1] W + E[t] with E [V][C], one rounding
 bool launch_tok_gemm_eadd_bf16(const uint16_t* src, int K1, const int32_t* tids, int V, const uint16_t* E,
                                const uint16_t* F1, uint16_t* out, int N, int C, hipStream_t s);
 
