@@ -22,7 +22,9 @@
 //
 // Block: TC output columns x TT tokens, 4 waves as 2 x 2, each wave a
 // (TC/2) x (TT/2) tile of 32 x 32 accumulators (columns = matrix-core rows,
-// tokens = matrix-core columns).  The contraction runs in chunks of 64: the
+// tokens = matrix-core columns): 256 x 256 with two ring slots where that
+// still fills the chip (the accumulators take all 256 AGPRs), else 256 x 128
+// or 128 x 128 with three or four.  The contraction runs in chunks of 64: the
 // chunk's weight fragments (TC/32 row blocks x 4 K-steps, 1 KB each) and its
 // TT token-row segments of 128 bytes are copied with global_load_lds straight
 // into slot c % S of an LDS ring, S - 1 chunks ahead.  Token row t keeps its
@@ -51,7 +53,7 @@ struct GemmRing {
   static constexpr size_t OUT = size_t(TC) * TT * 2;  // staged output tile (bf16)
   static constexpr size_t OUT32 = size_t(TC) * TT * 4;  // ... fp32, for the anchor-row epilogue
   static constexpr size_t BYTES = RING > OUT ? RING : OUT;
-  static_assert(RING >= OUT32, "the fp32 output tile must fit the ring");
+
   static_assert((WU + TU) % 256 == 0, "copies must split evenly over the 4 waves");
 };
 
@@ -167,6 +169,7 @@ __global__ __launch_bounds__(256) void k_tok_gemm(const bf16_t* __restrict__ src
   __syncthreads();
 
   if (EADD) {
+    static_assert(!EADD || GR::RING >= GR::OUT32, "the fp32 output tile must fit the ring");
     // stage the tile as fp32 rows [token][TC columns] (16-byte unit u of row t at
     // u ^ (t & 31)), then out[n] = bf16(tile[n] + E[t_n]) with 16-byte loads and stores
     constexpr int RU4 = TC / 4;  // 16-byte fp32 units per staged row
@@ -258,6 +261,13 @@ bool launch_tok_gemm_bf16(const uint16_t* src, int K1, const int32_t* tids, int 
                           const uint16_t* F1, const uint16_t* F2, uint16_t* out, int N, int C, hipStream_t s) {
   const bool anc = E != nullptr && K2 > 0;
   if (K1 % kKC != 0 || (anc && K2 % kKC != 0)) return false;
+  // 256 x 256 tiles (two 64 KB slots, 128 x 128 per wave) where they still give
+  // every compute unit a block: fewer LDS bytes per matrix-core operation
+  if (C % 256 == 0 && int64_t(C / 256) * ((N + 255) / 256) >= 256) {
+    if (anc) launch_gemm<256, 256, 2, true>(src, K1, tids, V, E, K2, F1, F2, out, N, C, s);
+    else launch_gemm<256, 256, 2, false>(src, K1, tids, V, E, K2, F1, F2, out, N, C, s);
+    return true;
+  }
   if (C % 256 == 0) {
     if (anc) launch_gemm<256, 128, 3, true>(src, K1, tids, V, E, K2, F1, F2, out, N, C, s);
     else launch_gemm<256, 128, 3, false>(src, K1, tids, V, E, K2, F1, F2, out, N, C, s);
