@@ -87,6 +87,10 @@ def test_compress_validation(lib):
     assert _compress(lib, ra=0, X=None, tids=None, E=None, P=None, V=0) == ENULL
     assert _compress(lib, ra=1024, B=0) == OK        # full anchor
     assert _compress(lib, dt=F32, ra=100, pk=None, pk_bytes=0, B=0) == OK
+    # P = NULL stands for the identity only with the full-rank anchor (ra == d)
+    assert _compress(lib, ra=1024, P=None, B=0) == OK
+    assert _compress(lib, ra=128, P=None) == ENULL
+    assert _compress(lib, ra=1024, E=None, P=None) == ENULL
 
 
 def test_empty_batch_is_a_no_op(lib):
@@ -154,6 +158,9 @@ def test_anchor_grad_validation(lib):
     assert call(ra=0) == ESHAPE                                 # no anchor, no table
     assert call(ra=2048) == ESHAPE
     assert call(ra=256) == EWS                                  # the workspace holds N x ra rows
+    assert call(P=None) == ENULL                                # P = NULL only for ra == d
+    wsd = lib.mapl_anchor_grad_workspace_bytes(8, 2048, 1024, 32000)
+    assert call(ra=1024, P=None, pk=None, w=None, wb=wsd) == ENULL   # the identity reads no pack, but needs ws
     assert call(B=0, acc=1, Y=None, tids=None, P=None, w=None) == OK   # empty batch, accumulate: nothing to do
 
 
