@@ -175,7 +175,7 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids,
  * 16-byte aligned `ws` of mapl_anchor_grad_workspace_bytes() (MAPL_ERR_ARG if
  * misaligned): N*ra fp32 projected rows and partial maxima.  Shapes follow
  * the codec rules (bf16: d % 128 == 0, r a power of two in [32, 512], and the
- * anchor-rank rules above with 1 <= ra); V <= 2^22, N*ra <= 2^38. */
+ * anchor-rank rules above with 1 <= ra); V <= 2^22, N < 2^24, N*ra <= 2^38. */
 size_t mapl_anchor_grad_workspace_bytes(int64_t B, int64_t T, int64_t ra, int64_t V);
 int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* gE, float alpha,
                      int accumulate, int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, int64_t V,

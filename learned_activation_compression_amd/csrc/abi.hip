@@ -283,7 +283,8 @@ int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* g
   if ((accumulate != 0 && accumulate != 1) || (pk_ready != 0 && pk_ready != 1) || !std::isfinite(alpha))
     return MAPL_ERR_ARG;
   const int64_t N = B * T;
-  if (V > (int64_t(1) << 22) || N * ra > (int64_t(1) << 38)) return MAPL_ERR_SHAPE;
+  // the owner kernel packs a token index into 24 bits of its queue entries
+  if (V > (int64_t(1) << 22) || N >= (int64_t(1) << 24) || N * ra > (int64_t(1) << 38)) return MAPL_ERR_SHAPE;
   if (!gE) return MAPL_ERR_NULL;
   if (N == 0) {  // empty batch: gE = 0 (or unchanged when accumulating)
     if (accumulate) return MAPL_OK;

@@ -358,11 +358,8 @@ static void launch_reduce_dma(const uint16_t* in, const uint16_t* AtF, const int
                               float* Uf = nullptr, float alpha = 1.f, float* part = nullptr) {
   auto k = k_tok_reduce_dma<RBW, S, G, ANCHOR, OUTF>;
   const size_t lds = RedRing<RBW, S>::BYTES;
-  static bool attr = false;  // once per process: allow more than 64 KB of dynamic LDS
-  if (!attr) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-    attr = true;
-  }
+  static std::atomic<uint64_t> attr{0};  // devices with the raised LDS limit
+  allow_lds(reinterpret_cast<const void*>(k), int(lds), attr);
   hipLaunchKernelGGL(k, dim3((N + 63) / 64), dim3(256 * G), lds, s, in, AtF, tids, E, QnF, out, N, d, r, ra, V, Uf,
                      alpha, part);
 }

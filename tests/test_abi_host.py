@@ -154,6 +154,7 @@ def test_anchor_grad_validation(lib):
     assert call(r=96) == ESHAPE                                 # bf16 r a power of two
     assert call(V=0) == ESHAPE
     assert call(V=2 ** 22 + 1) == ESHAPE                        # owner blocks scale with V
+    assert call(B=1, T=2 ** 24) == ESHAPE                       # token indices take 24 bits
     assert call(dt=4) == EDTYPE
     assert call(ra=0) == ESHAPE                                 # no anchor, no table
     assert call(ra=2048) == ESHAPE
