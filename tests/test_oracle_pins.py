@@ -379,6 +379,82 @@ def test_spel_step_at_1b_shape_stays_on_stiefel_and_matches_svd_polar():
     np.testing.assert_allclose(D, _ns_closed_form(mn / np.linalg.norm(mn), 8), atol=1e-12)
 
 
+# ------------------------------------------------------ Polar Express pins --
+
+def _pe_interval_grid(lo, hi, n=400001):
+    return np.linspace(lo, hi, n)
+
+
+def test_polar_express_polynomials_are_minimax():
+    """Chebyshev's alternation theorem: p_t is the best uniform approximation
+    of 1 on [l_t, u_t] by odd quintics (a 3-dimensional Haar space) exactly
+    when 1 - p_t reaches its maximum E_t with alternating signs at 4 points;
+    and the next interval is p_t's range, [1 - E_t, 1 + E_t]."""
+    coefs, errs = spel.polar_express_coefficients(1e-3, 7)
+    lo, hi = 1e-3, 1.0
+    for (a, b, c), E in zip(coefs, errs):
+        if hi - lo < 1e-7:
+            break
+        x = _pe_interval_grid(lo, hi)
+        e = 1.0 - (a * x + b * x ** 3 + c * x ** 5)
+        assert np.max(np.abs(e)) <= E * (1 + 1e-8) + 1e-15
+        # alternation: scan the sign pattern of the near-extremal points
+        peaks = np.where(np.abs(e) >= E * (1 - 1e-6))[0]
+        signs = [np.sign(e[peaks[0]])]
+        for i in peaks[1:]:
+            if np.sign(e[i]) != signs[-1]:
+                signs.append(np.sign(e[i]))
+        assert len(signs) >= 4, (lo, hi, signs)
+        p = 1.0 - e
+        assert abs(p.min() - (1 - E)) <= 1e-9 * max(E, 1e-12) + 1e-14
+        assert abs(p.max() - (1 + E)) <= 1e-9 * max(E, 1e-12) + 1e-14
+        lo, hi = 1.0 - E, 1.0 + E
+
+
+def test_polar_express_narrow_interval_tends_to_the_limit_quintic():
+    """As the interval shrinks to {1}, the minimax quintic tends to the one
+    with p(1) = 1, p'(1) = p''(1) = 0: (15 x - 10 x^3 + 3 x^5) / 8."""
+    (a, b, c), E = spel._remez_odd_quintic(1 - 1e-4, 1 + 1e-4)
+    np.testing.assert_allclose([a, b, c], [15 / 8, -10 / 8, 3 / 8], atol=1e-6)
+    assert E < 1e-10
+
+
+def test_polar_express_matches_the_singular_value_closed_form():
+    """For X = U diag(s) V^T the schedule acts on singular values only:
+    PE(X) = U diag(phi(s / ||X||_F)) V^T, phi the composition of the scalar
+    quintics; and after 7 steps from ell = 1e-3 it is the SVD polar factor
+    U V^T to within the last error bound."""
+    rng = np.random.default_rng(71)
+    U, _ = np.linalg.qr(rng.standard_normal((48, 12)))
+    V, _ = np.linalg.qr(rng.standard_normal((12, 12)))
+    s = np.geomspace(1.0, 2e-3, 12) * 3.0
+    X = U @ np.diag(s) @ V.T
+    coefs, errs = spel.polar_express_coefficients(1e-3, 7)
+    y = s / np.sqrt(np.sum(s * s))
+    for a, b, c in coefs:
+        y = a * y + b * y ** 3 + c * y ** 5
+    np.testing.assert_allclose(spel.polar_express(X, 7), U @ np.diag(y) @ V.T, atol=1e-12)
+    np.testing.assert_allclose(spel.polar_express(X, 7), U @ V.T, atol=2 * errs[-1] + 1e-12)
+    assert np.all(np.abs(y - 1) <= errs[-1] * (1 + 1e-6))
+    # five steps (the LMO's) leave every singular value within E_5 of 1
+    y5 = s / np.sqrt(np.sum(s * s))
+    for a, b, c in coefs[:5]:
+        y5 = a * y5 + b * y5 ** 3 + c * y5 ** 5
+    assert np.all(np.abs(y5 - 1) <= errs[4] * (1 + 1e-9))
+
+
+def test_polar_express_step_shares_the_tangent_and_momentum_steps():
+    inp = synth.spel_inputs(72, 96, 16, 1e-3)
+    A, g, m = (inp[k].double().numpy() for k in ("A", "g", "m"))
+    A1, m1, D1, gR1 = spel.spel_step(A, g, m, 0.05, 0.9, 8)
+    A2, m2, D2, gR2 = spel.spel_step_polar_express(A, g, m, 0.05, 0.9, 5, 7)
+    np.testing.assert_array_equal(m1, m2)
+    np.testing.assert_array_equal(gR1, gR2)
+    np.testing.assert_allclose(A2.T @ A2, np.eye(16), atol=1e-8)
+    z = spel.polar_express(np.zeros((8, 4)), 5)
+    assert not np.any(z)
+
+
 def test_spel_degenerate_cases():
     rng = np.random.default_rng(10)
     A = synth.orthonormal_columns(rng, 30, 4)
