@@ -368,6 +368,22 @@ def run_cases(lac, dev, flush):
     spel_fn = lambda: lac.spel_step(A, gg, m, sp["alpha"], sp["beta"], sp["ns_iters"], ws=sws)
     flops = 4 * d * r * r * (1 + 2 * sp["ns_iters"])
     add("spel_step d2048 r256 NS8", _timed(spel_fn, flush), 4 * 4 * d * r, flops, "mfma", peak_tf=F32_PEAK_TFLOPS)
+    # the Polar Express polar map (5 LMO / 7 retraction steps): per step a Gram (2 d r^2 with
+    # both triangles), S^2 (2 r^3) and X M (2 d r^2)
+    pe_fn = lambda: lac.spel_step_polar_express(A, gg, m, sp["alpha"], sp["beta"], 5, 7, ws=sws)
+    pe_flops = 4 * d * r * r + 12 * (4 * d * r * r + 2 * r * r * r)
+    add("spel_step d2048 r256 Polar Express 5/7", _timed(pe_fn, flush), 4 * 4 * d * r, pe_flops, "mfma",
+        peak_tf=F32_PEAK_TFLOPS)
+    d2, r2 = C["150m"]["d"], C["150m"]["r"]
+    si2 = synth.spel_inputs(c["seed"], d2, r2, sp["g_var"])
+    A2, g2, m2 = si2["A"].to(dev), si2["g"].to(dev), si2["m"].to(dev)
+    sws2 = torch.empty(lac.spel_workspace_bytes(d2, r2), dtype=torch.uint8, device=dev)
+    ns2 = lambda: lac.spel_step(A2, g2, m2, sp["alpha"], sp["beta"], sp["ns_iters"], ws=sws2)
+    pe2 = lambda: lac.spel_step_polar_express(A2, g2, m2, sp["alpha"], sp["beta"], 5, 7, ws=sws2)
+    add("spel_step d1024 r128 NS8", _timed(ns2, flush), 4 * 4 * d2 * r2,
+        4 * d2 * r2 * r2 * (1 + 2 * sp["ns_iters"]), "mfma", peak_tf=F32_PEAK_TFLOPS)
+    add("spel_step d1024 r128 Polar Express 5/7", _timed(pe2, flush), 4 * 4 * d2 * r2,
+        4 * d2 * r2 * r2 + 12 * (4 * d2 * r2 * r2 + 2 * r2 * r2 * r2), "mfma", peak_tf=F32_PEAK_TFLOPS)
     return res
 
 

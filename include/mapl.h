@@ -245,6 +245,28 @@ int spel_step(float* A, const float* g, float* m, float alpha, float beta, int n
               float* D_out, int64_t d, int64_t r, void* ws, size_t ws_bytes,
               hipStream_t stream);
 
+/* The same SPEL step with the Polar Express polar map that Section 3.3 and
+ * Table 8 name (5 LMO steps, 7 retraction steps; the pages print no
+ * coefficients).  Step t multiplies X on the right by a I + b S + c S^2,
+ * S = X^T X: the odd quintic a x + b x^3 + c x^5 of the singular values that
+ * best approximates 1, uniformly, on the interval [l_t, u_t] the values are
+ * known to lie in (Remez exchange); [l_1, u_1] = [ell, 1] and
+ * [l_{t+1}, u_{t+1}] = [1 - E_t, 1 + E_t], E_t the step's maximum error;
+ * intervals narrower than 1e-4 take the limit quintic (15 x - 10 x^3 +
+ * 3 x^5) / 8.  Both polar inputs, m and A - alpha D, are scaled by their
+ * Frobenius norms first (D = 0 when m == 0).  The schedule is computed on the
+ * host in double and rounded to fp32.  Buffers, workspace
+ * (spel_workspace_bytes) and the other limits as for spel_step;
+ * 1 <= lmo_steps, ret_steps <= 32, 0 < ell < 1 (MAPL_ERR_ARG otherwise). */
+int spel_step_polar_express(float* A, const float* g, float* m, float alpha, float beta, int lmo_steps,
+                            int ret_steps, float ell, float* D_out, int64_t d, int64_t r, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/* Host only: the Polar Express schedule above from [ell, 1]: coef [steps][3]
+ * = (a, b, c) of each step and, if err is not NULL, err [steps] = E_t.
+ * 0 < ell < 1, 1 <= steps <= 32 (MAPL_ERR_ARG otherwise). */
+int spel_polar_express_coefficients(double ell, int steps, double* coef, double* err);
+
 #ifdef __cplusplus
 }
 #endif

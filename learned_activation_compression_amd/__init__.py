@@ -26,6 +26,7 @@ __all__ = [
     "mapl_bwd_workspace_bytes", "mapl_reconstruct_bwd", "mapl_compress_bwd",
     "mapl_anchor_grad_workspace_bytes", "mapl_anchor_grad", "mapl_check_tids",
     "rvq_encode", "rvq_decode", "rvq_stream_apply", "spel_workspace_bytes", "spel_step",
+    "spel_step_polar_express", "spel_polar_express_coefficients",
     "MAPL_F32", "MAPL_BF16",
 ]
 
@@ -61,6 +62,9 @@ _SIGS = {
     "rvq_stream_apply": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
     "spel_workspace_bytes": (_sz, [_i64, _i64]),
     "spel_step": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _vp, _i64, _i64, _vp, _sz, _vp]),
+    "spel_step_polar_express": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _i32, _f32, _vp, _i64, _i64, _vp, _sz,
+                                       _vp]),
+    "spel_polar_express_coefficients": (_i32, [ctypes.c_double, _i32, _vp, _vp]),
 }
 
 _lib = None
@@ -394,3 +398,29 @@ def spel_step(A, g, m, alpha: float, beta: float, ns_iters: int = 8, D_out=None,
                             _dev(D_out, "D_out", torch.float32) if D_out is not None else None, d, r,
                             ws.data_ptr() if ws is not None else None, wb, _stream(stream)), "spel_step")
     return D_out
+
+
+def spel_step_polar_express(A, g, m, alpha: float, beta: float, lmo_steps: int = 5, ret_steps: int = 7,
+                            ell: float = 1e-3, D_out=None, ws=None, stream=None):
+    """One SPEL step with the Polar Express polar map (5 LMO / 7 retraction
+    steps by default) on fp32 A [d][r] and m (both in place).  Returns D_out
+    if given, else None."""
+    d, r = A.shape
+    ws, wb = _ws(ws, spel_workspace_bytes(d, r), A)
+    _check(load().spel_step_polar_express(_dev(A, "A", torch.float32), _dev(g, "g", torch.float32),
+                                          _dev(m, "m", torch.float32), float(alpha), float(beta), int(lmo_steps),
+                                          int(ret_steps), float(ell),
+                                          _dev(D_out, "D_out", torch.float32) if D_out is not None else None, d, r,
+                                          ws.data_ptr() if ws is not None else None, wb, _stream(stream)),
+           "spel_step_polar_express")
+    return D_out
+
+
+def spel_polar_express_coefficients(ell: float, steps: int):
+    """The host-side Polar Express schedule: (coef [steps][3] float64, err [steps])."""
+    import numpy as np
+    coef = np.zeros((int(steps), 3), dtype=np.float64)
+    err = np.zeros(int(steps), dtype=np.float64)
+    _check(load().spel_polar_express_coefficients(float(ell), int(steps), coef.ctypes.data, err.ctypes.data),
+           "spel_polar_express_coefficients")
+    return coef, err

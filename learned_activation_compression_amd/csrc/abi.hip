@@ -11,6 +11,7 @@ using namespace mapl;
 namespace {
 
 constexpr const char* kVersion = "mapl-gfx950 0.1.0";
+constexpr int kMaxPolarSteps = 32;
 
 // Launch status: clears any error left by an earlier call before enqueueing
 // and reports the launch error (if any) afterwards.
@@ -386,6 +387,38 @@ int spel_step(float* A, const float* g, float* m, float alpha, float beta, int n
     return MAPL_ERR_ARG;
   LaunchScope ls;
   launch_spel(A, g, m, alpha, beta, ns_iters, D_out, int(d), int(r), ws, stream);
+  return ls.done();
+}
+
+int spel_polar_express_coefficients(double ell, int steps, double* coef, double* err) {
+  if (!coef) return MAPL_ERR_NULL;
+  if (!(ell > 0.0 && ell < 1.0) || steps < 1 || steps > kMaxPolarSteps) return MAPL_ERR_ARG;
+  return polar_express_schedule(ell, steps, coef, err) == 0 ? MAPL_OK : MAPL_ERR_ARG;
+}
+
+int spel_step_polar_express(float* A, const float* g, float* m, float alpha, float beta, int lmo_steps,
+                            int ret_steps, float ell, float* D_out, int64_t d, int64_t r, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+  if (d < 1 || r < 1 || r > d || r > 1024 || d % 32 || r % 32 || d > (1 << 24)) return MAPL_ERR_SHAPE;
+  if (!A || !g || !m) return MAPL_ERR_NULL;
+  if (!(beta >= 0.f && beta < 1.f) || !(alpha >= 0.f && alpha <= 0.7f) || !(ell > 0.f && ell < 1.f) ||
+      lmo_steps < 1 || lmo_steps > kMaxPolarSteps || ret_steps < 1 || ret_steps > kMaxPolarSteps)
+    return MAPL_ERR_ARG;
+  const size_t need = spel_ws_bytes(d, r);
+  if (!ws) return MAPL_ERR_NULL;
+  if (ws_bytes < need) return MAPL_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(g) | reinterpret_cast<uintptr_t>(m) |
+       reinterpret_cast<uintptr_t>(D_out) | reinterpret_cast<uintptr_t>(ws)) & 15)
+    return MAPL_ERR_ARG;
+  // the schedules, on the host, rounded once to fp32 for the kernels
+  double cl[3 * kMaxPolarSteps], cr[3 * kMaxPolarSteps];
+  if (polar_express_schedule(ell, lmo_steps, cl, nullptr) || polar_express_schedule(ell, ret_steps, cr, nullptr))
+    return MAPL_ERR_ARG;
+  float fl[3 * kMaxPolarSteps], fr[3 * kMaxPolarSteps];
+  for (int i = 0; i < 3 * lmo_steps; ++i) fl[i] = float(cl[i]);
+  for (int i = 0; i < 3 * ret_steps; ++i) fr[i] = float(cr[i]);
+  LaunchScope ls;
+  launch_spel_pe(A, g, m, alpha, beta, fl, lmo_steps, fr, ret_steps, D_out, int(d), int(r), ws, stream);
   return ls.done();
 }
 

@@ -103,6 +103,12 @@ void launch_rvq_stream(float* C, const int32_t* idx, const float* vals, int n, i
 
 // ---- SPEL
 size_t spel_ws_bytes(int64_t d, int64_t r);
+// Polar Express: the greedy minimax odd-quintic schedule from [ell, 1] (coef [steps][3],
+// err [steps] or nullptr; returns 0, or -1 if a step is not finite), and the SPEL step
+// that uses it for both polar maps (fp32 coefficients [steps][3])
+int polar_express_schedule(double ell, int steps, double* coef, double* err);
+void launch_spel_pe(float* A, const float* g, float* m, float alpha, float beta, const float* coef_lmo, int lmo_steps,
+                    const float* coef_ret, int ret_steps, float* D_out, int d, int r, void* ws, hipStream_t s);
 void launch_spel(float* A, const float* g, float* m, float alpha, float beta, int ns_iters,
                  float* D_out, int d, int r, void* ws, hipStream_t s);
 

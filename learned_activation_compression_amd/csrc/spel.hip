@@ -27,6 +27,10 @@
 // All sums run in a fixed order, so a step is bitwise repeatable.  The scale
 // s = 1/||m||_F comes from per-block partial sums of squares written by the
 // momentum epilogue, added up in a fixed order by the one launch that uses it.
+#include <algorithm>
+#include <cmath>
+#include <utility>
+
 #include "common.h"
 #include "internal.h"
 
@@ -237,8 +241,81 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
     st4(out + o, val);
   } else {  // XM_NS_LAST_LMO: D = val ; Y0 = A - alpha D
     if (Dout) st4(Dout + o, val);
-    st4(Y0 + o, ld4(Acur + o) - alpha * val);
+    const f32x4 y0 = ld4(Acur + o) - alpha * val;
+    st4(Y0 + o, y0);
+    if (nparts_out) {  // this block's share of ||Y0||_F^2, as for m above
+      float local = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) local = fmaf(y0[q], y0[q], local);
+      for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
+      if (lane == 0) wsum[w] = local;
+      __syncthreads();
+      if (threadIdx.x == 0)
+        nparts_out[blockIdx.y * gridDim.x + blockIdx.x] = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
+    }
   }
+}
+
+// Polar Express step matrix M = s (a I + b s^2 S + c s^4 S^2) [r][r], S the
+// sum of the G Gram pieces, s = 1 / ||X||_F from per-block partial sums (the
+// first step) or 1.  One block per 32 x 32 tile (bi, bj); S^2's tile is
+// S[bi rows] S[bj rows]^T (S is symmetric), its r-long contraction taken in
+// chunks of 128 staged in LDS (the pieces summed while staging) and split
+// over the 4 waves, whose partial tiles are added in a fixed order.
+constexpr int kPolyKC = 128;
+
+__global__ __launch_bounds__(256) void k_spel_poly(const float* __restrict__ part, int groups,
+                                                   const float* __restrict__ nparts_in, int nparts_n, float* __restrict__ M,
+                                                   int r, float ca, float cb, float cc) {
+  __shared__ float sa[32][kPolyKC + 1], sb[32][kPolyKC + 1];
+  __shared__ float red[4 * 1024];
+  __shared__ float scs;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int h = lane >> 5, l32 = lane & 31;
+  const int bi = blockIdx.x, bj = blockIdx.y;
+  const float sx = nparts_in ? block_inv_norm(nparts_in, nparts_n, &scs) : 1.f;
+  const size_t rr = size_t(r) * r;
+
+  f32x16 acc = f32x16{};
+  for (int k0 = 0; k0 < r; k0 += kPolyKC) {
+    const int kn = min(kPolyKC, r - k0);  // a multiple of 32
+    // stage rows bi*32.. and bj*32.. of S, columns k0 .. k0 + kn: 32 x kn each
+    for (int e = threadIdx.x; e < 32 * (kn / 4); e += 256) {
+      const int row = e / (kn / 4), c4 = (e % (kn / 4)) * 4;
+      f32x4 va = ld4(part + size_t(bi * 32 + row) * r + k0 + c4);
+      f32x4 vb = ld4(part + size_t(bj * 32 + row) * r + k0 + c4);
+      for (int q = 1; q < groups; ++q) {
+        va += ld4(part + q * rr + size_t(bi * 32 + row) * r + k0 + c4);
+        vb += ld4(part + q * rr + size_t(bj * 32 + row) * r + k0 + c4);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sa[row][c4 + t] = va[t];
+        sb[row][c4 + t] = vb[t];
+      }
+    }
+    __syncthreads();
+    // wave w: k in [k0 + w kn/4, k0 + (w+1) kn/4), two per multiply (lane half h takes k + h)
+    const int kb = w * (kn / 4);
+    for (int k = kb; k < kb + kn / 4; k += 2) acc = mfma_f32_32x32x2(sa[l32][k + h], sb[l32][k + h], acc);
+    __syncthreads();
+  }
+  store_frag(red + w * 1024, acc, lane);
+  __syncthreads();
+  const int i = threadIdx.x >> 3, j = (threadIdx.x & 7) * 4;
+  const int fi = frag_index(i, j);
+  const f32x4 s2 = (ld4(red + fi) + ld4(red + 1024 + fi)) + (ld4(red + 2048 + fi) + ld4(red + 3072 + fi));
+  const size_t o = size_t(bi * 32 + i) * r + bj * 32 + j;
+  f32x4 s1 = ld4(part + o);
+  for (int q = 1; q < groups; ++q) s1 += ld4(part + q * rr + o);
+  const float x2 = sx * sx, x4 = x2 * x2;
+  f32x4 out;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const float id = (bi * 32 + i == bj * 32 + j + t) ? ca : 0.f;
+    out[t] = sx * (id + cb * x2 * s1[t] + cc * x4 * s2[t]);
+  }
+  st4(M + o, out);
 }
 
 // row groups of the Gram pieces: 1, 2 or 4, about 256 rows each
@@ -255,9 +332,12 @@ void launch_xm(int G, dim3 grid, hipStream_t s, const float* X, const float* npa
 
 }  // namespace
 
-// workspace: Xa | Xb | Xc [d][r] | part [groups][r][r] | nparts [(d/32)(r/32)]
+// workspace: Xa | Xb | Xc [d][r] | part [groups][r][r] | nparts [(d/32)(r/32)] |
+// (Polar Express) M [r][r] | nparts of Y0 [(d/32)(r/32)], each region 16-byte aligned
+static size_t a4(size_t n) { return (n + 3) & ~size_t(3); }
 size_t spel_ws_bytes(int64_t d, int64_t r) {
-  const size_t floats = 3 * size_t(d) * r + size_t(spel_groups(d)) * r * r + size_t(d / 32) * (r / 32);
+  const size_t np = a4(size_t(d / 32) * (r / 32));
+  const size_t floats = 3 * size_t(d) * r + size_t(spel_groups(d)) * r * r + np + size_t(r) * r + np;
   return (floats + 64) * sizeof(float);
 }
 
@@ -302,6 +382,141 @@ void launch_spel(float* A, const float* g, float* m, float alpha, float beta, in
     const int mode = (it == ns_iters - 1) ? int(XM_NS_LAST_RET) : int(XM_NS);
     launch_xm<true>(G, xgrid, s, cur, nullptr, part, nxt, d, r, mode, nullptr, nullptr, 0.f, nullptr, nullptr, 0.f,
                     nullptr, nullptr);
+    cur = nxt;
+  }
+}
+
+}  // namespace mapl
+
+namespace mapl {
+
+// ------------------------------------------------------ Polar Express (host) --
+// Minimax odd quintic a x + b x^3 + c x^5 for the constant 1 on [lo, hi] by
+// the Remez exchange on four alternation points (the two ends and p's two
+// interior critical points).  Returns E = max |1 - p| on [lo, hi].
+namespace {
+
+bool solve4(double m[4][5]) {  // Gaussian elimination with partial pivoting, in place
+  for (int c = 0; c < 4; ++c) {
+    int piv = c;
+    for (int i = c + 1; i < 4; ++i)
+      if (std::fabs(m[i][c]) > std::fabs(m[piv][c])) piv = i;
+    if (m[piv][c] == 0.0) return false;
+    for (int k = 0; k < 5; ++k) std::swap(m[c][k], m[piv][k]);
+    for (int i = 0; i < 4; ++i) {
+      if (i == c) continue;
+      const double f = m[i][c] / m[c][c];
+      for (int k = c; k < 5; ++k) m[i][k] -= f * m[c][k];
+    }
+  }
+  for (int i = 0; i < 4; ++i) m[i][4] /= m[i][i];
+  return true;
+}
+
+double remez_quintic(double lo, double hi, double coef[3]) {
+  double xs[4] = {lo, lo + 0.25 * (hi - lo), lo + 0.75 * (hi - lo), hi};
+  double E = 0.0;
+  for (int it = 0; it < 60; ++it) {
+    double m[4][5];
+    for (int i = 0; i < 4; ++i) {
+      const double x = xs[i], x2 = x * x;
+      m[i][0] = x;
+      m[i][1] = x * x2;
+      m[i][2] = x * x2 * x2;
+      m[i][3] = (i & 1) ? -1.0 : 1.0;
+      m[i][4] = 1.0;
+    }
+    if (!solve4(m)) break;
+    coef[0] = m[0][4];
+    coef[1] = m[1][4];
+    coef[2] = m[2][4];
+    E = std::fabs(m[3][4]);
+    const double a = coef[0], b = coef[1], c = coef[2];
+    const double disc = 9.0 * b * b - 20.0 * a * c;  // critical points: 5 c y^2 + 3 b y + a = 0, y = x^2
+    if (c == 0.0 || disc < 0.0) break;
+    double y0 = (-3.0 * b - std::sqrt(disc)) / (10.0 * c), y1 = (-3.0 * b + std::sqrt(disc)) / (10.0 * c);
+    if (y0 > y1) std::swap(y0, y1);
+    if (y0 <= 0.0) break;
+    const double x1 = std::sqrt(y0), x2 = std::sqrt(y1);
+    if (!(lo < x1 && x2 < hi)) break;
+    const double change = std::max(std::fabs(x1 - xs[1]), std::fabs(x2 - xs[2]));
+    xs[1] = x1;
+    xs[2] = x2;
+    if (change <= 1e-15 * hi) break;
+  }
+  return E;
+}
+
+}  // namespace
+
+int polar_express_schedule(double ell, int steps, double* coef, double* err) {
+  double lo = ell, hi = 1.0;
+  for (int t = 0; t < steps; ++t) {
+    double* c = coef + 3 * t;
+    double E;
+    if (hi - lo < 1e-4) {  // the limit of the minimax quintic as the interval shrinks to {1}
+      c[0] = 15.0 / 8.0;
+      c[1] = -10.0 / 8.0;
+      c[2] = 3.0 / 8.0;
+      auto p = [&](double x) { return c[0] * x + c[1] * x * x * x + c[2] * x * x * x * x * x; };
+      E = std::max(std::fabs(1.0 - p(lo)), std::fabs(1.0 - p(hi)));
+    } else {
+      E = remez_quintic(lo, hi, c);
+    }
+    if (!std::isfinite(E) || !std::isfinite(c[0]) || !std::isfinite(c[1]) || !std::isfinite(c[2])) return -1;
+    if (err) err[t] = E;
+    lo = 1.0 - E;
+    hi = 1.0 + E;
+  }
+  return 0;
+}
+
+void launch_spel_pe(float* A, const float* g, float* m, float alpha, float beta, const float* coef_lmo, int lmo_steps,
+                    const float* coef_ret, int ret_steps, float* D_out, int d, int r, void* ws, hipStream_t s) {
+  const int G = spel_groups(d);
+  float* Xa = static_cast<float*>(ws);
+  float* Xb = Xa + size_t(d) * r;
+  float* Xc = Xb + size_t(d) * r;
+  float* part = Xc + size_t(d) * r;
+  const int npn = (d / 32) * (r / 32);
+  float* nparts = part + size_t(G) * r * r;
+  float* Mb = nparts + a4(size_t(npn));
+  float* nparts2 = Mb + size_t(r) * r;
+
+  const int nb = r / 32;
+  const dim3 blk(256);
+  const dim3 ggrid(nb * (nb + 1) / 2 * G);
+  const dim3 xgrid(d / 32, r / 32);
+  const dim3 pgrid(nb, nb);
+
+  // Eq. (4)-(5) as in launch_spel
+  hipLaunchKernelGGL(k_spel_gram<1>, ggrid, blk, 0, s, A, g, part, d, r, G);
+  launch_xm<false>(G, xgrid, s, A, nullptr, part, nullptr, d, r, int(XM_TANGENT), g, m, beta, nparts, nullptr, 0.f,
+                   nullptr, nullptr);
+
+  // one Polar Express step: S from the Gram pieces, M = s (a I + b s^2 S + c s^4 S^2), out = X M
+  float* bufs[2] = {Xa, Xb};
+  auto step = [&](const float* cur, const float* np_in, const float* c3, float* out, int mode, float* np_out) {
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G);
+    hipLaunchKernelGGL(k_spel_poly, pgrid, blk, 0, s, part, G, np_in, npn, Mb, r, c3[0], c3[1], c3[2]);
+    launch_xm<false>(1, xgrid, s, cur, nullptr, Mb, out, d, r, mode, nullptr, nullptr, 0.f, np_out, A, alpha, D_out,
+                     Xc);
+  };
+  // Eq. (6): D = PE(m / ||m||_F); the last step forms Y0 = A - alpha D in Xc and its squares
+  const float* cur = m;
+  for (int t = 0; t < lmo_steps; ++t) {
+    const bool last = t == lmo_steps - 1;
+    float* nxt = bufs[t & 1];
+    step(cur, t == 0 ? nparts : nullptr, coef_lmo + 3 * t, nxt, last ? int(XM_NS_LAST_LMO) : int(XM_NS),
+         last ? nparts2 : nullptr);
+    cur = nxt;
+  }
+  // Eq. (7): A = PE(Y0 / ||Y0||_F)
+  cur = Xc;
+  for (int t = 0; t < ret_steps; ++t) {
+    const bool last = t == ret_steps - 1;
+    float* nxt = last ? A : bufs[t & 1];
+    step(cur, t == 0 ? nparts2 : nullptr, coef_ret + 3 * t, nxt, last ? int(XM_NS_LAST_RET) : int(XM_NS), nullptr);
     cur = nxt;
   }
 }

@@ -84,8 +84,9 @@ def spel_step(A, g, m, alpha: float, beta: float, iters: int = 8):
 # interval [l_t, u_t] (Remez exchange on four alternation points), and the
 # next interval is p_t's range there, [1 - E_t, 1 + E_t].  The input is scaled
 # by its Frobenius norm (all singular values <= 1) and the first interval is
-# [ell, 1].  Once an interval is narrower than 1e-7 the limit polynomial
-# (15 x - 10 x^3 + 3 x^5) / 8 is used.
+# [ell, 1].  Once an interval is narrower than 1e-4 the limit polynomial
+# (15 x - 10 x^3 + 3 x^5) / 8 is used: there the exchange system is
+# ill-conditioned, and the limit quintic's error is already O(width^3).
 
 
 def _remez_odd_quintic(lo: float, hi: float, iters: int = 60):
@@ -119,7 +120,7 @@ def polar_express_coefficients(ell: float, steps: int):
     lo, hi = float(ell), 1.0
     coefs, errs = [], []
     for _ in range(int(steps)):
-        if hi - lo < 1e-7:
+        if hi - lo < 1e-4:
             a, b, c = 15.0 / 8.0, -10.0 / 8.0, 3.0 / 8.0
             p = lambda x: a * x + b * x ** 3 + c * x ** 5
             E = max(abs(1.0 - p(lo)), abs(1.0 - p(hi)))

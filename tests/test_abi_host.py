@@ -4,6 +4,8 @@ codes before anything is enqueued.  No call here reaches a kernel launch, so
 these run without a GPU."""
 import ctypes
 
+import numpy as np
+
 import pytest
 
 import learned_activation_compression_amd as lac
@@ -20,7 +22,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = lac.exported_symbols()
-    assert len(names) == 17, names
+    assert len(names) == 19, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lac._SIGS), set(names) ^ set(lac._SIGS)
@@ -198,6 +200,44 @@ def test_spel_validation(lib):
     odd = ctypes.c_void_p(0x1004)
     assert f(odd, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 256, FAKE, ws, None) == EARG      # A not 16-B aligned
     assert f(FAKE, FAKE, odd, 1e-3, 0.9, 8, None, 2048, 256, FAKE, ws, None) == EARG      # m not 16-B aligned
+
+
+def test_spel_polar_express_validation(lib):
+    ws = lib.spel_workspace_bytes(1024, 128)
+    f = lib.spel_step_polar_express
+
+    def call(A=FAKE, m=FAKE, alpha=1e-3, beta=0.9, lmo=5, ret=7, ell=1e-3, d=1024, r=128, w=FAKE, wb=ws):
+        return f(A, FAKE, m, alpha, beta, lmo, ret, ell, None, d, r, w, wb, None)
+
+    assert call(A=None) == ENULL
+    assert call(w=None) == ENULL
+    assert call(wb=ws - 4) == EWS
+    assert call(lmo=0) == EARG
+    assert call(ret=33) == EARG
+    assert call(ell=0.0) == EARG
+    assert call(ell=1.0) == EARG
+    assert call(ell=float("nan")) == EARG
+    assert call(beta=1.0) == EARG
+    assert call(r=100) == ESHAPE
+    assert call(m=ctypes.c_void_p(0x1004)) == EARG
+    g = lib.spel_polar_express_coefficients
+    buf = (ctypes.c_double * 96)()
+    assert g(1e-3, 5, None, None) == ENULL
+    assert g(0.0, 5, buf, None) == EARG
+    assert g(1e-3, 0, buf, None) == EARG
+    assert g(1e-3, 33, buf, None) == EARG
+    assert g(1e-3, 32, buf, None) == OK
+
+
+def test_polar_express_schedule_host_matches_oracle():
+    """The library's host-side schedule (C++ Remez) against the oracle's
+    (NumPy Remez): two implementations of the same minimax steps."""
+    from oracle import spel
+    for ell in (1e-3, 0.05, 0.5):
+        c, e = lac.spel_polar_express_coefficients(ell, 9)
+        co, eo = spel.polar_express_coefficients(ell, 9)
+        np.testing.assert_allclose(c, np.array(co), rtol=0, atol=1e-8)
+        np.testing.assert_allclose(e, np.array(eo), rtol=1e-6, atol=1e-13)
 
 
 def test_check_tids_validation(lib):

@@ -79,3 +79,66 @@ def test_spel_repeat_is_bitwise_deterministic():
     b = run(inp["A"], inp["g"], inp["m"], 1e-3, 0.9, 8)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+# ------------------------------------------------------------ Polar Express --
+# The same step with the Polar Express polar map (5 LMO / 7 retraction steps,
+# the schedule from [1e-3, 1]) against the oracle's spel_step_polar_express.
+
+def run_pe(A, g, m, alpha, beta, lmo=5, ret=7):
+    Ad, gd, md = A.clone().to(DEV), g.clone().to(DEV), m.clone().to(DEV)
+    D = torch.empty_like(Ad)
+    lac.spel_step_polar_express(Ad, gd, md, alpha, beta, lmo, ret, D_out=D)
+    torch.cuda.synchronize()
+    return Ad, md, D
+
+
+def check_pe(A, g, m, alpha, beta, Ad, md, D, lmo=5, ret=7):
+    An, mn, Dn, _ = spel.spel_step_polar_express(np64(A), np64(g), np64(m), alpha, beta, lmo, ret)
+    assert_close(np64(md), mn, F32_TOL, "m")
+    assert_close(np64(D), Dn, F32_TOL, "D")
+    assert_close(np64(Ad), An, F32_TOL, "A")
+    r = A.shape[1]
+    An64 = np64(Ad)
+    orth = np.linalg.norm(An64.T @ An64 - np.eye(r)) / np.sqrt(r)
+    assert orth <= 1e-5, orth
+
+
+@pytest.mark.parametrize("d,r,alpha,beta", [(1024, 128, 1e-3, 0.9), (2048, 256, 2e-3, 0.95), (256, 32, 0.05, 0.9),
+                                            (96, 96, 0.1, 0.0), (1056, 160, 0.02, 0.9), (2048, 512, 1e-3, 0.9)])
+def test_spel_polar_express_shapes(d, r, alpha, beta):
+    inp = synth.spel_inputs(200 + d + r, d, r, 1e-3)
+    m0 = torch.from_numpy(synth.gaussian(synth.stream(9, d, r), (d, r), 1e-4).astype(np.float32))
+    Ad, md, D = run_pe(inp["A"], inp["g"], m0, alpha, beta)
+    check_pe(inp["A"], inp["g"], m0, alpha, beta, Ad, md, D)
+
+
+def test_spel_polar_express_other_step_counts():
+    inp = synth.spel_inputs(41, 512, 64, 1e-3)
+    Ad, md, D = run_pe(inp["A"], inp["g"], inp["m"], 0.01, 0.9, lmo=3, ret=9)
+    check_pe(inp["A"], inp["g"], inp["m"], 0.01, 0.9, Ad, md, D, lmo=3, ret=9)
+
+
+def test_spel_polar_express_zero_gradient_and_repeat():
+    inp = synth.spel_inputs(42, 1024, 128, 1e-3)
+    z = torch.zeros_like(inp["g"])
+    Ad, md, D = run_pe(inp["A"], z, z, 0.1, 0.9)
+    assert torch.count_nonzero(md) == 0 and torch.count_nonzero(D) == 0
+    assert_close(np64(Ad), np64(inp["A"]), F32_TOL, "A fixed point")
+    a = run_pe(inp["A"], inp["g"], inp["m"], 1e-3, 0.9)
+    b = run_pe(inp["A"], inp["g"], inp["m"], 1e-3, 0.9)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_spel_polar_express_two_consecutive_steps():
+    inp = synth.spel_inputs(43, 1024, 128, 1e-3)
+    A, g, m = inp["A"], inp["g"], inp["m"]
+    Ad, gd, md = A.clone().to(DEV), g.to(DEV), m.clone().to(DEV)
+    A64, m64 = np64(A), np64(m)
+    for _ in range(2):
+        lac.spel_step_polar_express(Ad, gd, md, 1e-3, 0.9)
+        A64, m64, _, _ = spel.spel_step_polar_express(A64, np64(g), m64, 1e-3, 0.9)
+    torch.cuda.synchronize()
+    assert_close(np64(md), m64, F32_TOL, "m after 2 steps")
+    assert_close(np64(Ad), A64, F32_TOL, "A after 2 steps")
