@@ -260,16 +260,24 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
 // sum of the G Gram pieces, s = 1 / ||X||_F from per-block partial sums (the
 // first step) or 1.  One block per 32 x 32 tile (bi, bj); S^2's tile is
 // S[bi rows] S[bj rows]^T (S is symmetric), its r-long contraction taken in
-// chunks of 128 staged in LDS (the pieces summed while staging) and split
-// over the 4 waves, whose partial tiles are added in a fixed order.
+// chunks of 128 staged in LDS -- every thread's piece loads issued before
+// they are summed -- and split over the 8 waves, whose partial tiles are
+// added in a fixed order (in the staging buffers, free by then).
 constexpr int kPolyKC = 128;
+constexpr int kPolyThreads = 512;
 
-__global__ __launch_bounds__(256) void k_spel_poly(const float* __restrict__ part, int groups,
-                                                   const float* __restrict__ nparts_in, int nparts_n, float* __restrict__ M,
-                                                   int r, float ca, float cb, float cc) {
-  __shared__ float sa[32][kPolyKC + 1], sb[32][kPolyKC + 1];
-  __shared__ float red[4 * 1024];
+template <int G>
+__global__ __launch_bounds__(kPolyThreads) void k_spel_poly(const float* __restrict__ part,
+                                                            const float* __restrict__ nparts_in, int nparts_n,
+                                                            float* __restrict__ M, int r, float ca, float cb,
+                                                            float cc) {
+  constexpr int NWV = kPolyThreads / 64;
+  constexpr int LD = kPolyKC + 1;
+  __shared__ float sm[2 * 32 * LD];  // rows bi.. and bj.. of S, one chunk; later the wave partials
   __shared__ float scs;
+  static_assert(NWV * 1024 <= 2 * 32 * LD, "the wave partials reuse the staging buffers");
+  float* sa = sm;
+  float* sb = sm + 32 * LD;
   const int lane = threadIdx.x & 63, w = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
   const int bi = blockIdx.x, bj = blockIdx.y;
@@ -279,35 +287,58 @@ __global__ __launch_bounds__(256) void k_spel_poly(const float* __restrict__ par
   f32x16 acc = f32x16{};
   for (int k0 = 0; k0 < r; k0 += kPolyKC) {
     const int kn = min(kPolyKC, r - k0);  // a multiple of 32
-    // stage rows bi*32.. and bj*32.. of S, columns k0 .. k0 + kn: 32 x kn each
-    for (int e = threadIdx.x; e < 32 * (kn / 4); e += 256) {
-      const int row = e / (kn / 4), c4 = (e % (kn / 4)) * 4;
-      f32x4 va = ld4(part + size_t(bi * 32 + row) * r + k0 + c4);
-      f32x4 vb = ld4(part + size_t(bj * 32 + row) * r + k0 + c4);
-      for (int q = 1; q < groups; ++q) {
-        va += ld4(part + q * rr + size_t(bi * 32 + row) * r + k0 + c4);
-        vb += ld4(part + q * rr + size_t(bj * 32 + row) * r + k0 + c4);
+    const int per_row = kn / 4;           // 16-byte pieces per staged row
+    // this thread's two pieces of each of the two row blocks: 4 G loads, all in flight
+    f32x4 va[2][G], vb[2][G];
+    int rw[2], cc4[2];
+    bool ok[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int e = threadIdx.x + kPolyThreads * it;
+      ok[it] = e < 32 * per_row;
+      const int ee = ok[it] ? e : 0;
+      rw[it] = ee / per_row;
+      cc4[it] = (ee % per_row) * 4;
+      const size_t oa = size_t(bi * 32 + rw[it]) * r + k0 + cc4[it];
+      const size_t ob = size_t(bj * 32 + rw[it]) * r + k0 + cc4[it];
+#pragma unroll
+      for (int q = 0; q < G; ++q) {
+        va[it][q] = ld4(part + q * rr + oa);
+        vb[it][q] = ld4(part + q * rr + ob);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      if (!ok[it]) continue;
+      f32x4 a = va[it][0], b = vb[it][0];
+#pragma unroll
+      for (int q = 1; q < G; ++q) {
+        a += va[it][q];
+        b += vb[it][q];
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        sa[row][c4 + t] = va[t];
-        sb[row][c4 + t] = vb[t];
+        sa[rw[it] * LD + cc4[it] + t] = a[t];
+        sb[rw[it] * LD + cc4[it] + t] = b[t];
       }
     }
     __syncthreads();
-    // wave w: k in [k0 + w kn/4, k0 + (w+1) kn/4), two per multiply (lane half h takes k + h)
-    const int kb = w * (kn / 4);
-    for (int k = kb; k < kb + kn / 4; k += 2) acc = mfma_f32_32x32x2(sa[l32][k + h], sb[l32][k + h], acc);
+    // wave w: k in [w kn/NWV, (w+1) kn/NWV), two per multiply (lane half h takes k + h)
+    const int kb = w * (kn / NWV);
+    for (int k = kb; k < kb + kn / NWV; k += 2) acc = mfma_f32_32x32x2(sa[l32 * LD + k + h], sb[l32 * LD + k + h], acc);
     __syncthreads();
   }
-  store_frag(red + w * 1024, acc, lane);
+  store_frag(sm + w * 1024, acc, lane);
   __syncthreads();
+  if (threadIdx.x >= 256) return;
   const int i = threadIdx.x >> 3, j = (threadIdx.x & 7) * 4;
   const int fi = frag_index(i, j);
-  const f32x4 s2 = (ld4(red + fi) + ld4(red + 1024 + fi)) + (ld4(red + 2048 + fi) + ld4(red + 3072 + fi));
+  f32x4 s2 = (ld4(sm + fi) + ld4(sm + 1024 + fi)) + (ld4(sm + 2048 + fi) + ld4(sm + 3072 + fi));
+  s2 += (ld4(sm + 4096 + fi) + ld4(sm + 5120 + fi)) + (ld4(sm + 6144 + fi) + ld4(sm + 7168 + fi));
   const size_t o = size_t(bi * 32 + i) * r + bj * 32 + j;
   f32x4 s1 = ld4(part + o);
-  for (int q = 1; q < groups; ++q) s1 += ld4(part + q * rr + o);
+#pragma unroll
+  for (int q = 1; q < G; ++q) s1 += ld4(part + q * rr + o);
   const float x2 = sx * sx, x4 = x2 * x2;
   f32x4 out;
 #pragma unroll
@@ -498,7 +529,8 @@ void launch_spel_pe(float* A, const float* g, float* m, float alpha, float beta,
   float* bufs[2] = {Xa, Xb};
   auto step = [&](const float* cur, const float* np_in, const float* c3, float* out, int mode, float* np_out) {
     hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G);
-    hipLaunchKernelGGL(k_spel_poly, pgrid, blk, 0, s, part, G, np_in, npn, Mb, r, c3[0], c3[1], c3[2]);
+    auto poly = G == 8 ? k_spel_poly<8> : G == 4 ? k_spel_poly<4> : G == 2 ? k_spel_poly<2> : k_spel_poly<1>;
+    hipLaunchKernelGGL(poly, pgrid, dim3(kPolyThreads), 0, s, part, np_in, npn, Mb, r, c3[0], c3[1], c3[2]);
     launch_xm<false>(1, xgrid, s, cur, nullptr, Mb, out, d, r, mode, nullptr, nullptr, 0.f, np_out, A, alpha, D_out,
                      Xc);
   };
