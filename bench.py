@@ -358,7 +358,10 @@ def run_cases(lac, dev, flush):
         N * r * R, "hbm", tokens=N, peak_tf=F32_PEAK_TFLOPS)
     del g, Z, Cb, codes, Zq, gZ, C2, codes2
 
-    # one spel_step on the fp32 2048 x 256 projector
+    # one spel_step on the fp32 2048 x 256 projector (the d x r iteration) and on the 1024 x 128 one (the r x r
+    # iteration of r <= 128: per polar map a Gram and X M, 2 d r^2 each, and 6 r^3 per step after the first)
+    def ns_flops(d, r, n):
+        return 12 * d * r * r + 12 * r ** 3 * (n - 1) if r <= 128 else 4 * d * r * r * (1 + 2 * n)
     c = C["1b"]
     d, r, sp = c["d"], c["r"], c["spel"]
     si = synth.spel_inputs(c["seed"], d, r, sp["g_var"])
@@ -366,7 +369,7 @@ def run_cases(lac, dev, flush):
     sws = torch.empty(lac.spel_workspace_bytes(d, r), dtype=torch.uint8, device=dev)
     # repeated steps from the same gradient: A stays on the manifold, m keeps accumulating
     spel_fn = lambda: lac.spel_step(A, gg, m, sp["alpha"], sp["beta"], sp["ns_iters"], ws=sws)
-    flops = 4 * d * r * r * (1 + 2 * sp["ns_iters"])
+    flops = ns_flops(d, r, sp["ns_iters"])
     add("spel_step d2048 r256 NS8", _timed(spel_fn, flush), 4 * 4 * d * r, flops, "mfma", peak_tf=F32_PEAK_TFLOPS)
     # the Polar Express polar map (5 LMO / 7 retraction steps): per step a Gram (2 d r^2 with
     # both triangles), S^2 (2 r^3) and X M (2 d r^2)
@@ -380,8 +383,8 @@ def run_cases(lac, dev, flush):
     sws2 = torch.empty(lac.spel_workspace_bytes(d2, r2), dtype=torch.uint8, device=dev)
     ns2 = lambda: lac.spel_step(A2, g2, m2, sp["alpha"], sp["beta"], sp["ns_iters"], ws=sws2)
     pe2 = lambda: lac.spel_step_polar_express(A2, g2, m2, sp["alpha"], sp["beta"], 5, 7, ws=sws2)
-    add("spel_step d1024 r128 NS8", _timed(ns2, flush), 4 * 4 * d2 * r2,
-        4 * d2 * r2 * r2 * (1 + 2 * sp["ns_iters"]), "mfma", peak_tf=F32_PEAK_TFLOPS)
+    add("spel_step d1024 r128 NS8", _timed(ns2, flush), 4 * 4 * d2 * r2, ns_flops(d2, r2, sp["ns_iters"]), "mfma",
+        peak_tf=F32_PEAK_TFLOPS)
     add("spel_step d1024 r128 Polar Express 5/7", _timed(pe2, flush), 4 * 4 * d2 * r2,
         4 * d2 * r2 * r2 + 12 * (4 * d2 * r2 * r2 + 2 * r2 * r2 * r2), "mfma", peak_tf=F32_PEAK_TFLOPS)
     return res

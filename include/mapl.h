@@ -236,6 +236,14 @@ int rvq_stream_apply(float* C, const int32_t* idx, const float* vals, int64_t n,
  * 16-byte aligned (MAPL_ERR_ARG otherwise) and no buffer may overlap another.
  * The workspace needs no initial contents; consecutive calls on one stream
  * may share it, calls that overlap in time may not.
+ * For r <= 128 both polar maps run as iterations on r x r matrices (every
+ * iterate is the input times a polynomial in its Gram matrix, so the result is
+ * the same up to rounding), each in one launch of r/4 + r/16 workgroups that
+ * wait for one another through flags in the workspace.  They need to be
+ * resident together, which an otherwise idle device always allows; should a
+ * wait last beyond about a second (a device kept full by other work), A comes
+ * back as NaN (and D too if the direction's iteration was the one that waited)
+ * rather than the call hanging.
  * Limits: r % 32 == 0, d % 32 == 0, r <= d, r <= 1024, 0 <= beta < 1,
  * 0 <= alpha <= 0.7, 1 <= ns_iters <= 64.
  * ---------------------------------------------------------------------- */

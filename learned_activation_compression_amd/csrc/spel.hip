@@ -71,12 +71,17 @@ __device__ __forceinline__ void pair_of(int p, int nb, int& bi, int& bj) {
 // TWO = 1 (Eq. (4)): piece = sym(A^T g) over the group's rows, from
 // acc1 = A_bi^T g_bj and acc2 = A_bj^T g_bi.  TWO = 0: piece = X_bi^T X_bj.
 // Tile (bi, bj) of part[grp] gets the piece, tile (bj, bi) its transpose.
+// `zero`, when given, holds kRsSyncWords words cleared for the launch that
+// follows (the arrival flags and the timeout flag of the Gram-space iteration).
+constexpr int kRsSyncWords = 68;
 template <int TWO>
 __global__ __launch_bounds__(256) void k_spel_gram(const float* __restrict__ Xl, const float* __restrict__ Xr,
-                                                   float* __restrict__ part, int d, int r, int groups) {
+                                                   float* __restrict__ part, int d, int r, int groups,
+                                                   unsigned* __restrict__ zero) {
   __shared__ float red[(1 + TWO) * 4 * 1024];
   __shared__ float tile[32 * 33];
   const int lane = threadIdx.x & 63, w = wave_id();
+  if (zero != nullptr && blockIdx.x == 0 && threadIdx.x < kRsSyncWords) zero[threadIdx.x] = 0u;
   const int h = lane >> 5, l32 = lane & 31;
   const int p = blockIdx.x / groups, grp = blockIdx.x % groups;
   int bi, bj;
@@ -256,6 +261,293 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
   }
 }
 
+// ------------------------------------------------ Gram-space Newton-Schulz --
+// For X = s X0 (d x r, d >= r) every cubic Newton-Schulz iterate is X times a
+// polynomial in S_0 = X^T X: X_k = X Q_k with Q_0 = I and, with
+// S_k = X_k^T X_k and T_k = 1.5 I - 0.5 S_k,
+//   Q_{k+1} = Q_k T_k = 1.5 Q_k - 0.5 Q_k S_k,
+//   S_{k+1} = T_k S_k T_k = 2.25 S_k - 1.5 S_k^2 + 0.25 S_k^3
+// (all are polynomials in S_0, so they commute).  After n steps
+// NS_n(X0) = X0 (s Q_n): one Gram, n steps on r x r matrices and one product,
+// in place of n Grams and n products on d x r matrices.
+//
+// One launch of r/4 + r/16 workgroups.  S workgroup J < r/4 owns rows
+// 4 J .. 4 J + 3 of the S_k: each step it forms its rows of S_k^2 and then of
+// S_k^3 (right factor S_k both times) and writes its rows of S_{k+1}.  Q
+// workgroup J owns rows 16 J .. 16 J + 15 of the Q_k and forms its rows of
+// Q_k S_k.  Right factors are read into registers straight from global
+// memory, row j of S_k standing for column j (S_k is symmetric up to
+// rounding).  The S_k live in two global buffers, and after every step each
+// workgroup raises its arrival flag in the workspace to the step number and
+// waits until all flags have reached it (one wave polls them all): arriving
+// means the step's stores are visible to the device (one release fence per
+// workgroup) and its reads of the older buffer are over.  A wait that exceeds
+// its bound (a second or two) sets the timeout word, and the Q workgroups
+// then write NaN: a wrong result is never silent and no wait is endless.  The
+// launch is ordinary; its few workgroups (at most 40) are resident together
+// on an otherwise idle device.
+//
+// Matrix cores (fp32):
+//   S rows, v_mfma_f32_4x4x1_16b_f32: 16 blocks of 4 x 4; lane l is row l % 4
+//     of block l / 4 in A, column l % 4 of block l / 4 in B and D (register v:
+//     row v).  With A the same in every block and block b of column group g
+//     taking columns 64 g + 4 b .. + 3, lane l of group g accumulates column
+//     64 g + l of the 4 output rows.  The 4 waves split K and add their
+//     partial rows in LDS in wave order.
+//   Q rows, v_mfma_f32_16x16x4_f32: lane l is row l % 16 (A) or column l % 16
+//     (B, D) with k slot l / 16; D register v is row 4 (l / 16) + v.  Lane
+//     (kq, c) takes k = 16 kb + 4 kq + e at step e of K block kb; each tile's
+//     sum runs as two chains (even and odd kb) added at the end.
+constexpr int kRsS = 4;   // rows of S_k per S workgroup
+constexpr int kRsQ = 16;  // rows of Q_k per Q workgroup
+constexpr unsigned kRsSpinLimit = 1u << 20;  // each spin is a sleep and an uncached load: about 1-2 s
+
+__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32_4x4x1(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
+}
+
+// Raise this workgroup's flag to `epoch` once every wave's stores are complete
+// and published (release fence), then wait until all nblk flags have reached
+// it and make the other workgroups' stores visible (acquire fence).  On
+// timeout the word flags[64] is set at once and false is returned.
+__device__ bool rs_sync(unsigned* flags, int nblk, unsigned epoch, int* slot) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    if (l == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_store(flags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    unsigned spins = 0;
+    int ok = 1;
+    for (;;) {
+      const unsigned v = (l < nblk) ? __hip_atomic_load(flags + l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : epoch;
+      if (__all(v >= epoch)) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kRsSpinLimit) {
+        ok = 0;
+        if (l == 0) __hip_atomic_store(flags + 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (l == 0) *slot = ok;
+  }
+  __syncthreads();
+  return *slot != 0;
+}
+
+// a[kb] = L[c][16 kb + 4 kq .. + 3] from 16 rows in LDS (stride R + 4)
+template <int R>
+__device__ __forceinline__ void rs_left(const float* __restrict__ Lsh, f32x4 (&a)[R / 16], int kq, int c) {
+#pragma unroll
+  for (int kb = 0; kb < R / 16; ++kb) a[kb] = ld4(Lsh + c * (R + 4) + 16 * kb + 4 * kq);
+}
+
+// S workgroup product: out = L S for the 4 rows L (LDS, stride R + 4).  Wave w
+// takes k in [w R/4, (w+1) R/4); its partial rows go to red, and thread t then
+// adds the 4 waves' parts for elements e = t + 256 p (row e / R, column e % R).
+template <int R>
+struct RsRows {
+  static constexpr int NG = (R + 63) / 64, KW = R / 4, KU = KW / 4, NE = (4 * R + 255) / 256;
+  f32x4 b[NG][KU];  // b[g][u] = S[64 g + l][w KW + 4 u .. + 3]
+  __device__ __forceinline__ void load(const float* __restrict__ S, int w, int l) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int u = 0; u < KU; ++u)
+        b[g][u] = (64 * g + l < R) ? ld4(S + size_t(64 * g + l) * R + w * KW + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void product(const float* __restrict__ Lsh, float* __restrict__ red, int w, int l,
+                                          float (&out)[NE]) const {
+    f32x4 a[KU];
+#pragma unroll
+    for (int u = 0; u < KU; ++u) a[u] = ld4(Lsh + (l & 3) * (R + 4) + w * KW + 4 * u);
+    f32x4 h[NG][2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) h[g][0] = h[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < KU; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) h[g][e & 1] = mfma_f32_4x4x1(a[u][e], b[g][u][e], h[g][e & 1]);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const f32x4 p = h[g][0] + h[g][1];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[((w * NG + g) * 4 + v) * 64 + l] = p[v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < NE; ++p) {
+      const int e = threadIdx.x + 256 * p;
+      const int i = e / R, j = e % R, g = j >> 6, jl = j & 63;
+      float sum = 0.f;
+      if (e < 4 * R) {
+        sum = red[((0 * NG + g) * 4 + i) * 64 + jl];
+#pragma unroll
+        for (int q = 1; q < 4; ++q) sum += red[((q * NG + g) * 4 + i) * 64 + jl];
+      }
+      out[p] = sum;
+    }
+  }
+};
+
+// The right factor of a Q workgroup's output tiles n = w + 4 t:
+// b[t][kb] = S[16 n + c][16 kb + 4 kq .. + 3] (zero for n >= R / 16).
+template <int R>
+struct RsRight {
+  static constexpr int NT = R / 16, TW = (NT + 3) / 4, KB = R / 16;
+  f32x4 b[TW][KB];
+  __device__ __forceinline__ void load(const float* __restrict__ S, int w, int kq, int c) {
+#pragma unroll
+    for (int t = 0; t < TW; ++t)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        b[t][kb] = (w + 4 * t < NT) ? ld4(S + (16 * (w + 4 * t) + c) * R + 16 * kb + 4 * kq) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// acc[t] = L S over a Q workgroup wave's output tiles
+template <int R>
+__device__ __forceinline__ void rs_product(const f32x4 (&a)[R / 16], const RsRight<R>& B,
+                                           f32x4 (&acc)[RsRight<R>::TW], int w) {
+  constexpr int TW = RsRight<R>::TW, KB = R / 16, NT = R / 16;
+  f32x4 h[TW][2];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) h[t][0] = h[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+        if (w + 4 * t < NT) h[t][kb & 1] = mfma_f32_16x16x4(a[kb][e], B.b[t][kb][e], h[t][kb & 1]);
+#pragma unroll
+  for (int t = 0; t < TW; ++t) acc[t] = h[t][0] + h[t][1];
+}
+
+// part: G Gram pieces [R][R] of X0 (their sum is X0^T X0); nparts: the nnp
+// partial sums of ||X0||_F^2 (s = 1/||X0||_F, 0 for X0 = 0) or null (s = 1);
+// Sbuf: 2 R x R floats; flags: kRsSyncWords words cleared by the launch
+// before; M: s Q_iters [R][R].
+template <int R>
+__global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part, int G,
+                                                 const float* __restrict__ nparts, int nnp, int iters,
+                                                 float* __restrict__ Sbuf, unsigned* __restrict__ flags,
+                                                 float* __restrict__ M) {
+  constexpr int RP = R + 4, NT = R / 16, TW = (NT + 3) / 4, KB = R / 16;
+  constexpr int NS = R / kRsS, NQ = R / kRsQ, NE = RsRows<R>::NE, NG = RsRows<R>::NG;
+  __shared__ __align__(16) float Lsh[kRsQ * RP];  // own rows of S_k (S workgroup) or Q_k (Q workgroup)
+  __shared__ __align__(16) float Psh[kRsS * RP];  // own rows of S_k^2
+  __shared__ float red[4 * NG * 4 * 64];
+  __shared__ float scs;
+  __shared__ int slot;
+  const int lane = threadIdx.x & 63, w = wave_id();
+  const int kq = lane >> 4, c = lane & 15;
+  const bool isS = blockIdx.x < NS;
+  const int nblk = NS + NQ;
+  const float sx = nparts ? block_inv_norm(nparts, nnp, &scs) : 1.f;
+
+  if (isS) {
+    const int r0 = blockIdx.x * kRsS;
+    // S_0 rows: s^2 times the pieces' sum, in piece order
+    constexpr int U = R / 4;
+    const float s2 = sx * sx;
+    if (threadIdx.x < kRsS * U) {
+      const size_t o = size_t(r0 + threadIdx.x / U) * R + 4 * (threadIdx.x % U);
+      f32x4 v = ld4(part + o);
+      for (int q = 1; q < G; ++q) v += ld4(part + size_t(q) * R * R + o);
+      st4(Sbuf + o, v * s2);
+    }
+    rs_sync(flags, nblk, 1u, &slot);
+    RsRows<R> B;
+    for (int k = 0; k + 1 < iters; ++k) {
+      const float* S = Sbuf + size_t(k & 1) * R * R;
+      B.load(S, w, lane);
+      if (threadIdx.x < kRsS * U) {  // own rows of S_k
+        const int i = threadIdx.x / U, j4 = 4 * (threadIdx.x % U);
+        st4(Lsh + i * RP + j4, ld4(S + size_t(r0 + i) * R + j4));
+      }
+      __syncthreads();
+      float sij[NE], s2v[NE], s3v[NE];
+#pragma unroll
+      for (int p = 0; p < NE; ++p) {
+        const int e = min(int(threadIdx.x) + 256 * p, 4 * R - 1);
+        sij[p] = Lsh[(e / R) * RP + e % R];
+      }
+      B.product(Lsh, red, w, lane, s2v);  // rows of S_k^2
+#pragma unroll
+      for (int p = 0; p < NE; ++p) {
+        const int e = threadIdx.x + 256 * p;
+        if (e < 4 * R) Psh[(e / R) * RP + e % R] = s2v[p];
+      }
+      __syncthreads();  // Psh complete; every wave is done reading red
+      B.product(Psh, red, w, lane, s3v);  // rows of S_k^3
+      float* dst = Sbuf + size_t((k + 1) & 1) * R * R;
+#pragma unroll
+      for (int p = 0; p < NE; ++p) {
+        const int e = threadIdx.x + 256 * p;
+        if (e < 4 * R) dst[size_t(r0 + e / R) * R + e % R] = (2.25f * sij[p] - 1.5f * s2v[p]) + 0.25f * s3v[p];
+      }
+      rs_sync(flags, nblk, unsigned(k + 2), &slot);
+    }
+    return;
+  }
+
+  // Q workgroup
+  const int r0 = (blockIdx.x - NS) * kRsQ;
+  bool ok = rs_sync(flags, nblk, 1u, &slot);
+  RsRight<R> B;
+  f32x4 a[KB];
+  f32x4 q[TW];
+  for (int k = 0; k < iters; ++k) {
+    const float* S = Sbuf + size_t(k & 1) * R * R;
+    if (k == 0) {  // Q_1 = T_0
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int i = r0 + 4 * kq + v, j = 16 * (w + 4 * t) + c;
+          q[t][v] = (w + 4 * t < NT) ? (i == j ? 1.5f : 0.f) - 0.5f * S[size_t(i) * R + j] : 0.f;
+        }
+    } else {
+      B.load(S, w, kq, c);
+      rs_left<R>(Lsh, a, kq, c);
+      f32x4 qs[TW];
+      rs_product<R>(a, B, qs, w);
+#pragma unroll
+      for (int t = 0; t < TW; ++t) q[t] = 1.5f * q[t] - 0.5f * qs[t];
+    }
+    if (k + 1 < iters) {
+      __syncthreads();  // every wave is done reading the old rows
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+        if (w + 4 * t < NT) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) Lsh[(4 * kq + v) * RP + 16 * (w + 4 * t) + c] = q[t][v];
+        }
+      if (!rs_sync(flags, nblk, unsigned(k + 2), &slot)) ok = false;
+    }
+  }
+  if (threadIdx.x == 0) slot = int(__hip_atomic_load(flags + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  __syncthreads();
+  if (slot != 0) ok = false;
+  const float nan = __builtin_nanf("");
+#pragma unroll
+  for (int t = 0; t < TW; ++t)
+    if (w + 4 * t < NT) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        M[size_t(r0 + 4 * kq + v) * R + 16 * (w + 4 * t) + c] = ok ? sx * q[t][v] : nan;
+    }
+}
+
 // Polar Express step matrix M = s (a I + b s^2 S + c s^4 S^2) [r][r], S the
 // sum of the G Gram pieces, s = 1 / ||X||_F from per-block partial sums (the
 // first step) or 1.  One block per 32 x 32 tile (bi, bj); S^2's tile is
@@ -361,14 +653,32 @@ void launch_xm(int G, dim3 grid, hipStream_t s, const float* X, const float* npa
                      alpha, Dout, Y0);
 }
 
+template <int R>
+void launch_rs(const float* part, int G, const float* nparts, int nnp, int iters, float* Sbuf, unsigned* sync,
+               float* M, hipStream_t s) {
+  hipLaunchKernelGGL(k_spel_rs<R>, dim3(R / kRsS + R / kRsQ), dim3(256), 0, s, part, G, nparts, nnp, iters, Sbuf,
+                     sync, M);
+}
+
+// M = s Q_iters of the Gram-space iteration (r <= 128)
+void launch_rs_any(int r, const float* part, int G, const float* nparts, int nnp, int iters, float* Sbuf,
+                   unsigned* sync, float* M, hipStream_t s) {
+  if (r == 32) launch_rs<32>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
+  else if (r == 64) launch_rs<64>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
+  else if (r == 96) launch_rs<96>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
+  else launch_rs<128>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
+}
+
 }  // namespace
 
 // workspace: Xa | Xb | Xc [d][r] | part [groups][r][r] | nparts [(d/32)(r/32)] |
-// (Polar Express) M [r][r] | nparts of Y0 [(d/32)(r/32)], each region 16-byte aligned
+// M [r][r] | nparts of Y0 [(d/32)(r/32)] | S buffers [2][r][r] | arrival and
+// timeout flags [kRsSyncWords], each region 16-byte aligned
 static size_t a4(size_t n) { return (n + 3) & ~size_t(3); }
 size_t spel_ws_bytes(int64_t d, int64_t r) {
   const size_t np = a4(size_t(d / 32) * (r / 32));
-  const size_t floats = 3 * size_t(d) * r + size_t(spel_groups(d)) * r * r + np + size_t(r) * r + np;
+  const size_t floats =
+      3 * size_t(d) * r + size_t(spel_groups(d)) * r * r + np + size_t(r) * r + np + 2 * size_t(r) * r + kRsSyncWords;
   return (floats + 64) * sizeof(float);
 }
 
@@ -387,9 +697,27 @@ void launch_spel(float* A, const float* g, float* m, float alpha, float beta, in
   const dim3 xgrid(d / 32, r / 32);
 
   // Eq. (4)-(5): M = sym(A^T g) ; m = beta m + (1 - beta)(g - A M) ; per-block sums of m^2
-  hipLaunchKernelGGL(k_spel_gram<1>, ggrid, blk, 0, s, A, g, part, d, r, G);
+  hipLaunchKernelGGL(k_spel_gram<1>, ggrid, blk, 0, s, A, g, part, d, r, G, nullptr);
   launch_xm<false>(G, xgrid, s, A, nullptr, part, nullptr, d, r, int(XM_TANGENT), g, m, beta, nparts, nullptr, 0.f,
                    nullptr, nullptr);
+
+  if (r <= 128) {
+    // Gram-space iteration: S_0 from the pieces of m^T m, M = s Q_n, then D = m M and
+    // Y0 = A - alpha D (Eq. (6)); the same for Y0 (unscaled) and A = Y0 M (Eq. (7))
+    const int npn = (d / 32) * (r / 32);
+    float* Mb = nparts + a4(size_t(npn));
+    float* Sbuf = Mb + size_t(r) * r + a4(size_t(npn));
+    unsigned* sync = reinterpret_cast<unsigned*>(Sbuf + 2 * size_t(r) * r);
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, m, m, part, d, r, G, sync);
+    launch_rs_any(r, part, G, nparts, npn, ns_iters, Sbuf, sync, Mb, s);
+    launch_xm<false>(1, xgrid, s, m, nullptr, Mb, nullptr, d, r, int(XM_NS_LAST_LMO), nullptr, nullptr, 0.f, nullptr,
+                     A, alpha, D_out, Xc);
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, Xc, Xc, part, d, r, G, sync);
+    launch_rs_any(r, part, G, nullptr, 0, ns_iters, Sbuf, sync, Mb, s);
+    launch_xm<false>(1, xgrid, s, Xc, nullptr, Mb, A, d, r, int(XM_NS_LAST_RET), nullptr, nullptr, 0.f, nullptr,
+                     nullptr, 0.f, nullptr, nullptr);
+    return;
+  }
 
   // Eq. (6): D = NS(s m), s = 1/||m||_F; the last step forms Y0 = A - alpha D in Xc
   const float* cur = m;
@@ -397,7 +725,7 @@ void launch_spel(float* A, const float* g, float* m, float alpha, float beta, in
   float* bufs[2] = {Xa, Xb};
   for (int it = 0; it < ns_iters; ++it) {
     float* nxt = bufs[it & 1];
-    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G);
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G, nullptr);
     const int mode = (it == ns_iters - 1) ? int(XM_NS_LAST_LMO) : int(XM_NS);
     launch_xm<true>(G, xgrid, s, cur, cur_np, part, nxt, d, r, mode, nullptr, nullptr, 0.f, nullptr, A, alpha, D_out,
                     Xc);
@@ -409,7 +737,7 @@ void launch_spel(float* A, const float* g, float* m, float alpha, float beta, in
   cur = Xc;
   for (int it = 0; it < ns_iters; ++it) {
     float* nxt = (it == ns_iters - 1) ? A : bufs[it & 1];
-    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G);
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G, nullptr);
     const int mode = (it == ns_iters - 1) ? int(XM_NS_LAST_RET) : int(XM_NS);
     launch_xm<true>(G, xgrid, s, cur, nullptr, part, nxt, d, r, mode, nullptr, nullptr, 0.f, nullptr, nullptr, 0.f,
                     nullptr, nullptr);
@@ -521,14 +849,14 @@ void launch_spel_pe(float* A, const float* g, float* m, float alpha, float beta,
   const dim3 pgrid(nb, nb);
 
   // Eq. (4)-(5) as in launch_spel
-  hipLaunchKernelGGL(k_spel_gram<1>, ggrid, blk, 0, s, A, g, part, d, r, G);
+  hipLaunchKernelGGL(k_spel_gram<1>, ggrid, blk, 0, s, A, g, part, d, r, G, nullptr);
   launch_xm<false>(G, xgrid, s, A, nullptr, part, nullptr, d, r, int(XM_TANGENT), g, m, beta, nparts, nullptr, 0.f,
                    nullptr, nullptr);
 
   // one Polar Express step: S from the Gram pieces, M = s (a I + b s^2 S + c s^4 S^2), out = X M
   float* bufs[2] = {Xa, Xb};
   auto step = [&](const float* cur, const float* np_in, const float* c3, float* out, int mode, float* np_out) {
-    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G);
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G, nullptr);
     auto poly = G == 8 ? k_spel_poly<8> : G == 4 ? k_spel_poly<4> : G == 2 ? k_spel_poly<2> : k_spel_poly<1>;
     hipLaunchKernelGGL(poly, pgrid, dim3(kPolyThreads), 0, s, part, np_in, npn, Mb, r, c3[0], c3[1], c3[2]);
     launch_xm<false>(1, xgrid, s, cur, nullptr, Mb, out, d, r, mode, nullptr, nullptr, 0.f, np_out, A, alpha, D_out,

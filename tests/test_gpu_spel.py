@@ -81,6 +81,30 @@ def test_spel_repeat_is_bitwise_deterministic():
         assert torch.equal(x, y)
 
 
+def test_spel_repeat_is_bitwise_deterministic_at_r128():
+    # r <= 128 runs the r x r (Gram-space) form of the iteration, whose workgroups meet at a counter
+    inp = synth.spel_inputs(34, 1024, 128, 1e-3)
+    m0 = torch.from_numpy(synth.gaussian(synth.stream(8, 1024, 128), (1024, 128), 1e-4).astype(np.float32))
+    a = run(inp["A"], inp["g"], m0, 1e-3, 0.9, 8)
+    b = run(inp["A"], inp["g"], m0, 1e-3, 0.9, 8)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("d,r,iters", [(1024, 128, 1), (1024, 128, 2), (256, 64, 3), (640, 96, 4), (128, 32, 6),
+                                       (1024, 128, 13)])
+def test_spel_few_and_many_iterations(d, r, iters):
+    # m, D and A against the oracle for step counts other than 8 (A is not yet orthonormal
+    # after one or two steps, so only the parity is checked)
+    inp = synth.spel_inputs(300 + d + r + iters, d, r, 1e-3)
+    m0 = torch.from_numpy(synth.gaussian(synth.stream(10, d, r), (d, r), 1e-4).astype(np.float32))
+    Ad, md, D = run(inp["A"], inp["g"], m0, 0.02, 0.9, iters)
+    An, mn, Dn, _ = spel.spel_step(np64(inp["A"]), np64(inp["g"]), np64(m0), 0.02, 0.9, iters)
+    assert_close(np64(md), mn, F32_TOL, "m")
+    assert_close(np64(D), Dn, F32_TOL, "D")
+    assert_close(np64(Ad), An, F32_TOL, "A")
+
+
 # ------------------------------------------------------------ Polar Express --
 # The same step with the Polar Express polar map (5 LMO / 7 retraction steps,
 # the schedule from [1e-3, 1]) against the oracle's spel_step_polar_express.
