@@ -29,6 +29,7 @@
 // momentum epilogue, added up in a fixed order by the one launch that uses it.
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <utility>
 
 #include "common.h"
@@ -300,7 +301,10 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
 //     sum runs as two chains (even and odd kb) added at the end.
 constexpr int kRsS = 4;   // rows of S_k per S workgroup
 constexpr int kRsQ = 16;  // rows of Q_k per Q workgroup
-constexpr unsigned kRsSpinLimit = 1u << 20;  // each spin is a sleep and an uncached load: about 1-2 s
+// each spin is a sleep and an uncached load: 2^20 spins take about 1-2 s.  The
+// environment variable MAPL_SPEL_SPIN_LIMIT lowers the bound, for tests of the
+// timeout path.
+constexpr unsigned kRsSpinLimit = 1u << 20;
 
 __device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -313,7 +317,7 @@ __device__ __forceinline__ f32x4 mfma_f32_4x4x1(float a, float b, f32x4 c) {
 // and published (release fence), then wait until all nblk flags have reached
 // it and make the other workgroups' stores visible (acquire fence).  On
 // timeout the word flags[64] is set at once and false is returned.
-__device__ bool rs_sync(unsigned* flags, int nblk, unsigned epoch, int* slot) {
+__device__ bool rs_sync(unsigned* flags, int nblk, unsigned epoch, unsigned limit, int* slot) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x < 64) {
@@ -328,7 +332,7 @@ __device__ bool rs_sync(unsigned* flags, int nblk, unsigned epoch, int* slot) {
       const unsigned v = (l < nblk) ? __hip_atomic_load(flags + l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : epoch;
       if (__all(v >= epoch)) break;
       __builtin_amdgcn_s_sleep(1);
-      if (++spins > kRsSpinLimit) {
+      if (++spins > limit) {
         ok = 0;
         if (l == 0) __hip_atomic_store(flags + 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
@@ -435,12 +439,12 @@ __device__ __forceinline__ void rs_product(const f32x4 (&a)[R / 16], const RsRig
 // part: G Gram pieces [R][R] of X0 (their sum is X0^T X0); nparts: the nnp
 // partial sums of ||X0||_F^2 (s = 1/||X0||_F, 0 for X0 = 0) or null (s = 1);
 // Sbuf: 2 R x R floats; flags: kRsSyncWords words cleared by the launch
-// before; M: s Q_iters [R][R].
+// before; M: s Q_iters [R][R]; limit: polls per wait before it gives up.
 template <int R>
 __global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part, int G,
                                                  const float* __restrict__ nparts, int nnp, int iters,
                                                  float* __restrict__ Sbuf, unsigned* __restrict__ flags,
-                                                 float* __restrict__ M) {
+                                                 float* __restrict__ M, unsigned limit) {
   constexpr int RP = R + 4, NT = R / 16, TW = (NT + 3) / 4, KB = R / 16;
   constexpr int NS = R / kRsS, NQ = R / kRsQ, NE = RsRows<R>::NE, NG = RsRows<R>::NG;
   __shared__ __align__(16) float Lsh[kRsQ * RP];  // own rows of S_k (S workgroup) or Q_k (Q workgroup)
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part,
       for (int q = 1; q < G; ++q) v += ld4(part + size_t(q) * R * R + o);
       st4(Sbuf + o, v * s2);
     }
-    rs_sync(flags, nblk, 1u, &slot);
+    rs_sync(flags, nblk, 1u, limit, &slot);
     RsRows<R> B;
     for (int k = 0; k + 1 < iters; ++k) {
       const float* S = Sbuf + size_t(k & 1) * R * R;
@@ -495,14 +499,14 @@ __global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part,
         const int e = threadIdx.x + 256 * p;
         if (e < 4 * R) dst[size_t(r0 + e / R) * R + e % R] = (2.25f * sij[p] - 1.5f * s2v[p]) + 0.25f * s3v[p];
       }
-      rs_sync(flags, nblk, unsigned(k + 2), &slot);
+      rs_sync(flags, nblk, unsigned(k + 2), limit, &slot);
     }
     return;
   }
 
   // Q workgroup
   const int r0 = (blockIdx.x - NS) * kRsQ;
-  bool ok = rs_sync(flags, nblk, 1u, &slot);
+  bool ok = rs_sync(flags, nblk, 1u, limit, &slot);
   RsRight<R> B;
   f32x4 a[KB];
   f32x4 q[TW];
@@ -532,7 +536,7 @@ __global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part,
 #pragma unroll
           for (int v = 0; v < 4; ++v) Lsh[(4 * kq + v) * RP + 16 * (w + 4 * t) + c] = q[t][v];
         }
-      if (!rs_sync(flags, nblk, unsigned(k + 2), &slot)) ok = false;
+      if (!rs_sync(flags, nblk, unsigned(k + 2), limit, &slot)) ok = false;
     }
   }
   if (threadIdx.x == 0) slot = int(__hip_atomic_load(flags + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -653,11 +657,18 @@ void launch_xm(int G, dim3 grid, hipStream_t s, const float* X, const float* npa
                      alpha, Dout, Y0);
 }
 
+unsigned rs_spin_limit() {
+  const char* e = std::getenv("MAPL_SPEL_SPIN_LIMIT");
+  if (e == nullptr || *e == 0) return kRsSpinLimit;
+  const unsigned long v = std::strtoul(e, nullptr, 10);
+  return v < kRsSpinLimit ? unsigned(v) : kRsSpinLimit;
+}
+
 template <int R>
 void launch_rs(const float* part, int G, const float* nparts, int nnp, int iters, float* Sbuf, unsigned* sync,
                float* M, hipStream_t s) {
   hipLaunchKernelGGL(k_spel_rs<R>, dim3(R / kRsS + R / kRsQ), dim3(256), 0, s, part, G, nparts, nnp, iters, Sbuf,
-                     sync, M);
+                     sync, M, rs_spin_limit());
 }
 
 // M = s Q_iters of the Gram-space iteration (r <= 128)

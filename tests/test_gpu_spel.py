@@ -91,6 +91,19 @@ def test_spel_repeat_is_bitwise_deterministic_at_r128():
         assert torch.equal(x, y)
 
 
+def test_spel_wait_timeout_gives_nan_then_recovers(monkeypatch):
+    # the r x r iteration's workgroups wait for one another with a bounded wait; a test hook
+    # lowers the bound to zero, so the first wait gives up: the call must still end, with NaN
+    # in A and D, and the next call with the normal bound must be correct again
+    inp = synth.spel_inputs(35, 1024, 128, 1e-3)
+    monkeypatch.setenv("MAPL_SPEL_SPIN_LIMIT", "0")
+    Ad, md, D = run(inp["A"], inp["g"], inp["m"], 1e-3, 0.9, 8)
+    assert torch.isnan(Ad).all() and torch.isnan(D).all()
+    monkeypatch.delenv("MAPL_SPEL_SPIN_LIMIT")
+    Ad, md, D = run(inp["A"], inp["g"], inp["m"], 1e-3, 0.9, 8)
+    check(inp["A"], inp["g"], inp["m"], 1e-3, 0.9, 8, Ad, md, D)
+
+
 @pytest.mark.parametrize("d,r,iters", [(1024, 128, 1), (1024, 128, 2), (256, 64, 3), (640, 96, 4), (128, 32, 6),
                                        (1024, 128, 13)])
 def test_spel_few_and_many_iterations(d, r, iters):
