@@ -200,9 +200,11 @@ int mapl_check_tids(const int32_t* tids, int64_t N, int64_t V, int32_t* bad_coun
  * ---------------------------------------------------------------------- */
 
 /* Encode: for rho = 0..R-1 and each group, code = argmin_k ||res - c_k||^2
- * (squared Euclidean, evaluated as ||c_k||^2 - 2<res, c_k> in fp32 on the
- * matrix cores; exact ties go to the lowest k; a NaN distance never wins), then
- * res -= c_code.  res starts as Z (z_dt: MAPL_BF16 or MAPL_F32). */
+ * (squared Euclidean, evaluated as ||c_k||^2 - 2<res, c_k> in fp32; exact ties
+ * go to the lowest k; a NaN distance never wins), then res -= c_code.  res
+ * starts as Z (z_dt: MAPL_BF16 or MAPL_F32).  For w >= 16 the K codewords are
+ * first scored in bf16 with a proven error bound and only those that can still
+ * be the argmin are scored in fp32; the result is the same fp32 argmin. */
 int rvq_encode(const void* Z, mapl_dtype z_dt, const float* C, int64_t C_round_stride,
                uint8_t* codes, int64_t N, int64_t r, int64_t G, int64_t K, int64_t R,
                hipStream_t stream);

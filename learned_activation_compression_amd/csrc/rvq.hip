@@ -6,9 +6,10 @@
 // Appendix F (streamed codebook sync: the receiver overwrites the codewords
 // the sender streams).
 //
-// Encode: one block owns one group g and 256 tokens, one 32-token tile per
-// wave (8 waves, two per SIMD, so that one wave's argmin overlaps the other's
-// matrix-core work).  The round's codebook for g sits in LDS transposed
+// Encode (w < 16; wider groups use the bf16-scored kernel further down): one
+// block owns one group g and 256 tokens, one 32-token tile per wave (8 waves,
+// two per SIMD, so that one wave's argmin overlaps the other's matrix-core
+// work).  The round's codebook for g sits in LDS transposed
 // ([dim][codeword]) with its squared norms.  Lane half h holds dims
 // [h W/2, (h+1) W/2) of token l & 31, pre-scaled by -2, and 32 codewords at a
 // time are scored with v_mfma_f32_32x32x2_f32 on an accumulator that starts
@@ -164,18 +165,247 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode(const ZT* __restr
   }
 }
 
+// ---------------------------------------------- encode, bf16-scored (w >= 16) --
+// The same argmin, with the scan over the K codewords on bf16 matrix cores
+// and an exact fp32 check of the few codewords that can still win.  For token
+// n the bf16 score of codeword k is
+//   a_k = <bf16(-2 res), bf16(c_k)> + hi_k + lo_k    (products exact, fp32 sums)
+// with hi_k + lo_k the two-part bf16 split of ||c_k||^2 (fed to the matrix
+// core as two more dimensions against a constant 1).  Each bf16 rounding is a
+// relative 2^-9 at most, so against the exact s_k = ||c_k||^2 - 2 <res, c_k>
+//   |a_k - s_k| <= 2^-7 (1 + 2^-9) ||res|| ||c_k|| + 2^-17 ||c_k||^2 + (fp32 sums)
+// (Cauchy-Schwarz); taken twice over and uniformly in k,
+//   delta = 2^-6 ||res|| max_k ||c_k|| + 2^-14 max_k ||c_k||^2 + 1e-30.
+// The exact argmin k* has a_k* <= s_k* + delta <= s_j + delta <= a_j + 2 delta
+// for every j, so it is among the codewords with a_k <= min_j a_j + 2 delta;
+// those are rescored exactly in fp32 (dims in order, one fused multiply-add
+// each, as fma(-2, <res, c_k>, ||c_k||^2)) and the best of them is the code:
+// the fp32 argmin over all K, from a handful of exact scores per token.  NaN
+// scores pass no test and never win; exact ties go to the lowest k.
+//
+// Layout as in k_rvq_encode (one block: group g, 256 tokens, a 32-token tile
+// per wave; lane half h holds dims [h W/2, (h+1) W/2) of token l & 31).  The
+// bf16 MFMA takes 8 dims per lane per K-step: at step t < W/16 lane half h
+// supplies dims h W/2 + 8 t .. + 7 of codeword and residual alike; step W/16
+// carries (hi_k, lo_k) against (1, 1) in half 0 and zeros in half 1.  The two
+// scans (minimum, then candidates) are the same instructions, so a_k is the
+// same in both; candidates are kept as a 128-bit mask per lane (16 rows of
+// each of the K/32 codeword blocks).
+template <int W, typename ZT>
+__global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __restrict__ Z,
+                                                                  const float* __restrict__ C, int64_t stride,
+                                                                  uint8_t* __restrict__ codes, int N, int r, int G,
+                                                                  int K, int R) {
+  constexpr int H = W / 2, T = W / 16, FP = W + 4, WB = W + 16;  // dims per lane, K-steps, fp32 / bf16 row pitch
+  extern __shared__ __attribute__((aligned(16))) float sh[];
+  float* cbF = sh;              // [K][FP] fp32 codewords
+  float* nrm = cbF + 256 * FP;  // [K] ||c_k||^2
+  float* bnd = nrm + 256;       // [4]: max ||c_k||^2 (the block's reduction)
+  bf16_t* cbB = reinterpret_cast<bf16_t*>(bnd + 4);  // [K][WB] bf16 codewords, then hi_k, lo_k, zeros
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int h = lane >> 5, l32 = lane & 31;
+  const int g = blockIdx.x;
+  const int n = blockIdx.y * (kRvqWaves * 32) + wave * 32 + l32;
+  const int nb = K / 32;
+
+  float res[H];
+  {
+    const ZT* zr = Z + size_t(min(n, N - 1)) * r + g * W + h * H;
+    if (sizeof(ZT) == 2) {
+#pragma unroll
+      for (int s = 0; s < H; s += 8) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(zr + s);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          res[s + 2 * e] = __uint_as_float(u[e] << 16);
+          res[s + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < H; s += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(zr + s);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[s + e] = to_f32<ZT>(v[e]);
+      }
+    }
+    if (n >= N) {
+#pragma unroll
+      for (int s = 0; s < H; ++s) res[s] = 0.f;
+    }
+  }
+
+  for (int rho = 0; rho < R; ++rho) {
+    if (rho == 0 || stride != 0) {
+      __syncthreads();
+      const float* book = C + rho * stride + size_t(g) * K * W;
+      // W/4 consecutive threads per codeword (16 bytes each); squared norm by a fixed-order butterfly.
+      // Every load of the thread is issued before the first is used.
+      constexpr int UPT = (256 * W / 4 + 64 * kRvqWaves - 1) / (64 * kRvqWaves);  // units per thread at K = 256
+      f32x4 cv[UPT];
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int e = threadIdx.x + u * 64 * kRvqWaves;
+        if (e < K * W / 4) cv[u] = *reinterpret_cast<const f32x4*>(book + size_t(e / (W / 4)) * W + 4 * (e % (W / 4)));
+      }
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int e = threadIdx.x + u * 64 * kRvqWaves;
+        if (e >= K * W / 4) continue;  // uniform over a codeword's W/4 threads
+        const int k = e / (W / 4), j0 = 4 * (e % (W / 4));
+        const f32x4 v = cv[u];
+        *reinterpret_cast<f32x4*>(cbF + k * FP + j0) = v;
+        *reinterpret_cast<u32x2*>(cbB + k * WB + j0) = u32x2{pack2bf(v[0], v[1]), pack2bf(v[2], v[3])};
+        float s2 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s2 = fmaf(v[q], v[q], s2);
+#pragma unroll
+        for (int off = 1; off < W / 4; off <<= 1) s2 += __shfl_xor(s2, off);
+        if (j0 == 0) {
+          nrm[k] = s2;
+          const float hi = bf2f(f2bf(s2));
+          const u32x4 z4 = u32x4{pack2bf(hi, s2 - hi), 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(cbB + k * WB + W) = z4;
+          *reinterpret_cast<u32x4*>(cbB + k * WB + W + 8) = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      __syncthreads();
+      if (wave == 0) {  // max ||c_k||^2 (a max: order does not matter; NaN drops out)
+        float mx = 0.f;
+        for (int k = lane; k < K; k += 64) mx = fmaxf(mx, nrm[k]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        if (lane == 0) bnd[0] = mx;
+      }
+      __syncthreads();
+    }
+    // the residual's bf16 operand (pre-scaled by -2; the norm step's (1, 1) in half 0),
+    // its norm, the partner half's dims and the per-token bound
+    bf16x8 bB[T + 1];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      u32x4 u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = pack2bf(-2.f * res[8 * t + 2 * e], -2.f * res[8 * t + 2 * e + 1]);
+      bB[t] = __builtin_bit_cast(bf16x8, u);
+    }
+    bB[T] = __builtin_bit_cast(bf16x8, u32x4{h == 0 ? pack2bf(1.f, 1.f) : 0u, 0u, 0u, 0u});
+    float rn2 = 0.f, pres[H];
+#pragma unroll
+    for (int s = 0; s < H; ++s) {
+      rn2 = fmaf(res[s], res[s], rn2);
+      pres[s] = __shfl_xor(res[s], 32);
+    }
+    rn2 += __shfl_xor(rn2, 32);
+    const float nmax = bnd[0];
+    const float delta = fmaf(0x1p-6f * sqrtf(rn2), sqrtf(nmax), fmaf(0x1p-14f, nmax, 1e-30f));
+
+    auto scan = [&](int b) {  // bf16 scores of codewords 32 b .. 32 b + 31 (rows of the accumulator)
+      const bf16_t* row = cbB + (32 * b + l32) * WB;
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc = mfma_bf16_32x32x16(ld_bf16x8(row + H * h + 8 * t), bB[t], acc);
+      acc = mfma_bf16_32x32x16(ld_bf16x8(row + W + 8 * h), bB[T], acc);
+      return acc;
+    };
+    // scan 1: the smallest bf16 score (NaN drops out of fminf)
+    float amin = __builtin_inff();
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      if (b < nb) {
+        const f32x16 acc = scan(b);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) amin = fminf(amin, acc[v]);
+      }
+    }
+    amin = fminf(amin, __shfl_xor(amin, 32));
+    const float lim = fmaf(2.f, delta, amin);
+    // scan 2: candidate mask, bit 16 (b & 1) + v of word b >> 1
+    uint32_t mask[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      if (b < nb) {
+        const f32x16 acc = scan(b);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (acc[v] <= lim) mask[b >> 1] |= 1u << (16 * (b & 1) + v);
+      }
+    }
+    // exact fp32 scores of the candidates, in increasing k
+    float best = __builtin_inff();
+    int bk = 0;
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      uint32_t m = mask[wd];
+      while (__any(m != 0u)) {
+        if (m != 0u) {
+          const int bit = __builtin_ctz(m);
+          m &= m - 1u;
+          const int k = 64 * wd + 32 * (bit >> 4) + mfma32_row(bit & 15, h);
+          const float* ck = cbF + k * FP;
+          float dot = 0.f;
+#pragma unroll
+          for (int j = 0; j < W; j += 4) {
+            const f32x4 c4 = *reinterpret_cast<const f32x4*>(ck + j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int jj = j + e;  // dim jj: lane half jj / H holds it, at jj % H
+              const float rv = ((jj < H) == (h == 0)) ? res[jj % H] : pres[jj % H];
+              dot = fmaf(c4[e], rv, dot);
+            }
+          }
+          const float sc = fmaf(-2.f, dot, nrm[k]);
+          if (sc < best || (sc == best && k < bk)) {
+            best = sc;
+            bk = k;
+          }
+        }
+      }
+    }
+    const float ob = __shfl_xor(best, 32);
+    const int ok = __shfl_xor(bk, 32);
+    if (ob < best || (ob == best && ok < bk)) {
+      best = ob;
+      bk = ok;
+    }
+    if (h == 0 && n < N) codes[(size_t(n) * R + rho) * G + g] = uint8_t(bk);
+#pragma unroll
+    for (int s = 0; s < H; ++s) res[s] -= cbF[bk * FP + h * H + s];
+  }
+}
+
+// LDS of the bf16-scored encode: fp32 codewords [256][W+4], norms [256], bound [4], bf16 rows [256][W+16]
+template <int W>
+constexpr size_t rvq_bf_lds() {
+  return (size_t(256) * (W + 4) + 256 + 4) * sizeof(float) + size_t(256) * (W + 16) * sizeof(bf16_t);
+}
+
 template <int W>
 static void rvq_encode_w(const void* Z, int z_bf16, const float* C, int64_t stride, uint8_t* codes, int N, int r,
                          int G, int K, int R, hipStream_t s) {
   const int tpb = kRvqWaves * 32;
   dim3 grid(G, (N + tpb - 1) / tpb);
-  const size_t lds = (size_t(W) * (K + 2) + K) * sizeof(float);
-  if (z_bf16)
-    hipLaunchKernelGGL((k_rvq_encode<W, bf16_t>), grid, dim3(64 * kRvqWaves), lds, s, static_cast<const bf16_t*>(Z),
-                       C, stride, codes, N, r, G, K, R);
-  else
-    hipLaunchKernelGGL((k_rvq_encode<W, float>), grid, dim3(64 * kRvqWaves), lds, s, static_cast<const float*>(Z), C,
-                       stride, codes, N, r, G, K, R);
+  if constexpr (W >= 16) {
+    constexpr int lds = int(rvq_bf_lds<W>());
+    static std::atomic<uint64_t> done16{0}, done32{0};
+    if (z_bf16) {
+      if (lds > 65536) allow_lds(reinterpret_cast<const void*>(k_rvq_encode_bf<W, bf16_t>), lds, done16);
+      hipLaunchKernelGGL((k_rvq_encode_bf<W, bf16_t>), grid, dim3(64 * kRvqWaves), lds, s,
+                         static_cast<const bf16_t*>(Z), C, stride, codes, N, r, G, K, R);
+    } else {
+      if (lds > 65536) allow_lds(reinterpret_cast<const void*>(k_rvq_encode_bf<W, float>), lds, done32);
+      hipLaunchKernelGGL((k_rvq_encode_bf<W, float>), grid, dim3(64 * kRvqWaves), lds, s, static_cast<const float*>(Z),
+                         C, stride, codes, N, r, G, K, R);
+    }
+  } else {  // w < 16: fp32 scores on the matrix cores
+    const size_t lds = (size_t(W) * (K + 2) + K) * sizeof(float);
+    if (z_bf16)
+      hipLaunchKernelGGL((k_rvq_encode<W, bf16_t>), grid, dim3(64 * kRvqWaves), lds, s, static_cast<const bf16_t*>(Z),
+                         C, stride, codes, N, r, G, K, R);
+    else
+      hipLaunchKernelGGL((k_rvq_encode<W, float>), grid, dim3(64 * kRvqWaves), lds, s, static_cast<const float*>(Z),
+                         C, stride, codes, N, r, G, K, R);
+  }
 }
 
 void launch_rvq_encode(const void* Z, int z_bf16, const float* C, int64_t stride, uint8_t* codes, int N, int r, int G,
