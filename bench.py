@@ -176,6 +176,13 @@ def counter_traffic():
         return None
 
 
+def _device_info():
+    """Name, architecture and compute-unit count of cuda:0, as the runtime reports them."""
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "arch": getattr(p, "gcnArchName", ""), "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2 ** 30, 1)}
+
+
 def cpu_baseline(inp, n_tok, reps):
     """The fp64 oracle of the same step on a token sample (host cores), run
     `reps` times; the rate is the sample's tokens over the mean time."""
@@ -206,7 +213,13 @@ def cpu_baseline(inp, n_tok, reps):
         spel.spel_step(sp["A"].double().numpy(), gA1 + gA2, sp["m"].double().numpy(), S.alpha, S.beta, S.ns)
         del Xh, gX
     dt = (time.perf_counter() - t0) / reps
-    return {"value": n_tok / dt, "unit": "boundary tokens/s", "cores": int(cores), "kind": "oracle",
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:  # pragma: no cover
+        pass
+    return {"value": n_tok / dt, "unit": "boundary tokens/s", "cores": int(cores), "kind": "oracle", "cpu": model,
             "sample": f"one full step of the fp64 oracle (codec fwd+bwd, RVQ encode/decode, one spel_step on "
                       f"1024x128) on {n_tok} of the {S.N} tokens, {reps} runs, mean {dt:.2f} s per run"}
 
@@ -340,8 +353,11 @@ def run_cases(lac, dev, flush):
     Zq = torch.empty((N, r), dtype=torch.float32, device=dev)
     enc = lambda: lac.rvq_encode(Z, Cb, G, K, R, codes=codes)
     dec = lambda: lac.rvq_decode(codes, Cb, G, K, R, r, Zq=Zq)
-    add("rvq r256 G8 K256 R2 encode", _timed(enc, flush), N * (2 * r + R * G) + Cb.numel() * 4,
-        N * 2 * r * K * R, "mfma", tokens=N, peak_tf=F32_PEAK_TFLOPS)
+    # w = 32 >= 16: two bf16 matrix-core scans of the K codewords (w + 16 dims each: the norm rides along) and
+    # a few exact fp32 scores; the executed flops are the scans', against the bf16 peak (2 r K R = 262144
+    # flops per token would be the fp32-equivalent count)
+    add("rvq r256 G8 K256 R2 encode (bf16 scan)", _timed(enc, flush), N * (2 * r + R * G) + Cb.numel() * 4,
+        N * G * R * 2 * 2 * (r // G + 16) * K, "alu", tokens=N, peak_tf=BF16_PEAK_TFLOPS)
     add("rvq r256 G8 K256 R2 decode (fp32)", _timed(dec, flush), N * (R * G + 4 * r) + Cb.numel() * 4,
         N * r * R, "hbm", tokens=N, peak_tf=F32_PEAK_TFLOPS)
     # the backward gradient gZ = gXhat A in the paper's grouping: 128 groups of width 2, K = 256, R = 2
@@ -489,6 +505,7 @@ def main():
                  "algorithmic_bytes": pair_bytes, "flops": pair_flops},
         "phase_ms": {p: round(v, 5) for p, v in med.items()},
         "wall_s_timed_loop": round(wall, 3),
+        "device": _device_info(),
         "distinct_tids": alg["n_distinct"],
     }
     if not args.no_cpu_baseline:
