@@ -150,9 +150,10 @@ def test_rvq_duplicate_codewords_pick_the_lowest_index():
     assert np.all(codes.cpu().numpy() == 9)
 
 
-def test_rvq_nan_group_gets_code_zero_and_others_unaffected():
+@pytest.mark.parametrize("w", [8, 32])
+def test_rvq_nan_group_gets_code_zero_and_others_unaffected(w):
     rng = np.random.default_rng(7)
-    N, G, K, w = 64, 2, 32, 8
+    N, G, K = 64, 2, 32
     C = rng.standard_normal((1, G, K, w)).astype(np.float32)
     Z = rng.standard_normal((N, G * w)).astype(np.float32)
     Z[5, :w] = np.nan
@@ -165,6 +166,33 @@ def test_rvq_nan_group_gets_code_zero_and_others_unaffected():
     mask = np.ones_like(gc, dtype=bool)
     mask[5, 0, 0] = False
     assert np.array_equal(gc[mask], ref[mask])
+
+
+def test_rvq_nan_codeword_never_wins():
+    # w = 32 scans in bf16 and rescores candidates in fp32: a codeword with a NaN is never a candidate
+    rng = np.random.default_rng(9)
+    N, G, K, w = 700, 2, 64, 32
+    C = (rng.standard_normal((1, G, K, w)) / math.sqrt(w)).astype(np.float32)
+    Z = np.concatenate([C[0, g][rng.integers(0, K, N)] for g in range(G)], axis=1)
+    Z = (Z + 0.05 * rng.standard_normal(Z.shape)).astype(np.float32)
+    C[0, 0, 5, 3] = np.nan
+    codes = lac.rvq_encode(torch.from_numpy(Z).to(DEV), torch.from_numpy(C).to(DEV), G, K, 1).cpu().numpy()
+    assert not np.any(codes[:, 0, 0] == 5)
+    Cf = C.copy()
+    Cf[0, 0, 5] = 1e6  # the oracle with that codeword out of reach
+    ora = rvq.encode(Z.astype(np.float64), Cf.astype(np.float64), G, K, 1, teacher=codes)
+    check_codes(codes, ora, "NaN codeword")
+
+
+def test_rvq_identical_codewords_all_tie_to_index_zero():
+    # every codeword equal: all K are within the bf16 bound, all are rescored, the lowest index wins
+    rng = np.random.default_rng(10)
+    N, G, K, w = 300, 2, 256, 32
+    C = np.broadcast_to(rng.standard_normal((1, G, 1, w)).astype(np.float32), (1, G, K, w)).copy()
+    Z = rng.standard_normal((N, G * w)).astype(np.float32)
+    codes = lac.rvq_encode(torch.from_numpy(Z).to(DEV), torch.from_numpy(C).to(DEV), G, K, 2)
+    torch.cuda.synchronize()
+    assert np.all(codes.cpu().numpy() == 0)
 
 
 def test_rvq_repeat_is_bitwise_deterministic():
