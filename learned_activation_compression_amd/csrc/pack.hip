@@ -90,64 +90,71 @@ void launch_pack_PF(const uint16_t* P, uint16_t* PF, int d, int ra, hipStream_t 
   frag_pack(P, /*sm*/ d, /*sk*/ 1, ra, d, PF, s);  // W(m, k) = P[m][k]
 }
 
-// The four A / P sections in one launch: unit u of the concatenation
-// [AtF | AF | PtF | PF] (section boundaries at multiples of 64 units).
-__global__ __launch_bounds__(256) void k_frag_pack4(const bf16_t* __restrict__ A, const bf16_t* __restrict__ P,
-                                                    bf16_t* __restrict__ AtF, bf16_t* __restrict__ AF,
-                                                    bf16_t* __restrict__ PtF, bf16_t* __restrict__ PF, int d,
-                                                    int r, int ra) {
-  const int64_t u0 = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t n1 = int64_t(d / 16) * (r / 32) * 64;   // AtF, and AF, units
-  const int64_t n3 = int64_t(ra / 16) * (d / 32) * 64;  // PtF, and PF, units
-  const bf16_t* src;
-  int64_t sm, sk, u;
-  int M;
-  bf16_t* dst;
-  if (u0 < n1) {
-    src = A, sm = 1, sk = r, M = r, dst = AtF, u = u0;  // W(m, k) = A[k][m]
-  } else if (u0 < 2 * n1) {
-    src = A, sm = r, sk = 1, M = d, dst = AF, u = u0 - n1;  // W(m, k) = A[m][k]
-  } else if (u0 < 2 * n1 + n3) {
-    src = P, sm = 1, sk = d, M = d, dst = PtF, u = u0 - 2 * n1;  // W(m, k) = P[k][m]
-  } else if (u0 < 2 * n1 + 2 * n3) {
-    src = P, sm = d, sk = 1, M = ra, dst = PF, u = u0 - 2 * n1 - n3;  // W(m, k) = P[m][k]
-  } else {
-    return;
-  }
-  const int MB = M / 32;
-  const int l = int(u & 63);
-  const int64_t frag = u >> 6;
-  const int st = int(frag / MB), mb = int(frag % MB);
-  const int m = mb * 32 + (l & 31);
-  const int k0 = st * 16 + 8 * (l >> 5);
-  uint32_t w[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const uint32_t lo = src[m * sm + int64_t(k0 + 2 * e) * sk];
-    const uint32_t hi = src[m * sm + int64_t(k0 + 2 * e + 1) * sk];
-    w[e] = lo | (hi << 16);
-  }
-  reinterpret_cast<u32x4*>(dst)[u] = u32x4{w[0], w[1], w[2], w[3]};
-}
-
-// QnF = fragments of W = -(P A)^T (M = r, K = ra), rounded once to bf16.  One block
-// per 32 x 32 tile (i, j) of P A; its 16 waves split the d-long contraction
-// (the matrix-core A operand is 16 bytes of a row of P, the B operand the AtF
-// fragment of the same K-step), and the 16 partial tiles are added in LDS in
-// a fixed order, each wave summing 64 of the tile's elements.
+// Full pack in one launch of 1024-thread blocks.  Blocks [0, nq) form QnF,
+// one 32 x 32 tile of P A each (nq = (ra/32)(r/32); 0 without a P); the
+// others write one 16-byte unit each of the concatenation [AtF | AF | PtF | PF]
+// (section boundaries at multiples of 64 units) and, for the identity anchor
+// (eye: P = I, no P), the matching unit of QnF = -AtF with each AtF unit.
+//
+// QnF tile (i, j): fragments of W = -(P A)^T (M = r, K = ra), rounded once to
+// bf16.  Its 16 waves split the d-long contraction (the matrix-core A operand
+// is 16 bytes of a row of P, the B operand 8 rows of one column of A, read
+// directly), and the 16 partial tiles are added in LDS in a fixed order, each
+// wave summing 64 of the tile's elements.
 constexpr int kQnWaves = 16;
 
-__global__ __launch_bounds__(64 * kQnWaves) void k_qn_direct(const bf16_t* __restrict__ P,
-                                                            const bf16_t* __restrict__ AtF,
-                                                            bf16_t* __restrict__ QnF, int d, int r) {
-  // grid (ra / 32, r / 32): blockIdx.x walks the ra rows of P A, blockIdx.y its r columns
+__global__ __launch_bounds__(64 * kQnWaves) void k_pack_all(const bf16_t* __restrict__ A, const bf16_t* __restrict__ P,
+                                                           bf16_t* __restrict__ AtF, bf16_t* __restrict__ AF,
+                                                           bf16_t* __restrict__ PtF, bf16_t* __restrict__ PF,
+                                                           bf16_t* __restrict__ QnF, int d, int r, int ra, int nq,
+                                                           int eye) {
   __shared__ float red[kQnWaves * 1024];
+  if (int(blockIdx.x) >= nq) {
+    // ---- fragment packing: one unit per thread
+    const int64_t u0 = int64_t(blockIdx.x - nq) * (64 * kQnWaves) + threadIdx.x;
+    const int64_t n1 = int64_t(d / 16) * (r / 32) * 64;   // AtF, and AF, units
+    const int64_t n3 = int64_t(ra / 16) * (d / 32) * 64;  // PtF, and PF, units
+    const bf16_t* src;
+    int64_t sm, sk, u;
+    int M;
+    bf16_t* dst;
+    if (u0 < n1) {
+      src = A, sm = 1, sk = r, M = r, dst = AtF, u = u0;  // W(m, k) = A[k][m]
+    } else if (u0 < 2 * n1) {
+      src = A, sm = r, sk = 1, M = d, dst = AF, u = u0 - n1;  // W(m, k) = A[m][k]
+    } else if (u0 < 2 * n1 + n3) {
+      src = P, sm = 1, sk = d, M = d, dst = PtF, u = u0 - 2 * n1;  // W(m, k) = P[k][m]
+    } else if (u0 < 2 * n1 + 2 * n3) {
+      src = P, sm = d, sk = 1, M = ra, dst = PF, u = u0 - 2 * n1 - n3;  // W(m, k) = P[m][k]
+    } else {
+      return;
+    }
+    const int MB = M / 32;
+    const int l = int(u & 63);
+    const int64_t frag = u >> 6;
+    const int st = int(frag / MB), mb = int(frag % MB);
+    const int m = mb * 32 + (l & 31);
+    const int k0 = st * 16 + 8 * (l >> 5);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = src[m * sm + int64_t(k0 + 2 * e) * sk];
+      const uint32_t hi = src[m * sm + int64_t(k0 + 2 * e + 1) * sk];
+      w[e] = lo | (hi << 16);
+    }
+    const u32x4 v = u32x4{w[0], w[1], w[2], w[3]};
+    reinterpret_cast<u32x4*>(dst)[u] = v;
+    if (eye && dst == AtF) reinterpret_cast<u32x4*>(QnF)[u] = v ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    return;
+  }
+  // ---- QnF tile: rows i0.. of P A (ra / 32 row blocks), column block mbj
   const int lane = threadIdx.x & 63, w = wave_id();
   const int hi = lane >> 5, l32 = lane & 31;
-  const int i0 = blockIdx.x * 32, mbj = blockIdx.y;  // rows i0.. of P A, column block mbj
+  const int i0 = (int(blockIdx.x) % (ra / 32)) * 32, mbj = int(blockIdx.x) / (ra / 32);
   const int MB = r / 32;
   const int S = d / 16, sb = S * w / kQnWaves, se = S * (w + 1) / kQnWaves;
   const bf16_t* prow = P + size_t(i0 + l32) * d + 8 * hi;
+  const bf16_t* acol = A + size_t(8 * hi) * r + mbj * 32 + l32;  // A[16 st + 8 hi + e][mbj 32 + l32] at + (16 st + e) r
   f32x16 acc = f32x16{};
   for (int s0 = sb; s0 < se; s0 += 8) {
     bf16x8 a[8], b[8];
@@ -155,7 +162,14 @@ __global__ __launch_bounds__(64 * kQnWaves) void k_qn_direct(const bf16_t* __res
     for (int t = 0; t < 8; ++t) {
       const int st = min(s0 + t, se - 1);
       a[t] = ld_bf16x8(prow + 16 * st);
-      b[t] = ld_bf16x8(AtF + ((size_t(st) * MB + mbj) * 64 + lane) * 8);
+      u32x4 bw;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = acol[size_t(16 * st + 2 * e) * r];
+        const uint32_t hi2 = acol[size_t(16 * st + 2 * e + 1) * r];
+        bw[e] = lo | (hi2 << 16);
+      }
+      b[t] = __builtin_bit_cast(bf16x8, bw);
     }
 #pragma unroll
     for (int t = 0; t < 8; ++t)
@@ -185,29 +199,17 @@ __global__ __launch_bounds__(64 * kQnWaves) void k_qn_direct(const bf16_t* __res
   }
 }
 
-// dst = -src on n 16-byte units of bf16 (a sign flip: exact)
-__global__ __launch_bounds__(256) void k_negate_units(const u32x4* __restrict__ src, u32x4* __restrict__ dst,
-                                                      int64_t n) {
-  const int64_t u = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (u < n) dst[u] = src[u] ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-}
-
-// Full pack: the four A / P sections, then QnF from P and the fresh AtF
+// Full pack: the four A / P sections and QnF from P and A in one launch
 // (ra == 0: no anchor, the A sections only; P == nullptr with ra == d: the
 // identity anchor, QnF = -AtF).
 void launch_pack_all(const uint16_t* P, const uint16_t* A, PackView v, int d, int r, int ra, hipStream_t s) {
   const bool eye = ra > 0 && P == nullptr;
   const int rp = eye ? 0 : ra;  // P sections to fill
   const int64_t units = 2 * int64_t(d / 16) * (r / 32) * 64 + 2 * int64_t(rp / 16) * (d / 32) * 64;
-  hipLaunchKernelGGL(k_frag_pack4, dim3(unsigned((units + 255) / 256)), dim3(256), 0, s, A, P, v.AtF, v.AF, v.PtF,
-                     v.PF, d, r, rp);
-  if (eye) {
-    const int64_t n = int64_t(d / 16) * (r / 32) * 64;  // AtF units
-    hipLaunchKernelGGL(k_negate_units, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s,
-                       reinterpret_cast<const u32x4*>(v.AtF), reinterpret_cast<u32x4*>(v.QnF), n);
-  } else if (ra > 0) {
-    hipLaunchKernelGGL(k_qn_direct, dim3(ra / 32, r / 32), dim3(64 * kQnWaves), 0, s, P, v.AtF, v.QnF, d, r);
-  }
+  const int nq = (ra > 0 && !eye) ? (ra / 32) * (r / 32) : 0;
+  const int per = 64 * kQnWaves;
+  hipLaunchKernelGGL(k_pack_all, dim3(unsigned(nq + (units + per - 1) / per)), dim3(per), 0, s, A, P, v.AtF, v.AF,
+                     v.PtF, v.PF, v.QnF, d, r, rp, nq, int(eye));
 }
 
 }  // namespace mapl
