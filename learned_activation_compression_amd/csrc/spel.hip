@@ -352,6 +352,24 @@ __device__ __forceinline__ void rs_left(const float* __restrict__ Lsh, f32x4 (&a
   for (int kb = 0; kb < R / 16; ++kb) a[kb] = ld4(Lsh + c * (R + 4) + 16 * kb + 4 * kq);
 }
 
+// S [R][R] (global, row-major) -> LDS rows of pitch R + 4, every thread's 16-byte loads issued before
+// the first is stored (consecutive threads read consecutive 16 bytes)
+template <int R>
+__device__ __forceinline__ void rs_stage(const float* __restrict__ src, float* __restrict__ sh) {
+  constexpr int U = R / 4, TOTAL = R * U, PER = (TOTAL + 255) / 256;
+  f32x4 v[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int u = threadIdx.x + 256 * p;
+    if (u < TOTAL) v[p] = ld4(src + 4 * u);
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int u = threadIdx.x + 256 * p;
+    if (u < TOTAL) st4(sh + (u / U) * (R + 4) + 4 * (u % U), v[p]);
+  }
+}
+
 // S workgroup product: out = L S for the 4 rows L (LDS, stride R + 4).  Wave w
 // takes k in [w R/4, (w+1) R/4); its partial rows go to red, and thread t then
 // adds the 4 waves' parts for elements e = t + 256 p (row e / R, column e % R).
@@ -359,12 +377,12 @@ template <int R>
 struct RsRows {
   static constexpr int NG = (R + 63) / 64, KW = R / 4, KU = KW / 4, NE = (4 * R + 255) / 256;
   f32x4 b[NG][KU];  // b[g][u] = S[64 g + l][w KW + 4 u .. + 3]
-  __device__ __forceinline__ void load(const float* __restrict__ S, int w, int l) {
+  __device__ __forceinline__ void load(const float* __restrict__ Ssh, int w, int l) {  // S_k staged in LDS
 #pragma unroll
     for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int u = 0; u < KU; ++u)
-        b[g][u] = (64 * g + l < R) ? ld4(S + size_t(64 * g + l) * R + w * KW + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
+        b[g][u] = (64 * g + l < R) ? ld4(Ssh + (64 * g + l) * (R + 4) + w * KW + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   __device__ __forceinline__ void product(const float* __restrict__ Lsh, float* __restrict__ red, int w, int l,
                                           float (&out)[NE]) const {
@@ -408,12 +426,13 @@ template <int R>
 struct RsRight {
   static constexpr int NT = R / 16, TW = (NT + 3) / 4, KB = R / 16;
   f32x4 b[TW][KB];
-  __device__ __forceinline__ void load(const float* __restrict__ S, int w, int kq, int c) {
+  __device__ __forceinline__ void load(const float* __restrict__ Ssh, int w, int kq, int c) {  // S_k staged in LDS
 #pragma unroll
     for (int t = 0; t < TW; ++t)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        b[t][kb] = (w + 4 * t < NT) ? ld4(S + (16 * (w + 4 * t) + c) * R + 16 * kb + 4 * kq) : f32x4{0.f, 0.f, 0.f, 0.f};
+        b[t][kb] = (w + 4 * t < NT) ? ld4(Ssh + (16 * (w + 4 * t) + c) * (R + 4) + 16 * kb + 4 * kq)
+                                    : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 };
 
@@ -447,7 +466,8 @@ __global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part,
                                                  float* __restrict__ M, unsigned limit) {
   constexpr int RP = R + 4, NT = R / 16, TW = (NT + 3) / 4, KB = R / 16;
   constexpr int NS = R / kRsS, NQ = R / kRsQ, NE = RsRows<R>::NE, NG = RsRows<R>::NG;
-  __shared__ __align__(16) float Lsh[kRsQ * RP];  // own rows of S_k (S workgroup) or Q_k (Q workgroup)
+  extern __shared__ __align__(16) float Ssh[];     // S_k [R][RP], staged each step
+  __shared__ __align__(16) float Lsh[kRsQ * RP];  // own rows of Q_k (Q workgroup)
   __shared__ __align__(16) float Psh[kRsS * RP];  // own rows of S_k^2
   __shared__ float red[4 * NG * 4 * 64];
   __shared__ float scs;
@@ -471,21 +491,18 @@ __global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part,
     }
     rs_sync(flags, nblk, 1u, limit, &slot);
     RsRows<R> B;
+    const float* Own = Ssh + r0 * RP;  // own rows of S_k, in the staged copy
     for (int k = 0; k + 1 < iters; ++k) {
-      const float* S = Sbuf + size_t(k & 1) * R * R;
-      B.load(S, w, lane);
-      if (threadIdx.x < kRsS * U) {  // own rows of S_k
-        const int i = threadIdx.x / U, j4 = 4 * (threadIdx.x % U);
-        st4(Lsh + i * RP + j4, ld4(S + size_t(r0 + i) * R + j4));
-      }
+      rs_stage<R>(Sbuf + size_t(k & 1) * R * R, Ssh);
       __syncthreads();
+      B.load(Ssh, w, lane);
       float sij[NE], s2v[NE], s3v[NE];
 #pragma unroll
       for (int p = 0; p < NE; ++p) {
         const int e = min(int(threadIdx.x) + 256 * p, 4 * R - 1);
-        sij[p] = Lsh[(e / R) * RP + e % R];
+        sij[p] = Own[(e / R) * RP + e % R];
       }
-      B.product(Lsh, red, w, lane, s2v);  // rows of S_k^2
+      B.product(Own, red, w, lane, s2v);  // rows of S_k^2
 #pragma unroll
       for (int p = 0; p < NE; ++p) {
         const int e = threadIdx.x + 256 * p;
@@ -511,17 +528,18 @@ __global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part,
   f32x4 a[KB];
   f32x4 q[TW];
   for (int k = 0; k < iters; ++k) {
-    const float* S = Sbuf + size_t(k & 1) * R * R;
+    rs_stage<R>(Sbuf + size_t(k & 1) * R * R, Ssh);
+    __syncthreads();
     if (k == 0) {  // Q_1 = T_0
 #pragma unroll
       for (int t = 0; t < TW; ++t)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int i = r0 + 4 * kq + v, j = 16 * (w + 4 * t) + c;
-          q[t][v] = (w + 4 * t < NT) ? (i == j ? 1.5f : 0.f) - 0.5f * S[size_t(i) * R + j] : 0.f;
+          q[t][v] = (w + 4 * t < NT) ? (i == j ? 1.5f : 0.f) - 0.5f * Ssh[i * RP + j] : 0.f;
         }
     } else {
-      B.load(S, w, kq, c);
+      B.load(Ssh, w, kq, c);
       rs_left<R>(Lsh, a, kq, c);
       f32x4 qs[TW];
       rs_product<R>(a, B, qs, w);
@@ -667,7 +685,10 @@ unsigned rs_spin_limit() {
 template <int R>
 void launch_rs(const float* part, int G, const float* nparts, int nnp, int iters, float* Sbuf, unsigned* sync,
                float* M, hipStream_t s) {
-  hipLaunchKernelGGL(k_spel_rs<R>, dim3(R / kRsS + R / kRsQ), dim3(256), 0, s, part, G, nparts, nnp, iters, Sbuf,
+  constexpr int lds = R * (R + 4) * int(sizeof(float));  // the staged S_k
+  static std::atomic<uint64_t> done{0};
+  if (lds > 48 * 1024) allow_lds(reinterpret_cast<const void*>(k_spel_rs<R>), lds, done);
+  hipLaunchKernelGGL(k_spel_rs<R>, dim3(R / kRsS + R / kRsQ), dim3(256), lds, s, part, G, nparts, nnp, iters, Sbuf,
                      sync, M, rs_spin_limit());
 }
 
