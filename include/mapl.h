@@ -113,6 +113,20 @@ int mapl_compress(const void* X, const int32_t* tids, const void* E_small,
                   mapl_dtype dt, void* pk, size_t pk_bytes, int pk_ready,
                   hipStream_t stream);
 
+/* Instrumentation for benchmarks (not part of the method): arms the calling
+ * thread so that the compress kernel of its next mapl_compress call is
+ * launched with hipExtLaunchKernelGGL carrying `start` and `stop`
+ * (hipEvent_t, created by the caller with timing enabled and owned by it).
+ * The events then take that kernel's own begin and end time stamps, which
+ * hipEventRecord markers around the call cannot give (each marker is a packet
+ * of its own on the queue).  The next mapl_compress call on the thread takes
+ * the arming whatever its outcome; one that cannot be timed this way (dt !=
+ * MAPL_BF16, r >= 512, or B * T == 0) returns MAPL_ERR_ARG and launches
+ * nothing.  The events bracket the compress kernel only, not the pack kernel
+ * of a call with pk_ready == 0.  Both NULL disarms; exactly one NULL returns
+ * MAPL_ERR_NULL. */
+int mapl_time_next_compress_kernel(void* start, void* stop);
+
 /* Eq. (2): Xhat[N][d] = Z A^T + E_small[tids] P.  Pass the RECEIVING stage's
  * anchor (E_{p+1}, P_{p+1}) and the sender's projector A. */
 int mapl_reconstruct(const void* Z, const int32_t* tids, const void* E_small,

@@ -22,7 +22,7 @@ import torch
 
 __all__ = [
     "MaplError", "LIB_PATH", "load", "exported_symbols",
-    "mapl_pack_bytes", "mapl_pack", "mapl_compress", "mapl_reconstruct",
+    "mapl_pack_bytes", "mapl_pack", "mapl_compress", "mapl_time_next_compress_kernel", "mapl_reconstruct",
     "mapl_bwd_workspace_bytes", "mapl_reconstruct_bwd", "mapl_compress_bwd",
     "mapl_anchor_grad_workspace_bytes", "mapl_anchor_grad", "mapl_check_tids",
     "rvq_encode", "rvq_decode", "rvq_stream_apply", "spel_workspace_bytes", "spel_step",
@@ -44,6 +44,7 @@ _SIGS = {
     "mapl_version": (ctypes.c_char_p, []),
     "mapl_pack_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "mapl_pack": (_i32, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32, _vp]),
+    "mapl_time_next_compress_kernel": (_i32, [_vp, _vp]),
     "mapl_compress": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _sz, _i32,
                              _vp]),
     "mapl_reconstruct": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp, _sz,
@@ -217,6 +218,24 @@ def mapl_compress(X, tids, E_small, P, A, Z=None, pk=None, pk_ready=False, strea
                                 V, dt, pk.data_ptr() if pk is not None else None, nb, int(bool(pk_ready)),
                                 _stream(stream)), "mapl_compress")
     return Z
+
+
+def mapl_time_next_compress_kernel(start=None, stop=None) -> None:
+    """Instrumentation: the compress kernel of this thread's next mapl_compress
+    call is launched with the torch.cuda.Event objects `start` and `stop`
+    (enable_timing=True) as its own begin and end stamps; None, None disarms.
+    torch creates an event at its first record(), so each must have been
+    recorded once.  The next mapl_compress call takes the arming and fails
+    for calls that cannot be timed this way (fp32 data, r >= 512, no tokens)."""
+    def raw(e, name):
+        if e is None:
+            return None
+        h = int(e.cuda_event)
+        if h == 0:
+            raise MaplError(f"mapl_time_next_compress_kernel: {name} has no event yet (record it once first)")
+        return h
+    _check(load().mapl_time_next_compress_kernel(raw(start, "start"), raw(stop, "stop")),
+           "mapl_time_next_compress_kernel")
 
 
 def mapl_reconstruct(Z, tids, E_small, P, A, Xhat=None, pk=None, pk_ready=False, stream=None) -> torch.Tensor:

@@ -108,9 +108,22 @@ int mapl_pack(const void* P, const void* A, void* pk, size_t pk_bytes, int64_t d
   return ls.done();
 }
 
+// events armed by mapl_time_next_compress_kernel for this thread's next mapl_compress
+static thread_local KernelEvents t_compress_events;
+
+int mapl_time_next_compress_kernel(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return MAPL_ERR_NULL;
+  t_compress_events.start = static_cast<hipEvent_t>(start);
+  t_compress_events.stop = static_cast<hipEvent_t>(stop);
+  return MAPL_OK;
+}
+
 int mapl_compress(const void* X, const int32_t* tids, const void* E_small, const void* P, const void* A, void* Z,
                   int64_t B, int64_t T, int64_t d, int64_t r, int64_t ra, int64_t V, mapl_dtype dt, void* pk,
                   size_t pk_bytes, int pk_ready, hipStream_t stream) {
+  const KernelEvents ev = t_compress_events;  // taken by this call whatever its outcome
+  t_compress_events = KernelEvents{};
+  if (ev.armed() && (dt != MAPL_BF16 || r >= 512 || B * T == 0)) return MAPL_ERR_ARG;
   int st = check_codec_shape(B, T, d, r, ra, V, dt, true);
   if (st) return st;
   if (pk_ready != 0 && pk_ready != 1) return MAPL_ERR_ARG;
@@ -131,7 +144,7 @@ int mapl_compress(const void* X, const int32_t* tids, const void* E_small, const
                     stream);
   launch_tok_reduce_bf16(static_cast<const uint16_t*>(X), v.AtF, tids,
                          ra > 0 ? static_cast<const uint16_t*>(E_small) : nullptr, v.QnF, static_cast<uint16_t*>(Z),
-                         N, int(d), int(r), int(ra), int(V), stream);
+                         N, int(d), int(r), int(ra), int(V), stream, ev);
   return ls.done();
 }
 

@@ -355,13 +355,13 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
 template <int RBW, int S, int G, bool ANCHOR, bool OUTF = false>
 static void launch_reduce_dma(const uint16_t* in, const uint16_t* AtF, const int32_t* tids, const uint16_t* E,
                               const uint16_t* QnF, uint16_t* out, int N, int d, int r, int ra, int V, hipStream_t s,
-                              float* Uf = nullptr, float alpha = 1.f, float* part = nullptr) {
+                              float* Uf = nullptr, float alpha = 1.f, float* part = nullptr, KernelEvents ev = {}) {
   auto k = k_tok_reduce_dma<RBW, S, G, ANCHOR, OUTF>;
   const size_t lds = RedRing<RBW, S>::BYTES;
   static std::atomic<uint64_t> attr{0};  // devices with the raised LDS limit
   allow_lds(reinterpret_cast<const void*>(k), int(lds), attr);
-  hipLaunchKernelGGL(k, dim3((N + 63) / 64), dim3(256 * G), lds, s, in, AtF, tids, E, QnF, out, N, d, r, ra, V, Uf,
-                     alpha, part);
+  launch_k(ev, k, dim3((N + 63) / 64), dim3(256 * G), uint32_t(lds), s, in, AtF, tids, E, QnF, out, N, d, r, ra, V,
+           Uf, alpha, part);
 }
 
 bool launch_tok_reduce_f32out(const uint16_t* in, const uint16_t* F, float* U, float alpha, float* part, int N,
@@ -380,24 +380,26 @@ bool launch_tok_reduce_f32out(const uint16_t* in, const uint16_t* F, float* U, f
 }
 
 void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32_t* tids, const uint16_t* E,
-                            const uint16_t* QnF, uint16_t* out, int N, int d, int r, int ra, int V, hipStream_t s) {
-  // ANCHOR = true is the compress map of Eq. (1); false is the plain product (gZ = gXhat A)
+                            const uint16_t* QnF, uint16_t* out, int N, int d, int r, int ra, int V, hipStream_t s,
+                            KernelEvents ev) {
+  // ANCHOR = true is the compress map of Eq. (1); false is the plain product (gZ = gXhat A).
+  // `ev` (optional) brackets the one compress kernel for r < 512.
   const bool anc = E != nullptr && ra > 0;
   if (!anc) E = nullptr;
   if (r >= 512 && launch_tok_gemm_bf16(in, d, tids, V, E, anc ? ra : 0, AtF, QnF, out, N, r, s)) return;
   if (r == 128) {
-    if (anc) launch_reduce_dma<1, 6, 2, true>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
-    else launch_reduce_dma<1, 6, 2, false>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
+    if (anc) launch_reduce_dma<1, 6, 2, true>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s, nullptr, 1.f, nullptr, ev);
+    else launch_reduce_dma<1, 6, 2, false>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s, nullptr, 1.f, nullptr, ev);
     return;
   }
   if (r == 256) {
-    if (anc) launch_reduce_dma<2, 3, 1, true>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
-    else launch_reduce_dma<2, 3, 1, false>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
+    if (anc) launch_reduce_dma<2, 3, 1, true>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s, nullptr, 1.f, nullptr, ev);
+    else launch_reduce_dma<2, 3, 1, false>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s, nullptr, 1.f, nullptr, ev);
     return;
   }
   if (r == 512) {
-    if (anc) launch_reduce_dma<4, 2, 1, true>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
-    else launch_reduce_dma<4, 2, 1, false>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s);
+    if (anc) launch_reduce_dma<4, 2, 1, true>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s, nullptr, 1.f, nullptr, ev);
+    else launch_reduce_dma<4, 2, 1, false>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s, nullptr, 1.f, nullptr, ev);
     return;
   }
   const int nb = r / 32;
@@ -406,7 +408,7 @@ void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32
   auto k = anc ? (RB == 4 ? k_tok_reduce<4, 4, true> : RB == 2 ? k_tok_reduce<2, 6, true> : k_tok_reduce<1, 8, true>)
                : (RB == 4 ? k_tok_reduce<4, 4, false> : RB == 2 ? k_tok_reduce<2, 6, false>
                                                                : k_tok_reduce<1, 8, false>);
-  hipLaunchKernelGGL(k, grid, dim3(256), 0, s, in, AtF, tids, E, QnF, out, N, d, r, ra, V);
+  launch_k(ev, k, grid, dim3(256), 0u, s, in, AtF, tids, E, QnF, out, N, d, r, ra, V);
 }
 
 // ---------------------------------------------------------------- expand --

@@ -11,6 +11,7 @@
 // assignment of contraction indices to k slots gives the same sum.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -95,6 +96,25 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Host side: a kernel launch that, given both events, goes through
+// hipExtLaunchKernelGGL so that the events take the kernel's own begin and end
+// time stamps (no marker packets between them and the kernel).  Each argument
+// is converted to the kernel's parameter type before it is packed.
+struct KernelEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool armed() const { return start != nullptr && stop != nullptr; }
+};
+
+template <typename... Formals, typename... Actuals>
+inline void launch_k(KernelEvents ev, void (*k)(Formals...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                     Actuals... a) {
+  static_assert(sizeof...(Formals) == sizeof...(Actuals), "argument count");
+  if (ev.armed())
+    hipExtLaunchKernelGGL(k, grid, block, lds, s, ev.start, ev.stop, 0u, Formals(a)...);
+  else
+    hipLaunchKernelGGL(k, grid, block, lds, s, Formals(a)...);
 }
 
 // Host side: raise a kernel's dynamic-LDS limit above 64 KB on the current

@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "common.h"
 #include <stddef.h>
 #include <stdint.h>
 
@@ -32,7 +34,7 @@ void launch_pack_all(const uint16_t* P, const uint16_t* A, PackView v, int d, in
 // ra == 0 drops the anchor term
 void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32_t* tids,
                             const uint16_t* E, const uint16_t* QnF, uint16_t* out,
-                            int N, int d, int r, int ra, int V, hipStream_t s);
+                            int N, int d, int r, int ra, int V, hipStream_t s, KernelEvents ev = {});
 // U[N][r] = alpha * in[N][d] W^T with W's fragments F (M = r, K = d), fp32 rows, and
 // the max |U| of each output wave in part[4 * (N / 64 block) + wave]; covers r = 128
 // and 256 (returns false, launching nothing, otherwise)

@@ -22,7 +22,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = lac.exported_symbols()
-    assert len(names) == 19, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lac._SIGS), set(names) ^ set(lac._SIGS)
@@ -62,6 +62,27 @@ def _compress(lib, **kw):
     a.update(kw)
     return lib.mapl_compress(a["X"], a["tids"], a["E"], a["P"], a["A"], a["Z"], a["B"], a["T"], a["d"], a["r"],
                              a["ra"], a["V"], a["dt"], a["pk"], a["pk_bytes"], a["pk_ready"], a["s"])
+
+
+def test_compress_kernel_timing_arming(lib):
+    # exactly one event is an error; both NULL disarm
+    assert lib.mapl_time_next_compress_kernel(FAKE, None) == ENULL
+    assert lib.mapl_time_next_compress_kernel(None, FAKE) == ENULL
+    assert lib.mapl_time_next_compress_kernel(None, None) == OK
+    # an armed call that cannot be timed fails before any validation or launch ...
+    for bad in (dict(dt=F32), dict(r=512), dict(B=0)):
+        assert lib.mapl_time_next_compress_kernel(FAKE, FAKE) == OK
+        assert _compress(lib, **bad) == EARG
+        # ... and takes the arming: the same call disarmed reaches its own validation
+        assert _compress(lib, **bad, X=None) in (ENULL, OK)
+    # a failing call also takes the arming: the next one validates normally
+    assert lib.mapl_time_next_compress_kernel(FAKE, FAKE) == OK
+    assert _compress(lib, X=None) == ENULL
+    assert _compress(lib, d=1000) == ESHAPE
+    # disarming before the call leaves it unaffected
+    assert lib.mapl_time_next_compress_kernel(FAKE, FAKE) == OK
+    assert lib.mapl_time_next_compress_kernel(None, None) == OK
+    assert _compress(lib, dt=F32, X=None) == ENULL
 
 
 def test_compress_validation(lib):

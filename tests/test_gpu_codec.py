@@ -120,6 +120,35 @@ def test_bf16_prepacked_weights_give_identical_bits():
     assert torch.equal(Z0, Z1) and torch.equal(Xh0, Xh1)
 
 
+@pytest.mark.parametrize("N,d,r", [(1000, 1024, 128), (777, 2048, 256), (130, 384, 64)])
+def test_bf16_compress_with_kernel_events(N, d, r):
+    # the instrumented launch (hipExtLaunchKernelGGL with the caller's events) computes the same
+    # bits, stamps a positive kernel time, and the arming lasts for one call only
+    inp = synth.codec_inputs(24, N, d, r, 5000, "bf16")
+    g = to_dev(inp)
+    Z0 = lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    torch.cuda.synchronize()
+    lac.mapl_time_next_compress_kernel(e0, e1)
+    Z1 = lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"])
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    assert 0.0 < ms < 100.0, ms
+    Z2 = lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"])  # not armed any more
+    torch.cuda.synchronize()
+    assert e0.elapsed_time(e1) == ms
+    assert torch.equal(Z0, Z1) and torch.equal(Z0, Z2)
+    # an armed call that cannot be timed launches nothing and leaves Z alone
+    Zf = torch.full((N, r), 7.0, device=DEV)
+    lac.mapl_time_next_compress_kernel(e0, e1)
+    with pytest.raises(lac.MaplError):
+        lac.mapl_compress(g["X"].float(), g["tids"], g["E"].float(), g["P"].float(), g["A"].float(), Z=Zf)
+    torch.cuda.synchronize()
+    assert bool((Zf == 7.0).all())
+
+
 def test_bf16_repeat_is_bitwise_deterministic():
     inp = synth.codec_inputs(23, 2048, 1024, 128, 32000, "bf16")
     g = to_dev(inp)
