@@ -30,7 +30,13 @@
  *    gA is always fp32.
  *  - Token ids are int32.  A token id outside [0, V) is a caller error; the
  *    kernels never read out of bounds for it (its anchor row is taken as
- *    zero), and mapl_check_tids counts such ids on the device.
+ *    zero), and mapl_check_tids counts such ids on the device (the Python
+ *    binding, with MAPL_CHECK=1 in the environment, runs it before every map
+ *    that reads ids and raises MAPL_ERR_TID).
+ *  - Before its first launch on a device every entry point raises the
+ *    dynamic-LDS limit of the kernels that use more than 64 KB (mapl_init);
+ *    if the runtime refuses, the call returns MAPL_ERR_HIP and enqueues
+ *    nothing.
  *  - Shape limits of the bf16 codec path: d % 128 == 0, r a power of two
  *    with 32 <= r <= 512, r <= d.  The fp32 path needs 1 <= r <= d <= 4096.
  *  - The library holds no state between calls and is reentrant; calls on
@@ -56,7 +62,10 @@ enum {
   MAPL_ERR_DTYPE = -3,     /* unsupported dtype                                */
   MAPL_ERR_ARG = -4,       /* a scalar argument is out of range                */
   MAPL_ERR_WORKSPACE = -5, /* workspace or pack buffer too small               */
-  MAPL_ERR_HIP = -6        /* the HIP runtime reported an error on launch      */
+  MAPL_ERR_HIP = -6,       /* the HIP runtime reported an error (device set-up  *
+                            * or launch)                                        */
+  MAPL_ERR_TID = -7        /* a token id is outside [0, V) (raised by the       *
+                            * binding's MAPL_CHECK=1 mode from mapl_check_tids) */
 };
 
 /* Human-readable text for a status code (static storage, never NULL). */
@@ -64,6 +73,14 @@ const char* mapl_status_string(int status);
 
 /* Library version string (static storage). */
 const char* mapl_version(void);
+
+/* Prepare the current device: raise the dynamic-LDS limit of every kernel
+ * that needs more than the default 64 KB (at most 160 KB, the LDS of one
+ * gfx950 workgroup).  Every entry point does this itself, once per device,
+ * before its first launch; calling it first only moves that cost.  Returns
+ * MAPL_OK, or MAPL_ERR_HIP when there is no usable device or the runtime
+ * refuses a limit. */
+int mapl_init(void);
 
 /* ------------------------------------------------------------------------
  * Packed weights.
@@ -182,8 +199,11 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids,
  * are exact 64-bit fixed-point accumulations at one power-of-two scale chosen
  * from max |alpha Y[n] P^T| (every sum fits; each term is rounded once, by
  * at most 2^-30 times that maximum), so the result does not depend on the
- * order of the additions: it is bitwise repeatable.  Inputs must be finite
- * (alpha non-finite: MAPL_ERR_ARG).  bf16 reads P through the pack (pk,
+ * order of the additions: it is bitwise repeatable.  If any projected value
+ * alpha Y[n] P^T is not finite (Y holds NaN or Inf, or the product
+ * overflows), no such scale exists and every row of gE is set to NaN
+ * (accumulate == 1 included), so a diverging gradient is never silently lost
+ * or clipped (alpha non-finite: MAPL_ERR_ARG).  bf16 reads P through the pack (pk,
  * pk_bytes, pk_ready as for the codec; pk_ready == 0 rebuilds only its P
  * part from this P, so a receiver passes the pack of its own P').  Uses a
  * 16-byte aligned `ws` of mapl_anchor_grad_workspace_bytes() (MAPL_ERR_ARG if
@@ -209,16 +229,21 @@ int mapl_check_tids(const int32_t* tids, int64_t N, int64_t V, int32_t* bad_coun
  * shares one codebook across all rounds (the paper's single per-stage C_p);
  * C_round_stride >= r*K gives each round its own.  Codes are uint8
  * [N][R][G] at codes[(n*R + rho)*G + g], so K <= 256.
- * Limits: w in {2, 4, 8, 16, 32, 64}, K % 32 == 0, 32 <= K <= 256, R >= 1, and
- * (w (K + 2) + K) * 4 <= 65536 (one group's codebook fits in LDS).
+ * Limits: w in {2, 4, 8, 16, 32, 64}, 1 <= K <= 256, 1 <= R <= 64;
+ * C 16-byte aligned and C_round_stride a multiple of 4 (codeword rows move as
+ * 16-byte vectors; MAPL_ERR_ARG otherwise); rvq_encode also needs Z 16-byte
+ * aligned.
  * ---------------------------------------------------------------------- */
 
 /* Encode: for rho = 0..R-1 and each group, code = argmin_k ||res - c_k||^2
- * (squared Euclidean, evaluated as ||c_k||^2 - 2<res, c_k> in fp32; exact ties
- * go to the lowest k; a NaN distance never wins), then res -= c_code.  res
- * starts as Z (z_dt: MAPL_BF16 or MAPL_F32).  For w >= 16 the K codewords are
- * first scored in bf16 with a proven error bound and only those that can still
- * be the argmin are scored in fp32; the result is the same fp32 argmin. */
+ * (squared Euclidean; exact ties go to the lowest k; a NaN distance never
+ * wins; a group whose distances are all NaN gets code 0), then res -= c_code.
+ * res starts as Z (z_dt: MAPL_BF16 or MAPL_F32) and is kept in fp64, which
+ * holds z - c_1 - ... exactly for inputs of ordinary range, so the codes are
+ * those of exact arithmetic.  The K codewords are first scored on the matrix
+ * cores (bf16 for w >= 16, fp32 below) with a proven bound on the scoring
+ * error, and every codeword that can still be the argmin is then scored
+ * exactly as sum_j (res_j - c_kj)^2 in fp64. */
 int rvq_encode(const void* Z, mapl_dtype z_dt, const float* C, int64_t C_round_stride,
                uint8_t* codes, int64_t N, int64_t r, int64_t G, int64_t K, int64_t R,
                hipStream_t stream);
@@ -257,16 +282,20 @@ int rvq_stream_apply(float* C, const int32_t* idx, const float* vals, int64_t n,
  * the same up to rounding), each in one launch of r/4 + r/16 workgroups that
  * wait for one another through flags in the workspace.  They need to be
  * resident together, which an otherwise idle device always allows; should a
- * wait last beyond about a second (a device kept full by other work), A comes
- * back as NaN (and D too if the direction's iteration was the one that waited)
- * rather than the call hanging.
+ * wait last beyond about a second (a device kept full by other work), the
+ * step is abandoned rather than the call hanging.
+ * The step is transactional: the new m and A are formed in the workspace and
+ * the last launch writes both only if no wait timed out; an abandoned step
+ * leaves A and m exactly as they were (D_out, if given, is then unspecified).
+ * `status`, if not NULL, is a device int32 set to 0 when the step was applied
+ * and to 1 when it was abandoned.
  * Limits: r % 32 == 0, d % 32 == 0, r <= d, r <= 1024, 0 <= beta < 1,
- * 0 <= alpha <= 0.7, 1 <= ns_iters <= 64.
+ * 0 <= alpha <= 0.7, 1 <= ns_iters <= 64; status 4-byte aligned.
  * ---------------------------------------------------------------------- */
 size_t spel_workspace_bytes(int64_t d, int64_t r);
 
 int spel_step(float* A, const float* g, float* m, float alpha, float beta, int ns_iters,
-              float* D_out, int64_t d, int64_t r, void* ws, size_t ws_bytes,
+              float* D_out, int32_t* status, int64_t d, int64_t r, void* ws, size_t ws_bytes,
               hipStream_t stream);
 
 /* The same SPEL step with the Polar Express polar map that Section 3.3 and
@@ -280,11 +309,12 @@ int spel_step(float* A, const float* g, float* m, float alpha, float beta, int n
  * 3 x^5) / 8.  Both polar inputs, m and A - alpha D, are scaled by their
  * Frobenius norms first (D = 0 when m == 0).  The schedule is computed on the
  * host in double and rounded to fp32.  Buffers, workspace
- * (spel_workspace_bytes) and the other limits as for spel_step;
+ * (spel_workspace_bytes), status and the other limits as for spel_step (this
+ * form has no waits between workgroups, so the step is always applied);
  * 1 <= lmo_steps, ret_steps <= 32, 0 < ell < 1 (MAPL_ERR_ARG otherwise). */
 int spel_step_polar_express(float* A, const float* g, float* m, float alpha, float beta, int lmo_steps,
-                            int ret_steps, float ell, float* D_out, int64_t d, int64_t r, void* ws,
-                            size_t ws_bytes, hipStream_t stream);
+                            int ret_steps, float ell, float* D_out, int32_t* status, int64_t d, int64_t r,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Host only: the Polar Express schedule above from [ell, 1]: coef [steps][3]
  * = (a, b, c) of each step and, if err is not NULL, err [steps] = E_t.

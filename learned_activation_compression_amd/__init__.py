@@ -21,7 +21,7 @@ import re
 import torch
 
 __all__ = [
-    "MaplError", "LIB_PATH", "load", "exported_symbols",
+    "MaplError", "LIB_PATH", "load", "exported_symbols", "mapl_init",
     "mapl_pack_bytes", "mapl_pack", "mapl_compress", "mapl_time_next_compress_kernel", "mapl_reconstruct",
     "mapl_bwd_workspace_bytes", "mapl_reconstruct_bwd", "mapl_compress_bwd",
     "mapl_anchor_grad_workspace_bytes", "mapl_anchor_grad", "mapl_check_tids",
@@ -35,6 +35,7 @@ LIB_PATH = os.path.join(_HERE, "libmapl.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "mapl.h")
 
 MAPL_F32, MAPL_BF16 = 0, 1
+MAPL_ERR_TID = -7
 
 _vp, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_float
 
@@ -42,6 +43,7 @@ _vp, _i64, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctyp
 _SIGS = {
     "mapl_status_string": (ctypes.c_char_p, [_i32]),
     "mapl_version": (ctypes.c_char_p, []),
+    "mapl_init": (_i32, []),
     "mapl_pack_bytes": (_sz, [_i64, _i64, _i64, _i32]),
     "mapl_pack": (_i32, [_vp, _vp, _vp, _sz, _i64, _i64, _i64, _i32, _vp]),
     "mapl_time_next_compress_kernel": (_i32, [_vp, _vp]),
@@ -62,8 +64,8 @@ _SIGS = {
     "rvq_decode": (_i32, [_vp, _vp, _i64, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _vp]),
     "rvq_stream_apply": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
     "spel_workspace_bytes": (_sz, [_i64, _i64]),
-    "spel_step": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _vp, _i64, _i64, _vp, _sz, _vp]),
-    "spel_step_polar_express": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _i32, _f32, _vp, _i64, _i64, _vp, _sz,
+    "spel_step": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),
+    "spel_step_polar_express": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _i32, _f32, _vp, _vp, _i64, _i64, _vp, _sz,
                                        _vp]),
     "spel_polar_express_coefficients": (_i32, [ctypes.c_double, _i32, _vp, _vp]),
 }
@@ -141,6 +143,28 @@ def _check(status: int, where: str):
         raise MaplError(status, where)
 
 
+def _checking() -> bool:
+    """MAPL_CHECK=1 in the environment: count out-of-range token ids on the
+    device before every map that reads them, and raise MAPL_ERR_TID."""
+    return os.environ.get("MAPL_CHECK", "0") not in ("", "0")
+
+
+def _check_tids(tids, V: int, where: str, stream=None):
+    if tids is None or not _checking():
+        return
+    bad = mapl_check_tids(tids, V, stream=stream)
+    if stream is not None:
+        stream.synchronize()
+    n_bad = int(bad.item())  # a copy to the host: waits for the count
+    if n_bad:
+        raise MaplError(MAPL_ERR_TID, where, f"{n_bad} token id(s) outside [0, {V})")
+
+
+def mapl_init() -> None:
+    """Prepare the current device (raise the kernels' dynamic-LDS limits)."""
+    _check(load().mapl_init(), "mapl_init")
+
+
 def _tokens(t: torch.Tensor, width: int, name: str):
     if t.dim() == 3:
         B, T, w = t.shape
@@ -213,6 +237,8 @@ def mapl_compress(X, tids, E_small, P, A, Z=None, pk=None, pk_ready=False, strea
     if Z is None:
         Z = _empty((*X.shape[:-1], r), X.dtype, X)
     pk, nb = _pk(pk, d, r, ra, dt, X)
+    if ra > 0:
+        _check_tids(tids, V, "mapl_compress", stream)
     _check(load().mapl_compress(_dev(X, "X"), _opt(tids, "tids", torch.int32), _opt(E_small, "E_small", X.dtype),
                                 _opt(P, "P", X.dtype), _dev(A, "A", X.dtype), _dev(Z, "Z", X.dtype), B, T, d, r, ra,
                                 V, dt, pk.data_ptr() if pk is not None else None, nb, int(bool(pk_ready)),
@@ -232,7 +258,7 @@ def mapl_time_next_compress_kernel(start=None, stop=None) -> None:
             return None
         h = int(e.cuda_event)
         if h == 0:
-            raise MaplError(f"mapl_time_next_compress_kernel: {name} has no event yet (record it once first)")
+            raise MaplError(-1, "mapl_time_next_compress_kernel", f"{name} has no event yet (record it once first)")
         return h
     _check(load().mapl_time_next_compress_kernel(raw(start, "start"), raw(stop, "stop")),
            "mapl_time_next_compress_kernel")
@@ -248,6 +274,8 @@ def mapl_reconstruct(Z, tids, E_small, P, A, Xhat=None, pk=None, pk_ready=False,
     if Xhat is None:
         Xhat = _empty((*Z.shape[:-1], d), Z.dtype, Z)
     pk, nb = _pk(pk, d, r, ra, dt, Z)
+    if ra > 0:
+        _check_tids(tids, V, "mapl_reconstruct", stream)
     _check(load().mapl_reconstruct(_dev(Z, "Z"), _opt(tids, "tids", torch.int32),
                                    _opt(E_small, "E_small", Z.dtype), _opt(P, "P", Z.dtype), _dev(A, "A", Z.dtype),
                                    _dev(Xhat, "Xhat", Z.dtype), B, T, d, r, ra, V, dt,
@@ -308,6 +336,8 @@ def mapl_compress_bwd(gZ, X, tids, E_small, P, A, gX=None, gA=None, accumulate=F
             _empty((d, r), torch.float32, gZ)
     pk, nb = _pk(pk, d, r, ra, dt, gZ)
     ws, wb = _ws(ws, int(load().mapl_bwd_workspace_bytes(B, T, d, r, ra, dt)), gZ)
+    if ra > 0:
+        _check_tids(tids, V, "mapl_compress_bwd", stream)
     _check(load().mapl_compress_bwd(_dev(gZ, "gZ"), _dev(X, "X", gZ.dtype), _opt(tids, "tids", torch.int32),
                                     _opt(E_small, "E_small", gZ.dtype), _opt(P, "P", gZ.dtype),
                                     _dev(A, "A", gZ.dtype), _dev(gX, "gX", gZ.dtype), _dev(gA, "gA", torch.float32),
@@ -342,6 +372,7 @@ def mapl_anchor_grad(Y, tids, P, V: int, alpha: float = 1.0, gE=None, accumulate
             _empty((V, ra), torch.float32, Y)
     pk, nb = _pk(pk, d, r, ra, dt, Y) if P is not None else (None, 0)
     ws, wb = _ws(ws, int(load().mapl_anchor_grad_workspace_bytes(B, T, ra, V)), Y)
+    _check_tids(tids, V, "mapl_anchor_grad", stream)
     _check(load().mapl_anchor_grad(_dev(Y, "Y"), _dev(tids, "tids", torch.int32), _opt(P, "P", Y.dtype),
                                    _dev(gE, "gE", torch.float32), float(alpha), int(bool(accumulate)), B, T, d, r, ra,
                                    V, dt, pk.data_ptr() if pk is not None else None, nb, int(bool(pk_ready)),
@@ -407,20 +438,24 @@ def spel_workspace_bytes(d: int, r: int) -> int:
     return int(load().spel_workspace_bytes(d, r))
 
 
-def spel_step(A, g, m, alpha: float, beta: float, ns_iters: int = 8, D_out=None, ws=None, stream=None):
+def spel_step(A, g, m, alpha: float, beta: float, ns_iters: int = 8, D_out=None, status=None, ws=None,
+              stream=None):
     """One SPEL step on fp32 A [d][r] and momentum m (both in place).
-    Returns D_out (the LMO direction) if given, else None."""
+    Returns D_out (the LMO direction) if given, else None.  status: optional
+    device int32 [1], set to 0 when the step was applied and to 1 when a wait
+    between workgroups timed out (A and m then keep their values)."""
     d, r = A.shape
     ws, wb = _ws(ws, spel_workspace_bytes(d, r), A)
     _check(load().spel_step(_dev(A, "A", torch.float32), _dev(g, "g", torch.float32), _dev(m, "m", torch.float32),
                             float(alpha), float(beta), int(ns_iters),
-                            _dev(D_out, "D_out", torch.float32) if D_out is not None else None, d, r,
+                            _dev(D_out, "D_out", torch.float32) if D_out is not None else None,
+                            _opt(status, "status", torch.int32), d, r,
                             ws.data_ptr() if ws is not None else None, wb, _stream(stream)), "spel_step")
     return D_out
 
 
 def spel_step_polar_express(A, g, m, alpha: float, beta: float, lmo_steps: int = 5, ret_steps: int = 7,
-                            ell: float = 1e-3, D_out=None, ws=None, stream=None):
+                            ell: float = 1e-3, D_out=None, status=None, ws=None, stream=None):
     """One SPEL step with the Polar Express polar map (5 LMO / 7 retraction
     steps by default) on fp32 A [d][r] and m (both in place).  Returns D_out
     if given, else None."""
@@ -429,7 +464,8 @@ def spel_step_polar_express(A, g, m, alpha: float, beta: float, lmo_steps: int =
     _check(load().spel_step_polar_express(_dev(A, "A", torch.float32), _dev(g, "g", torch.float32),
                                           _dev(m, "m", torch.float32), float(alpha), float(beta), int(lmo_steps),
                                           int(ret_steps), float(ell),
-                                          _dev(D_out, "D_out", torch.float32) if D_out is not None else None, d, r,
+                                          _dev(D_out, "D_out", torch.float32) if D_out is not None else None,
+                                          _opt(status, "status", torch.int32), d, r,
                                           ws.data_ptr() if ws is not None else None, wb, _stream(stream)),
            "spel_step_polar_express")
     return D_out

@@ -1,6 +1,7 @@
 // C ABI of the MAPL codec library: host-side validation, then launches.
 // The operations and their sources are documented in include/mapl.h.
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 
 #include "../../include/mapl.h"
@@ -8,15 +9,59 @@
 
 using namespace mapl;
 
+// ------------------------------------------------ dynamic-LDS limit registry --
+namespace mapl {
+namespace {
+constexpr int kMaxLdsKernels = 256;
+struct LdsEntry {
+  const void* kernel;
+  int bytes;
+};
+// filled during the library's static initialisation (constant-initialised storage, so
+// registrations from any translation unit find it ready)
+LdsEntry g_lds[kMaxLdsKernels];
+int g_lds_count = 0;
+bool g_lds_overflow = false;
+std::atomic<uint64_t> g_lds_ready{0};  // devices whose limits are raised (bit = device index < 64)
+}  // namespace
+
+void lds_register(const void* kernel, int bytes) {
+  if (g_lds_count < kMaxLdsKernels) g_lds[g_lds_count++] = LdsEntry{kernel, bytes};
+  else g_lds_overflow = true;
+}
+
+hipError_t lds_prepare_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t(1) << dev) : 0;
+  if (bit != 0 && (g_lds_ready.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  if (g_lds_overflow) return hipErrorInvalidValue;
+  for (int i = 0; i < g_lds_count; ++i) {
+    e = hipFuncSetAttribute(g_lds[i].kernel, hipFuncAttributeMaxDynamicSharedMemorySize, g_lds[i].bytes);
+    if (e != hipSuccess) return e;
+  }
+  if (bit != 0) g_lds_ready.fetch_or(bit, std::memory_order_acq_rel);
+  return hipSuccess;
+}
+}  // namespace mapl
+
 namespace {
 
 constexpr const char* kVersion = "mapl-gfx950 0.1.0";
 constexpr int kMaxPolarSteps = 32;
 
-// Launch status: clears any error left by an earlier call before enqueueing
-// and reports the launch error (if any) afterwards.
+// Launch status: clears any error left by an earlier call and prepares the
+// current device (the dynamic-LDS limits) before anything is enqueued; an
+// entry point returns MAPL_ERR_HIP without launching when that fails
+// (ready() false), and reports the launch error (if any) afterwards.
 struct LaunchScope {
-  LaunchScope() { (void)hipGetLastError(); }
+  hipError_t prep;
+  LaunchScope() {
+    (void)hipGetLastError();
+    prep = lds_prepare_device();
+  }
+  bool ready() const { return prep == hipSuccess; }
   int done() const { return hipGetLastError() == hipSuccess ? MAPL_OK : MAPL_ERR_HIP; }
 };
 
@@ -82,12 +127,18 @@ const char* mapl_status_string(int status) {
     case MAPL_ERR_DTYPE: return "unsupported dtype";
     case MAPL_ERR_ARG: return "a scalar argument is out of range";
     case MAPL_ERR_WORKSPACE: return "workspace or pack buffer too small";
-    case MAPL_ERR_HIP: return "the HIP runtime reported a launch error";
+    case MAPL_ERR_HIP: return "the HIP runtime reported an error (device set-up or launch)";
+    case MAPL_ERR_TID: return "a token id is outside [0, V)";
     default: return "unknown status";
   }
 }
 
 const char* mapl_version(void) { return kVersion; }
+
+int mapl_init(void) {
+  (void)hipGetLastError();
+  return lds_prepare_device() == hipSuccess ? MAPL_OK : MAPL_ERR_HIP;
+}
 
 size_t mapl_pack_bytes(int64_t d, int64_t r, int64_t ra, mapl_dtype dt) {
   if (dt != MAPL_BF16 || check_codec_shape(1, 1, d, r, ra, 1, dt, false)) return 0;
@@ -102,6 +153,7 @@ int mapl_pack(const void* P, const void* A, void* pk, size_t pk_bytes, int64_t d
   if (!A || (ra > 0 && !P && ra != d)) return MAPL_ERR_NULL;
   if ((st = check_pack(pk, pk_bytes, d, r, ra, dt))) return st;
   LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
   PackView v = pack_view(pk, d, r, ra);
   launch_pack_all(static_cast<const uint16_t*>(P), static_cast<const uint16_t*>(A), v, int(d), int(r), int(ra),
                   stream);
@@ -132,6 +184,7 @@ int mapl_compress(const void* X, const int32_t* tids, const void* E_small, const
   if (!X || !A || !Z || !anchor_ptrs_ok(ra, d, tids, E_small, P)) return MAPL_ERR_NULL;
   if ((st = check_pack(pk, pk_bytes, d, r, ra, dt))) return st;
   LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
   if (dt == MAPL_F32) {
     launch_compress_f32(static_cast<const float*>(X), tids, static_cast<const float*>(E_small),
                         static_cast<const float*>(P), static_cast<const float*>(A), static_cast<float*>(Z), N, int(d),
@@ -159,6 +212,7 @@ int mapl_reconstruct(const void* Z, const int32_t* tids, const void* E_small, co
   if (!Z || !A || !Xhat || !anchor_ptrs_ok(ra, d, tids, E_small, P)) return MAPL_ERR_NULL;
   if ((st = check_pack(pk, pk_bytes, d, r, ra, dt))) return st;
   LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
   if (dt == MAPL_F32) {
     launch_reconstruct_f32(static_cast<const float*>(Z), tids, static_cast<const float*>(E_small),
                            static_cast<const float*>(P), static_cast<const float*>(A), static_cast<float*>(Xhat), N,
@@ -199,6 +253,7 @@ int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A, void* 
   if (N == 0) {  // empty batch: gA = 0 (or unchanged when accumulating)
     if (accumulate) return MAPL_OK;
     LaunchScope ls0;
+    if (!ls0.ready()) return MAPL_ERR_HIP;
     launch_fill_f32(gA, d * r, 0.f, stream);
     return ls0.done();
   }
@@ -207,6 +262,7 @@ int mapl_reconstruct_bwd(const void* gXhat, const void* Z, const void* A, void* 
   const size_t need = bwd_ws_bytes(N, d, r, 0, dt);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return ws == nullptr ? MAPL_ERR_NULL : MAPL_ERR_WORKSPACE;
   LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
   if (dt == MAPL_F32) {
     if (N > 0)
       launch_rowmap_f32(static_cast<const float*>(gXhat), static_cast<const float*>(A), static_cast<float*>(gZ),
@@ -242,6 +298,7 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const 
   if (N == 0) {  // empty batch: gA = 0 (or unchanged when accumulating)
     if (accumulate) return MAPL_OK;
     LaunchScope ls0;
+    if (!ls0.ready()) return MAPL_ERR_HIP;
     launch_fill_f32(gA, d * r, 0.f, stream);
     return ls0.done();
   }
@@ -250,6 +307,7 @@ int mapl_compress_bwd(const void* gZ, const void* X, const int32_t* tids, const 
   const size_t need = bwd_ws_bytes(N, d, r, ra, dt);
   if (need > 0 && (ws == nullptr || ws_bytes < need)) return ws == nullptr ? MAPL_ERR_NULL : MAPL_ERR_WORKSPACE;
   LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
   if (dt == MAPL_F32) {
     float* R = static_cast<float*>(ws);
     if (N > 0) {
@@ -303,6 +361,7 @@ int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* g
   if (N == 0) {  // empty batch: gE = 0 (or unchanged when accumulating)
     if (accumulate) return MAPL_OK;
     LaunchScope ls0;
+    if (!ls0.ready()) return MAPL_ERR_HIP;
     launch_fill_f32(gE, V * ra, 0.f, stream);
     return ls0.done();
   }
@@ -312,6 +371,7 @@ int mapl_anchor_grad(const void* Y, const int32_t* tids, const void* P, float* g
   if (ws_bytes < anchor_grad_ws_bytes(N, ra, V)) return MAPL_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) & 15) return MAPL_ERR_ARG;
   LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
   const uint16_t* PF = nullptr;
   if (dt == MAPL_BF16 && P != nullptr) {
     PackView v = pack_view(pk, d, r, ra);
@@ -327,6 +387,7 @@ int mapl_check_tids(const int32_t* tids, int64_t N, int64_t V, int32_t* bad_coun
   if (!bad_count || (N > 0 && !tids)) return MAPL_ERR_NULL;
   if (N < 0 || N > INT32_MAX || V < 1 || V > INT32_MAX) return MAPL_ERR_SHAPE;
   LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
   launch_check_tids(tids, int(N), int(V), bad_count, stream);
   return ls.done();
 }
@@ -336,9 +397,12 @@ static int check_rvq_shape(int64_t N, int64_t r, int64_t G, int64_t K, int64_t R
   if (N < 0 || N > INT32_MAX || r < 1 || G < 1 || K < 1 || R < 1 || R > 64) return MAPL_ERR_SHAPE;
   if (r % G != 0 || K > 256) return MAPL_ERR_SHAPE;
   if (N * r > (int64_t(1) << 40)) return MAPL_ERR_SHAPE;
-  if (stride != 0 && stride < r * K) return MAPL_ERR_ARG;
+  // codebook rows move as 16-byte vectors: every round's book starts 16-byte aligned
+  if ((stride != 0 && stride < r * K) || stride % 4 != 0) return MAPL_ERR_ARG;
   return MAPL_OK;
 }
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 int rvq_encode(const void* Z, mapl_dtype z_dt, const float* C, int64_t C_round_stride, uint8_t* codes, int64_t N,
                int64_t r, int64_t G, int64_t K, int64_t R, hipStream_t stream) {
@@ -348,10 +412,10 @@ int rvq_encode(const void* Z, mapl_dtype z_dt, const float* C, int64_t C_round_s
   if (!Z || !C || !codes) return MAPL_ERR_NULL;
   const int64_t w = r / G;
   if (!(w == 2 || w == 4 || w == 8 || w == 16 || w == 32 || w == 64)) return MAPL_ERR_SHAPE;
-  if (K % 32 != 0 || K < 32) return MAPL_ERR_SHAPE;
-  if ((w * (K + 2) + K) * int64_t(sizeof(float)) > 65536) return MAPL_ERR_SHAPE;  // encode's LDS codebook
+  if (!aligned16(Z) || !aligned16(C)) return MAPL_ERR_ARG;
   if (N == 0) return MAPL_OK;
   LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
   launch_rvq_encode(Z, z_dt == MAPL_BF16, C, C_round_stride, codes, int(N), int(r), int(G), int(K), int(R), stream);
   return ls.done();
 }
@@ -362,8 +426,10 @@ int rvq_decode(const uint8_t* codes, const float* C, int64_t C_round_stride, voi
   if (st) return st;
   if (!dtype_ok(out_dt)) return MAPL_ERR_DTYPE;
   if (!codes || !C || !Zq) return MAPL_ERR_NULL;
+  if (!aligned16(C)) return MAPL_ERR_ARG;
   if (N == 0) return MAPL_OK;
   LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
   launch_rvq_decode(codes, C, C_round_stride, Zq, out_dt == MAPL_BF16, int(N), int(r), int(G), int(K), int(R),
                     stream);
   return ls.done();
@@ -375,6 +441,7 @@ int rvq_stream_apply(float* C, const int32_t* idx, const float* vals, int64_t n,
   if (!C || (n > 0 && (!idx || !vals))) return MAPL_ERR_NULL;
   if (n == 0) return MAPL_OK;
   LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
   launch_rvq_stream(C, idx, vals, int(n), int(r / G), R_c * G * K, stream);
   return ls.done();
 }
@@ -385,8 +452,8 @@ size_t spel_workspace_bytes(int64_t d, int64_t r) {
   return spel_ws_bytes(d, r);
 }
 
-int spel_step(float* A, const float* g, float* m, float alpha, float beta, int ns_iters, float* D_out, int64_t d,
-              int64_t r, void* ws, size_t ws_bytes, hipStream_t stream) {
+int spel_step(float* A, const float* g, float* m, float alpha, float beta, int ns_iters, float* D_out,
+              int32_t* status, int64_t d, int64_t r, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (d < 1 || r < 1 || r > d || r > 1024 || d % 32 || r % 32 || d > (1 << 24)) return MAPL_ERR_SHAPE;
   if (!A || !g || !m) return MAPL_ERR_NULL;
   if (!(beta >= 0.f && beta < 1.f) || !(alpha >= 0.f && alpha <= 0.7f) || ns_iters < 1 || ns_iters > 64)
@@ -398,8 +465,10 @@ int spel_step(float* A, const float* g, float* m, float alpha, float beta, int n
   if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(g) | reinterpret_cast<uintptr_t>(m) |
        reinterpret_cast<uintptr_t>(D_out) | reinterpret_cast<uintptr_t>(ws)) & 15)
     return MAPL_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(status) & 3) return MAPL_ERR_ARG;
   LaunchScope ls;
-  launch_spel(A, g, m, alpha, beta, ns_iters, D_out, int(d), int(r), ws, stream);
+  if (!ls.ready()) return MAPL_ERR_HIP;
+  launch_spel(A, g, m, alpha, beta, ns_iters, D_out, status, int(d), int(r), ws, stream);
   return ls.done();
 }
 
@@ -410,8 +479,8 @@ int spel_polar_express_coefficients(double ell, int steps, double* coef, double*
 }
 
 int spel_step_polar_express(float* A, const float* g, float* m, float alpha, float beta, int lmo_steps,
-                            int ret_steps, float ell, float* D_out, int64_t d, int64_t r, void* ws, size_t ws_bytes,
-                            hipStream_t stream) {
+                            int ret_steps, float ell, float* D_out, int32_t* status, int64_t d, int64_t r, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
   if (d < 1 || r < 1 || r > d || r > 1024 || d % 32 || r % 32 || d > (1 << 24)) return MAPL_ERR_SHAPE;
   if (!A || !g || !m) return MAPL_ERR_NULL;
   if (!(beta >= 0.f && beta < 1.f) || !(alpha >= 0.f && alpha <= 0.7f) || !(ell > 0.f && ell < 1.f) ||
@@ -423,6 +492,7 @@ int spel_step_polar_express(float* A, const float* g, float* m, float alpha, flo
   if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(g) | reinterpret_cast<uintptr_t>(m) |
        reinterpret_cast<uintptr_t>(D_out) | reinterpret_cast<uintptr_t>(ws)) & 15)
     return MAPL_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(status) & 3) return MAPL_ERR_ARG;
   // the schedules, on the host, rounded once to fp32 for the kernels
   double cl[3 * kMaxPolarSteps], cr[3 * kMaxPolarSteps];
   if (polar_express_schedule(ell, lmo_steps, cl, nullptr) || polar_express_schedule(ell, ret_steps, cr, nullptr))
@@ -431,7 +501,8 @@ int spel_step_polar_express(float* A, const float* g, float* m, float alpha, flo
   for (int i = 0; i < 3 * lmo_steps; ++i) fl[i] = float(cl[i]);
   for (int i = 0; i < 3 * ret_steps; ++i) fr[i] = float(cr[i]);
   LaunchScope ls;
-  launch_spel_pe(A, g, m, alpha, beta, fl, lmo_steps, fr, ret_steps, D_out, int(d), int(r), ws, stream);
+  if (!ls.ready()) return MAPL_ERR_HIP;
+  launch_spel_pe(A, g, m, alpha, beta, fl, lmo_steps, fr, ret_steps, D_out, status, int(d), int(r), ws, stream);
   return ls.done();
 }
 

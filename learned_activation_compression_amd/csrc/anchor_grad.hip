@@ -40,6 +40,11 @@ static_assert(kOwnQueue >= kOwnChunk, "a chunk must fit in an empty queue");
 constexpr int kOwnBatch = 32;       // queued tokens whose U loads one wave keeps in flight
 constexpr int kOwnBatchQ = 16;      // the same in 16-byte loads (4 tokens per wave instruction)
 
+// running max |x| that lets a non-finite value through: NaN counts as +inf
+// (fmaxf alone would drop it), so a non-finite projection reaches the owner
+// kernel's scale, which then marks the whole table NaN
+__device__ __forceinline__ float absmax_nf(float m, float x) { return fmaxf(m, x == x ? fabsf(x) : __builtin_inff()); }
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
   return v;
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(256) void k_ag_project_bf16(const bf16_t* __restric
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           v[e] = alpha * acc[4 * q + e];
-          local = fmaxf(local, fabsf(v[e]));
+          local = absmax_nf(local, v[e]);
         }
         *reinterpret_cast<f32x4*>(ur + 8 * q) = v;
       }
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(256) void k_ag_project_f32(const float* __restrict_
     for (int k = 0; k < d; ++k) s = fmaf(yr[k], pr[k], s);
     const float v = alpha * s;
     U[e] = v;
-    local = fmaxf(local, fabsf(v));
+    local = absmax_nf(local, v);
   }
   const float m = block_max<4>(local, red);
   if (threadIdx.x == 0) part[blockIdx.x] = m;
@@ -154,7 +159,7 @@ __global__ __launch_bounds__(256) void k_ag_identity(const void* __restrict__ Yv
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) local = fmaxf(local, fabsf(v[h][e]));
+        for (int e = 0; e < 4; ++e) local = absmax_nf(local, v[h][e]);
         reinterpret_cast<f32x4*>(U)[2 * u + h] = v[h];
       }
     }
@@ -163,7 +168,7 @@ __global__ __launch_bounds__(256) void k_ag_identity(const void* __restrict__ Yv
     for (int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x; e < ne; e += step) {
       const float v = alpha * Y[e];
       U[e] = v;
-      local = fmaxf(local, fabsf(v));
+      local = absmax_nf(local, v);
     }
   }
   const float m = block_max<4>(local, red);
@@ -229,6 +234,18 @@ __global__ __launch_bounds__(kOwnThreads, 2) void k_ag_own(const float* __restri
   for (int i = threadIdx.x; i < kOwnVR * 64; i += kOwnThreads) acc[i] = 0ull;
   if (threadIdx.x == 0) q_count = 0;
   m = block_max<NW>(m, red);  // its barriers also publish the zeroed table and count
+  if (!(m < __builtin_inff())) {
+    // a projected value is not finite (Y overflowed or holds NaN): no fixed-point scale
+    // exists, and every row of the table becomes NaN rather than a silently wrong number
+    if (!colok) return;
+    const float nan = __builtin_nanf("");
+    for (int sl = w; sl < kOwnVR; sl += NW) {
+      const int64_t v = int64_t(sl) * B + b;
+      if (v >= V) break;
+      gE[size_t(v) * r + col] = nan;
+    }
+    return;
+  }
   const int ex = fixed_exponent(m);
 
   // QUAD (r % 4 == 0): lane = (entry g = lane >> 4, columns 4 (lane & 15) + 0..3);

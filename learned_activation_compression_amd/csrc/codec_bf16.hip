@@ -327,7 +327,7 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             v[e] = alpha * acc[tb][i][4 * q + e];
-            local = fmaxf(local, fabsf(v[e]));
+            local = fmaxf(local, v[e] == v[e] ? fabsf(v[e]) : __builtin_inff());  // NaN counts as +inf
           }
           *reinterpret_cast<f32x4*>(row + 8 * q) = v;
         }
@@ -357,9 +357,7 @@ static void launch_reduce_dma(const uint16_t* in, const uint16_t* AtF, const int
                               const uint16_t* QnF, uint16_t* out, int N, int d, int r, int ra, int V, hipStream_t s,
                               float* Uf = nullptr, float alpha = 1.f, float* part = nullptr, KernelEvents ev = {}) {
   auto k = k_tok_reduce_dma<RBW, S, G, ANCHOR, OUTF>;
-  const size_t lds = RedRing<RBW, S>::BYTES;
-  static std::atomic<uint64_t> attr{0};  // devices with the raised LDS limit
-  allow_lds(reinterpret_cast<const void*>(k), int(lds), attr);
+  const int lds = LdsLimit<k_tok_reduce_dma<RBW, S, G, ANCHOR, OUTF>, int(RedRing<RBW, S>::BYTES)>::bytes();
   launch_k(ev, k, dim3((N + 63) / 64), dim3(256 * G), uint32_t(lds), s, in, AtF, tids, E, QnF, out, N, d, r, ra, V,
            Uf, alpha, part);
 }

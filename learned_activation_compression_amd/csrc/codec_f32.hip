@@ -125,8 +125,7 @@ __global__ __launch_bounds__(256) void k_reconstruct_f32(const float* __restrict
 void launch_reconstruct_f32(const float* Z, const int32_t* tids, const float* E, const float* P, const float* A,
                             float* Xh, int N, int d, int r, int ra, int V, hipStream_t s) {
   const size_t lds = size_t(kTokPerBlock) * (r + ra) * sizeof(float);  // <= 128 KB (r, ra <= d <= 4096)
-  static std::atomic<uint64_t> attr{0};  // devices with the raised LDS limit
-  allow_lds(reinterpret_cast<const void*>(k_reconstruct_f32), int(kTokPerBlock * 2 * 4096 * sizeof(float)), attr);
+  (void)LdsLimit<k_reconstruct_f32, int(kTokPerBlock * 2 * 4096 * sizeof(float))>::bytes();  // the largest launch
   hipLaunchKernelGGL(k_reconstruct_f32, dim3((N + kTokPerBlock - 1) / kTokPerBlock), dim3(256), lds, s, Z, tids, E,
                      P, A, Xh, N, d, r, ra, V);
 }

@@ -243,9 +243,7 @@ template <int TC, int TT, int S, bool ANCHOR, bool EADD = false>
 void launch_gemm(const uint16_t* src, int K1, const int32_t* tids, int V, const uint16_t* E, int K2,
                  const uint16_t* F1, const uint16_t* F2, uint16_t* out, int N, int C, hipStream_t s) {
   auto k = k_tok_gemm<TC, TT, S, ANCHOR, EADD>;
-  const size_t lds = GemmRing<TC, TT, S>::BYTES;
-  static std::atomic<uint64_t> attr{0};  // devices with the raised LDS limit
-  allow_lds(reinterpret_cast<const void*>(k), int(lds), attr);
+  const int lds = LdsLimit<k_tok_gemm<TC, TT, S, ANCHOR, EADD>, int(GemmRing<TC, TT, S>::BYTES)>::bytes();
   const int ntc = C / TC, ntt = (N + TT - 1) / TT;
   hipLaunchKernelGGL(k, dim3(unsigned(ntc * ntt)), dim3(256), lds, s, src, K1, tids, V, E, K2, F1, F2, out, N, C, ntc);
 }

@@ -117,20 +117,29 @@ inline void launch_k(KernelEvents ev, void (*k)(Formals...), dim3 grid, dim3 blo
     hipLaunchKernelGGL(k, grid, block, lds, s, Formals(a)...);
 }
 
-// Host side: raise a kernel's dynamic-LDS limit above 64 KB on the current
-// device, once per device (bit `dev` of `done`); threads that race both set
-// the same value.
-inline void allow_lds(const void* kernel, int bytes, std::atomic<uint64_t>& done) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
-    (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    return;
-  }
-  const uint64_t bit = uint64_t(1) << dev;
-  if (done.load(std::memory_order_acquire) & bit) return;
-  (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  done.fetch_or(bit, std::memory_order_acq_rel);
-}
+// LDS of one gfx950 workgroup (static plus dynamic).
+constexpr int kMaxLdsBytes = 160 * 1024;
 
+// Host side: kernels launched with more dynamic LDS than the default 64 KB
+// limit.  LdsLimit<kernel, BYTES>::bytes() (used at the launch site) fails to
+// compile for more than a workgroup can have, and registers the kernel at
+// library load; lds_prepare_device() (abi.hip) raises the limit of every
+// registered kernel on the current device once, before an entry point's first
+// launch, so a refusal by the runtime is reported before anything is enqueued.
+void lds_register(const void* kernel, int bytes);
+hipError_t lds_prepare_device();
+
+template <auto K, int BYTES>
+struct LdsLimit {
+  static_assert(BYTES > 0 && BYTES <= kMaxLdsBytes, "dynamic LDS above what a gfx950 workgroup has");
+  struct Reg {
+    Reg() { lds_register(reinterpret_cast<const void*>(K), BYTES); }
+  };
+  static inline Reg reg;
+  static int bytes() {
+    (void)&reg;
+    return BYTES;
+  }
+};
 
 }  // namespace mapl

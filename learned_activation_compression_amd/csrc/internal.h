@@ -109,9 +109,12 @@ size_t spel_ws_bytes(int64_t d, int64_t r);
 // err [steps] or nullptr; returns 0, or -1 if a step is not finite), and the SPEL step
 // that uses it for both polar maps (fp32 coefficients [steps][3])
 int polar_express_schedule(double ell, int steps, double* coef, double* err);
+// status (device int, optional): 0 when the step was committed, 1 when a wait
+// between workgroups timed out and A and m were left as they were
 void launch_spel_pe(float* A, const float* g, float* m, float alpha, float beta, const float* coef_lmo, int lmo_steps,
-                    const float* coef_ret, int ret_steps, float* D_out, int d, int r, void* ws, hipStream_t s);
+                    const float* coef_ret, int ret_steps, float* D_out, int* status, int d, int r, void* ws,
+                    hipStream_t s);
 void launch_spel(float* A, const float* g, float* m, float alpha, float beta, int ns_iters,
-                 float* D_out, int d, int r, void* ws, hipStream_t s);
+                 float* D_out, int* status, int d, int r, void* ws, hipStream_t s);
 
 }  // namespace mapl

@@ -6,80 +6,164 @@
 // Appendix F (streamed codebook sync: the receiver overwrites the codewords
 // the sender streams).
 //
-// Encode (w < 16; wider groups use the bf16-scored kernel further down): one
-// block owns one group g and 256 tokens, one 32-token tile per wave (8 waves,
-// two per SIMD, so that one wave's argmin overlaps the other's matrix-core
-// work).  The round's codebook for g sits in LDS transposed
-// ([dim][codeword]) with its squared norms.  Lane half h holds dims
-// [h W/2, (h+1) W/2) of token l & 31, pre-scaled by -2, and 32 codewords at a
-// time are scored with v_mfma_f32_32x32x2_f32 on an accumulator that starts
-// at the codewords' squared norms: score_k = ||c_k||^2 - 2 <res, c_k>.
-// Candidates are visited in increasing k within a lane and merged with the
-// partner half-wave preferring the lower index, so exact ties resolve to the
-// lowest codeword index; NaN scores never compare smaller.
+// Encode.  For every token, round and group the code is the exact argmin over
+// k of ||res - c_k||^2 (lowest k on exact ties; a NaN distance never wins).
+// The residual res is kept in fp64: it starts as the stored Z and each round
+// subtracts the chosen fp32 codeword, which for inputs of ordinary range is
+// exact, so the codes are those of exact arithmetic.  Each kernel first scores
+// all K codewords on the matrix cores, a_k ~ s_k = ||c_k||^2 - 2 <res, c_k>
+// (s_k orders the codewords as the distance does), with a proven bound
+// |a_k - s_k| <= delta.  The exact argmin k* then has
+//   a_k* <= s_k* + delta <= s_j + delta <= a_j + 2 delta   for every j,
+// so it is among the codewords with a_k <= min_j a_j + 2 delta; those few get
+// their exact distance sum_j (res_j - c_kj)^2 in fp64, and the smallest wins.
+//
+// Layout of both kernels: one block owns one group g and 256 tokens, one
+// 32-token tile per wave (8 waves, two per SIMD, so that one wave's vector
+// work overlaps the other's matrix-core work).  Lane half h of a wave holds
+// dims [h W/2, (h+1) W/2) of token l & 31; in the 32 x 32 score tile of a
+// block of 32 codewords, lane l holds that token's scores for the codewords
+// 32 b + mfma32_row(v, h), v < 16.  K is padded to Kp = 32 ceil(K / 32) with
+// codewords that can never win (norm +inf).
 #include "common.h"
 #include "internal.h"
 
 namespace mapl {
 
 constexpr int kRvqWaves = 8;  // 32-token tiles per block, one per wave
+constexpr int kRvqMaxK = 256;
 
+// The H dims of the token's residual that lane half h holds (columns
+// col .. col + H - 1 of row n), widened exactly to fp64; zero past N.
+template <int H, typename ZT>
+__device__ __forceinline__ void rvq_load_res(const ZT* __restrict__ Z, int n, int N, int r, int col,
+                                             double (&res)[H]) {
+  const ZT* zr = Z + size_t(min(n, N - 1)) * r + col;
+  if (sizeof(ZT) == 2 && H % 8 == 0) {  // bf16: 16-byte loads of 8 values
+#pragma unroll
+    for (int s = 0; s < H; s += 8) {
+      const u32x4 u = *reinterpret_cast<const u32x4*>(zr + s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        res[s + 2 * e] = double(__uint_as_float(u[e] << 16));
+        res[s + 2 * e + 1] = double(__uint_as_float(u[e] & 0xffff0000u));
+      }
+    }
+  } else if (sizeof(ZT) == 4 && H % 4 == 0) {  // fp32: 16-byte loads of 4 values
+#pragma unroll
+    for (int s = 0; s < H; s += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(zr + s);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) res[s + e] = double(to_f32<float>(v[e]));
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < H; ++s) res[s] = double(to_f32<ZT>(zr[s]));
+  }
+  if (n >= N) {
+#pragma unroll
+    for (int s = 0; s < H; ++s) res[s] = 0.0;
+  }
+}
+
+// ||res||^2 of the whole token (both halves), rounded to fp32.
+template <int H>
+__device__ __forceinline__ float rvq_norm2(const double (&res)[H]) {
+  double s2 = 0.0;
+#pragma unroll
+  for (int s = 0; s < H; ++s) s2 = fma(res[s], res[s], s2);
+  const float f = float(s2);
+  return f + __shfl_xor(f, 32);
+}
+
+// Exact fp64 rescoring of one token's candidates.  mine[] holds this lane's
+// candidate bits: bit 16 (b & 1) + v of word b >> 1 marks codeword
+// 32 b + mfma32_row(v, h).  The partner lane (same token, other half) holds
+// its own bits.  Both lanes walk the union in the same order, each computes
+// the squared distance over its H dims (part(k), fp64), and the two halves are
+// added (fp addition commutes, so both lanes get the same value).  Exact ties
+// keep the lower index; codewords past K (padding) are skipped; NaN never
+// wins.  With no candidate (all scores NaN) the code is 0.
+template <typename PartFn>
+__device__ __forceinline__ int rvq_rescore(const uint32_t (&mine)[4], int h, int K, PartFn part) {
+  uint32_t m0[4], m1[4];  // candidates of half 0 and of half 1
+#pragma unroll
+  for (int wd = 0; wd < 4; ++wd) {
+    const uint32_t o = __shfl_xor(mine[wd], 32);
+    m0[wd] = h == 0 ? mine[wd] : o;
+    m1[wd] = h == 0 ? o : mine[wd];
+  }
+  double best = __builtin_inf();
+  int bk = 0;
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      uint32_t m = hh == 0 ? m0[wd] : m1[wd];
+      while (__any(m != 0u)) {
+        if (m != 0u) {  // the same in both lanes of the token, so both take the exchange below
+          const int bit = __builtin_ctz(m);
+          m &= m - 1u;
+          const int k = 64 * wd + 32 * (bit >> 4) + mfma32_row(bit & 15, hh);
+          const double p = part(k);
+          const double dk = p + __shfl_xor(p, 32);
+          if (k < K && (dk < best || (dk == best && k < bk))) {
+            best = dk;
+            bk = k;
+          }
+        }
+      }
+    }
+  return bk;
+}
+
+// ------------------------------------------------- encode, fp32-scored (w < 16) --
+// The round's codebook for g sits in LDS transposed ([dim][codeword], row
+// pitch Kp + 2 so that the two lane halves read rows H apart in other banks)
+// with its squared norms.  Scores come from v_mfma_f32_32x32x2_f32 on an
+// accumulator that starts at ||c_k||^2, with -2 res (rounded to fp32) as the
+// other operand.  Bound: nrm_k carries at most W roundings of ||c_k||^2,
+// -2 res one rounding of 2 |res|, and the accumulator at most W + 1 roundings
+// of sums no larger than ||c_k||^2 + 2 ||res|| ||c_k|| (one per product and
+// per addition, whatever the hardware fuses), so with u = 2^-24
+//   |a_k - s_k| <= (2 W + 4) u (||c_k||^2 + 2 ||res|| ||c_k||) (1 + small);
+// delta is twice that, with max_k ||c_k|| for ||c_k||, plus 1e-30 for
+// underflow.  One pass keeps, per lane, the smallest score, its codeword and
+// the second smallest (v_med3); after the halves are merged, a token whose
+// second score is more than 2 delta above its best has that codeword as its
+// exact argmin (every other s_j > s_best).  Only tokens without that margin
+// (a few in a thousand) take a second pass that marks every codeword within
+// 2 delta and rescores them exactly.
 template <int W, typename ZT>
 __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode(const ZT* __restrict__ Z, const float* __restrict__ C,
                                                                int64_t stride, uint8_t* __restrict__ codes, int N,
                                                                int r, int G, int K, int R) {
   constexpr int H = W / 2;  // dims per lane (k steps of the 32x32x2 MFMA)
   extern __shared__ __attribute__((aligned(16))) float sh[];
-  const int P = K + 2;       // row pitch: the two lane halves read rows H apart in other banks
-  float* cbT = sh;           // [W][P]
-  float* nrm = sh + W * P;   // [K]
+  const int Kp = (K + 31) & ~31;
+  const int P = Kp + 2;        // row pitch
+  float* cbT = sh;             // [W][P]
+  float* nrm = sh + W * P;     // [Kp], +inf past K
+  float* bnd = nrm + Kp;       // [1]: max ||c_k||^2 over k < K
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
   const int g = blockIdx.x;
   const int n = blockIdx.y * (kRvqWaves * 32) + wave * 32 + l32;
+  const float inf = __builtin_inff();
 
-  float res[H];
-  {
-    const ZT* zr = Z + size_t(min(n, N - 1)) * r + g * W + h * H;
-    if (sizeof(ZT) == 2 && H % 8 == 0) {  // bf16: 16-byte loads of 8 values
-#pragma unroll
-      for (int s = 0; s < H; s += 8) {
-        const u32x4 u = *reinterpret_cast<const u32x4*>(zr + s);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          res[s + 2 * e] = __uint_as_float(u[e] << 16);
-          res[s + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
-        }
-      }
-    } else if (sizeof(ZT) == 4 && H % 4 == 0) {  // fp32: 16-byte loads of 4 values
-#pragma unroll
-      for (int s = 0; s < H; s += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(zr + s);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) res[s + e] = v[e];
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < H; ++s) res[s] = to_f32<ZT>(zr[s]);
-    }
-    if (n >= N) {
-#pragma unroll
-      for (int s = 0; s < H; ++s) res[s] = 0.f;
-    }
-  }
+  double res[H];
+  rvq_load_res<H, ZT>(Z, n, N, r, g * W + h * H, res);
 
   for (int rho = 0; rho < R; ++rho) {
     if (rho == 0 || stride != 0) {
       __syncthreads();
       const float* book = C + rho * stride + size_t(g) * K * W;
-      // coalesced reads of codeword k, written transposed
-      if (W % 4 == 0 && W <= 64) {
+      if (W % 4 == 0) {
         // 16 bytes (dims j0..j0+3) per thread; the W/4 threads of a codeword are
-        // consecutive lanes, whose partial squared norms are added by a
-        // fixed-order butterfly
-        for (int e = threadIdx.x; e < K * W / 4; e += 64 * kRvqWaves) {
+        // consecutive lanes, whose partial squared norms are added by a butterfly
+        for (int e = threadIdx.x; e < Kp * W / 4; e += 64 * kRvqWaves) {
           const int k = e / (W / 4), j0 = 4 * (e % (W / 4));
-          const f32x4 v = *reinterpret_cast<const f32x4*>(book + size_t(k) * W + j0);
+          const f32x4 v = k < K ? *reinterpret_cast<const f32x4*>(book + size_t(k) * W + j0) : f32x4{0.f, 0.f, 0.f, 0.f};
           float s2 = 0.f;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -88,26 +172,33 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode(const ZT* __restr
           }
 #pragma unroll
           for (int off = 1; off < W / 4; off <<= 1) s2 += __shfl_xor(s2, off);
-          if (j0 == 0) nrm[k] = s2;
+          if (j0 == 0) nrm[k] = k < K ? s2 : inf;
         }
-        __syncthreads();
-      } else {
-        for (int e = threadIdx.x; e < K * W; e += 64 * kRvqWaves) cbT[(e % W) * P + e / W] = book[e];
-        __syncthreads();
-        for (int k = threadIdx.x; k < K; k += 64 * kRvqWaves) {
-          float s2 = 0.f;
-#pragma unroll
-          for (int j = 0; j < W; ++j) s2 = fmaf(cbT[j * P + k], cbT[j * P + k], s2);
-          nrm[k] = s2;
+      } else {  // W == 2: one thread per codeword
+        for (int k = threadIdx.x; k < Kp; k += 64 * kRvqWaves) {
+          const float c0 = k < K ? book[2 * k] : 0.f, c1 = k < K ? book[2 * k + 1] : 0.f;
+          cbT[k] = c0;
+          cbT[P + k] = c1;
+          nrm[k] = k < K ? fmaf(c1, c1, c0 * c0) : inf;
         }
-        __syncthreads();
       }
+      __syncthreads();
+      if (wave == 0) {  // max ||c_k||^2 over the real codewords (a max: order does not matter; NaN drops out)
+        float mx = 0.f;
+        for (int k = lane; k < K; k += 64) mx = fmaxf(mx, nrm[k]);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        if (lane == 0) bnd[0] = mx;
+      }
+      __syncthreads();
     }
     float b[H];
 #pragma unroll
-    for (int s = 0; s < H; ++s) b[s] = -2.f * res[s];
-    float best = __builtin_inff();
-    int bk = 0;
+    for (int s = 0; s < H; ++s) b[s] = float(-2.0 * res[s]);
+    const float rn2 = rvq_norm2<H>(res);
+    const float nmax = bnd[0];
+    const float delta = float(2 * W + 4) * 0x1p-23f * fmaf(2.f * sqrtf(rn2), sqrtf(nmax), nmax) + 1e-30f;
+
     // accumulator row 8 q + 4 h + e (e < 4) starts at that codeword's squared norm
     auto init = [&](int kb) {
       f32x16 acc;
@@ -119,18 +210,28 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode(const ZT* __restr
       }
       return acc;
     };
+    auto score = [&](int kb) {
+      f32x16 acc = init(kb);
+#pragma unroll
+      for (int s = 0; s < H; ++s) acc = mfma_f32_32x32x2(cbT[(h * H + s) * P + kb + l32], b[s], acc);
+      return acc;
+    };
+    float best = inf, second = inf;
+    int bk = 0;
     auto pick = [&](const f32x16& acc, int kb) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        if (acc[v] < best) {
-          best = acc[v];
+        const float a = acc[v];
+        second = __builtin_amdgcn_fmed3f(best, second, a);  // second smallest so far
+        if (a < best) {
+          best = a;
           bk = kb + mfma32_row(v, h);
         }
       }
     };
     int kb = 0;
     // two blocks of 32 codewords at a time: two independent accumulator chains
-    for (; kb + 64 <= K; kb += 64) {
+    for (; kb + 64 <= Kp; kb += 64) {
       f32x16 acc0 = init(kb), acc1 = init(kb + 32);
       float a0[H], a1[H];
 #pragma unroll
@@ -147,50 +248,67 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode(const ZT* __restr
       pick(acc0, kb);
       pick(acc1, kb + 32);
     }
-    if (kb < K) {  // K % 64 == 32: the last 32 codewords
-      f32x16 acc = init(kb);
-#pragma unroll
-      for (int s = 0; s < H; ++s) acc = mfma_f32_32x32x2(cbT[(h * H + s) * P + kb + l32], b[s], acc);
-      pick(acc, kb);
+    if (kb < Kp) pick(score(kb), kb);  // Kp % 64 == 32: the last 32 codewords
+    {  // merge the halves: best (lower index on ties) and the token's second smallest score
+      const float ob = __shfl_xor(best, 32), os = __shfl_xor(second, 32);
+      const int ok = __shfl_xor(bk, 32);
+      second = fminf(fmaxf(best, ob), fminf(second, os));
+      if (ob < best || (ob == best && ok < bk)) {
+        best = ob;
+        bk = ok;
+      }
     }
-    const float ob = __shfl_xor(best, 32);
-    const int ok = __shfl_xor(bk, 32);
-    if (ob < best || (ob == best && ok < bk)) {
-      best = ob;
-      bk = ok;
+    const bool need = !(second - best > 2.f * delta);  // no proven margin (NaN included)
+    if (__any(need)) {
+      const float lim = need ? fmaf(2.f, delta, best) : __builtin_nanf("");
+      uint32_t mask[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int bb = 0; bb < kRvqMaxK / 32; ++bb) {
+        if (32 * bb < Kp) {
+          const f32x16 acc = score(32 * bb);
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            if (acc[v] <= lim) mask[bb >> 1] |= 1u << (16 * (bb & 1) + v);
+        }
+      }
+      const int rk = rvq_rescore(mask, h, K, [&](int k) {
+        double p = 0.0;
+#pragma unroll
+        for (int s = 0; s < H; ++s) {
+          const double dd = res[s] - double(cbT[(h * H + s) * P + k]);
+          p = fma(dd, dd, p);
+        }
+        return p;
+      });
+      if (need) bk = rk;
     }
     if (h == 0 && n < N) codes[(size_t(n) * R + rho) * G + g] = uint8_t(bk);
 #pragma unroll
-    for (int s = 0; s < H; ++s) res[s] -= cbT[(h * H + s) * P + bk];
+    for (int s = 0; s < H; ++s) res[s] -= double(cbT[(h * H + s) * P + bk]);
   }
 }
 
 // ---------------------------------------------- encode, bf16-scored (w >= 16) --
-// The same argmin, with the scan over the K codewords on bf16 matrix cores
-// and an exact fp32 check of the few codewords that can still win.  For token
-// n the bf16 score of codeword k is
+// The scan over the K codewords runs on bf16 matrix cores.  For token n the
+// bf16 score of codeword k is
 //   a_k = <bf16(-2 res), bf16(c_k)> + hi_k + lo_k    (products exact, fp32 sums)
 // with hi_k + lo_k the two-part bf16 split of ||c_k||^2 (fed to the matrix
 // core as two more dimensions against a constant 1).  Each bf16 rounding is a
-// relative 2^-9 at most, so against the exact s_k = ||c_k||^2 - 2 <res, c_k>
-//   |a_k - s_k| <= 2^-7 (1 + 2^-9) ||res|| ||c_k|| + 2^-17 ||c_k||^2 + (fp32 sums)
+// relative 2^-9 at most (2^-9 + 2^-24 for -2 res, rounded from fp64 through
+// fp32), so against the exact s_k = ||c_k||^2 - 2 <res, c_k>
+//   |a_k - s_k| <= 2^-7 (1 + 2^-8) ||res|| ||c_k|| + 2^-17 ||c_k||^2 + (fp32 sums)
 // (Cauchy-Schwarz); taken twice over and uniformly in k,
 //   delta = 2^-6 ||res|| max_k ||c_k|| + 2^-14 max_k ||c_k||^2 + 1e-30.
-// The exact argmin k* has a_k* <= s_k* + delta <= s_j + delta <= a_j + 2 delta
-// for every j, so it is among the codewords with a_k <= min_j a_j + 2 delta;
-// those are rescored exactly in fp32 (dims in order, one fused multiply-add
-// each, as fma(-2, <res, c_k>, ||c_k||^2)) and the best of them is the code:
-// the fp32 argmin over all K, from a handful of exact scores per token.  NaN
-// scores pass no test and never win; exact ties go to the lowest k.
+// A first scan finds min_j a_j, a second (the same instructions, so the same
+// a_k) marks every codeword with a_k <= min_j a_j + 2 delta in a 128-bit mask
+// per lane, and those are rescored exactly in fp64 (rvq_rescore): about 1.3
+// codewords per token at the step's workload.
 //
-// Layout as in k_rvq_encode (one block: group g, 256 tokens, a 32-token tile
-// per wave; lane half h holds dims [h W/2, (h+1) W/2) of token l & 31).  The
-// bf16 MFMA takes 8 dims per lane per K-step: at step t < W/16 lane half h
-// supplies dims h W/2 + 8 t .. + 7 of codeword and residual alike; step W/16
-// carries (hi_k, lo_k) against (1, 1) in half 0 and zeros in half 1.  The two
-// scans (minimum, then candidates) are the same instructions, so a_k is the
-// same in both; candidates are kept as a 128-bit mask per lane (16 rows of
-// each of the K/32 codeword blocks).
+// The bf16 MFMA takes 8 dims per lane per K-step: at step t < W/16 lane half
+// h supplies dims h W/2 + 8 t .. + 7 of codeword and residual alike; step
+// W/16 carries (hi_k, lo_k) against (1, 1) in half 0 and zeros in half 1.
+// Padding codewords (k >= K) have zero dims and hi = +inf, so their score is
+// +inf.
 template <int W, typename ZT>
 __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __restrict__ Z,
                                                                   const float* __restrict__ C, int64_t stride,
@@ -198,42 +316,19 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
                                                                   int K, int R) {
   constexpr int H = W / 2, T = W / 16, FP = W + 4, WB = W + 16;  // dims per lane, K-steps, fp32 / bf16 row pitch
   extern __shared__ __attribute__((aligned(16))) float sh[];
-  float* cbF = sh;              // [K][FP] fp32 codewords
-  float* nrm = cbF + 256 * FP;  // [K] ||c_k||^2
-  float* bnd = nrm + 256;       // [4]: max ||c_k||^2 (the block's reduction)
-  bf16_t* cbB = reinterpret_cast<bf16_t*>(bnd + 4);  // [K][WB] bf16 codewords, then hi_k, lo_k, zeros
+  float* cbF = sh;                   // [256][FP] fp32 codewords
+  float* nrm = cbF + kRvqMaxK * FP;  // [256] ||c_k||^2
+  float* bnd = nrm + kRvqMaxK;       // [4]: max ||c_k||^2 (the block's reduction)
+  bf16_t* cbB = reinterpret_cast<bf16_t*>(bnd + 4);  // [256][WB] bf16 codewords, then hi_k, lo_k, zeros
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
   const int g = blockIdx.x;
   const int n = blockIdx.y * (kRvqWaves * 32) + wave * 32 + l32;
-  const int nb = K / 32;
+  const int Kp = (K + 31) & ~31;
+  const int nb = Kp / 32;
 
-  float res[H];
-  {
-    const ZT* zr = Z + size_t(min(n, N - 1)) * r + g * W + h * H;
-    if (sizeof(ZT) == 2) {
-#pragma unroll
-      for (int s = 0; s < H; s += 8) {
-        const u32x4 u = *reinterpret_cast<const u32x4*>(zr + s);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          res[s + 2 * e] = __uint_as_float(u[e] << 16);
-          res[s + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int s = 0; s < H; s += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(zr + s);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) res[s + e] = to_f32<ZT>(v[e]);
-      }
-    }
-    if (n >= N) {
-#pragma unroll
-      for (int s = 0; s < H; ++s) res[s] = 0.f;
-    }
-  }
+  double res[H];
+  rvq_load_res<H, ZT>(Z, n, N, r, g * W + h * H, res);
 
   for (int rho = 0; rho < R; ++rho) {
     if (rho == 0 || stride != 0) {
@@ -241,17 +336,19 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
       const float* book = C + rho * stride + size_t(g) * K * W;
       // W/4 consecutive threads per codeword (16 bytes each); squared norm by a fixed-order butterfly.
       // Every load of the thread is issued before the first is used.
-      constexpr int UPT = (256 * W / 4 + 64 * kRvqWaves - 1) / (64 * kRvqWaves);  // units per thread at K = 256
+      constexpr int UPT = (kRvqMaxK * W / 4 + 64 * kRvqWaves - 1) / (64 * kRvqWaves);  // units per thread at K = 256
       f32x4 cv[UPT];
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
         const int e = threadIdx.x + u * 64 * kRvqWaves;
-        if (e < K * W / 4) cv[u] = *reinterpret_cast<const f32x4*>(book + size_t(e / (W / 4)) * W + 4 * (e % (W / 4)));
+        const int k = e / (W / 4);
+        cv[u] = (k < K) ? *reinterpret_cast<const f32x4*>(book + size_t(k) * W + 4 * (e % (W / 4)))
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
         const int e = threadIdx.x + u * 64 * kRvqWaves;
-        if (e >= K * W / 4) continue;  // uniform over a codeword's W/4 threads
+        if (e >= Kp * W / 4) continue;  // uniform over a codeword's W/4 threads
         const int k = e / (W / 4), j0 = 4 * (e % (W / 4));
         const f32x4 v = cv[u];
         *reinterpret_cast<f32x4*>(cbF + k * FP + j0) = v;
@@ -263,14 +360,14 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
         for (int off = 1; off < W / 4; off <<= 1) s2 += __shfl_xor(s2, off);
         if (j0 == 0) {
           nrm[k] = s2;
-          const float hi = bf2f(f2bf(s2));
-          const u32x4 z4 = u32x4{pack2bf(hi, s2 - hi), 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(cbB + k * WB + W) = z4;
+          const float hi = k < K ? bf2f(f2bf(s2)) : __builtin_inff();
+          const float lo = k < K ? s2 - hi : 0.f;
+          *reinterpret_cast<u32x4*>(cbB + k * WB + W) = u32x4{pack2bf(hi, lo), 0u, 0u, 0u};
           *reinterpret_cast<u32x4*>(cbB + k * WB + W + 8) = u32x4{0u, 0u, 0u, 0u};
         }
       }
       __syncthreads();
-      if (wave == 0) {  // max ||c_k||^2 (a max: order does not matter; NaN drops out)
+      if (wave == 0) {  // max ||c_k||^2 over the real codewords (a max: order does not matter; NaN drops out)
         float mx = 0.f;
         for (int k = lane; k < K; k += 64) mx = fmaxf(mx, nrm[k]);
 #pragma unroll
@@ -280,23 +377,18 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
       __syncthreads();
     }
     // the residual's bf16 operand (pre-scaled by -2; the norm step's (1, 1) in half 0),
-    // its norm, the partner half's dims and the per-token bound
+    // its norm and the per-token bound
     bf16x8 bB[T + 1];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       u32x4 u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = pack2bf(-2.f * res[8 * t + 2 * e], -2.f * res[8 * t + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e)
+        u[e] = pack2bf(float(-2.0 * res[8 * t + 2 * e]), float(-2.0 * res[8 * t + 2 * e + 1]));
       bB[t] = __builtin_bit_cast(bf16x8, u);
     }
     bB[T] = __builtin_bit_cast(bf16x8, u32x4{h == 0 ? pack2bf(1.f, 1.f) : 0u, 0u, 0u, 0u});
-    float rn2 = 0.f, pres[H];
-#pragma unroll
-    for (int s = 0; s < H; ++s) {
-      rn2 = fmaf(res[s], res[s], rn2);
-      pres[s] = __shfl_xor(res[s], 32);
-    }
-    rn2 += __shfl_xor(rn2, 32);
+    const float rn2 = rvq_norm2<H>(res);
     const float nmax = bnd[0];
     const float delta = fmaf(0x1p-6f * sqrtf(rn2), sqrtf(nmax), fmaf(0x1p-14f, nmax, 1e-30f));
 
@@ -311,7 +403,7 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
     // scan 1: the smallest bf16 score (NaN drops out of fminf)
     float amin = __builtin_inff();
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < kRvqMaxK / 32; ++b) {
       if (b < nb) {
         const f32x16 acc = scan(b);
 #pragma unroll
@@ -323,7 +415,7 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
     // scan 2: candidate mask, bit 16 (b & 1) + v of word b >> 1
     uint32_t mask[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int b = 0; b < kRvqMaxK / 32; ++b) {
       if (b < nb) {
         const f32x16 acc = scan(b);
 #pragma unroll
@@ -331,54 +423,38 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
           if (acc[v] <= lim) mask[b >> 1] |= 1u << (16 * (b & 1) + v);
       }
     }
-    // exact fp32 scores of the candidates, in increasing k
-    float best = __builtin_inff();
-    int bk = 0;
+    const int bk = rvq_rescore(mask, h, K, [&](int k) {
+      const float* ck = cbF + k * FP + h * H;
+      double p = 0.0;
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      uint32_t m = mask[wd];
-      while (__any(m != 0u)) {
-        if (m != 0u) {
-          const int bit = __builtin_ctz(m);
-          m &= m - 1u;
-          const int k = 64 * wd + 32 * (bit >> 4) + mfma32_row(bit & 15, h);
-          const float* ck = cbF + k * FP;
-          float dot = 0.f;
+      for (int s = 0; s < H; s += 4) {
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(ck + s);
 #pragma unroll
-          for (int j = 0; j < W; j += 4) {
-            const f32x4 c4 = *reinterpret_cast<const f32x4*>(ck + j);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int jj = j + e;  // dim jj: lane half jj / H holds it, at jj % H
-              const float rv = ((jj < H) == (h == 0)) ? res[jj % H] : pres[jj % H];
-              dot = fmaf(c4[e], rv, dot);
-            }
-          }
-          const float sc = fmaf(-2.f, dot, nrm[k]);
-          if (sc < best || (sc == best && k < bk)) {
-            best = sc;
-            bk = k;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const double dd = res[s + e] - double(c4[e]);
+          p = fma(dd, dd, p);
         }
       }
-    }
-    const float ob = __shfl_xor(best, 32);
-    const int ok = __shfl_xor(bk, 32);
-    if (ob < best || (ob == best && ok < bk)) {
-      best = ob;
-      bk = ok;
-    }
+      return p;
+    });
     if (h == 0 && n < N) codes[(size_t(n) * R + rho) * G + g] = uint8_t(bk);
 #pragma unroll
-    for (int s = 0; s < H; ++s) res[s] -= cbF[bk * FP + h * H + s];
+    for (int s = 0; s < H; ++s) res[s] -= double(cbF[bk * FP + h * H + s]);
   }
 }
 
 // LDS of the bf16-scored encode: fp32 codewords [256][W+4], norms [256], bound [4], bf16 rows [256][W+16]
 template <int W>
 constexpr size_t rvq_bf_lds() {
-  return (size_t(256) * (W + 4) + 256 + 4) * sizeof(float) + size_t(256) * (W + 16) * sizeof(bf16_t);
+  return (size_t(kRvqMaxK) * (W + 4) + kRvqMaxK + 4) * sizeof(float) + size_t(kRvqMaxK) * (W + 16) * sizeof(bf16_t);
 }
+// LDS of the fp32-scored encode: transposed codebook [W][Kp+2], norms [Kp], bound
+inline size_t rvq_f32_lds(int W, int K) {
+  const int Kp = (K + 31) & ~31;
+  return (size_t(W) * (Kp + 2) + Kp + 4) * sizeof(float);
+}
+static_assert(rvq_bf_lds<64>() <= size_t(kMaxLdsBytes), "bf16-scored encode LDS");
+static_assert((8 * (kRvqMaxK + 2) + kRvqMaxK + 4) * sizeof(float) <= 65536, "fp32-scored encode LDS");
 
 template <int W>
 static void rvq_encode_w(const void* Z, int z_bf16, const float* C, int64_t stride, uint8_t* codes, int N, int r,
@@ -386,19 +462,17 @@ static void rvq_encode_w(const void* Z, int z_bf16, const float* C, int64_t stri
   const int tpb = kRvqWaves * 32;
   dim3 grid(G, (N + tpb - 1) / tpb);
   if constexpr (W >= 16) {
-    constexpr int lds = int(rvq_bf_lds<W>());
-    static std::atomic<uint64_t> done16{0}, done32{0};
     if (z_bf16) {
-      if (lds > 65536) allow_lds(reinterpret_cast<const void*>(k_rvq_encode_bf<W, bf16_t>), lds, done16);
+      const int lds = LdsLimit<k_rvq_encode_bf<W, bf16_t>, int(rvq_bf_lds<W>())>::bytes();
       hipLaunchKernelGGL((k_rvq_encode_bf<W, bf16_t>), grid, dim3(64 * kRvqWaves), lds, s,
                          static_cast<const bf16_t*>(Z), C, stride, codes, N, r, G, K, R);
     } else {
-      if (lds > 65536) allow_lds(reinterpret_cast<const void*>(k_rvq_encode_bf<W, float>), lds, done32);
+      const int lds = LdsLimit<k_rvq_encode_bf<W, float>, int(rvq_bf_lds<W>())>::bytes();
       hipLaunchKernelGGL((k_rvq_encode_bf<W, float>), grid, dim3(64 * kRvqWaves), lds, s, static_cast<const float*>(Z),
                          C, stride, codes, N, r, G, K, R);
     }
   } else {  // w < 16: fp32 scores on the matrix cores
-    const size_t lds = (size_t(W) * (K + 2) + K) * sizeof(float);
+    const size_t lds = rvq_f32_lds(W, K);
     if (z_bf16)
       hipLaunchKernelGGL((k_rvq_encode<W, bf16_t>), grid, dim3(64 * kRvqWaves), lds, s, static_cast<const bf16_t*>(Z),
                          C, stride, codes, N, r, G, K, R);
@@ -541,25 +615,44 @@ void launch_rvq_decode(const uint8_t* codes, const float* C, int64_t stride, voi
 #undef MAPL_DEC
 }
 
-// Stream apply: C[idx[q]*W + j] = vals[q*W + j]; a later duplicate of idx[q]
-// in the same call wins, so an earlier one skips its write.
+// Stream apply: C[idx[q]*W + j] = vals[q*W + j].  One thread per streamed
+// codeword q; a later duplicate of idx[q] in the same call wins, so q writes
+// only if no later entry names the same codeword.  The later entries are
+// scanned in tiles of kStreamTile ids staged in LDS by the block (work n^2/2
+// for n codewords, all from LDS: a full-codebook sync of 64k codewords is a
+// fraction of a millisecond).
+constexpr int kStreamTile = 1024;
+
 __global__ __launch_bounds__(256) void k_rvq_stream(float* __restrict__ C, const int32_t* __restrict__ idx,
                                                     const float* __restrict__ vals, int n, int W, int64_t total) {
-  const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (e >= int64_t(n) * W) return;
-  const int q = int(e / W), j = int(e % W);
-  const int64_t dst = idx[q];
-  if (dst < 0 || dst >= total) return;
-  for (int q2 = q + 1; q2 < n; ++q2)
-    if (idx[q2] == dst) return;
-  C[dst * W + j] = vals[e];
+  __shared__ int32_t tile[kStreamTile];
+  const int q = blockIdx.x * 256 + threadIdx.x;
+  const int64_t dst = q < n ? idx[q] : -1;
+  bool win = q < n && dst >= 0 && dst < total;
+  for (int t0 = blockIdx.x * 256; t0 < n; t0 += kStreamTile) {
+    __syncthreads();
+    const int lim = min(kStreamTile, n - t0);
+    for (int e = threadIdx.x; e < lim; e += 256) tile[e] = idx[t0 + e];
+    __syncthreads();
+    if (win) {
+      for (int e = max(0, q + 1 - t0); e < lim; ++e)
+        if (tile[e] == dst) {
+          win = false;
+          break;
+        }
+    }
+  }
+  if (win) {
+    const float* v = vals + size_t(q) * W;
+    float* c = C + dst * W;
+    for (int j = 0; j < W; ++j) c[j] = v[j];
+  }
 }
 
 void launch_rvq_stream(float* C, const int32_t* idx, const float* vals, int n, int w, int64_t total_codewords,
                        hipStream_t s) {
-  const int64_t tot = int64_t(n) * w;
-  if (tot == 0) return;
-  hipLaunchKernelGGL(k_rvq_stream, dim3(unsigned((tot + 255) / 256)), dim3(256), 0, s, C, idx, vals, n, w,
+  if (n <= 0) return;
+  hipLaunchKernelGGL(k_rvq_stream, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, C, idx, vals, n, w,
                      total_codewords);
 }
 

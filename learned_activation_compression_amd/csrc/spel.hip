@@ -72,17 +72,20 @@ __device__ __forceinline__ void pair_of(int p, int nb, int& bi, int& bj) {
 // TWO = 1 (Eq. (4)): piece = sym(A^T g) over the group's rows, from
 // acc1 = A_bi^T g_bj and acc2 = A_bj^T g_bi.  TWO = 0: piece = X_bi^T X_bj.
 // Tile (bi, bj) of part[grp] gets the piece, tile (bj, bi) its transpose.
-// `zero`, when given, holds kRsSyncWords words cleared for the launch that
-// follows (the arrival flags and the timeout flag of the Gram-space iteration).
+// `zero`, when given, holds nzero words cleared for the launches that follow:
+// the arrival flags [0, 64) and the timeout word [64] of the Gram-space
+// iteration, and (cleared by the step's first launch only) the step's sticky
+// timeout word [65], which decides at the end whether the step is committed.
 constexpr int kRsSyncWords = 68;
+constexpr int kRsTimeoutWord = 64, kRsStickyWord = 65;
 template <int TWO>
 __global__ __launch_bounds__(256) void k_spel_gram(const float* __restrict__ Xl, const float* __restrict__ Xr,
                                                    float* __restrict__ part, int d, int r, int groups,
-                                                   unsigned* __restrict__ zero) {
+                                                   unsigned* __restrict__ zero, int nzero) {
   __shared__ float red[(1 + TWO) * 4 * 1024];
   __shared__ float tile[32 * 33];
   const int lane = threadIdx.x & 63, w = wave_id();
-  if (zero != nullptr && blockIdx.x == 0 && threadIdx.x < kRsSyncWords) zero[threadIdx.x] = 0u;
+  if (zero != nullptr && blockIdx.x == 0 && int(threadIdx.x) < nzero) zero[threadIdx.x] = 0u;
   const int h = lane >> 5, l32 = lane & 31;
   const int p = blockIdx.x / groups, grp = blockIdx.x % groups;
   int bi, bj;
@@ -184,10 +187,12 @@ __device__ float block_inv_norm(const float* nparts, int n, float* slot) {
 template <int G, bool NS>
 __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, const float* __restrict__ nparts_in,
                                                  const float* __restrict__ part, float* __restrict__ out, int d, int r,
-                                                 int mode, const float* __restrict__ g, float* __restrict__ m,
+                                                 int mode, const float* __restrict__ g, const float* __restrict__ m,
                                                  float beta, float* __restrict__ nparts_out,
                                                  const float* __restrict__ Acur, float alpha, float* __restrict__ Dout,
-                                                 float* __restrict__ Y0) {
+                                                 float* __restrict__ Y0, const unsigned* __restrict__ sticky,
+                                                 const float* __restrict__ mnew, float* __restrict__ mcommit,
+                                                 int* __restrict__ status) {
   __shared__ float red[4 * 1024];
   __shared__ float wsum[4];
   __shared__ float scs;
@@ -224,7 +229,8 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
   const size_t o = size_t(i0 + i) * r + j0 + j;
 
   if (mode == XM_TANGENT) {
-    // Eq. (4)-(5): g_R = g - A sym(A^T g) ; m = beta m + (1 - beta) g_R
+    // Eq. (4)-(5): g_R = g - A sym(A^T g) ; m_new = beta m + (1 - beta) g_R, into `out`
+    // (the caller's m is updated only when the step commits)
     const f32x4 gv = ld4(g + o), mv = ld4(m + o);
     f32x4 mn;
     float local = 0.f;
@@ -233,7 +239,7 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
       mn[q] = beta * mv[q] + (1.f - beta) * (gv[q] - v[q]);
       local = fmaf(mn[q], mn[q], local);
     }
-    st4(m + o, mn);
+    st4(out + o, mn);
     // this block's share of ||m||_F^2: xor-butterfly within the wave, waves in order
     for (int off = 32; off > 0; off >>= 1) local += __shfl_xor(local, off);
     if (lane == 0) wsum[w] = local;
@@ -243,8 +249,16 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
     return;
   }
   const f32x4 val = v * sx;
-  if (mode == XM_NS || mode == XM_NS_LAST_RET) {
+  if (mode == XM_NS) {
     st4(out + o, val);
+  } else if (mode == XM_NS_LAST_RET) {
+    // commit: the new A and m, unless a wait of the Gram-space iteration timed out
+    const bool ok = sticky == nullptr || *sticky == 0u;
+    if (ok) {
+      st4(out + o, val);
+      st4(mcommit + o, ld4(mnew + o));
+    }
+    if (status != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = ok ? 0 : 1;
   } else {  // XM_NS_LAST_LMO: D = val ; Y0 = A - alpha D
     if (Dout) st4(Dout + o, val);
     const f32x4 y0 = ld4(Acur + o) - alpha * val;
@@ -316,7 +330,8 @@ __device__ __forceinline__ f32x4 mfma_f32_4x4x1(float a, float b, f32x4 c) {
 // Raise this workgroup's flag to `epoch` once every wave's stores are complete
 // and published (release fence), then wait until all nblk flags have reached
 // it and make the other workgroups' stores visible (acquire fence).  On
-// timeout the word flags[64] is set at once and false is returned.
+// timeout the iteration's timeout word flags[64] and the step's sticky word
+// flags[65] are set at once and false is returned.
 __device__ bool rs_sync(unsigned* flags, int nblk, unsigned epoch, unsigned limit, int* slot) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -334,7 +349,10 @@ __device__ bool rs_sync(unsigned* flags, int nblk, unsigned epoch, unsigned limi
       __builtin_amdgcn_s_sleep(1);
       if (++spins > limit) {
         ok = 0;
-        if (l == 0) __hip_atomic_store(flags + 64, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (l == 0) {
+          __hip_atomic_store(flags + kRsTimeoutWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(flags + kRsStickyWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         break;
       }
     }
@@ -557,7 +575,7 @@ __global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part,
       if (!rs_sync(flags, nblk, unsigned(k + 2), limit, &slot)) ok = false;
     }
   }
-  if (threadIdx.x == 0) slot = int(__hip_atomic_load(flags + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  if (threadIdx.x == 0) slot = int(__hip_atomic_load(flags + kRsTimeoutWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   __syncthreads();
   if (slot != 0) ok = false;
   const float nan = __builtin_nanf("");
@@ -666,13 +684,21 @@ __global__ __launch_bounds__(kPolyThreads) void k_spel_poly(const float* __restr
 // row groups of the Gram pieces: 1, 2 or 4, about 256 rows each
 int spel_groups(int64_t d) { return d >= 1024 ? 4 : d >= 512 ? 2 : 1; }
 
+// the xm launch; `sticky`, `mnew`, `mcommit` and `status` serve only XM_NS_LAST_RET (the commit)
+struct XmCommit {
+  const unsigned* sticky = nullptr;
+  const float* mnew = nullptr;
+  float* mcommit = nullptr;
+  int* status = nullptr;
+};
+
 template <bool NS>
 void launch_xm(int G, dim3 grid, hipStream_t s, const float* X, const float* nparts_in, const float* part, float* out,
-               int d, int r, int mode, const float* g, float* m, float beta, float* nparts_out, const float* Acur,
-               float alpha, float* Dout, float* Y0) {
+               int d, int r, int mode, const float* g, const float* m, float beta, float* nparts_out,
+               const float* Acur, float alpha, float* Dout, float* Y0, XmCommit cm = {}) {
   auto k = G == 4 ? k_spel_xm<4, NS> : G == 2 ? k_spel_xm<2, NS> : k_spel_xm<1, NS>;
   hipLaunchKernelGGL(k, grid, dim3(256), 0, s, X, nparts_in, part, out, d, r, mode, g, m, beta, nparts_out, Acur,
-                     alpha, Dout, Y0);
+                     alpha, Dout, Y0, cm.sticky, cm.mnew, cm.mcommit, cm.status);
 }
 
 unsigned rs_spin_limit() {
@@ -686,8 +712,10 @@ template <int R>
 void launch_rs(const float* part, int G, const float* nparts, int nnp, int iters, float* Sbuf, unsigned* sync,
                float* M, hipStream_t s) {
   constexpr int lds = R * (R + 4) * int(sizeof(float));  // the staged S_k
-  static std::atomic<uint64_t> done{0};
-  if (lds > 48 * 1024) allow_lds(reinterpret_cast<const void*>(k_spel_rs<R>), lds, done);
+  // with the kernel's static arrays (own Q and S^2 rows, the wave partials)
+  static_assert(lds + (kRsQ + kRsS) * (R + 4) * 4 + 4 * RsRows<R>::NG * 4 * 64 * 4 + 64 <= kMaxLdsBytes,
+                "Gram-space iteration LDS");
+  (void)LdsLimit<k_spel_rs<R>, lds>::bytes();
   hipLaunchKernelGGL(k_spel_rs<R>, dim3(R / kRsS + R / kRsQ), dim3(256), lds, s, part, G, nparts, nnp, iters, Sbuf,
                      sync, M, rs_spin_limit());
 }
@@ -703,76 +731,99 @@ void launch_rs_any(int r, const float* part, int G, const float* nparts, int nnp
 
 }  // namespace
 
-// workspace: Xa | Xb | Xc [d][r] | part [groups][r][r] | nparts [(d/32)(r/32)] |
-// M [r][r] | nparts of Y0 [(d/32)(r/32)] | S buffers [2][r][r] | arrival and
-// timeout flags [kRsSyncWords], each region 16-byte aligned
+// workspace: Xa | Xb | Xc | Xm [d][r] | part [groups][r][r] | nparts
+// [(d/32)(r/32)] | M [r][r] | nparts of Y0 [(d/32)(r/32)] | S buffers
+// [2][r][r] | arrival, timeout and sticky words [kRsSyncWords], each region
+// 16-byte aligned.  Xm holds the new momentum until the step commits.
 static size_t a4(size_t n) { return (n + 3) & ~size_t(3); }
+
+struct SpelWs {
+  float *Xa, *Xb, *Xc, *Xm, *part, *nparts, *Mb, *nparts2, *Sbuf;
+  unsigned* sync;
+};
+
+static SpelWs spel_ws(void* ws, int d, int r) {
+  const size_t dr = size_t(d) * r, rr = size_t(r) * r, np = a4(size_t(d / 32) * (r / 32));
+  SpelWs w;
+  w.Xa = static_cast<float*>(ws);
+  w.Xb = w.Xa + dr;
+  w.Xc = w.Xb + dr;
+  w.Xm = w.Xc + dr;
+  w.part = w.Xm + dr;
+  w.nparts = w.part + size_t(spel_groups(d)) * rr;
+  w.Mb = w.nparts + np;
+  w.nparts2 = w.Mb + rr;
+  w.Sbuf = w.nparts2 + np;
+  w.sync = reinterpret_cast<unsigned*>(w.Sbuf + 2 * rr);
+  return w;
+}
+
 size_t spel_ws_bytes(int64_t d, int64_t r) {
   const size_t np = a4(size_t(d / 32) * (r / 32));
   const size_t floats =
-      3 * size_t(d) * r + size_t(spel_groups(d)) * r * r + np + size_t(r) * r + np + 2 * size_t(r) * r + kRsSyncWords;
+      4 * size_t(d) * r + size_t(spel_groups(d)) * r * r + np + size_t(r) * r + np + 2 * size_t(r) * r + kRsSyncWords;
   return (floats + 64) * sizeof(float);
 }
 
-void launch_spel(float* A, const float* g, float* m, float alpha, float beta, int ns_iters, float* D_out, int d, int r,
-                 void* ws, hipStream_t s) {
+void launch_spel(float* A, const float* g, float* m, float alpha, float beta, int ns_iters, float* D_out, int* status,
+                 int d, int r, void* ws, hipStream_t s) {
   const int G = spel_groups(d);
-  float* Xa = static_cast<float*>(ws);
-  float* Xb = Xa + size_t(d) * r;
-  float* Xc = Xb + size_t(d) * r;
-  float* part = Xc + size_t(d) * r;
-  float* nparts = part + size_t(G) * r * r;
-
+  const SpelWs w = spel_ws(ws, d, r);
+  float* part = w.part;
   const int nb = r / 32;
   const dim3 blk(256);
   const dim3 ggrid(nb * (nb + 1) / 2 * G);
   const dim3 xgrid(d / 32, r / 32);
+  // the last launch commits A and m = Xm unless the step's sticky timeout word is set
+  XmCommit cm;
+  cm.sticky = w.sync + kRsStickyWord;
+  cm.mnew = w.Xm;
+  cm.mcommit = m;
+  cm.status = status;
 
-  // Eq. (4)-(5): M = sym(A^T g) ; m = beta m + (1 - beta)(g - A M) ; per-block sums of m^2
-  hipLaunchKernelGGL(k_spel_gram<1>, ggrid, blk, 0, s, A, g, part, d, r, G, nullptr);
-  launch_xm<false>(G, xgrid, s, A, nullptr, part, nullptr, d, r, int(XM_TANGENT), g, m, beta, nparts, nullptr, 0.f,
+  // Eq. (4)-(5): M = sym(A^T g) ; Xm = beta m + (1 - beta)(g - A M) ; per-block sums of Xm^2.
+  // The first launch clears every sync word, the sticky one included.
+  hipLaunchKernelGGL(k_spel_gram<1>, ggrid, blk, 0, s, A, g, part, d, r, G, w.sync, kRsSyncWords);
+  launch_xm<false>(G, xgrid, s, A, nullptr, part, w.Xm, d, r, int(XM_TANGENT), g, m, beta, w.nparts, nullptr, 0.f,
                    nullptr, nullptr);
 
   if (r <= 128) {
-    // Gram-space iteration: S_0 from the pieces of m^T m, M = s Q_n, then D = m M and
+    // Gram-space iteration: S_0 from the pieces of Xm^T Xm, M = s Q_n, then D = Xm M and
     // Y0 = A - alpha D (Eq. (6)); the same for Y0 (unscaled) and A = Y0 M (Eq. (7))
     const int npn = (d / 32) * (r / 32);
-    float* Mb = nparts + a4(size_t(npn));
-    float* Sbuf = Mb + size_t(r) * r + a4(size_t(npn));
-    unsigned* sync = reinterpret_cast<unsigned*>(Sbuf + 2 * size_t(r) * r);
-    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, m, m, part, d, r, G, sync);
-    launch_rs_any(r, part, G, nparts, npn, ns_iters, Sbuf, sync, Mb, s);
-    launch_xm<false>(1, xgrid, s, m, nullptr, Mb, nullptr, d, r, int(XM_NS_LAST_LMO), nullptr, nullptr, 0.f, nullptr,
-                     A, alpha, D_out, Xc);
-    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, Xc, Xc, part, d, r, G, sync);
-    launch_rs_any(r, part, G, nullptr, 0, ns_iters, Sbuf, sync, Mb, s);
-    launch_xm<false>(1, xgrid, s, Xc, nullptr, Mb, A, d, r, int(XM_NS_LAST_RET), nullptr, nullptr, 0.f, nullptr,
-                     nullptr, 0.f, nullptr, nullptr);
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, w.Xm, w.Xm, part, d, r, G, w.sync, kRsStickyWord);
+    launch_rs_any(r, part, G, w.nparts, npn, ns_iters, w.Sbuf, w.sync, w.Mb, s);
+    launch_xm<false>(1, xgrid, s, w.Xm, nullptr, w.Mb, nullptr, d, r, int(XM_NS_LAST_LMO), nullptr, nullptr, 0.f,
+                     nullptr, A, alpha, D_out, w.Xc);
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, w.Xc, w.Xc, part, d, r, G, w.sync, kRsStickyWord);
+    launch_rs_any(r, part, G, nullptr, 0, ns_iters, w.Sbuf, w.sync, w.Mb, s);
+    launch_xm<false>(1, xgrid, s, w.Xc, nullptr, w.Mb, A, d, r, int(XM_NS_LAST_RET), nullptr, nullptr, 0.f, nullptr,
+                     nullptr, 0.f, nullptr, nullptr, cm);
     return;
   }
 
-  // Eq. (6): D = NS(s m), s = 1/||m||_F; the last step forms Y0 = A - alpha D in Xc
-  const float* cur = m;
-  const float* cur_np = nparts;
-  float* bufs[2] = {Xa, Xb};
+  // Eq. (6): D = NS(s Xm), s = 1/||Xm||_F; the last step forms Y0 = A - alpha D in Xc
+  const float* cur = w.Xm;
+  const float* cur_np = w.nparts;
+  float* bufs[2] = {w.Xa, w.Xb};
   for (int it = 0; it < ns_iters; ++it) {
     float* nxt = bufs[it & 1];
-    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G, nullptr);
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G, nullptr, 0);
     const int mode = (it == ns_iters - 1) ? int(XM_NS_LAST_LMO) : int(XM_NS);
     launch_xm<true>(G, xgrid, s, cur, cur_np, part, nxt, d, r, mode, nullptr, nullptr, 0.f, nullptr, A, alpha, D_out,
-                    Xc);
+                    w.Xc);
     cur = nxt;
     cur_np = nullptr;
   }
 
-  // Eq. (7): A = NS(A - alpha D), input unscaled; the last step writes A
-  cur = Xc;
+  // Eq. (7): A = NS(A - alpha D), input unscaled; the last step writes A (and commits m)
+  cur = w.Xc;
   for (int it = 0; it < ns_iters; ++it) {
-    float* nxt = (it == ns_iters - 1) ? A : bufs[it & 1];
-    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G, nullptr);
-    const int mode = (it == ns_iters - 1) ? int(XM_NS_LAST_RET) : int(XM_NS);
-    launch_xm<true>(G, xgrid, s, cur, nullptr, part, nxt, d, r, mode, nullptr, nullptr, 0.f, nullptr, nullptr, 0.f,
-                    nullptr, nullptr);
+    const bool last = it == ns_iters - 1;
+    float* nxt = last ? A : bufs[it & 1];
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G, nullptr, 0);
+    launch_xm<true>(G, xgrid, s, cur, nullptr, part, nxt, d, r, last ? int(XM_NS_LAST_RET) : int(XM_NS), nullptr,
+                    nullptr, 0.f, nullptr, nullptr, 0.f, nullptr, nullptr, last ? cm : XmCommit{});
     cur = nxt;
   }
 }
@@ -863,52 +914,54 @@ int polar_express_schedule(double ell, int steps, double* coef, double* err) {
 }
 
 void launch_spel_pe(float* A, const float* g, float* m, float alpha, float beta, const float* coef_lmo, int lmo_steps,
-                    const float* coef_ret, int ret_steps, float* D_out, int d, int r, void* ws, hipStream_t s) {
+                    const float* coef_ret, int ret_steps, float* D_out, int* status, int d, int r, void* ws,
+                    hipStream_t s) {
   const int G = spel_groups(d);
-  float* Xa = static_cast<float*>(ws);
-  float* Xb = Xa + size_t(d) * r;
-  float* Xc = Xb + size_t(d) * r;
-  float* part = Xc + size_t(d) * r;
+  const SpelWs w = spel_ws(ws, d, r);
+  float* part = w.part;
   const int npn = (d / 32) * (r / 32);
-  float* nparts = part + size_t(G) * r * r;
-  float* Mb = nparts + a4(size_t(npn));
-  float* nparts2 = Mb + size_t(r) * r;
-
   const int nb = r / 32;
   const dim3 blk(256);
   const dim3 ggrid(nb * (nb + 1) / 2 * G);
   const dim3 xgrid(d / 32, r / 32);
   const dim3 pgrid(nb, nb);
+  XmCommit cm;  // no waits here: the sticky word stays clear and the last launch always commits
+  cm.sticky = w.sync + kRsStickyWord;
+  cm.mnew = w.Xm;
+  cm.mcommit = m;
+  cm.status = status;
 
   // Eq. (4)-(5) as in launch_spel
-  hipLaunchKernelGGL(k_spel_gram<1>, ggrid, blk, 0, s, A, g, part, d, r, G, nullptr);
-  launch_xm<false>(G, xgrid, s, A, nullptr, part, nullptr, d, r, int(XM_TANGENT), g, m, beta, nparts, nullptr, 0.f,
+  hipLaunchKernelGGL(k_spel_gram<1>, ggrid, blk, 0, s, A, g, part, d, r, G, w.sync, kRsSyncWords);
+  launch_xm<false>(G, xgrid, s, A, nullptr, part, w.Xm, d, r, int(XM_TANGENT), g, m, beta, w.nparts, nullptr, 0.f,
                    nullptr, nullptr);
 
   // one Polar Express step: S from the Gram pieces, M = s (a I + b s^2 S + c s^4 S^2), out = X M
-  float* bufs[2] = {Xa, Xb};
-  auto step = [&](const float* cur, const float* np_in, const float* c3, float* out, int mode, float* np_out) {
-    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G, nullptr);
+  float* bufs[2] = {w.Xa, w.Xb};
+  auto step = [&](const float* cur, const float* np_in, const float* c3, float* out, int mode, float* np_out,
+                  XmCommit c) {
+    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, cur, cur, part, d, r, G, nullptr, 0);
     auto poly = G == 8 ? k_spel_poly<8> : G == 4 ? k_spel_poly<4> : G == 2 ? k_spel_poly<2> : k_spel_poly<1>;
-    hipLaunchKernelGGL(poly, pgrid, dim3(kPolyThreads), 0, s, part, np_in, npn, Mb, r, c3[0], c3[1], c3[2]);
-    launch_xm<false>(1, xgrid, s, cur, nullptr, Mb, out, d, r, mode, nullptr, nullptr, 0.f, np_out, A, alpha, D_out,
-                     Xc);
+    hipLaunchKernelGGL(poly, pgrid, dim3(kPolyThreads), 0, s, part, np_in, npn, w.Mb, r, c3[0], c3[1], c3[2]);
+    launch_xm<false>(1, xgrid, s, cur, nullptr, w.Mb, out, d, r, mode, nullptr, nullptr, 0.f, np_out, A, alpha, D_out,
+                     w.Xc, c);
   };
-  // Eq. (6): D = PE(m / ||m||_F); the last step forms Y0 = A - alpha D in Xc and its squares
-  const float* cur = m;
+  // Eq. (6): D = PE(Xm / ||Xm||_F); the last step forms Y0 = A - alpha D in Xc and its squares
+  const float* cur = w.Xm;
   for (int t = 0; t < lmo_steps; ++t) {
     const bool last = t == lmo_steps - 1;
     float* nxt = bufs[t & 1];
-    step(cur, t == 0 ? nparts : nullptr, coef_lmo + 3 * t, nxt, last ? int(XM_NS_LAST_LMO) : int(XM_NS),
-         last ? nparts2 : nullptr);
+    step(cur, t == 0 ? w.nparts : nullptr, coef_lmo + 3 * t, nxt, last ? int(XM_NS_LAST_LMO) : int(XM_NS),
+         last ? w.nparts2 : nullptr, XmCommit{});
     cur = nxt;
   }
-  // Eq. (7): A = PE(Y0 / ||Y0||_F)
-  cur = Xc;
+  // Eq. (7): A = PE(Y0 / ||Y0||_F); the last step writes A and commits m
+  cur = w.Xc;
   for (int t = 0; t < ret_steps; ++t) {
     const bool last = t == ret_steps - 1;
     float* nxt = last ? A : bufs[t & 1];
-    step(cur, t == 0 ? nparts2 : nullptr, coef_ret + 3 * t, nxt, last ? int(XM_NS_LAST_RET) : int(XM_NS), nullptr);
+    step(cur, t == 0 ? w.nparts2 : nullptr, coef_ret + 3 * t, nxt, last ? int(XM_NS_LAST_RET) : int(XM_NS), nullptr,
+         last ? cm : XmCommit{});
     cur = nxt;
   }
 }

@@ -37,9 +37,8 @@ def encode(Z, C, G: int, K: int, R: int, teacher=None, chunk: int = 2048) -> dic
     Z [N][r]; C [R_c][G][K][w] with R_c in {1, R}.  Returns a dict with
       codes    int64 [N][R][G]: argmin over k of sum_j (res_j - C_k,j)^2,
                lowest k on exact ties;
-      d1, d2   the smallest and second-smallest distances per (n, rho, g);
-      scale    ||residual group||^2 + max_k ||c_k||^2 per (n, rho, g): the size of
-               the terms of the expanded distance ||c||^2 - 2<z, c> + ||z||^2;
+      d1, d2   the smallest and second-smallest distances per (n, rho, g)
+               (d2 = inf when K = 1);
       d_teacher distance of the teacher's codeword (if `teacher` is given);
       energy   [R+1] total residual energy before round 0 and after each round;
       grew     [R] count of (n, g) whose group residual energy increased;
@@ -60,7 +59,6 @@ def encode(Z, C, G: int, K: int, R: int, teacher=None, chunk: int = 2048) -> dic
     d1 = np.zeros((N, R, G))
     d2 = np.full((N, R, G), np.inf)
     d_t = np.zeros((N, R, G)) if teacher is not None else None
-    scale = np.zeros((N, R, G))
     energy = [float(np.sum(res * res))]
     grew = []
     for rho in range(R):
@@ -83,13 +81,12 @@ def encode(Z, C, G: int, K: int, R: int, teacher=None, chunk: int = 2048) -> dic
                 if d_t is not None:
                     d_t[s:e, rho, g] = D[np.arange(e - s), chosen]
                 before = np.sum(sub[s:e] * sub[s:e], axis=1)
-                scale[s:e, rho, g] = before + np.max(np.sum(cb * cb, axis=1))
                 sub[s:e] -= cb[chosen]
                 after = np.sum(sub[s:e] * sub[s:e], axis=1)
                 n_grew += int(np.count_nonzero(after > before))
         energy.append(float(np.sum(res * res)))
         grew.append(n_grew)
-    return dict(codes=codes, d1=d1, d2=d2, d_teacher=d_t, scale=scale, energy=np.array(energy),
+    return dict(codes=codes, d1=d1, d2=d2, d_teacher=d_t, energy=np.array(energy),
                 grew=np.array(grew), residual=res)
 
 

@@ -1,7 +1,9 @@
 """Host-side checks of the C ABI: the library loads, exports every symbol that
 include/mapl.h declares, and its host validation returns the documented status
 codes before anything is enqueued.  No call here reaches a kernel launch, so
-these run without a GPU."""
+these run without a GPU: calls that pass validation stop at the device set-up
+(raising the kernels' LDS limits), which reports MAPL_ERR_HIP when there is no
+device -- the path a refused limit takes on a GPU."""
 import ctypes
 
 import numpy as np
@@ -10,7 +12,7 @@ import pytest
 
 import learned_activation_compression_amd as lac
 
-OK, ENULL, ESHAPE, EDTYPE, EARG, EWS, EHIP = 0, -1, -2, -3, -4, -5, -6
+OK, ENULL, ESHAPE, EDTYPE, EARG, EWS, EHIP, ETID = 0, -1, -2, -3, -4, -5, -6, -7
 F32, BF16 = lac.MAPL_F32, lac.MAPL_BF16
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
 
@@ -22,15 +24,16 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = lac.exported_symbols()
-    assert len(names) == 20, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lac._SIGS), set(names) ^ set(lac._SIGS)
 
 
 def test_status_strings_and_version(lib):
-    for s in (OK, ENULL, ESHAPE, EDTYPE, EARG, EWS, EHIP):
-        assert lib.mapl_status_string(s)
+    for s in (OK, ENULL, ESHAPE, EDTYPE, EARG, EWS, EHIP, ETID):
+        assert lib.mapl_status_string(s) != b"unknown status"
+    assert b"token id" in lib.mapl_status_string(ETID)
     assert lib.mapl_status_string(-99) == b"unknown status"
     assert lib.mapl_version().startswith(b"mapl-gfx950")
 
@@ -52,7 +55,7 @@ def test_pack_and_workspace_sizes(lib):
     assert lib.mapl_bwd_workspace_bytes(8, 2048, d, r, 0, BF16) < lib.mapl_bwd_workspace_bytes(8, 2048, d, r, d, BF16)
     assert lib.mapl_bwd_workspace_bytes(1, 128, 256, 32, 32, F32) == 128 * 256 * 4
     assert lib.mapl_bwd_workspace_bytes(1, 128, 1000, 32, 32, BF16) == 0     # d % 64 != 0
-    assert lib.spel_workspace_bytes(2048, 256) >= 3 * 2048 * 256 * 4
+    assert lib.spel_workspace_bytes(2048, 256) >= 4 * 2048 * 256 * 4    # 3 iterates + the uncommitted momentum
     assert lib.spel_workspace_bytes(2048, 250) == 0                      # r % 32 != 0
 
 
@@ -193,11 +196,16 @@ def test_rvq_validation(lib):
     assert e(None, BF16, FAKE, 0, FAKE, 16384, 256, 8, 256, 2, None) == ENULL
     assert e(FAKE, BF16, FAKE, 0, FAKE, 16384, 256, 7, 256, 2, None) == ESHAPE   # r % G
     assert e(FAKE, BF16, FAKE, 0, FAKE, 16384, 256, 8, 512, 2, None) == ESHAPE   # K > 256 (uint8 codes)
-    assert e(FAKE, BF16, FAKE, 0, FAKE, 16384, 256, 8, 100, 2, None) == ESHAPE   # K % 32
+    assert e(FAKE, BF16, FAKE, 0, FAKE, 16384, 256, 8, 0, 2, None) == ESHAPE     # K >= 1
     assert e(FAKE, BF16, FAKE, 0, FAKE, 16384, 384, 3, 256, 2, None) == ESHAPE   # w = 128 unsupported
     assert e(FAKE, BF16, FAKE, 0, FAKE, 16384, 256, 8, 256, 0, None) == ESHAPE   # R >= 1
     assert e(FAKE, BF16, FAKE, 100, FAKE, 16384, 256, 8, 256, 2, None) == EARG   # 0 < stride < r*K
     assert e(FAKE, 5, FAKE, 0, FAKE, 16384, 256, 8, 256, 2, None) == EDTYPE
+    odd = ctypes.c_void_p(0x1004)
+    assert e(odd, BF16, FAKE, 0, FAKE, 16384, 256, 8, 256, 2, None) == EARG    # Z not 16-B aligned
+    assert e(FAKE, BF16, odd, 0, FAKE, 16384, 256, 8, 256, 2, None) == EARG    # C not 16-B aligned
+    assert e(FAKE, BF16, FAKE, 256 * 256 + 2, FAKE, 16384, 256, 8, 256, 2, None) == EARG  # stride % 4
+    assert lib.rvq_decode(FAKE, odd, 0, FAKE, F32, 16384, 256, 8, 256, 2, None) == EARG
     d = lib.rvq_decode
     assert d(FAKE, FAKE, 0, None, F32, 16384, 256, 8, 256, 2, None) == ENULL
     assert d(FAKE, FAKE, 0, FAKE, 9, 16384, 256, 8, 256, 2, None) == EDTYPE
@@ -209,18 +217,20 @@ def test_rvq_validation(lib):
 def test_spel_validation(lib):
     ws = lib.spel_workspace_bytes(2048, 256)
     f = lib.spel_step
-    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 256, FAKE, ws - 1, None) == EWS
-    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 256, None, ws, None) == ENULL
-    assert f(None, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 256, FAKE, ws, None) == ENULL
-    assert f(FAKE, FAKE, FAKE, 1e-3, 1.0, 8, None, 2048, 256, FAKE, ws, None) == EARG     # beta < 1
-    assert f(FAKE, FAKE, FAKE, 0.9, 0.9, 8, None, 2048, 256, FAKE, ws, None) == EARG      # alpha <= 0.7
-    assert f(FAKE, FAKE, FAKE, float("nan"), 0.9, 8, None, 2048, 256, FAKE, ws, None) == EARG
-    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 0, None, 2048, 256, FAKE, ws, None) == EARG     # ns_iters >= 1
-    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 250, FAKE, ws, None) == ESHAPE
-    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, 256, 512, FAKE, ws, None) == ESHAPE    # r > d
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, None, 2048, 256, FAKE, ws - 1, None) == EWS
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, None, 2048, 256, None, ws, None) == ENULL
+    assert f(None, FAKE, FAKE, 1e-3, 0.9, 8, None, None, 2048, 256, FAKE, ws, None) == ENULL
+    assert f(FAKE, FAKE, FAKE, 1e-3, 1.0, 8, None, None, 2048, 256, FAKE, ws, None) == EARG     # beta < 1
+    assert f(FAKE, FAKE, FAKE, 0.9, 0.9, 8, None, None, 2048, 256, FAKE, ws, None) == EARG      # alpha <= 0.7
+    assert f(FAKE, FAKE, FAKE, float("nan"), 0.9, 8, None, None, 2048, 256, FAKE, ws, None) == EARG
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 0, None, None, 2048, 256, FAKE, ws, None) == EARG     # ns_iters >= 1
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, None, 2048, 250, FAKE, ws, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, None, 256, 512, FAKE, ws, None) == ESHAPE    # r > d
     odd = ctypes.c_void_p(0x1004)
-    assert f(odd, FAKE, FAKE, 1e-3, 0.9, 8, None, 2048, 256, FAKE, ws, None) == EARG      # A not 16-B aligned
-    assert f(FAKE, FAKE, odd, 1e-3, 0.9, 8, None, 2048, 256, FAKE, ws, None) == EARG      # m not 16-B aligned
+    assert f(odd, FAKE, FAKE, 1e-3, 0.9, 8, None, None, 2048, 256, FAKE, ws, None) == EARG      # A not 16-B aligned
+    assert f(FAKE, FAKE, odd, 1e-3, 0.9, 8, None, None, 2048, 256, FAKE, ws, None) == EARG      # m not 16-B aligned
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, ctypes.c_void_p(0x1002), 2048, 256, FAKE, ws,
+             None) == EARG                                                                     # status 4-B aligned
 
 
 def test_spel_polar_express_validation(lib):
@@ -228,7 +238,7 @@ def test_spel_polar_express_validation(lib):
     f = lib.spel_step_polar_express
 
     def call(A=FAKE, m=FAKE, alpha=1e-3, beta=0.9, lmo=5, ret=7, ell=1e-3, d=1024, r=128, w=FAKE, wb=ws):
-        return f(A, FAKE, m, alpha, beta, lmo, ret, ell, None, d, r, w, wb, None)
+        return f(A, FAKE, m, alpha, beta, lmo, ret, ell, None, None, d, r, w, wb, None)
 
     assert call(A=None) == ENULL
     assert call(w=None) == ENULL
@@ -272,3 +282,31 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(lac.MaplError):
         lac.mapl_compress(X, torch.zeros(4, dtype=torch.int32), torch.zeros(8, 32, dtype=torch.bfloat16),
                           torch.zeros(32, 64, dtype=torch.bfloat16), torch.zeros(64, 32, dtype=torch.bfloat16))
+
+
+def test_valid_calls_without_a_device_stop_at_device_setup(lib):
+    """A call that passes validation first prepares the device (the kernels'
+    dynamic-LDS limits); with no device that fails, and the call returns
+    MAPL_ERR_HIP having enqueued nothing -- the same path as a limit the
+    runtime refuses.  mapl_init reports the same."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present: the set-up succeeds")
+    assert lib.mapl_init() == EHIP
+    assert _compress(lib) == EHIP
+    ws = lib.spel_workspace_bytes(1024, 128)
+    assert lib.spel_step(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, None, 1024, 128, FAKE, ws, None) == EHIP
+    assert lib.rvq_encode(FAKE, BF16, FAKE, 0, FAKE, 16384, 256, 128, 17, 2, None) == EHIP   # K = 17 is valid
+    assert lib.rvq_stream_apply(FAKE, FAKE, FAKE, 8, 256, 8, 256, 1, None) == EHIP
+
+
+def test_tid_check_mode_of_the_binding(monkeypatch):
+    """MAPL_CHECK=1 makes the binding count out-of-range ids before a map that
+    reads them (mapl_check_tids) and raise MAPL_ERR_TID; without it no count
+    is taken.  Checked here through the binding's own switch."""
+    monkeypatch.setenv("MAPL_CHECK", "1")
+    assert lac._checking()
+    monkeypatch.setenv("MAPL_CHECK", "0")
+    assert not lac._checking()
+    monkeypatch.delenv("MAPL_CHECK")
+    assert not lac._checking()

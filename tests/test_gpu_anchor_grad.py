@@ -156,6 +156,32 @@ def test_zero_gradient_and_empty_batch():
     assert bool((gE == 0).all())
 
 
+@pytest.mark.parametrize("dtype,r,ident", [("bf16", 128, False), ("bf16", 64, False), ("f32", 32, False),
+                                           ("bf16", 256, True), ("f32", 256, True)])
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_non_finite_gradient_marks_the_table(dtype, r, ident, bad):
+    """A NaN or an Inf in Y has no fixed-point scale: the whole table becomes
+    NaN (also when accumulating) instead of the value vanishing or saturating.
+    Covers each projection path: the codec's streaming kernel (bf16 r = 128),
+    the plain bf16 and fp32 kernels and the identity (full-rank anchor)."""
+    N, d, V = 333, 256, 70
+    inp = synth.codec_inputs(64, N, d, r, V, dtype)
+    g = to_dev(inp)
+    Y = g["gXhat"].clone()
+    Y[17, 5] = bad
+    P = None if ident else g["P"]
+    ra = d if ident else r
+    gE = lac.mapl_anchor_grad(Y, g["tids"], P, V, 1.0, r=r)
+    gE2 = torch.ones((V, ra), dtype=torch.float32, device=DEV)
+    lac.mapl_anchor_grad(Y, g["tids"], P, V, -1.0, gE=gE2, accumulate=True, r=r)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(gE).all()) and bool(torch.isnan(gE2).all())
+    # the same call on finite data is finite again (nothing is left behind)
+    gE3 = lac.mapl_anchor_grad(g["gXhat"], g["tids"], P, V, 1.0, r=r)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(gE3).all())
+
+
 @pytest.mark.parametrize("name,r", [("150m", None), ("sweep", 512), ("1b", None)])
 def test_full_size(name, r):
     c = synth.CONFIGS[name]

@@ -2,9 +2,10 @@
 codebook sync (Appendix F) against the fp64 oracle, through the C ABI.
 
 Codes must equal the oracle's argmin except where the oracle's top-2 distance
-gap is below 1e-6 relative; each round is judged teacher-forced on the GPU's
-own codes of earlier rounds.  Decoding in fp32 is within 1e-5 relative L2;
-stream sync is bit-exact."""
+gap is below 1e-6 relative to the smallest distance; each round is judged
+teacher-forced on the GPU's own codes of earlier rounds, and every token is
+checked.  Decoding in fp32 is within 1e-5 relative L2; stream sync is
+bit-exact."""
 import math
 
 import numpy as np
@@ -41,7 +42,7 @@ def test_rvq_config_full_size(R_c):
     Z = lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"])
     C = synth.rvq_codebooks(c["seed"], R_c, c["G"], c["K"], c["r"] // c["G"], c["codebook_var"]).to(DEV)
     codes, ora, n_mis, stride = encode_and_check(Z, C, c["G"], c["K"], c["R"], f"rvq R_c={R_c}")
-    assert n_mis <= 4, n_mis   # near-ties at fp32 resolution are rare
+    assert n_mis <= 2, n_mis   # the kernel's codes are exact: only ties at fp64 resolution may differ
     # decode in fp32 and bf16
     Zq = lac.rvq_decode(codes, C, c["G"], c["K"], c["R"], c["r"], round_stride=stride)
     Zq16 = lac.rvq_decode(codes, C, c["G"], c["K"], c["R"], c["r"], round_stride=stride, out_dtype=torch.bfloat16)
@@ -54,14 +55,15 @@ def test_rvq_config_full_size(R_c):
     assert e[1] <= e[0] and e[2] <= e[1]
 
 
-@pytest.mark.parametrize("G,var,step", [(8, 1.0 / 32.0, 1), (128, 1.0, 4)])
-def test_rvq_of_the_backward_gradient(G, var, step):
+@pytest.mark.parametrize("G,var", [(8, 1.0 / 32.0), (128, 1.0)])
+def test_rvq_of_the_backward_gradient(G, var):
     """Section 3.5 quantizes the backward gradients too: gZ = gXhat A from the
     receiver's backward map at the RVQ workload (r = 256, K = 256, R = 2),
     grouped as configured (G = 8 x w = 32) and as in the paper's Table 1
     (G = 128 x w = 2, 2 rounds: 256 code bytes per token).  Codebooks match
-    the scale of gZ (unit variance per entry for w = 2).  Tokens are
-    independent, so at w = 2 the oracle checks every `step`-th token."""
+    the scale of gZ (unit variance per entry for w = 2).  Every token of every
+    group and round is checked."""
+    step = 1
     c = synth.CONFIGS["rvq"]
     N, r, K, R = c["B"] * c["T"], c["r"], c["K"], c["R"]
     inp = synth.codec_inputs(c["seed"], N, c["d"], r, c["V"], "bf16")
@@ -79,7 +81,7 @@ def test_rvq_of_the_backward_gradient(G, var, step):
     gc = codes.cpu().numpy()[sel]
     ora = rvq.encode(np64(gZ)[sel], np64(C), G, K, R, teacher=gc)
     n_mis = check_codes(gc, ora, f"gZ G={G}")
-    assert n_mis <= max(4, gc.size // 100000), n_mis
+    assert n_mis <= 2, n_mis
     ref = rvq.decode(gc, np64(C), G, K, R)
     assert_close(np64(Zq)[sel], ref, F32_TOL, "decode")
     Zq16 = lac.rvq_decode(codes, C, G, K, R, r, out_dtype=torch.bfloat16)
@@ -98,6 +100,24 @@ def test_rvq_shapes(w, K, R, R_c, N):
     Z = torch.from_numpy(rng.standard_normal((N, r)).astype(np.float32)).to(DEV)
     C = torch.from_numpy((rng.standard_normal((R_c, G, K, w)) / math.sqrt(w)).astype(np.float32)).to(DEV)
     codes, ora, n_mis, stride = encode_and_check(Z, C, G, K, R, f"w={w} K={K}")
+    Zq = lac.rvq_decode(codes, C, G, K, R, r, round_stride=stride)
+    torch.cuda.synchronize()
+    assert_close(np64(Zq), rvq.decode(codes.cpu().numpy(), np64(C), G, K, R), F32_TOL, "decode")
+
+
+@pytest.mark.parametrize("w,K", [(2, 1), (2, 5), (2, 255), (4, 17), (8, 33), (16, 100), (32, 1), (32, 47),
+                                 (64, 200)])
+def test_rvq_codebook_sizes_not_a_multiple_of_32(w, K):
+    """1 <= K <= 256 in any size: the kernels pad the codebook to a multiple of
+    32 with codewords that never win."""
+    G, R, N = 4 if w < 64 else 2, 2, 700
+    r = G * w
+    rng = np.random.default_rng(w * 1000 + K)
+    Z = torch.from_numpy(rng.standard_normal((N, r)).astype(np.float32)).to(DEV).to(torch.bfloat16)
+    C = torch.from_numpy((rng.standard_normal((R, G, K, w)) / math.sqrt(w)).astype(np.float32)).to(DEV)
+    codes, ora, n_mis, stride = encode_and_check(Z, C, G, K, R, f"w={w} K={K}")
+    assert n_mis <= 1
+    assert int(codes.max()) < K
     Zq = lac.rvq_decode(codes, C, G, K, R, r, round_stride=stride)
     torch.cuda.synchronize()
     assert_close(np64(Zq), rvq.decode(codes.cpu().numpy(), np64(C), G, K, R), F32_TOL, "decode")
@@ -168,14 +188,15 @@ def test_rvq_nan_group_gets_code_zero_and_others_unaffected(w):
     assert np.array_equal(gc[mask], ref[mask])
 
 
-def test_rvq_nan_codeword_never_wins():
-    # w = 32 scans in bf16 and rescores candidates in fp32: a codeword with a NaN is never a candidate
+@pytest.mark.parametrize("w", [2, 8, 32])
+def test_rvq_nan_codeword_never_wins(w):
+    # a codeword with a NaN scores NaN on the matrix cores and is never a candidate
     rng = np.random.default_rng(9)
-    N, G, K, w = 700, 2, 64, 32
+    N, G, K = 700, 2, 64
     C = (rng.standard_normal((1, G, K, w)) / math.sqrt(w)).astype(np.float32)
     Z = np.concatenate([C[0, g][rng.integers(0, K, N)] for g in range(G)], axis=1)
     Z = (Z + 0.05 * rng.standard_normal(Z.shape)).astype(np.float32)
-    C[0, 0, 5, 3] = np.nan
+    C[0, 0, 5, w - 1] = np.nan
     codes = lac.rvq_encode(torch.from_numpy(Z).to(DEV), torch.from_numpy(C).to(DEV), G, K, 1).cpu().numpy()
     assert not np.any(codes[:, 0, 0] == 5)
     Cf = C.copy()

@@ -14,12 +14,23 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def run(A, g, m, alpha, beta, iters):
+def run(A, g, m, alpha, beta, iters, expect_status=0):
     Ad, gd, md = A.clone().to(DEV), g.clone().to(DEV), m.clone().to(DEV)
     D = torch.empty_like(Ad)
-    lac.spel_step(Ad, gd, md, alpha, beta, iters, D_out=D)
+    st = torch.full((1,), -1, dtype=torch.int32, device=DEV)
+    lac.spel_step(Ad, gd, md, alpha, beta, iters, D_out=D, status=st)
     torch.cuda.synchronize()
+    assert int(st.item()) == expect_status
     return Ad, md, D
+
+
+def spectrum_matrix(seed, d, r, cond):
+    """A d x r matrix with singular values geometrically spread over [1/cond, 1] (times 1e-3)."""
+    rng = np.random.default_rng(seed)
+    U = np.linalg.qr(rng.standard_normal((d, r)))[0]
+    V = np.linalg.qr(rng.standard_normal((r, r)))[0]
+    sv = np.geomspace(1.0 / cond, 1.0, r)
+    return torch.from_numpy((1e-3 * (U * sv) @ V.T).astype(np.float32))
 
 
 def check(A, g, m, alpha, beta, iters, Ad, md, D):
@@ -91,17 +102,84 @@ def test_spel_repeat_is_bitwise_deterministic_at_r128():
         assert torch.equal(x, y)
 
 
-def test_spel_wait_timeout_gives_nan_then_recovers(monkeypatch):
+def test_spel_wait_timeout_leaves_the_state_unchanged_then_recovers(monkeypatch):
     # the r x r iteration's workgroups wait for one another with a bounded wait; a test hook
-    # lowers the bound to zero, so the first wait gives up: the call must still end, with NaN
-    # in A and D, and the next call with the normal bound must be correct again
+    # lowers the bound to zero, so the first wait gives up and every kernel still exits: the
+    # step must then be abandoned -- A and m bit-for-bit as they were, status 1 -- and the next
+    # call with the normal bound must be correct again
     inp = synth.spel_inputs(35, 1024, 128, 1e-3)
+    m0 = torch.from_numpy(synth.gaussian(synth.stream(11, 1024, 128), (1024, 128), 1e-4).astype(np.float32))
     monkeypatch.setenv("MAPL_SPEL_SPIN_LIMIT", "0")
-    Ad, md, D = run(inp["A"], inp["g"], inp["m"], 1e-3, 0.9, 8)
-    assert torch.isnan(Ad).all() and torch.isnan(D).all()
+    Ad, md, D = run(inp["A"], inp["g"], m0, 1e-3, 0.9, 8, expect_status=1)
+    assert torch.equal(Ad.cpu(), inp["A"]) and torch.equal(md.cpu(), m0)
     monkeypatch.delenv("MAPL_SPEL_SPIN_LIMIT")
-    Ad, md, D = run(inp["A"], inp["g"], inp["m"], 1e-3, 0.9, 8)
-    check(inp["A"], inp["g"], inp["m"], 1e-3, 0.9, 8, Ad, md, D)
+    Ad, md, D = run(inp["A"], inp["g"], m0, 1e-3, 0.9, 8)
+    check(inp["A"], inp["g"], m0, 1e-3, 0.9, 8, Ad, md, D)
+
+
+@pytest.mark.parametrize("d,r,cond", [(1024, 128, 1e2), (1024, 128, 1e4), (256, 32, 1e4), (640, 96, 1e3),
+                                      (2048, 256, 1e2), (2048, 256, 1e4), (1056, 160, 1e4)])
+def test_spel_ill_conditioned_momentum(d, r, cond):
+    """The LMO's input spread over a wide spectrum (condition number 1e2 to
+    1e4), in both forms of the iteration: the r x r Gram-space one (r <= 128)
+    and the d x r one.  g = 0 leaves m = beta m0, so the prescribed spectrum
+    reaches the polar map unchanged."""
+    inp = synth.spel_inputs(400 + d + r, d, r, 1e-3)
+    m0 = spectrum_matrix(int(cond) + d + r, d, r, cond)
+    z = torch.zeros_like(inp["g"])
+    Ad, md, D = run(inp["A"], z, m0, 0.05, 0.9, 8)
+    check(inp["A"], z, m0, 0.05, 0.9, 8, Ad, md, D)
+
+
+@pytest.mark.parametrize("d,r,cond", [(1024, 128, 1e3), (2048, 256, 1e3)])
+def test_spel_ill_conditioned_gradient(d, r, cond):
+    """The Euclidean gradient itself ill-conditioned, with a non-zero momentum."""
+    inp = synth.spel_inputs(500 + d + r, d, r, 1e-3)
+    g = spectrum_matrix(7 + d, d, r, cond) * 10.0
+    m0 = spectrum_matrix(8 + d, d, r, 10.0)
+    Ad, md, D = run(inp["A"], g, m0, 1e-2, 0.9, 8)
+    check(inp["A"], g, m0, 1e-2, 0.9, 8, Ad, md, D)
+
+
+def test_spel_fed_by_the_codecs_own_projector_gradient():
+    """Algorithm 1 end to end on the 150M boundary: gA from both backward maps
+    of the bf16 codec (fp32 [1024][128]) is the Euclidean gradient of one
+    spel_step on the fp32 projector; judged against the oracle on the same gA."""
+    c = synth.CONFIGS["150m"]
+    N = c["B"] * c["T"]
+    inp = synth.codec_inputs(c["seed"], N, c["d"], c["r"], c["V"], "bf16")
+    g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    Z = lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"])
+    gZ, gA = lac.mapl_reconstruct_bwd(g["gXhat"], Z, g["A"])
+    lac.mapl_compress_bwd(gZ, g["X"], g["tids"], g["E"], g["P"], g["A"], gA=gA, accumulate=True)
+    torch.cuda.synchronize()
+    sp = synth.spel_inputs(c["seed"], c["d"], c["r"], 1e-3)
+    gA = gA.cpu()
+    assert torch.isfinite(gA).all()
+    m0 = torch.from_numpy(synth.gaussian(synth.stream(12, c["d"], c["r"]), (c["d"], c["r"]), 1.0).astype(np.float32))
+    Ad, md, D = run(sp["A"], gA, m0, 1e-3, 0.9, 8)
+    check(sp["A"], gA, m0, 1e-3, 0.9, 8, Ad, md, D)
+
+
+@pytest.mark.parametrize("d,r", [(1024, 128), (2048, 256)])
+def test_spel_state_saved_and_reloaded_continues_bit_exactly(d, r):
+    """Algorithm 1 threads (A_p, m_p) from step to step: two steps in place
+    equal one step, a round trip of A and m through host memory into fresh
+    device buffers, and a second step -- bit for bit."""
+    inp = synth.spel_inputs(600 + d, d, r, 1e-3)
+    gd = inp["g"].to(DEV)
+    A1, m1 = inp["A"].clone().to(DEV), inp["m"].clone().to(DEV)
+    lac.spel_step(A1, gd, m1, 1e-3, 0.9, 8)
+    lac.spel_step(A1, gd, m1, 1e-3, 0.9, 8)
+    A2, m2 = inp["A"].clone().to(DEV), inp["m"].clone().to(DEV)
+    lac.spel_step(A2, gd, m2, 1e-3, 0.9, 8)
+    torch.cuda.synchronize()
+    saved = (A2.cpu().numpy().copy(), m2.cpu().numpy().copy())
+    del A2, m2
+    A3, m3 = torch.from_numpy(saved[0]).to(DEV), torch.from_numpy(saved[1]).to(DEV)
+    lac.spel_step(A3, gd, m3, 1e-3, 0.9, 8)
+    torch.cuda.synchronize()
+    assert torch.equal(A1, A3) and torch.equal(m1, m3)
 
 
 @pytest.mark.parametrize("d,r,iters", [(1024, 128, 1), (1024, 128, 2), (256, 64, 3), (640, 96, 4), (128, 32, 6),

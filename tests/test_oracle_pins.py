@@ -508,6 +508,84 @@ def test_rvq_matches_brute_force_loops(R_c):
     np.testing.assert_allclose(rvq.decode(codes, C, G, K, R) + res, Z, atol=1e-13)
 
 
+def _loop_dists(res_rows, book_g):
+    """Squared distances of each residual row to each codeword, by explicit loops."""
+    out = np.zeros((len(res_rows), len(book_g)))
+    for n, x in enumerate(res_rows):
+        for k, c in enumerate(book_g):
+            out[n, k] = sum((float(x[j]) - float(c[j])) ** 2 for j in range(len(c)))
+    return out
+
+
+@pytest.mark.parametrize("R_c", [1, 3])
+def test_rvq_teacher_forcing_follows_the_teacher_and_reports_exact_distances(R_c):
+    """With teacher codes, each round's residual is Z minus the TEACHER's
+    codewords of the earlier rounds (not the oracle's own), d_teacher is the
+    teacher codeword's distance, and codes / d1 / d2 are the argmin and the two
+    smallest distances on that residual -- all checked by explicit loops.  The
+    teacher picks the second-nearest codeword in round 0, so its residual
+    differs from the oracle's own."""
+    rng = np.random.default_rng(31)
+    N, G, K, w, R = 9, 3, 6, 2, 3
+    C = rng.standard_normal((R_c, G, K, w))
+    Z = rng.standard_normal((N, G * w))
+    own = rvq.encode(Z, C, G, K, R)
+    teacher = own["codes"].copy()
+    for n in range(N):
+        for g in range(G):
+            dd = _loop_dists([Z[n, g * w:(g + 1) * w]], C[0, g])[0]
+            teacher[n, 0, g] = int(np.argsort(dd, kind="stable")[1])   # second nearest
+    teacher[:, 1:, :] = rng.integers(0, K, size=(N, R - 1, G))
+    out = rvq.encode(Z, C, G, K, R, teacher=teacher)
+    res = Z.copy()
+    for rho in range(R):
+        book = C[rho if R_c > 1 else 0]
+        for g in range(G):
+            sl = slice(g * w, (g + 1) * w)
+            D = _loop_dists(res[:, sl], book[g])
+            srt = np.sort(D, axis=1)
+            np.testing.assert_array_equal(out["codes"][:, rho, g], np.argmin(D, axis=1))
+            np.testing.assert_allclose(out["d1"][:, rho, g], srt[:, 0], rtol=1e-12, atol=1e-15)
+            np.testing.assert_allclose(out["d2"][:, rho, g], srt[:, 1], rtol=1e-12, atol=1e-15)
+            np.testing.assert_allclose(out["d_teacher"][:, rho, g], D[np.arange(N), teacher[:, rho, g]],
+                                       rtol=1e-12, atol=1e-15)
+            res[:, sl] = res[:, sl] - book[g][teacher[:, rho, g]]
+    # the final residual is Z minus the teacher's codewords, exactly as decode forms them
+    np.testing.assert_allclose(out["residual"], res, atol=1e-13)
+    np.testing.assert_allclose(rvq.decode(teacher, C, G, K, R) + out["residual"], Z, atol=1e-13)
+    # round 0 is judged on Z itself: the teacher's second-nearest pick is never the argmin
+    assert np.all(out["d_teacher"][:, 0, :] >= out["d1"][:, 0, :])
+    assert np.all(out["d_teacher"][:, 0, :] == out["d2"][:, 0, :])
+
+
+def test_rvq_teacher_equal_to_own_codes_changes_nothing():
+    rng = np.random.default_rng(32)
+    N, G, K, w, R = 40, 4, 16, 4, 2
+    C = rng.standard_normal((R, G, K, w))
+    Z = rng.standard_normal((N, G * w))
+    own = rvq.encode(Z, C, G, K, R)
+    tf = rvq.encode(Z, C, G, K, R, teacher=own["codes"])
+    for key in ("codes", "d1", "d2", "residual", "energy"):
+        np.testing.assert_array_equal(tf[key], own[key])
+    np.testing.assert_array_equal(tf["d_teacher"], own["d1"])
+
+
+def test_rvq_single_codeword_and_odd_codebook_sizes():
+    """K = 1 gives code 0 and d2 = inf; for K not a multiple of anything the
+    argmin still matches explicit loops (the kernels pad K)."""
+    rng = np.random.default_rng(33)
+    N, G, w = 11, 2, 4
+    Z = rng.standard_normal((N, G * w))
+    one = rvq.encode(Z, rng.standard_normal((1, G, 1, w)), G, 1, 2)
+    assert np.all(one["codes"] == 0) and np.all(np.isinf(one["d2"]))
+    for K in (5, 33):
+        C = rng.standard_normal((1, G, K, w))
+        out = rvq.encode(Z, C, G, K, 1)
+        for g in range(G):
+            D = _loop_dists(Z[:, g * w:(g + 1) * w], C[0, g])
+            np.testing.assert_array_equal(out["codes"][:, 0, g], np.argmin(D, axis=1))
+
+
 def test_rvq_codeword_inputs_come_back_with_zero_residual():
     rng = np.random.default_rng(12)
     N, G, K, w = 50, 4, 16, 8
