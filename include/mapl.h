@@ -298,6 +298,25 @@ int spel_step(float* A, const float* g, float* m, float alpha, float beta, int n
               float* D_out, int32_t* status, int64_t d, int64_t r, void* ws, size_t ws_bytes,
               hipStream_t stream);
 
+/* For callers that cannot allocate -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: spel_step with no `ws`
+ * argument.  Its workspace is a static device array of the library,
+ * MAPL_STATIC_SCRATCH_BYTES long, of which each GPU the library runs on holds
+ * its own copy until the process ends; its address is looked up once per
+ * device when the device is set up (mapl_init, or the first call on that
+ * device).  The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine).  Shapes whose spel_workspace_bytes(d, r) exceeds
+ * MAPL_STATIC_SCRATCH_BYTES (e.g. d x r = 2048 x 256 fits, 4096 x 256 does
+ * not) are rejected with MAPL_ERR_WORKSPACE.  The array keeps the last call's
+ * contents, and everything the step needs cleared it clears itself, in a
+ * kernel.  Every call on one GPU shares that GPU's array: calls that overlap
+ * in time on one GPU (different streams, or several threads) race and give
+ * wrong results; calls on one stream are ordered and safe.  Arguments,
+ * results, status and errors otherwise as for spel_step. */
+#define MAPL_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int spel_step_static(float* A, const float* g, float* m, float alpha, float beta, int ns_iters,
+                     float* D_out, int32_t* status, int64_t d, int64_t r, hipStream_t stream);
+
 /* The same SPEL step with the Polar Express polar map that Section 3.3 and
  * Table 8 name (5 LMO steps, 7 retraction steps; the pages print no
  * coefficients).  Step t multiplies X on the right by a I + b S + c S^2,

@@ -26,7 +26,7 @@ __all__ = [
     "mapl_bwd_workspace_bytes", "mapl_reconstruct_bwd", "mapl_compress_bwd",
     "mapl_anchor_grad_workspace_bytes", "mapl_anchor_grad", "mapl_check_tids",
     "rvq_encode", "rvq_decode", "rvq_stream_apply", "spel_workspace_bytes", "spel_step",
-    "spel_step_polar_express", "spel_polar_express_coefficients",
+    "spel_step_static", "spel_step_polar_express", "spel_polar_express_coefficients",
     "MAPL_F32", "MAPL_BF16",
 ]
 
@@ -65,6 +65,7 @@ _SIGS = {
     "rvq_stream_apply": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
     "spel_workspace_bytes": (_sz, [_i64, _i64]),
     "spel_step": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),
+    "spel_step_static": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _vp, _vp, _i64, _i64, _vp]),
     "spel_step_polar_express": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _i32, _f32, _vp, _vp, _i64, _i64, _vp, _sz,
                                        _vp]),
     "spel_polar_express_coefficients": (_i32, [ctypes.c_double, _i32, _vp, _vp]),
@@ -451,6 +452,18 @@ def spel_step(A, g, m, alpha: float, beta: float, ns_iters: int = 8, D_out=None,
                             _dev(D_out, "D_out", torch.float32) if D_out is not None else None,
                             _opt(status, "status", torch.int32), d, r,
                             ws.data_ptr() if ws is not None else None, wb, _stream(stream)), "spel_step")
+    return D_out
+
+
+def spel_step_static(A, g, m, alpha: float, beta: float, ns_iters: int = 8, D_out=None, status=None, stream=None):
+    """spel_step with its workspace in the library's static device array
+    (nothing is allocated: usable under graph capture).  Calls that overlap
+    in time on one GPU race; see include/mapl.h."""
+    d, r = A.shape
+    _check(load().spel_step_static(_dev(A, "A", torch.float32), _dev(g, "g", torch.float32),
+                                   _dev(m, "m", torch.float32), float(alpha), float(beta), int(ns_iters),
+                                   _dev(D_out, "D_out", torch.float32) if D_out is not None else None,
+                                   _opt(status, "status", torch.int32), d, r, _stream(stream)), "spel_step_static")
     return D_out
 
 

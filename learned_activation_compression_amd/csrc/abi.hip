@@ -23,6 +23,15 @@ LdsEntry g_lds[kMaxLdsKernels];
 int g_lds_count = 0;
 bool g_lds_overflow = false;
 std::atomic<uint64_t> g_lds_ready{0};  // devices whose limits are raised (bit = device index < 64)
+
+// The scratch of spel_step_static, for callers that cannot allocate: one array per device
+// (each GPU the library runs on holds its own copy until the process ends).  Host code never
+// uses the array's name as an address: its device address is looked up once per device, with
+// that device current, when the device is prepared (g_scratch), and only that address is
+// passed to kernels.
+constexpr size_t kScratchBytes = MAPL_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void* g_scratch[64] = {};
 }  // namespace
 
 void lds_register(const void* kernel, int bytes) {
@@ -30,6 +39,8 @@ void lds_register(const void* kernel, int bytes) {
   else g_lds_overflow = true;
 }
 
+// Device set-up, once per device (devices 0..63; others are set up on every call): the
+// dynamic-LDS limits, and the device address of the static scratch array.
 hipError_t lds_prepare_device() {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -41,8 +52,21 @@ hipError_t lds_prepare_device() {
     e = hipFuncSetAttribute(g_lds[i].kernel, hipFuncAttributeMaxDynamicSharedMemorySize, g_lds[i].bytes);
     if (e != hipSuccess) return e;
   }
-  if (bit != 0) g_lds_ready.fetch_or(bit, std::memory_order_acq_rel);
+  if (bit != 0) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;  // a racing thread stores the same address
+    g_lds_ready.fetch_or(bit, std::memory_order_acq_rel);
+  }
   return hipSuccess;
+}
+
+// The current device's scratch address (after a successful lds_prepare_device), or NULL.
+static void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  return g_scratch[dev];
 }
 }  // namespace mapl
 
@@ -468,6 +492,25 @@ int spel_step(float* A, const float* g, float* m, float alpha, float beta, int n
   if (reinterpret_cast<uintptr_t>(status) & 3) return MAPL_ERR_ARG;
   LaunchScope ls;
   if (!ls.ready()) return MAPL_ERR_HIP;
+  launch_spel(A, g, m, alpha, beta, ns_iters, D_out, status, int(d), int(r), ws, stream);
+  return ls.done();
+}
+
+int spel_step_static(float* A, const float* g, float* m, float alpha, float beta, int ns_iters, float* D_out,
+                     int32_t* status, int64_t d, int64_t r, hipStream_t stream) {
+  if (d < 1 || r < 1 || r > d || r > 1024 || d % 32 || r % 32 || d > (1 << 24)) return MAPL_ERR_SHAPE;
+  if (!A || !g || !m) return MAPL_ERR_NULL;
+  if (!(beta >= 0.f && beta < 1.f) || !(alpha >= 0.f && alpha <= 0.7f) || ns_iters < 1 || ns_iters > 64)
+    return MAPL_ERR_ARG;
+  if (spel_ws_bytes(d, r) > kScratchBytes) return MAPL_ERR_WORKSPACE;  // beyond the static scratch
+  if ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(g) | reinterpret_cast<uintptr_t>(m) |
+       reinterpret_cast<uintptr_t>(D_out)) & 15)
+    return MAPL_ERR_ARG;
+  if (reinterpret_cast<uintptr_t>(status) & 3) return MAPL_ERR_ARG;
+  LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
+  void* ws = device_scratch();
+  if (ws == nullptr) return MAPL_ERR_HIP;
   launch_spel(A, g, m, alpha, beta, ns_iters, D_out, status, int(d), int(r), ws, stream);
   return ls.done();
 }

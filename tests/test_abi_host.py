@@ -24,7 +24,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = lac.exported_symbols()
-    assert len(names) == 21, names
+    assert len(names) == 22, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lac._SIGS), set(names) ^ set(lac._SIGS)
@@ -231,6 +231,15 @@ def test_spel_validation(lib):
     assert f(FAKE, FAKE, odd, 1e-3, 0.9, 8, None, None, 2048, 256, FAKE, ws, None) == EARG      # m not 16-B aligned
     assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, ctypes.c_void_p(0x1002), 2048, 256, FAKE, ws,
              None) == EARG                                                                     # status 4-B aligned
+
+
+def test_spel_step_static_validation(lib):
+    f = lib.spel_step_static
+    assert f(None, FAKE, FAKE, 1e-3, 0.9, 8, None, None, 1024, 128, None) == ENULL
+    assert f(FAKE, FAKE, FAKE, 1e-3, 1.0, 8, None, None, 1024, 128, None) == EARG      # beta < 1
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, None, 1024, 100, None) == ESHAPE    # r % 32
+    assert f(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, None, 4096, 256, None) == EWS       # beyond the 16 MiB scratch
+    assert f(ctypes.c_void_p(0x1004), FAKE, FAKE, 1e-3, 0.9, 8, None, None, 1024, 128, None) == EARG
 
 
 def test_spel_polar_express_validation(lib):
