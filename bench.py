@@ -36,6 +36,89 @@ BF16_PEAK_TFLOPS = 2500.0    # dense bf16 matrix
 F32_PEAK_TFLOPS = 157.3      # fp32 matrix
 
 
+def _only_codec(lac, dev, cfg, r, maps, x_kind="gauss"):
+    """The codec maps of one configuration at rank r, on resident inputs."""
+    import synth
+    c = synth.CONFIGS[cfg]
+    N, d = c["B"] * c["T"], c["d"]
+    inp = synth.codec_inputs(c["seed"], N, d, r, c["V"], "bf16", x_kind=x_kind)
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    pk = lac.mapl_pack(g["P"], g["A"])
+    Z = lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"], pk=pk, pk_ready=True)
+    Xh = torch.empty((N, d), dtype=torch.bfloat16, device=dev)
+    gZ, gX = torch.empty_like(Z), torch.empty_like(Xh)
+    gA = torch.empty((d, r), dtype=torch.float32, device=dev)
+    ws = torch.empty(lac.mapl_bwd_workspace_bytes(c["B"], c["T"], d, r), dtype=torch.uint8, device=dev)
+    fns = {
+        "compress": lambda: lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"], Z=Z, pk=pk, pk_ready=True),
+        "reconstruct": lambda: lac.mapl_reconstruct(Z, g["tids"], g["E"], g["P"], g["A"], Xhat=Xh, pk=pk,
+                                                    pk_ready=True),
+        "reconstruct_bwd": lambda: lac.mapl_reconstruct_bwd(g["gXhat"], Z, g["A"], gZ=gZ, gA=gA, pk=pk,
+                                                            pk_ready=True, ws=ws),
+        "compress_bwd": lambda: lac.mapl_compress_bwd(gZ, g["X"], g["tids"], g["E"], g["P"], g["A"], gX=gX, gA=gA,
+                                                      accumulate=True, pk=pk, pk_ready=True, ws=ws),
+    }
+    return lambda: [fns[m]() for m in maps]
+
+
+def _only_rvq(lac, dev, width):
+    """RVQ encode at the rvq workload: Z (r = 256) from the codec in 8 groups of width 32, or the
+    receiver's gZ in the paper's 128 groups of width 2; K = 256, R = 2."""
+    import synth
+    c = synth.CONFIGS["rvq"]
+    N, d, r, K, R = c["B"] * c["T"], c["d"], c["r"], c["K"], c["R"]
+    inp = synth.codec_inputs(c["seed"], N, d, r, c["V"], "bf16")
+    g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    Z = lac.mapl_compress(g["X"], g["tids"], g["E"], g["P"], g["A"])
+    if width == 2:
+        Z, _ = lac.mapl_reconstruct_bwd(g["gXhat"], Z, g["A"])
+        G, var = r // 2, 1.0
+    else:
+        G, var = c["G"], c["codebook_var"]
+    C = synth.rvq_codebooks(c["seed"], 1, G, K, r // G, var, sub=1 if width == 2 else 0).to(dev)
+    codes = torch.empty((N, R, G), dtype=torch.uint8, device=dev)
+    return lambda: lac.rvq_encode(Z, C, G, K, R, codes=codes)
+
+
+def _only_spel(lac, dev, d, r):
+    import synth
+    sp = synth.CONFIGS["1b"]["spel"]
+    si = synth.spel_inputs(5, d, r, sp["g_var"])
+    A, gg, m = si["A"].to(dev), si["g"].to(dev), si["m"].to(dev)
+    ws = torch.empty(lac.spel_workspace_bytes(d, r), dtype=torch.uint8, device=dev)
+    return lambda: lac.spel_step(A, gg, m, sp["alpha"], sp["beta"], sp["ns_iters"], ws=ws)
+
+
+def _only_copy(lac, dev):
+    """A plain 256 MiB device copy: the known-size reference for the HBM byte counters."""
+    src = torch.ones(1 << 26, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    return lambda: dst.copy_(src)
+
+
+ONLY_CASES = {
+    "compress-150m": lambda lac, dev: _only_codec(lac, dev, "150m", 128, ["compress"]),
+    "reconstruct-150m": lambda lac, dev: _only_codec(lac, dev, "150m", 128, ["reconstruct"]),
+    "bwd-150m": lambda lac, dev: _only_codec(lac, dev, "150m", 128, ["reconstruct_bwd", "compress_bwd"]),
+    "pair-r256": lambda lac, dev: _only_codec(lac, dev, "sweep", 256, ["compress", "reconstruct"], "lowrank"),
+    "pair-r512": lambda lac, dev: _only_codec(lac, dev, "sweep", 512, ["compress", "reconstruct"], "lowrank"),
+    "rvq-w32": lambda lac, dev: _only_rvq(lac, dev, 32),
+    "rvq-w2": lambda lac, dev: _only_rvq(lac, dev, 2),
+    "spel-1024x128": lambda lac, dev: _only_spel(lac, dev, 1024, 128),
+    "spel-2048x256": lambda lac, dev: _only_spel(lac, dev, 2048, 256),
+    "copy-256mib": _only_copy,
+}
+
+
+def run_only(lac, dev, case, reps):
+    fn = ONLY_CASES[case](lac, dev)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    print(f"only {case}: {reps} runs done", flush=True)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -44,11 +127,15 @@ def parse():
     p.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=16384, help="token sample of the CPU-oracle baseline")
-    p.add_argument("--cpu-reps", type=int, default=5, help="repetitions of the CPU-oracle sample")
+    p.add_argument("--cpu-reps", type=int, default=3, help="timed repetitions of the CPU-oracle sample (median)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run one plain 256 MiB device copy first (a known-size reference for HBM byte counters)")
     p.add_argument("--cases", metavar="FILE", default=None,
                    help="also time every workload of the measurement table and write them to FILE (JSON)")
+    p.add_argument("--only", metavar="CASE", default=None, choices=sorted(ONLY_CASES),
+                   help="run one workload --reps times (warm, untimed) and exit: the command that hardware-counter "
+                        "profiles (rocprofv3 --pmc) run")
+    p.add_argument("--reps", type=int, default=3, help="repetitions of --only")
     return p.parse_args()
 
 
@@ -184,16 +271,21 @@ def _device_info():
 
 
 def cpu_baseline(inp, n_tok, reps):
-    """The fp64 oracle of the same step on a token sample (host cores), run
-    `reps` times; the rate is the sample's tokens over the mean time."""
+    """The fp64 oracle of the same step on a token sample (host cores): one
+    warm-up run, then `reps` timed runs; the rate is the sample's tokens over
+    the median time.  BLAS is threaded over the cores this process may run on
+    (its affinity mask, capped by OMP_NUM_THREADS when that is set)."""
     from oracle import codec, rvq, spel
     import synth
     S = Shape
+    cores = len(os.sched_getaffinity(0))
+    if os.environ.get("OMP_NUM_THREADS", "").isdigit():
+        cores = max(1, min(cores, int(os.environ["OMP_NUM_THREADS"])))
     try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+        limiter = None
     sl = slice(0, n_tok)
     X = inp["X"][sl].double().numpy()
     t = inp["tids"][sl].numpy()
@@ -202,17 +294,24 @@ def cpu_baseline(inp, n_tok, reps):
     w = S.r // S.G
     C = synth.rvq_codebooks(S.seed, 1, S.G, S.K, w, 1.0 / 32.0).double().numpy()
     sp = synth.spel_inputs(S.seed, S.d, S.r, 1e-3)
-    t0 = time.perf_counter()
-    for _ in range(reps):
+    def one():
         Z = codec.compress(X, t, E, P, A)
         enc = rvq.encode(Z, C, S.G, S.K, S.R)
         Zq = rvq.decode(enc["codes"], C, S.G, S.K, S.R)
-        Xh = codec.reconstruct(Zq, t, E, P, A)
+        codec.reconstruct(Zq, t, E, P, A)
         gZ, gA1 = codec.reconstruct_bwd(gXh, Zq, A)
-        gX, gA2 = codec.compress_bwd(gZ, X, t, E, P, A)
+        _, gA2 = codec.compress_bwd(gZ, X, t, E, P, A)
         spel.spel_step(sp["A"].double().numpy(), gA1 + gA2, sp["m"].double().numpy(), S.alpha, S.beta, S.ns)
-        del Xh, gX
-    dt = (time.perf_counter() - t0) / reps
+
+    one()  # warm-up
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        one()
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    if limiter is not None:
+        limiter.restore_original_limits()
     model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -221,7 +320,7 @@ def cpu_baseline(inp, n_tok, reps):
         pass
     return {"value": n_tok / dt, "unit": "boundary tokens/s", "cores": int(cores), "kind": "oracle", "cpu": model,
             "sample": f"one full step of the fp64 oracle (codec fwd+bwd, RVQ encode/decode, one spel_step on "
-                      f"1024x128) on {n_tok} of the {S.N} tokens, {reps} runs, mean {dt:.2f} s per run"}
+                      f"1024x128) on {n_tok} of the {S.N} tokens: 1 warm-up, median of {reps} runs, {dt:.2f} s per run"}
 
 
 def _evict(flush):
@@ -419,6 +518,9 @@ def main():
     lac.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only:
+        run_only(lac, dev, args.only, max(1, args.reps))
+        return
     S = Shape
     inp, g = make_inputs(dev)
     b = alloc(g, lac)
