@@ -422,7 +422,8 @@ static int check_rvq_shape(int64_t N, int64_t r, int64_t G, int64_t K, int64_t R
   if (r % G != 0 || K > 256) return MAPL_ERR_SHAPE;
   if (N * r > (int64_t(1) << 40)) return MAPL_ERR_SHAPE;
   // codebook rows move as 16-byte vectors: every round's book starts 16-byte aligned
-  if ((stride != 0 && stride < r * K) || stride % 4 != 0) return MAPL_ERR_ARG;
+  if ((stride != 0 && stride < r * K) || stride % 4 != 0 || stride < 0 || stride > (int64_t(1) << 40))
+    return MAPL_ERR_ARG;
   return MAPL_OK;
 }
 
