@@ -73,11 +73,12 @@ __device__ __forceinline__ void pair_of(int p, int nb, int& bi, int& bj) {
 // acc1 = A_bi^T g_bj and acc2 = A_bj^T g_bi.  TWO = 0: piece = X_bi^T X_bj.
 // Tile (bi, bj) of part[grp] gets the piece, tile (bj, bi) its transpose.
 // `zero`, when given, holds nzero words cleared for the launches that follow:
-// the arrival flags [0, 64) and the timeout word [64] of the Gram-space
+// the progress counters [0, 128) and the timeout word [128] of the Gram-space
 // iteration, and (cleared by the step's first launch only) the step's sticky
-// timeout word [65], which decides at the end whether the step is committed.
-constexpr int kRsSyncWords = 68;
-constexpr int kRsTimeoutWord = 64, kRsStickyWord = 65;
+// timeout word [129], which decides at the end whether the step is committed.
+constexpr int kRsFlagWords = 128;
+constexpr int kRsTimeoutWord = 128, kRsStickyWord = 129;
+constexpr int kRsSyncWords = 132;
 template <int TWO>
 __global__ __launch_bounds__(256) void k_spel_gram(const float* __restrict__ Xl, const float* __restrict__ Xr,
                                                    float* __restrict__ part, int d, int r, int groups,
@@ -286,35 +287,43 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
 // NS_n(X0) = X0 (s Q_n): one Gram, n steps on r x r matrices and one product,
 // in place of n Grams and n products on d x r matrices.
 //
-// One launch of r/4 + r/16 workgroups.  S workgroup J < r/4 owns rows
-// 4 J .. 4 J + 3 of the S_k: each step it forms its rows of S_k^2 and then of
-// S_k^3 (right factor S_k both times) and writes its rows of S_{k+1}.  Q
-// workgroup J owns rows 16 J .. 16 J + 15 of the Q_k and forms its rows of
-// Q_k S_k.  Right factors are read into registers straight from global
-// memory, row j of S_k standing for column j (S_k is symmetric up to
-// rounding).  The S_k live in two global buffers, and after every step each
-// workgroup raises its arrival flag in the workspace to the step number and
-// waits until all flags have reached it (one wave polls them all): arriving
-// means the step's stores are visible to the device (one release fence per
-// workgroup) and its reads of the older buffer are over.  A wait that exceeds
-// its bound (a second or two) sets the timeout word, and the Q workgroups
-// then write NaN: a wrong result is never silent and no wait is endless.  The
-// launch is ordinary; its few workgroups (at most 40) are resident together
-// on an otherwise idle device.
+// Two steps per exchange.  Since S_{k+1} = h(S_k) with
+// h(x) = 2.25 x - 1.5 x^2 + 0.25 x^3, rows of S_{k+1}, S_{k+1}^2 = S_{k+1} h(S_k)
+// and S_{k+1}^3 = S_{k+1}^2 h(S_k), hence of S_{k+2}, are all rows times
+// powers of S_k: each "times h(S_k)" is three products with right factor S_k
+// (Horner), so S_{k+2} takes 8 products and only even S_k are ever
+// exchanged.  Likewise Q_{k+2} = B (1.5 I - 0.5 h(S_k)) with B = Q_k T_k
+// (4 products), and an odd step count ends with one plain step on the last
+// even S_k.
 //
-// Matrix cores (fp32):
-//   S rows, v_mfma_f32_4x4x1_16b_f32: 16 blocks of 4 x 4; lane l is row l % 4
-//     of block l / 4 in A, column l % 4 of block l / 4 in B and D (register v:
-//     row v).  With A the same in every block and block b of column group g
-//     taking columns 64 g + 4 b .. + 3, lane l of group g accumulates column
-//     64 g + l of the 4 output rows.  The 4 waves split K and add their
-//     partial rows in LDS in wave order.
-//   Q rows, v_mfma_f32_16x16x4_f32: lane l is row l % 16 (A) or column l % 16
-//     (B, D) with k slot l / 16; D register v is row 4 (l / 16) + v.  Lane
-//     (kq, c) takes k = 16 kb + 4 kq + e at step e of K block kb; each tile's
-//     sum runs as two chains (even and odd kb) added at the end.
-constexpr int kRsS = 4;   // rows of S_k per S workgroup
-constexpr int kRsQ = 16;  // rows of Q_k per Q workgroup
+// One launch of r/2 workgroups of 256 threads, each owning 4 rows: S
+// workgroup J < r/4 rows 4 J .. 4 J + 3 of the even S_k, Q workgroup J rows
+// 4 J .. 4 J + 3 of the Q_k.  Only the S_k chain is sequential: the S
+// workgroups wait for each other and never for the Q workgroups, which follow
+// the chain one exchanged S_k at a time and hold nothing back but a buffer
+// (the exchanged S_k live in a ring of kRsRing buffers; a slot is written
+// again only after every Q workgroup has read what it held).
+//
+// Exchange.  Each workgroup owns a progress counter: an S workgroup's is the
+// number of S_k whose rows it has stored, a Q workgroup's the number of S_k it
+// has read.  The S_k travel as device-coherent loads and stores (the sc1
+// cache policy: they bypass the per-XCD caches that the device's other XCDs
+// do not see) and the counters as device-scope atomics, so no cache-wide
+// write-back or invalidate is needed: a workgroup's stores are complete
+// (s_waitcnt) before its counter moves, and a reader loads S_k only after it
+// has seen every counter it needs.  A wait that exceeds its bound (a second or
+// two) sets the timeout word, and the Q workgroups then write NaN: a wrong
+// result is never silent and no wait is endless.  The launch is ordinary; its
+// few workgroups (at most 64) are resident together on an otherwise idle
+// device.
+//
+// Matrix cores (fp32), v_mfma_f32_4x4x1_16b_f32: 16 blocks of 4 x 4; lane l
+// is row l % 4 of block l / 4 in A, column l % 4 of block l / 4 in B and D
+// (register v: row v).  With A the same in every block and block b of column
+// group g taking columns 64 g + 4 b .. + 3, lane l of group g accumulates
+// column 64 g + l of the 4 output rows.  The 4 waves split K and add their
+// partial rows in LDS in wave order.
+constexpr int kRsS = 4;  // rows of S_k or Q_k per workgroup
 // each spin is a sleep and an uncached load: 2^20 spins take about 1-2 s.  The
 // environment variable MAPL_SPEL_SPIN_LIMIT lowers the bound, for tests of the
 // timeout path.
@@ -327,25 +336,43 @@ __device__ __forceinline__ f32x4 mfma_f32_4x4x1(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
-// Raise this workgroup's flag to `epoch` once every wave's stores are complete
-// and published (release fence), then wait until all nblk flags have reached
-// it and make the other workgroups' stores visible (acquire fence).  On
-// timeout the iteration's timeout word flags[64] and the step's sticky word
-// flags[65] are set at once and false is returned.
-__device__ bool rs_sync(unsigned* flags, int nblk, unsigned epoch, unsigned limit, int* slot) {
+constexpr int kRsRing = 4;  // S_k buffers
+
+// Device-coherent (sc1) 16-byte accesses through a buffer resource: the
+// compiler tracks them like its own loads and stores.  Offsets in bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rs_rsrc(const float* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ f32x4 rs_ld(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16));
+}
+__device__ __forceinline__ void rs_st(__amdgpu_buffer_rsrc_t rs, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 16);
+}
+
+// Move this workgroup's progress counter to `val` once every wave's stores are
+// complete.
+__device__ __forceinline__ void rs_publish(unsigned* flags, int idx, unsigned val) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(flags + idx, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wait (one wave polls) until counters [0, ns) are >= sneed and counters
+// [ns, ns + nq) are >= qneed.  On timeout the iteration's timeout word and
+// the step's sticky word are set and false is returned.
+__device__ bool rs_wait(unsigned* flags, int ns, unsigned sneed, int nq, unsigned qneed, unsigned limit, int* slot) {
   if (threadIdx.x < 64) {
     const int l = threadIdx.x;
-    if (l == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_store(flags + blockIdx.x, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
     unsigned spins = 0;
     int ok = 1;
     for (;;) {
-      const unsigned v = (l < nblk) ? __hip_atomic_load(flags + l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : epoch;
-      if (__all(v >= epoch)) break;
+      bool done = true;
+      for (int i = l; i < ns + nq; i += 64) {
+        const unsigned v = __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        done = done && v >= (i < ns ? sneed : qneed);
+      }
+      if (__all(done)) break;
       __builtin_amdgcn_s_sleep(1);
       if (++spins > limit) {
         ok = 0;
@@ -356,30 +383,25 @@ __device__ bool rs_sync(unsigned* flags, int nblk, unsigned epoch, unsigned limi
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (l == 0) *slot = ok;
   }
   __syncthreads();
-  return *slot != 0;
+  const bool ok = *slot != 0;
+  __syncthreads();  // every wave has read the slot before it is written again
+  return ok;
 }
 
-// a[kb] = L[c][16 kb + 4 kq .. + 3] from 16 rows in LDS (stride R + 4)
+// S [R][R] (ring slot, row-major) -> LDS rows of pitch R + 4, every thread's
+// 16-byte loads issued before the first is stored (consecutive threads read
+// consecutive 16 bytes)
 template <int R>
-__device__ __forceinline__ void rs_left(const float* __restrict__ Lsh, f32x4 (&a)[R / 16], int kq, int c) {
-#pragma unroll
-  for (int kb = 0; kb < R / 16; ++kb) a[kb] = ld4(Lsh + c * (R + 4) + 16 * kb + 4 * kq);
-}
-
-// S [R][R] (global, row-major) -> LDS rows of pitch R + 4, every thread's 16-byte loads issued before
-// the first is stored (consecutive threads read consecutive 16 bytes)
-template <int R>
-__device__ __forceinline__ void rs_stage(const float* __restrict__ src, float* __restrict__ sh) {
+__device__ __forceinline__ void rs_stage(__amdgpu_buffer_rsrc_t rs, int base, float* __restrict__ sh) {
   constexpr int U = R / 4, TOTAL = R * U, PER = (TOTAL + 255) / 256;
   f32x4 v[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
     const int u = threadIdx.x + 256 * p;
-    if (u < TOTAL) v[p] = ld4(src + 4 * u);
+    if (u < TOTAL) v[p] = rs_ld(rs, base + 16 * u);
   }
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
@@ -438,154 +460,144 @@ struct RsRows {
   }
 };
 
-// The right factor of a Q workgroup's output tiles n = w + 4 t:
-// b[t][kb] = S[16 n + c][16 kb + 4 kq .. + 3] (zero for n >= R / 16).
-template <int R>
-struct RsRight {
-  static constexpr int NT = R / 16, TW = (NT + 3) / 4, KB = R / 16;
-  f32x4 b[TW][KB];
-  __device__ __forceinline__ void load(const float* __restrict__ Ssh, int w, int kq, int c) {  // S_k staged in LDS
-#pragma unroll
-    for (int t = 0; t < TW; ++t)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        b[t][kb] = (w + 4 * t < NT) ? ld4(Ssh + (16 * (w + 4 * t) + c) * (R + 4) + 16 * kb + 4 * kq)
-                                    : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-};
-
-// acc[t] = L S over a Q workgroup wave's output tiles
-template <int R>
-__device__ __forceinline__ void rs_product(const f32x4 (&a)[R / 16], const RsRight<R>& B,
-                                           f32x4 (&acc)[RsRight<R>::TW], int w) {
-  constexpr int TW = RsRight<R>::TW, KB = R / 16, NT = R / 16;
-  f32x4 h[TW][2];
-#pragma unroll
-  for (int t = 0; t < TW; ++t) h[t][0] = h[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int t = 0; t < TW; ++t)
-        if (w + 4 * t < NT) h[t][kb & 1] = mfma_f32_16x16x4(a[kb][e], B.b[t][kb][e], h[t][kb & 1]);
-#pragma unroll
-  for (int t = 0; t < TW; ++t) acc[t] = h[t][0] + h[t][1];
-}
-
 // part: G Gram pieces [R][R] of X0 (their sum is X0^T X0); nparts: the nnp
 // partial sums of ||X0||_F^2 (s = 1/||X0||_F, 0 for X0 = 0) or null (s = 1);
-// Sbuf: 2 R x R floats; flags: kRsSyncWords words cleared by the launch
+// Sring: kRsRing R x R floats; flags: kRsSyncWords words cleared by the launch
 // before; M: s Q_iters [R][R]; limit: polls per wait before it gives up.
 template <int R>
 __global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part, int G,
                                                  const float* __restrict__ nparts, int nnp, int iters,
-                                                 float* __restrict__ Sbuf, unsigned* __restrict__ flags,
+                                                 float* __restrict__ Sring, unsigned* __restrict__ flags,
                                                  float* __restrict__ M, unsigned limit) {
-  constexpr int RP = R + 4, NT = R / 16, TW = (NT + 3) / 4, KB = R / 16;
-  constexpr int NS = R / kRsS, NQ = R / kRsQ, NE = RsRows<R>::NE, NG = RsRows<R>::NG;
-  extern __shared__ __align__(16) float Ssh[];     // S_k [R][RP], staged each step
-  __shared__ __align__(16) float Lsh[kRsQ * RP];  // own rows of Q_k (Q workgroup)
-  __shared__ __align__(16) float Psh[kRsS * RP];  // own rows of S_k^2
+  constexpr int RP = R + 4, NS = R / kRsS, NE = RsRows<R>::NE, NG = RsRows<R>::NG, U4 = R / 4;
+  constexpr int SLOT = R * R * 4;  // bytes per ring slot
+  static_assert(2 * NS <= kRsFlagWords, "one progress counter per workgroup");
+  extern __shared__ __align__(16) float Ssh[];     // the exchanged S_k [R][RP], staged
+  __shared__ __align__(16) float Xsh[kRsS * RP];  // left operand rows of the next product
   __shared__ float red[4 * NG * 4 * 64];
   __shared__ float scs;
   __shared__ int slot;
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int kq = lane >> 4, c = lane & 15;
   const bool isS = blockIdx.x < NS;
-  const int nblk = NS + NQ;
+  const int J = isS ? blockIdx.x : blockIdx.x - NS, r0 = J * kRsS;
   const float sx = nparts ? block_inv_norm(nparts, nnp, &scs) : 1.f;
+  const __amdgpu_buffer_rsrc_t rs = rs_rsrc(Sring);
+  RsRows<R> B;  // right factor: the staged S_k, this wave's K range
+  // element e = threadIdx.x + 256 p of the 4 rows: row e / R, column e % R
+  auto put = [&](const float (&v)[NE]) {  // v -> Xsh, visible to every wave
+#pragma unroll
+    for (int p = 0; p < NE; ++p) {
+      const int e = threadIdx.x + 256 * p;
+      if (e < 4 * R) Xsh[(e / R) * RP + e % R] = v[p];
+    }
+    __syncthreads();
+  };
+  auto mul = [&](float (&out)[NE]) { B.product(Xsh, red, w, lane, out); };  // out = Xsh S_k
+  // rows times h(S_k) = 2.25 S - 1.5 S^2 + 0.25 S^3 (the rows are in Xsh)
+  auto mul_h = [&](float (&out)[NE]) {
+    float a1[NE], a2[NE], a3[NE];
+    mul(a1);
+    put(a1);
+    mul(a2);
+    put(a2);
+    mul(a3);
+#pragma unroll
+    for (int p = 0; p < NE; ++p) out[p] = (2.25f * a1[p] - 1.5f * a2[p]) + 0.25f * a3[p];
+  };
+  const int nx = (iters - 1) / 2;  // exchanges after S_0: S_2, S_4, .., S_{2 nx}
 
   if (isS) {
-    const int r0 = blockIdx.x * kRsS;
     // S_0 rows: s^2 times the pieces' sum, in piece order
-    constexpr int U = R / 4;
     const float s2 = sx * sx;
-    if (threadIdx.x < kRsS * U) {
-      const size_t o = size_t(r0 + threadIdx.x / U) * R + 4 * (threadIdx.x % U);
+    if (threadIdx.x < kRsS * U4) {
+      const size_t o = size_t(r0 + threadIdx.x / U4) * R + 4 * (threadIdx.x % U4);
       f32x4 v = ld4(part + o);
       for (int q = 1; q < G; ++q) v += ld4(part + size_t(q) * R * R + o);
-      st4(Sbuf + o, v * s2);
+      rs_st(rs, int(o) * 4, v * s2);
     }
-    rs_sync(flags, nblk, 1u, limit, &slot);
-    RsRows<R> B;
-    const float* Own = Ssh + r0 * RP;  // own rows of S_k, in the staged copy
-    for (int k = 0; k + 1 < iters; ++k) {
-      rs_stage<R>(Sbuf + size_t(k & 1) * R * R, Ssh);
+    rs_publish(flags, J, 1u);
+    for (int x = 0; x < nx; ++x) {  // S_{2x} -> S_{2x+2}
+      // S_{2x} complete, and slot (x + 1) mod kRsRing read by every Q workgroup (S_{2(x+1-kRsRing)})
+      const int qneed = x + 2 - kRsRing;
+      if (!rs_wait(flags, NS, unsigned(x + 1), qneed > 0 ? NS : 0, unsigned(max(qneed, 0)), limit, &slot)) return;
+      rs_stage<R>(rs, (x % kRsRing) * SLOT, Ssh);
       __syncthreads();
       B.load(Ssh, w, lane);
-      float sij[NE], s2v[NE], s3v[NE];
+      float s0[NE], t1[NE], t2[NE], u[NE], wv[NE], y[NE];
 #pragma unroll
       for (int p = 0; p < NE; ++p) {
         const int e = min(int(threadIdx.x) + 256 * p, 4 * R - 1);
-        sij[p] = Own[(e / R) * RP + e % R];
+        s0[p] = Ssh[(r0 + e / R) * RP + e % R];
       }
-      B.product(Own, red, w, lane, s2v);  // rows of S_k^2
+      put(s0);
+      mul(t1);  // rows of S^2
+      put(t1);
+      mul(t2);  // rows of S^3
 #pragma unroll
-      for (int p = 0; p < NE; ++p) {
-        const int e = threadIdx.x + 256 * p;
-        if (e < 4 * R) Psh[(e / R) * RP + e % R] = s2v[p];
-      }
-      __syncthreads();  // Psh complete; every wave is done reading red
-      B.product(Psh, red, w, lane, s3v);  // rows of S_k^3
-      float* dst = Sbuf + size_t((k + 1) & 1) * R * R;
+      for (int p = 0; p < NE; ++p) u[p] = (2.25f * s0[p] - 1.5f * t1[p]) + 0.25f * t2[p];  // rows of S_{k+1}
+      put(u);
+      mul_h(wv);  // rows of S_{k+1}^2
+      put(wv);
+      mul_h(y);  // rows of S_{k+1}^3
 #pragma unroll
-      for (int p = 0; p < NE; ++p) {
-        const int e = threadIdx.x + 256 * p;
-        if (e < 4 * R) dst[size_t(r0 + e / R) * R + e % R] = (2.25f * sij[p] - 1.5f * s2v[p]) + 0.25f * s3v[p];
+      for (int p = 0; p < NE; ++p) y[p] = (2.25f * u[p] - 1.5f * wv[p]) + 0.25f * y[p];  // rows of S_{k+2}
+      put(y);
+      if (threadIdx.x < kRsS * U4) {
+        const int i = threadIdx.x / U4, j = 4 * (threadIdx.x % U4);
+        rs_st(rs, ((x + 1) % kRsRing) * SLOT + ((r0 + i) * R + j) * 4, ld4(Xsh + i * RP + j));
       }
-      rs_sync(flags, nblk, unsigned(k + 2), limit, &slot);
+      rs_publish(flags, J, unsigned(x + 2));
     }
     return;
   }
 
-  // Q workgroup
-  const int r0 = (blockIdx.x - NS) * kRsQ;
-  bool ok = rs_sync(flags, nblk, 1u, limit, &slot);
-  RsRight<R> B;
-  f32x4 a[KB];
-  f32x4 q[TW];
-  for (int k = 0; k < iters; ++k) {
-    rs_stage<R>(Sbuf + size_t(k & 1) * R * R, Ssh);
-    __syncthreads();
-    if (k == 0) {  // Q_1 = T_0
+  // Q workgroup: Q_{k+2} = B (1.5 I - 0.5 h(S_k)), B = Q_k T_k, for k = 0, 2, ..; an odd
+  // step count ends with Q_n = Q_{n-1} T_{n-1}
+  bool ok = true;
+  float q[NE] = {};
+  for (int x = 0; 2 * x < iters; ++x) {
+    if (!rs_wait(flags, NS, unsigned(x + 1), 0, 0u, limit, &slot)) {
+      ok = false;
+      break;
+    }
+    rs_stage<R>(rs, (x % kRsRing) * SLOT, Ssh);
+    rs_publish(flags, NS + J, unsigned(x + 1));  // S_{2x} read (its loads are complete)
+    B.load(Ssh, w, lane);
+    float b[NE];
+    if (x == 0) {  // B = T_0
 #pragma unroll
-      for (int t = 0; t < TW; ++t)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int i = r0 + 4 * kq + v, j = 16 * (w + 4 * t) + c;
-          q[t][v] = (w + 4 * t < NT) ? (i == j ? 1.5f : 0.f) - 0.5f * Ssh[i * RP + j] : 0.f;
-        }
+      for (int p = 0; p < NE; ++p) {
+        const int e = min(int(threadIdx.x) + 256 * p, 4 * R - 1), i = r0 + e / R, j = e % R;
+        b[p] = (i == j ? 1.5f : 0.f) - 0.5f * Ssh[i * RP + j];
+      }
     } else {
-      B.load(Ssh, w, kq, c);
-      rs_left<R>(Lsh, a, kq, c);
-      f32x4 qs[TW];
-      rs_product<R>(a, B, qs, w);
+      put(q);
+      float t[NE];
+      mul(t);
 #pragma unroll
-      for (int t = 0; t < TW; ++t) q[t] = 1.5f * q[t] - 0.5f * qs[t];
+      for (int p = 0; p < NE; ++p) b[p] = 1.5f * q[p] - 0.5f * t[p];
     }
-    if (k + 1 < iters) {
-      __syncthreads();  // every wave is done reading the old rows
+    if (2 * x + 1 == iters) {  // the last, single step
 #pragma unroll
-      for (int t = 0; t < TW; ++t)
-        if (w + 4 * t < NT) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) Lsh[(4 * kq + v) * RP + 16 * (w + 4 * t) + c] = q[t][v];
-        }
-      if (!rs_sync(flags, nblk, unsigned(k + 2), limit, &slot)) ok = false;
+      for (int p = 0; p < NE; ++p) q[p] = b[p];
+      break;
     }
+    put(b);
+    float bh[NE];
+    mul_h(bh);
+#pragma unroll
+    for (int p = 0; p < NE; ++p) q[p] = 1.5f * b[p] - 0.5f * bh[p];
+    __syncthreads();  // every wave is done with the staged S_k before the next is staged
   }
   if (threadIdx.x == 0) slot = int(__hip_atomic_load(flags + kRsTimeoutWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   __syncthreads();
   if (slot != 0) ok = false;
   const float nan = __builtin_nanf("");
-#pragma unroll
-  for (int t = 0; t < TW; ++t)
-    if (w + 4 * t < NT) {
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        M[size_t(r0 + 4 * kq + v) * R + 16 * (w + 4 * t) + c] = ok ? sx * q[t][v] : nan;
-    }
+  put(q);
+  if (threadIdx.x < kRsS * U4) {
+    const int i = threadIdx.x / U4, j = 4 * (threadIdx.x % U4);
+    st4(M + size_t(r0 + i) * R + j, ok ? ld4(Xsh + i * RP + j) * sx : f32x4{nan, nan, nan, nan});
+  }
 }
 
 // Polar Express step matrix M = s (a I + b s^2 S + c s^4 S^2) [r][r], S the
@@ -713,10 +725,10 @@ void launch_rs(const float* part, int G, const float* nparts, int nnp, int iters
                float* M, hipStream_t s) {
   constexpr int lds = R * (R + 4) * int(sizeof(float));  // the staged S_k
   // with the kernel's static arrays (own Q and S^2 rows, the wave partials)
-  static_assert(lds + (kRsQ + kRsS) * (R + 4) * 4 + 4 * RsRows<R>::NG * 4 * 64 * 4 + 64 <= kMaxLdsBytes,
+  static_assert(lds + kRsS * (R + 4) * 4 + 4 * RsRows<R>::NG * 4 * 64 * 4 + 64 <= kMaxLdsBytes,
                 "Gram-space iteration LDS");
   (void)LdsLimit<k_spel_rs<R>, lds>::bytes();
-  hipLaunchKernelGGL(k_spel_rs<R>, dim3(R / kRsS + R / kRsQ), dim3(256), lds, s, part, G, nparts, nnp, iters, Sbuf,
+  hipLaunchKernelGGL(k_spel_rs<R>, dim3(2 * (R / kRsS)), dim3(256), lds, s, part, G, nparts, nnp, iters, Sbuf,
                      sync, M, rs_spin_limit());
 }
 
@@ -732,8 +744,8 @@ void launch_rs_any(int r, const float* part, int G, const float* nparts, int nnp
 }  // namespace
 
 // workspace: Xa | Xb | Xc | Xm [d][r] | part [groups][r][r] | nparts
-// [(d/32)(r/32)] | M [r][r] | nparts of Y0 [(d/32)(r/32)] | S buffers
-// [2][r][r] | arrival, timeout and sticky words [kRsSyncWords], each region
+// [(d/32)(r/32)] | M [r][r] | nparts of Y0 [(d/32)(r/32)] | S ring
+// [kRsRing][r][r] | progress, timeout and sticky words [kRsSyncWords], each region
 // 16-byte aligned.  Xm holds the new momentum until the step commits.
 static size_t a4(size_t n) { return (n + 3) & ~size_t(3); }
 
@@ -754,14 +766,14 @@ static SpelWs spel_ws(void* ws, int d, int r) {
   w.Mb = w.nparts + np;
   w.nparts2 = w.Mb + rr;
   w.Sbuf = w.nparts2 + np;
-  w.sync = reinterpret_cast<unsigned*>(w.Sbuf + 2 * rr);
+  w.sync = reinterpret_cast<unsigned*>(w.Sbuf + kRsRing * rr);
   return w;
 }
 
 size_t spel_ws_bytes(int64_t d, int64_t r) {
   const size_t np = a4(size_t(d / 32) * (r / 32));
   const size_t floats =
-      4 * size_t(d) * r + size_t(spel_groups(d)) * r * r + np + size_t(r) * r + np + 2 * size_t(r) * r + kRsSyncWords;
+      4 * size_t(d) * r + size_t(spel_groups(d)) * r * r + np + size_t(r) * r + np + kRsRing * size_t(r) * r + kRsSyncWords;
   return (floats + 64) * sizeof(float);
 }
 
