@@ -279,8 +279,8 @@ int rvq_stream_apply(float* C, const int32_t* idx, const float* vals, int64_t n,
  * may share it, calls that overlap in time may not.
  * For r <= 128 both polar maps run as iterations on r x r matrices (every
  * iterate is the input times a polynomial in its Gram matrix, so the result is
- * the same up to rounding), each in one launch of r/4 + r/16 workgroups that
- * wait for one another through flags in the workspace.  They need to be
+ * the same up to rounding), each in one launch of r/2 workgroups that wait
+ * for one another through counters in the workspace.  They need to be
  * resident together, which an otherwise idle device always allows; should a
  * wait last beyond about a second (a device kept full by other work), the
  * step is abandoned rather than the call hanging.
