@@ -154,9 +154,10 @@ __global__ __launch_bounds__(256) void k_tok_reduce(const bf16_t* __restrict__ X
 }
 
 // ------------------------------------------------------ reduce, streamed --
-// For r >= 128.  One block: 64 tokens x all r output columns; wave w owns the
-// r-blocks [w RBW, (w+1) RBW) over the whole contraction, so no partial tiles
-// are summed.  The contraction runs in chunks of 64 channels: d/64 chunks of
+// For r >= 128.  One block: 64 tokens x 128 RBW output columns (all r, or the
+// blockIdx.y-th such slice when the token tiles alone would not cover the
+// chip); wave w owns the r-blocks [w RBW, (w+1) RBW) of the slice over the
+// whole contraction, so no partial tiles are summed.  The contraction runs in chunks of 64 channels: d/64 chunks of
 // the token rows against AtF, then (ANCHOR) r/64 chunks of the anchor rows
 // E[t] against QnF.  Each chunk -- 64 token rows of 128 bytes and the chunk's
 // weight fragments of every wave -- is copied by global_load_lds straight into
@@ -202,6 +203,7 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
   const int hi = lane >> 5, l32 = lane & 31;
   const int tok0 = blockIdx.x * 64;
   const int MB = r >> 5;
+  const int cb = blockIdx.y * 4 * RBW;  // first 32-column block of the block's slice
   const int cx = d / kRedKC, nch = cx + (ANCHOR ? ra / kRedKC : 0);
 
   // copy role: this lane copies unit (lane & 7) of rows 16 w + 8 q + (lane >> 3), q = 0, 1;
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int i = 0; i < RBW; ++i)
-        copy16_to_lds(wb + (size_t(ks * MB + w * RBW + i) * 64 + lane) * 8,
+        copy16_to_lds(wb + (size_t(ks * MB + cb + w * RBW + i) * 64 + lane) * 8,
                       slot + RR::XU + ((w * 4 + ks) * RBW + i) * 64);
   };
 
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
       if (n >= N) continue;
 #pragma unroll
       for (int i = 0; i < RBW; ++i) {
-        float* row = Uf + size_t(n) * r + (w * RBW + i) * 32 + 4 * hi;
+        float* row = Uf + size_t(n) * r + (cb + w * RBW + i) * 32 + 4 * hi;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           f32x4 v;
@@ -334,7 +336,7 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
       }
     }
     for (int off = 32; off > 0; off >>= 1) local = fmaxf(local, __shfl_xor(local, off));
-    if (lane == 0) part[4 * blockIdx.x + w] = local;
+    if (lane == 0) part[4 * (blockIdx.y * gridDim.x + blockIdx.x) + w] = local;
     return;
   }
 #pragma unroll
@@ -343,7 +345,7 @@ __global__ __launch_bounds__(256 * G) void k_tok_reduce_dma(const bf16_t* __rest
     if (n >= N) continue;
 #pragma unroll
     for (int i = 0; i < RBW; ++i) {
-      bf16_t* row = Z + size_t(n) * r + (w * RBW + i) * 32 + 4 * hi;
+      bf16_t* row = Z + size_t(n) * r + (cb + w * RBW + i) * 32 + 4 * hi;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<u32x2*>(row + 8 * q) =
@@ -358,8 +360,9 @@ static void launch_reduce_dma(const uint16_t* in, const uint16_t* AtF, const int
                               float* Uf = nullptr, float alpha = 1.f, float* part = nullptr, KernelEvents ev = {}) {
   auto k = k_tok_reduce_dma<RBW, S, G, ANCHOR, OUTF>;
   const int lds = LdsLimit<k_tok_reduce_dma<RBW, S, G, ANCHOR, OUTF>, int(RedRing<RBW, S>::BYTES)>::bytes();
-  launch_k(ev, k, dim3((N + 63) / 64), dim3(256 * G), uint32_t(lds), s, in, AtF, tids, E, QnF, out, N, d, r, ra, V,
-           Uf, alpha, part);
+  // r / (128 RBW) column slices over blockIdx.y
+  launch_k(ev, k, dim3((N + 63) / 64, r / (128 * RBW)), dim3(256 * G), uint32_t(lds), s, in, AtF, tids, E, QnF, out,
+           N, d, r, ra, V, Uf, alpha, part);
 }
 
 bool launch_tok_reduce_f32out(const uint16_t* in, const uint16_t* F, float* U, float alpha, float* part, int N,
@@ -391,6 +394,11 @@ void launch_tok_reduce_bf16(const uint16_t* in, const uint16_t* AtF, const int32
     return;
   }
   if (r == 256) {
+    if ((N + 63) / 64 < 256) {  // too few token tiles to fill the chip: two 128-column slices per tile
+      if (anc) launch_reduce_dma<1, 6, 2, true>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s, nullptr, 1.f, nullptr, ev);
+      else launch_reduce_dma<1, 6, 2, false>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s, nullptr, 1.f, nullptr, ev);
+      return;
+    }
     if (anc) launch_reduce_dma<2, 3, 1, true>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s, nullptr, 1.f, nullptr, ev);
     else launch_reduce_dma<2, 3, 1, false>(in, AtF, tids, E, QnF, out, N, d, r, ra, V, s, nullptr, 1.f, nullptr, ev);
     return;
