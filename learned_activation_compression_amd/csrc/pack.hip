@@ -90,18 +90,20 @@ void launch_pack_PF(const uint16_t* P, uint16_t* PF, int d, int ra, hipStream_t 
   frag_pack(P, /*sm*/ d, /*sk*/ 1, ra, d, PF, s);  // W(m, k) = P[m][k]
 }
 
-// Full pack in one launch of 1024-thread blocks.  Blocks [0, nq) form QnF,
+// Full pack in one launch of 512-thread blocks.  Blocks [0, nq) form QnF,
 // one 32 x 32 tile of P A each (nq = (ra/32)(r/32); 0 without a P); the
 // others write one 16-byte unit each of the concatenation [AtF | AF | PtF | PF]
 // (section boundaries at multiples of 64 units) and, for the identity anchor
 // (eye: P = I, no P), the matching unit of QnF = -AtF with each AtF unit.
 //
 // QnF tile (i, j): fragments of W = -(P A)^T (M = r, K = ra), rounded once to
-// bf16.  Its 16 waves split the d-long contraction (the matrix-core A operand
+// bf16.  Its 8 waves split the d-long contraction (the matrix-core A operand
 // is 16 bytes of a row of P, the B operand 8 rows of one column of A, read
-// directly), and the 16 partial tiles are added in LDS in a fixed order, each
-// wave summing 64 of the tile's elements.
-constexpr int kQnWaves = 16;
+// directly), and the 8 partial tiles are added in LDS in a fixed order, each
+// thread summing two of the tile's elements.  (512-thread blocks: 16 waves put
+// the packing units on half as many CUs, 4 waves serialise the tiles' loads;
+// 8.2 us at 150M against 10.8 and 9.5.)
+constexpr int kQnWaves = 8;
 
 __global__ __launch_bounds__(64 * kQnWaves) void k_pack_all(const bf16_t* __restrict__ A, const bf16_t* __restrict__ P,
                                                            bf16_t* __restrict__ AtF, bf16_t* __restrict__ AF,
@@ -179,12 +181,18 @@ __global__ __launch_bounds__(64 * kQnWaves) void k_pack_all(const bf16_t* __rest
   for (int v = 0; v < 16; ++v) red[w * 1024 + v * 64 + lane] = acc[v];
   __syncthreads();
   // element e = v 64 + lane of the tile (fragment order): the partials in wave order
-  const int e = w * 64 + lane;
-  float sum = red[e];
+  constexpr int EPT = 1024 / (64 * kQnWaves);  // elements per thread
+  float sum[EPT];
 #pragma unroll
-  for (int q = 1; q < kQnWaves; ++q) sum += red[q * 1024 + e];
+  for (int x = 0; x < EPT; ++x) {
+    const int e = threadIdx.x + 64 * kQnWaves * x;
+    sum[x] = red[e];
+#pragma unroll
+    for (int q = 1; q < kQnWaves; ++q) sum[x] += red[q * 1024 + e];
+  }
   __syncthreads();
-  red[e] = sum;
+#pragma unroll
+  for (int x = 0; x < EPT; ++x) red[threadIdx.x + 64 * kQnWaves * x] = sum[x];
   __syncthreads();
   if (w != 0) return;
   // lane (column j = mbj*32 + l32) holds rows i = i0 + 8 q + 4 hi + t of P A (t < 4),
