@@ -200,9 +200,9 @@ def step(lac, g, b, it, ev=None):
     lac.rvq_encode(b["Z"], g["C"], S.G, S.K, S.R, codes=b["codes"])
     mark("rvq_encode", 1)
     idx, vals = g["packets"][it % len(g["packets"])]
-    lac.rvq_stream_apply(g["C"], idx, vals)
     mark("rvq_decode", 0)
-    lac.rvq_decode(b["codes"], g["C"], S.G, S.K, S.R, S.r, Zq=b["Zq"])
+    # the receiver's codebook sync and decode, one launch
+    lac.rvq_stream_decode(g["C"], idx, vals, b["codes"], S.G, S.K, S.R, S.r, Zq=b["Zq"])
     mark("rvq_decode", 1)
     mark("reconstruct", 0)
     lac.mapl_reconstruct(b["Zq"], g["tids"], g["E"], g["P"], g["A"], Xhat=b["Xh"], pk=b["pk"], pk_ready=True)

@@ -262,6 +262,20 @@ int rvq_decode(const uint8_t* codes, const float* C, int64_t C_round_stride,
 int rvq_stream_apply(float* C, const int32_t* idx, const float* vals, int64_t n,
                      int64_t r, int64_t G, int64_t K, int64_t R_c, hipStream_t stream);
 
+/* The receiver's codebook sync followed by its decode (Section 3.5 "Codebook
+ * Synchronization" and the decode above), in one launch: bit for bit the
+ * effect of rvq_stream_apply(C, idx, vals, n, r, G, K, R_c) and then
+ * rvq_decode(codes, C, C_round_stride, Zq, out_dt, N, r, G, K, R), with every
+ * argument meaning what it means there (C updated in place, R_c books for the
+ * sync, R rounds for the decode).  One launch covers packets of up to 64
+ * codewords with w >= 8, w % 4 == 0, vals 16-byte aligned and C_round_stride
+ * a multiple of w; other calls run the two launches in that order.
+ * Errors: those of the two calls (shape, null, dtype, alignment of C). */
+int rvq_stream_decode(float* C, int64_t C_round_stride, int64_t R_c, const int32_t* idx,
+                      const float* vals, int64_t n, const uint8_t* codes, void* Zq,
+                      mapl_dtype out_dt, int64_t N, int64_t r, int64_t G, int64_t K, int64_t R,
+                      hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * SPEL projector update (Section 3.3, Eq. (4)-(7), Algorithm 1 step 4).
  *

@@ -25,7 +25,7 @@ __all__ = [
     "mapl_pack_bytes", "mapl_pack", "mapl_compress", "mapl_time_next_compress_kernel", "mapl_reconstruct",
     "mapl_bwd_workspace_bytes", "mapl_reconstruct_bwd", "mapl_compress_bwd",
     "mapl_anchor_grad_workspace_bytes", "mapl_anchor_grad", "mapl_check_tids",
-    "rvq_encode", "rvq_decode", "rvq_stream_apply", "spel_workspace_bytes", "spel_step",
+    "rvq_encode", "rvq_decode", "rvq_stream_apply", "rvq_stream_decode", "spel_workspace_bytes", "spel_step",
     "spel_step_static", "spel_step_polar_express", "spel_polar_express_coefficients",
     "MAPL_F32", "MAPL_BF16",
 ]
@@ -63,6 +63,7 @@ _SIGS = {
     "rvq_encode": (_i32, [_vp, _i32, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
     "rvq_decode": (_i32, [_vp, _vp, _i64, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _vp]),
     "rvq_stream_apply": (_i32, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _vp]),
+    "rvq_stream_decode": (_i32, [_vp, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _i32, _i64, _i64, _i64, _i64, _i64, _vp]),
     "spel_workspace_bytes": (_sz, [_i64, _i64]),
     "spel_step": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _vp, _vp, _i64, _i64, _vp, _sz, _vp]),
     "spel_step_static": (_i32, [_vp, _vp, _vp, _f32, _f32, _i32, _vp, _vp, _i64, _i64, _vp]),
@@ -431,6 +432,22 @@ def rvq_stream_apply(C, idx, vals, stream=None) -> torch.Tensor:
                                    _dev(vals, "vals", torch.float32), n, G * w, G, K, R_c, _stream(stream)),
            "rvq_stream_apply")
     return C
+
+
+def rvq_stream_decode(C, idx, vals, codes, G: int, K: int, R: int, r: int, round_stride: int = 0,
+                      out_dtype=torch.float32, Zq=None, stream=None) -> torch.Tensor:
+    """rvq_stream_apply(C, idx, vals) then rvq_decode(codes, C, ...) in one launch for small packets:
+    C [R_c][G][K][w] is updated in place and the codes [N][R][G] are decoded with the updated books."""
+    N = codes.shape[0]
+    R_c = C.shape[0]
+    _check_books(C, r, K, R, round_stride, "rvq_stream_decode")
+    if Zq is None:
+        Zq = _empty((N, r), out_dtype, codes)
+    n = idx.numel()
+    _check(load().rvq_stream_decode(_dev(C, "C", torch.float32), round_stride, R_c, _dev(idx, "idx", torch.int32),
+                                    _dev(vals, "vals", torch.float32), n, _dev(codes, "codes", torch.uint8),
+                                    _dev(Zq, "Zq"), _dt(Zq), N, r, G, K, R, _stream(stream)), "rvq_stream_decode")
+    return Zq
 
 
 # ------------------------------------------------------------------- spel --

@@ -471,6 +471,23 @@ int rvq_stream_apply(float* C, const int32_t* idx, const float* vals, int64_t n,
   return ls.done();
 }
 
+int rvq_stream_decode(float* C, int64_t C_round_stride, int64_t R_c, const int32_t* idx, const float* vals,
+                      int64_t n, const uint8_t* codes, void* Zq, mapl_dtype out_dt, int64_t N, int64_t r, int64_t G,
+                      int64_t K, int64_t R, hipStream_t stream) {
+  int st = check_rvq_shape(N, r, G, K, R, C_round_stride);
+  if (st) return st;
+  if (n < 0 || n > INT32_MAX || R_c < 1) return MAPL_ERR_SHAPE;
+  if (!dtype_ok(out_dt)) return MAPL_ERR_DTYPE;
+  if (!C || !codes || !Zq || (n > 0 && (!idx || !vals))) return MAPL_ERR_NULL;
+  if (!aligned16(C)) return MAPL_ERR_ARG;
+  if (N == 0 && n == 0) return MAPL_OK;
+  LaunchScope ls;
+  if (!ls.ready()) return MAPL_ERR_HIP;
+  launch_rvq_stream_decode(C, C_round_stride, R_c * G * K, idx, vals, int(n), codes, Zq, out_dt == MAPL_BF16, int(N),
+                           int(r), int(G), int(K), int(R), stream);
+  return ls.done();
+}
+
 // ----------------------------------------------------------------- SPEL --
 size_t spel_workspace_bytes(int64_t d, int64_t r) {
   if (d < 1 || r < 1 || r > d || r > 1024 || d % 32 || r % 32 || d > (1 << 24)) return 0;

@@ -102,6 +102,9 @@ void launch_rvq_decode(const uint8_t* codes, const float* C, int64_t stride, voi
                        int N, int r, int G, int K, int R, hipStream_t s);
 void launch_rvq_stream(float* C, const int32_t* idx, const float* vals, int n, int w,
                        int64_t total_codewords, hipStream_t s);
+void launch_rvq_stream_decode(float* C, int64_t stride, int64_t total, const int32_t* idx, const float* vals, int n,
+                              const uint8_t* codes, void* Zq, int out_bf16, int N, int r, int G, int K, int R,
+                              hipStream_t s);
 
 // ---- SPEL
 size_t spel_ws_bytes(int64_t d, int64_t r);

@@ -25,6 +25,8 @@
 // block of 32 codewords, lane l holds that token's scores for the codewords
 // 32 b + mfma32_row(v, h), v < 16.  K is padded to Kp = 32 ceil(K / 32) with
 // codewords that can never win (norm +inf).
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
@@ -498,23 +500,55 @@ void launch_rvq_encode(const void* Z, int z_bf16, const float* C, int64_t stride
 // Decode: Zq[n][g*W + j] = sum_rho C[rho*stride + (g*K + code)*W + j], rounds in
 // order.  A thread owns CH consecutive outputs of one (token, group): it reads
 // the R codes once and moves its codeword slices as 16-byte vectors.
-template <typename OT, int CH>
-__global__ __launch_bounds__(256) void k_rvq_decode(const uint8_t* __restrict__ codes, const float* __restrict__ C,
-                                                    int64_t stride, OT* __restrict__ Zq, int N, int r, int G, int K,
-                                                    int R) {
+// PKT (the codebook sync fused in; the round stride a multiple of W, so that
+// codeword k of group g in round rho has the flat index rho stride / W + g K + k,
+// the numbering of the sync, and `total` codewords exist): the n <= kPktMax codewords
+// idx[e] of a packet take the values vals[e] -- the last entry naming a codeword
+// wins -- both in the decoded sums (a codeword named in the packet is read from
+// vals, never from C) and in C itself, where global thread e < n stores entry e
+// unless a later entry names the same codeword.  No thread reads from C a
+// codeword that another thread stores, so the result is that of the sync
+// followed by the decode.
+constexpr int kPktMax = 64;
+
+template <typename OT, int CH, bool PKT = false>
+__global__ __launch_bounds__(256) void k_rvq_decode(const uint8_t* __restrict__ codes, const float* C, int64_t stride,
+                                                    OT* __restrict__ Zq, int N, int r, int G, int K, int R,
+                                                    float* Cw = nullptr, const int32_t* __restrict__ idx = nullptr,
+                                                    const float* __restrict__ vals = nullptr, int n = 0,
+                                                    int64_t total = 0) {
+  const int W = r / G;
+  __shared__ int32_t pid[PKT ? kPktMax : 1];
+  if (PKT) {
+    if (threadIdx.x < n) pid[threadIdx.x] = idx[threadIdx.x];
+    __syncthreads();
+    const int q = blockIdx.x * 256 + threadIdx.x;
+    if (q < n) {
+      const int64_t dst = pid[q];
+      bool win = dst >= 0 && dst < total;
+      for (int e = q + 1; e < n; ++e) win = win && pid[e] != dst;
+      if (win)
+        for (int j = 0; j < W; ++j) Cw[dst * W + j] = vals[size_t(q) * W + j];
+    }
+  }
   const int64_t e = int64_t(blockIdx.x) * 256 + threadIdx.x;  // chunk index
   const int per_tok = r / CH;
   if (e >= int64_t(N) * per_tok) return;
-  const int n = int(e / per_tok), col = int(e % per_tok) * CH;
-  const int W = r / G;
+  const int n_tok = int(e / per_tok), col = int(e % per_tok) * CH;
   const int g = col / W, j = col % W;
   float acc[CH];
 #pragma unroll
   for (int q = 0; q < CH; ++q) acc[q] = 0.f;
   for (int rho = 0; rho < R; ++rho) {
-    const int k = codes[(size_t(n) * R + rho) * G + g];
+    const int k = codes[(size_t(n_tok) * R + rho) * G + g];
     if (k >= K) continue;  // a code >= K (corrupt input) adds nothing
     const float* cw = C + rho * stride + (size_t(g) * K + k) * W + j;
+    if (PKT) {
+      const int64_t cq = rho * (stride / W) + int64_t(g) * K + k;  // the codeword's flat index
+      int slot = -1;
+      for (int t = 0; t < n; ++t) slot = pid[t] == cq ? t : slot;
+      if (slot >= 0) cw = vals + size_t(slot) * W + j;
+    }
     if (CH >= 4) {
 #pragma unroll
       for (int q = 0; q < CH; q += 4) {
@@ -527,7 +561,7 @@ __global__ __launch_bounds__(256) void k_rvq_decode(const uint8_t* __restrict__ 
       for (int q = 0; q < CH; ++q) acc[q] += cw[q];
     }
   }
-  OT* o = Zq + size_t(n) * r + col;
+  OT* o = Zq + size_t(n_tok) * r + col;
 #pragma unroll
   for (int q = 0; q < CH; ++q) o[q] = from_f32<OT>(acc[q]);
 }
@@ -654,6 +688,38 @@ void launch_rvq_stream(float* C, const int32_t* idx, const float* vals, int n, i
   if (n <= 0) return;
   hipLaunchKernelGGL(k_rvq_stream, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, C, idx, vals, n, w,
                      total_codewords);
+}
+
+// Sync then decode in one launch where the packet fits the decode kernel's table
+// (n <= kPktMax), the rows move as 16-byte vectors (w >= 8, w % 4 == 0, vals
+// 16-byte aligned) and the round stride is a whole number of codewords; the
+// narrow groups (w = 2, 4) keep their own decode kernel.  Otherwise the two
+// launches run in that order.
+void launch_rvq_stream_decode(float* C, int64_t stride, int64_t total, const int32_t* idx, const float* vals, int n,
+                              const uint8_t* codes, void* Zq, int out_bf16, int N, int r, int G, int K, int R,
+                              hipStream_t s) {
+  const int W = r / G;
+  const bool fuse = n > 0 && n <= kPktMax && W >= 8 && W % 4 == 0 && stride % W == 0 &&
+                    reinterpret_cast<uintptr_t>(vals) % 16 == 0;
+  if (!fuse) {
+    launch_rvq_stream(C, idx, vals, n, W, total, s);
+    if (N > 0) launch_rvq_decode(codes, C, stride, Zq, out_bf16, N, r, G, K, R, s);
+    return;
+  }
+  const int CH = (W % 8 == 0) ? 8 : 4;
+  const int64_t tot = int64_t(N) * r / CH;
+  dim3 grid(unsigned(std::max<int64_t>(1, (tot + 255) / 256)));
+#define MAPL_DECP(OTv, CHv)                                                                                      \
+  hipLaunchKernelGGL((k_rvq_decode<OTv, CHv, true>), grid, dim3(256), 0, s, codes, C, stride, static_cast<OTv*>(Zq), \
+                     N, r, G, K, R, C, idx, vals, n, total)
+  if (out_bf16) {
+    if (CH == 8) MAPL_DECP(bf16_t, 8);
+    else MAPL_DECP(bf16_t, 4);
+  } else {
+    if (CH == 8) MAPL_DECP(float, 8);
+    else MAPL_DECP(float, 4);
+  }
+#undef MAPL_DECP
 }
 
 }  // namespace mapl

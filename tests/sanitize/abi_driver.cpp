@@ -87,6 +87,12 @@ int main() {
   expect(rvq_encode(F, MAPL_BF16, Ff, 0, Fu, big, 256, 8, 256, 2, nullptr), MAPL_ERR_SHAPE, "rvq huge N");
   expect(rvq_decode(Fu, Ff, 0, F, MAPL_F32, 16384, 256, 8, 256, 65, nullptr), MAPL_ERR_SHAPE, "rvq R = 65");
   expect(rvq_stream_apply(Ff, Fi, Ff, -1, 256, 8, 256, 1, nullptr), MAPL_ERR_SHAPE, "stream n < 0");
+  expect(rvq_stream_decode(Ff, 0, 1, Fi, Ff, -1, Fu, F, MAPL_F32, 16384, 256, 8, 256, 2, nullptr), MAPL_ERR_SHAPE,
+         "stream+decode n < 0");
+  expect(rvq_stream_decode(Ff, big - 3, 1, Fi, Ff, 8, Fu, F, MAPL_F32, 16384, 256, 8, 256, 2, nullptr), MAPL_ERR_ARG,
+         "stream+decode huge round stride");
+  expect_in(rvq_stream_decode(Ff, 0, 1, Fi, Ff, 8, Fu, F, MAPL_BF16, 16384, 256, 8, 256, 2, nullptr), MAPL_ERR_HIP,
+            MAPL_OK, "stream+decode valid");
   expect_in(rvq_encode(F, MAPL_BF16, Ff, 0, Fu, 16384, 256, 128, 17, 2, nullptr), MAPL_ERR_HIP, MAPL_OK,
             "rvq valid K = 17");
 

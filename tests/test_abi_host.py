@@ -24,7 +24,7 @@ def lib():
 
 def test_library_exports_every_declared_symbol(lib):
     names = lac.exported_symbols()
-    assert len(names) == 22, names
+    assert len(names) == 23, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(lac._SIGS), set(names) ^ set(lac._SIGS)
@@ -127,6 +127,7 @@ def test_empty_batch_is_a_no_op(lib):
     assert lib.rvq_encode(FAKE, BF16, FAKE, 0, FAKE, 0, 256, 8, 256, 2, None) == OK
     assert lib.rvq_decode(FAKE, FAKE, 0, FAKE, F32, 0, 256, 8, 256, 2, None) == OK
     assert lib.rvq_stream_apply(FAKE, FAKE, FAKE, 0, 256, 8, 256, 1, None) == OK
+    assert lib.rvq_stream_decode(FAKE, 0, 1, FAKE, FAKE, 0, FAKE, FAKE, F32, 0, 256, 8, 256, 2, None) == OK
 
 
 def test_backward_validation(lib):
@@ -212,6 +213,16 @@ def test_rvq_validation(lib):
     s = lib.rvq_stream_apply
     assert s(None, FAKE, FAKE, 8, 256, 8, 256, 1, None) == ENULL
     assert s(FAKE, FAKE, FAKE, 8, 250, 8, 256, 1, None) == ESHAPE
+    sd = lib.rvq_stream_decode
+    assert sd(None, 0, 1, FAKE, FAKE, 8, FAKE, FAKE, F32, 16384, 256, 8, 256, 2, None) == ENULL
+    assert sd(FAKE, 0, 1, None, FAKE, 8, FAKE, FAKE, F32, 16384, 256, 8, 256, 2, None) == ENULL   # n > 0 needs idx
+    assert sd(FAKE, 0, 1, FAKE, FAKE, 8, FAKE, None, F32, 16384, 256, 8, 256, 2, None) == ENULL
+    assert sd(FAKE, 0, 1, FAKE, FAKE, -1, FAKE, FAKE, F32, 16384, 256, 8, 256, 2, None) == ESHAPE
+    assert sd(FAKE, 0, 0, FAKE, FAKE, 8, FAKE, FAKE, F32, 16384, 256, 8, 256, 2, None) == ESHAPE   # R_c >= 1
+    assert sd(FAKE, 0, 1, FAKE, FAKE, 8, FAKE, FAKE, F32, 16384, 250, 8, 256, 2, None) == ESHAPE
+    assert sd(FAKE, 100, 1, FAKE, FAKE, 8, FAKE, FAKE, F32, 16384, 256, 8, 256, 2, None) == EARG  # 0 < stride < r*K
+    assert sd(odd, 0, 1, FAKE, FAKE, 8, FAKE, FAKE, F32, 16384, 256, 8, 256, 2, None) == EARG
+    assert sd(FAKE, 0, 1, FAKE, FAKE, 8, FAKE, FAKE, 9, 16384, 256, 8, 256, 2, None) == EDTYPE
 
 
 def test_spel_validation(lib):
@@ -307,6 +318,7 @@ def test_valid_calls_without_a_device_stop_at_device_setup(lib):
     assert lib.spel_step(FAKE, FAKE, FAKE, 1e-3, 0.9, 8, None, None, 1024, 128, FAKE, ws, None) == EHIP
     assert lib.rvq_encode(FAKE, BF16, FAKE, 0, FAKE, 16384, 256, 128, 17, 2, None) == EHIP   # K = 17 is valid
     assert lib.rvq_stream_apply(FAKE, FAKE, FAKE, 8, 256, 8, 256, 1, None) == EHIP
+    assert lib.rvq_stream_decode(FAKE, 0, 1, FAKE, FAKE, 8, FAKE, FAKE, F32, 16384, 256, 8, 256, 2, None) == EHIP
 
 
 def test_tid_check_mode_of_the_binding(monkeypatch):

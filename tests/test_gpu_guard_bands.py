@@ -73,10 +73,16 @@ def test_rvq_outputs_stay_inside_their_buffers(N, w, K):
     Cs.copy_(C)
     idx = torch.tensor([0, 5, R * G * K - 1], dtype=torch.int32, device=DEV)
     lac.rvq_stream_apply(Cs, idx, torch.ones((3, w), device=DEV))
+    Zf, rf = guarded((N, 256), torch.bfloat16)
+    Cf, rcf = guarded((R, G, K, w), torch.float32)
+    Cf.copy_(C)
+    lac.rvq_stream_decode(Cf, idx, torch.ones((3, w), device=DEV), codes, G, K, R, 256, round_stride=256 * K, Zq=Zf)
     torch.cuda.synchronize()
     assert tail_ok(rc, N * R * G, torch.uint8)
     assert tail_ok(rq, N * 256, torch.float32)
     assert tail_ok(rcs, R * G * K * w, torch.float32)
+    assert tail_ok(rf, N * 256, torch.bfloat16)
+    assert tail_ok(rcf, R * G * K * w, torch.float32)
 
 
 @pytest.mark.parametrize("d,r", [(1024, 128), (2048, 256), (96, 96)])

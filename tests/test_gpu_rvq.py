@@ -247,3 +247,62 @@ def test_stream_apply_is_bit_exact_and_converges_to_the_sender():
     lac.rvq_stream_apply(C, idx.to(DEV), vals.to(DEV))
     torch.cuda.synchronize()
     assert torch.equal(C.cpu(), sender)
+
+
+def _packet(rng, n, total, w, extra_bad=True):
+    idx = rng.integers(0, total, size=n).astype(np.int32)
+    if n >= 4:
+        idx[1] = idx[0]                    # a duplicate: the later entry wins
+        if extra_bad:
+            idx[2] = total                 # out of range: skipped
+            idx[3] = -7
+    vals = rng.standard_normal((n, w)).astype(np.float32)
+    return torch.from_numpy(idx).to(DEV), torch.from_numpy(vals).to(DEV)
+
+
+@pytest.mark.parametrize("N,r,G,K,R,R_c,stride_kind,n,out", [
+    (16384, 128, 4, 256, 2, 1, "shared", 4, torch.bfloat16),     # the step's receiver (one launch)
+    (1000, 256, 8, 256, 2, 2, "rounds", 16, torch.float32),      # a book per round (one launch)
+    (777, 64, 8, 17, 3, 3, "rounds", 64, torch.float32),         # w = 8, the largest fused packet, codes >= K
+    (333, 128, 2, 256, 1, 1, "shared", 9, torch.bfloat16),       # w = 64
+    (500, 64, 8, 17, 2, 2, "padded", 8, torch.float32),          # round stride not a whole codeword count
+    (640, 256, 8, 256, 2, 2, "rounds", 65, torch.float32),       # packet over the fused limit: two launches
+    (640, 64, 16, 256, 2, 1, "shared", 8, torch.bfloat16),       # w = 4: two launches
+    (1, 128, 4, 256, 2, 1, "shared", 4, torch.float32),          # one token
+])
+def test_stream_decode_is_the_sync_then_the_decode(N, r, G, K, R, R_c, stride_kind, n, out):
+    """rvq_stream_decode gives the bits of rvq_stream_apply followed by rvq_decode: the
+    decoded rows and the updated books, duplicates, out-of-range ids and codes >= K
+    included, on the single-launch path and on the fallbacks."""
+    w = r // G
+    rng = np.random.default_rng(N + r + n)
+    stride = {"shared": 0, "rounds": G * K * w, "padded": G * K * w + 4}[stride_kind]
+    # books held: R_c for a shared book, R with a book per round, one more as room for the padded stride
+    nb = {"shared": R_c, "rounds": R, "padded": R + 1}[stride_kind]
+    C0 = torch.from_numpy((rng.standard_normal((nb, G, K, w)) / np.sqrt(w)).astype(np.float32)).to(DEV)
+    codes = torch.from_numpy(rng.integers(0, 256 if K < 256 else K, size=(N, R, G)).astype(np.uint8)).to(DEV)
+    idx, vals = _packet(rng, n, nb * G * K, w)
+    Ca, Cb = C0.clone(), C0.clone()
+    lac.rvq_stream_apply(Cb, idx, vals)
+    ref = lac.rvq_decode(codes, Cb, G, K, R, r, round_stride=stride, out_dtype=out)
+    got = lac.rvq_stream_decode(Ca, idx, vals, codes, G, K, R, r, round_stride=stride, out_dtype=out)
+    torch.cuda.synchronize()
+    assert torch.equal(Ca, Cb)
+    assert torch.equal(got, ref)
+
+
+def test_stream_decode_with_unaligned_values_takes_two_launches():
+    N, r, G, K, R, w = 900, 256, 8, 256, 2, 32
+    rng = np.random.default_rng(5)
+    C0 = torch.from_numpy((rng.standard_normal((1, G, K, w)) / 8).astype(np.float32)).to(DEV)
+    codes = torch.from_numpy(rng.integers(0, K, size=(N, R, G)).astype(np.uint8)).to(DEV)
+    idx, vals = _packet(rng, 12, G * K, w)
+    buf = torch.empty(12 * w + 1, device=DEV)
+    odd = buf[1:].view(12, w)
+    odd.copy_(vals)
+    Ca, Cb = C0.clone(), C0.clone()
+    lac.rvq_stream_apply(Cb, idx, vals)
+    ref = lac.rvq_decode(codes, Cb, G, K, R, r)
+    got = lac.rvq_stream_decode(Ca, idx, odd, codes, G, K, R, r)
+    torch.cuda.synchronize()
+    assert torch.equal(Ca, Cb) and torch.equal(got, ref)
