@@ -18,11 +18,12 @@
 //         group); its 4 waves sum in LDS.  For Eq. (4) the block stores
 //         sym(.) of its piece (sym is linear, so the pieces add up to
 //         sym(A^T g)).
-//   xm    out = s X M  d x r with M = f(sum_q part[q]) formed while loading:
-//         f = identity for Eq. (4), 1.5 I - 0.5 s^2 (.) for a Newton-Schulz
-//         step.  One block per 32 x 32 output tile; the 4 waves split K = r
-//         and sum in LDS; the epilogue applies Eq. (4)-(5), a plain
-//         Newton-Schulz step, or the last step of Eq. (6) / Eq. (7).
+//   xm    out = s X M  d x r with M = f(sum_q part[q]): f = identity for
+//         Eq. (4), 1.5 I - 0.5 s^2 (.) for a Newton-Schulz step.  One block
+//         per 32 x 32 output tile; the block first forms its 32 columns of M
+//         in LDS (coalesced row reads, the pieces added in order), then the 4
+//         waves split K = r and sum in LDS; the epilogue applies Eq. (4)-(5),
+//         a plain Newton-Schulz step, or the last step of Eq. (6) / Eq. (7).
 //
 // All sums run in a fixed order, so a step is bitwise repeatable.  The scale
 // s = 1/||m||_F comes from per-block partial sums of squares written by the
@@ -142,31 +143,24 @@ __global__ __launch_bounds__(256) void k_spel_gram(const float* __restrict__ Xl,
 }
 
 // acc += X[row][kc .. kc+CH) * M[kc .. kc+CH)[col] on the 32x32x2 matrix core,
-// M = f(sum over G pieces).  At step t lane half h takes k = kc + (CH/2) h + t,
-// so each lane reads CH/2 consecutive floats of its X row as 16-byte loads;
-// all loads are issued before the first multiply.
-template <int CH, int G, bool NS>
-__device__ __forceinline__ void xm_chunk(const float* __restrict__ xr, const float* __restrict__ part, size_t rr,
-                                         int kc, int r, int col, int h, float sc2, f32x16& acc) {
+// with M's column col already formed in LDS (Mt: row c of the block's slab holds
+// column j0 + c of M).  At step t lane half h takes k = kc + (CH/2) h + t, so
+// each lane reads CH/2 consecutive floats of its X row and of its M column as
+// 16-byte loads; all of them are issued before the first multiply.
+template <int CH>
+__device__ __forceinline__ void xm_chunk(const float* __restrict__ xr, const float* mcol, int kc, int h,
+                                         f32x16& acc) {
   constexpr int HK = CH / 2;
-  f32x4 xa[HK / 4];
-  float mb[G][HK];
+  f32x4 xa[HK / 4], mb[HK / 4];
   const float* xk = xr + kc + HK * h;
+  const float* mk = mcol + kc + HK * h;
 #pragma unroll
   for (int q = 0; q < HK / 4; ++q) xa[q] = ld4(xk + 4 * q);
 #pragma unroll
-  for (int gq = 0; gq < G; ++gq)
-#pragma unroll
-    for (int t = 0; t < HK; ++t) mb[gq][t] = part[gq * rr + size_t(kc + HK * h + t) * r + col];
+  for (int q = 0; q < HK / 4; ++q) mb[q] = ld4(mk + 4 * q);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < HK; ++t) {
-    float sum = mb[0][t];
-#pragma unroll
-    for (int gq = 1; gq < G; ++gq) sum += mb[gq][t];
-    const float mv = NS ? ((kc + HK * h + t == col) ? 1.5f : 0.f) - 0.5f * (sc2 * sum) : sum;
-    acc = mfma_f32_32x32x2(xa[t >> 2][t & 3], mv, acc);
-  }
+  for (int t = 0; t < HK; ++t) acc = mfma_f32_32x32x2(xa[t >> 2][t & 3], mb[t >> 2][t & 3], acc);
 }
 
 // 1/||m||_F from n per-block partial sums, added in a fixed order by wave 0
@@ -194,7 +188,8 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
                                                  float* __restrict__ Y0, const unsigned* __restrict__ sticky,
                                                  const float* __restrict__ mnew, float* __restrict__ mcommit,
                                                  int* __restrict__ status) {
-  __shared__ float red[4 * 1024];
+  extern __shared__ __attribute__((aligned(16))) float xm_lds[];  // the M slab; then the wave partials
+  float* red = xm_lds;
   __shared__ float wsum[4];
   __shared__ float scs;
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -203,25 +198,44 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
   const float sx = nparts_in ? block_inv_norm(nparts_in, (d >> 5) * (r >> 5), &scs) : 1.f;
   const float sc2 = sx * sx;
   const size_t rr = size_t(r) * r;
+  const int mp = r + 4;  // LDS pitch of a slab row (one column of M)
+
+  // the block's 32 columns of M = f(sum of the G pieces), formed once: thread t reads
+  // 4 consecutive columns of row k (coalesced 16-byte loads, 8 threads per row segment),
+  // adds the pieces in order and stores the 4 values down the slab's rows
+  for (int k0 = 0; k0 < r; k0 += 32) {
+    const int k = k0 + int(threadIdx.x >> 3), c4 = int(threadIdx.x & 7) * 4;
+    const float* src = part + size_t(k) * r + j0 + c4;
+    f32x4 sum = ld4(src);
+#pragma unroll
+    for (int gq = 1; gq < G; ++gq) sum += ld4(src + gq * rr);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float v = NS ? ((k == j0 + c4 + e) ? 1.5f : 0.f) - 0.5f * (sc2 * sum[e]) : sum[e];
+      xm_lds[(c4 + e) * mp + k] = v;
+    }
+  }
+  __syncthreads();
 
   f32x16 acc = f32x16{};
   {
     const float* xr = X + size_t(i0 + l32) * r;
+    const float* mcol = xm_lds + l32 * mp;
     const int kq = r >> 2;
     int kc = w * kq;
     const int ke = kc + kq;
-    constexpr int CB = (G >= 4) ? 32 : 64;  // at most 64 pending scalar loads per lane
-    for (; kc + CB <= ke; kc += CB) xm_chunk<CB, G, NS>(xr, part, rr, kc, r, j0 + l32, h, sc2, acc);
-    if (CB == 64 && kc + 32 <= ke) {
-      xm_chunk<32, G, NS>(xr, part, rr, kc, r, j0 + l32, h, sc2, acc);
+    for (; kc + 64 <= ke; kc += 64) xm_chunk<64>(xr, mcol, kc, h, acc);
+    if (kc + 32 <= ke) {
+      xm_chunk<32>(xr, mcol, kc, h, acc);
       kc += 32;
     }
     if (kc + 16 <= ke) {
-      xm_chunk<16, G, NS>(xr, part, rr, kc, r, j0 + l32, h, sc2, acc);
+      xm_chunk<16>(xr, mcol, kc, h, acc);
       kc += 16;
     }
-    if (kc + 8 <= ke) xm_chunk<8, G, NS>(xr, part, rr, kc, r, j0 + l32, h, sc2, acc);
+    if (kc + 8 <= ke) xm_chunk<8>(xr, mcol, kc, h, acc);
   }
+  __syncthreads();  // the slab is read: its LDS takes the wave partials
   store_frag(red + w * 1024, acc, lane);
   __syncthreads();
   const int i = threadIdx.x >> 3, j = (threadIdx.x & 7) * 4;
@@ -709,7 +723,14 @@ void launch_xm(int G, dim3 grid, hipStream_t s, const float* X, const float* npa
                int d, int r, int mode, const float* g, const float* m, float beta, float* nparts_out,
                const float* Acur, float alpha, float* Dout, float* Y0, XmCommit cm = {}) {
   auto k = G == 4 ? k_spel_xm<4, NS> : G == 2 ? k_spel_xm<2, NS> : k_spel_xm<1, NS>;
-  hipLaunchKernelGGL(k, grid, dim3(256), 0, s, X, nparts_in, part, out, d, r, mode, g, m, beta, nparts_out, Acur,
+  // the M slab, 32 rows of pitch r + 4, or the 4 wave partials (16 KB) if larger; the
+  // limit is raised once for the largest r (1024)
+  constexpr int kXmLdsMax = 32 * (1024 + 4) * int(sizeof(float));
+  (void)LdsLimit<k_spel_xm<1, NS>, kXmLdsMax>::bytes();
+  (void)LdsLimit<k_spel_xm<2, NS>, kXmLdsMax>::bytes();
+  (void)LdsLimit<k_spel_xm<4, NS>, kXmLdsMax>::bytes();
+  const size_t lds = std::max<size_t>(size_t(32) * (r + 4) * sizeof(float), 4 * 1024 * sizeof(float));
+  hipLaunchKernelGGL(k, grid, dim3(256), lds, s, X, nparts_in, part, out, d, r, mode, g, m, beta, nparts_out, Acur,
                      alpha, Dout, Y0, cm.sticky, cm.mnew, cm.mcommit, cm.status);
 }
 
