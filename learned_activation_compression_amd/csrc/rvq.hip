@@ -86,36 +86,48 @@ __device__ __forceinline__ float rvq_norm2(const double (&res)[H]) {
 // added (fp addition commutes, so both lanes get the same value).  Exact ties
 // keep the lower index; codewords past K (padding) are skipped; NaN never
 // wins.  With no candidate (all scores NaN) the code is 0.
+// Every pass takes each lane's next candidate, wherever it sits in the eight
+// mask words, so the wave makes as many passes as its busiest token has
+// candidates (not one per mask word that any token uses).
 template <typename PartFn>
 __device__ __forceinline__ int rvq_rescore(const uint32_t (&mine)[4], int h, int K, PartFn part) {
-  uint32_t m0[4], m1[4];  // candidates of half 0 and of half 1
+  uint32_t mm[8];  // words 0-3: candidates of half 0, 4-7: of half 1 (the same in both lanes)
 #pragma unroll
   for (int wd = 0; wd < 4; ++wd) {
     const uint32_t o = __shfl_xor(mine[wd], 32);
-    m0[wd] = h == 0 ? mine[wd] : o;
-    m1[wd] = h == 0 ? o : mine[wd];
+    mm[wd] = h == 0 ? mine[wd] : o;
+    mm[4 + wd] = h == 0 ? o : mine[wd];
   }
+  auto left = [&]() {
+    uint32_t a = 0u;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a |= mm[q];
+    return a != 0u;
+  };
   double best = __builtin_inf();
   int bk = 0;
+  while (__any(left())) {
+    if (left()) {  // the same in both lanes of the token, so both take the exchange below
+      // the first set bit in word order, taken out of its word
+      int k = 0;
+      bool found = false;
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      uint32_t m = hh == 0 ? m0[wd] : m1[wd];
-      while (__any(m != 0u)) {
-        if (m != 0u) {  // the same in both lanes of the token, so both take the exchange below
-          const int bit = __builtin_ctz(m);
-          m &= m - 1u;
-          const int k = 64 * wd + 32 * (bit >> 4) + mfma32_row(bit & 15, hh);
-          const double p = part(k);
-          const double dk = p + __shfl_xor(p, 32);
-          if (k < K && (dk < best || (dk == best && k < bk))) {
-            best = dk;
-            bk = k;
-          }
+      for (int q = 0; q < 8; ++q) {
+        if (!found && mm[q] != 0u) {
+          const int bit = __builtin_ctz(mm[q]);
+          mm[q] &= mm[q] - 1u;
+          k = 64 * (q & 3) + 32 * (bit >> 4) + mfma32_row(bit & 15, q >> 2);
+          found = true;
         }
       }
+      const double p = part(k);
+      const double dk = p + __shfl_xor(p, 32);
+      if (k < K && (dk < best || (dk == best && k < bk))) {
+        best = dk;
+        bk = k;
+      }
     }
+  }
   return bk;
 }
 
