@@ -55,7 +55,8 @@ def test_spel_1b_config():
 @pytest.mark.parametrize("d,r,alpha,beta,iters", [(256, 32, 0.05, 0.9, 8), (1024, 128, 1e-3, 0.9, 8),
                                                   (512, 64, 0.3, 0.5, 5), (96, 96, 0.1, 0.0, 8),
                                                   (2048, 512, 2e-3, 0.95, 8),
-                                                  (1056, 160, 0.02, 0.9, 8)])
+                                                  (1056, 160, 0.02, 0.9, 8), (768, 192, 0.05, 0.9, 8),
+                                                  (224, 224, 0.1, 0.5, 8)])
 def test_spel_shapes_with_nonzero_momentum(d, r, alpha, beta, iters):
     inp = synth.spel_inputs(100 + d + r, d, r, 1e-3)
     m0 = torch.from_numpy(synth.gaussian(synth.stream(7, d, r), (d, r), 1e-4).astype(np.float32))
@@ -183,7 +184,8 @@ def test_spel_state_saved_and_reloaded_continues_bit_exactly(d, r):
 
 
 @pytest.mark.parametrize("d,r,iters", [(1024, 128, 1), (1024, 128, 2), (256, 64, 3), (640, 96, 4), (128, 32, 6),
-                                       (1024, 128, 13)])
+                                       (1024, 128, 13), (2048, 256, 1), (2048, 256, 2), (512, 160, 3),
+                                       (2048, 256, 13)])
 def test_spel_few_and_many_iterations(d, r, iters):
     # m, D and A against the oracle for step counts other than 8 (A is not yet orthonormal
     # after one or two steps, so only the parity is checked)
