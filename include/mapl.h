@@ -291,13 +291,14 @@ int rvq_stream_decode(float* C, int64_t C_round_stride, int64_t R_c, const int32
  * 16-byte aligned (MAPL_ERR_ARG otherwise) and no buffer may overlap another.
  * The workspace needs no initial contents; consecutive calls on one stream
  * may share it, calls that overlap in time may not.
- * For r <= 128 both polar maps run as iterations on r x r matrices (every
+ * For r <= 256 both polar maps run as iterations on r x r matrices (every
  * iterate is the input times a polynomial in its Gram matrix, so the result is
- * the same up to rounding), each in one launch of r/2 workgroups that wait
- * for one another through counters in the workspace.  They need to be
- * resident together, which an otherwise idle device always allows; should a
- * wait last beyond about a second (a device kept full by other work), the
- * step is abandoned rather than the call hanging.
+ * the same up to rounding).  For r <= 128 each map is one launch of r/2
+ * workgroups that wait for one another through counters in the workspace.
+ * They need to be resident together, which an otherwise idle device always
+ * allows; should a wait last beyond about a second (a device kept full by
+ * other work), the step is abandoned rather than the call hanging.  For
+ * 128 < r <= 256 every half step is its own launch, with no such wait.
  * The step is transactional: the new m and A are formed in the workspace and
  * the last launch writes both only if no wait timed out; an abandoned step
  * leaves A and m exactly as they were (D_out, if given, is then unspecified).

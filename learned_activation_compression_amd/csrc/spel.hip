@@ -890,7 +890,7 @@ void launch_rs(const float* part, int G, const float* nparts, int nnp, int iters
                      sync, M, rs_spin_limit());
 }
 
-// M = s Q_iters of the Gram-space iteration (r <= 128)
+// M = s Q_iters of the Gram-space iteration inside one launch (r <= 128)
 void launch_rs_any(int r, const float* part, int G, const float* nparts, int nnp, int iters, float* Sbuf,
                    unsigned* sync, float* M, hipStream_t s) {
   if (r == 32) launch_rs<32>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
