@@ -42,6 +42,8 @@ namespace {
 
 enum { XM_TANGENT = 0, XM_NS = 1, XM_NS_LAST_LMO = 2, XM_NS_LAST_RET = 3 };
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kChunk = 32;  // rows per wave per Gram chunk (16 matrix-core K-steps)
 
 // Position of element (i, j) of a 32 x 32 tile in the accumulator fragment
@@ -74,12 +76,16 @@ __device__ __forceinline__ void pair_of(int p, int nb, int& bi, int& bj) {
 // acc1 = A_bi^T g_bj and acc2 = A_bj^T g_bi.  TWO = 0: piece = X_bi^T X_bj.
 // Tile (bi, bj) of part[grp] gets the piece, tile (bj, bi) its transpose.
 // `zero`, when given, holds nzero words cleared for the launches that follow:
-// the progress counters [0, 128) and the timeout word [128] of the Gram-space
-// iteration, and (cleared by the step's first launch only) the step's sticky
-// timeout word [129], which decides at the end whether the step is committed.
-constexpr int kRsFlagWords = 128;
-constexpr int kRsTimeoutWord = 128, kRsStickyWord = 129;
-constexpr int kRsSyncWords = 132;
+// the progress counters and the timeout word of the Gram-space iteration, and
+// (cleared by the step's first launch only) the step's sticky timeout word,
+// which decides at the end whether the step is committed.  Each of the 256
+// counters has a 64-byte line of its own (word 16 i): every workgroup of the
+// iteration polls all of them, and polls of one shared line queue up behind
+// each other.
+constexpr int kRsFlagWords = 256;
+constexpr int kRsFlagStride = 16;
+constexpr int kRsTimeoutWord = kRsFlagWords * kRsFlagStride, kRsStickyWord = kRsTimeoutWord + 1;
+constexpr int kRsSyncWords = kRsTimeoutWord + 4;
 template <int TWO>
 __global__ __launch_bounds__(256) void k_spel_gram(const float* __restrict__ Xl, const float* __restrict__ Xr,
                                                    float* __restrict__ part, int d, int r, int groups,
@@ -87,7 +93,8 @@ __global__ __launch_bounds__(256) void k_spel_gram(const float* __restrict__ Xl,
   __shared__ float red[(1 + TWO) * 4 * 1024];
   __shared__ float tile[32 * 33];
   const int lane = threadIdx.x & 63, w = wave_id();
-  if (zero != nullptr && blockIdx.x == 0 && int(threadIdx.x) < nzero) zero[threadIdx.x] = 0u;
+  if (zero != nullptr)
+    for (int i = blockIdx.x * 256 + threadIdx.x; i < nzero; i += gridDim.x * 256) zero[i] = 0u;
   const int h = lane >> 5, l32 = lane & 31;
   const int p = blockIdx.x / groups, grp = blockIdx.x % groups;
   int bi, bj;
@@ -310,13 +317,25 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
 // (4 products), and an odd step count ends with one plain step on the last
 // even S_k.
 //
-// One launch of r/2 workgroups of 256 threads, each owning 4 rows: S
-// workgroup J < r/4 rows 4 J .. 4 J + 3 of the even S_k, Q workgroup J rows
-// 4 J .. 4 J + 3 of the Q_k.  Only the S_k chain is sequential: the S
-// workgroups wait for each other and never for the Q workgroups, which follow
-// the chain one exchanged S_k at a time and hold nothing back but a buffer
-// (the exchanged S_k live in a ring of kRsRing buffers; a slot is written
-// again only after every Q workgroup has read what it held).
+// One launch of 2 r workgroups of 2 r threads, each owning one row: S
+// workgroup J < r row J of the even S_k, Q workgroup J row J of the Q_k.  Only
+// the S_k chain is sequential: the S workgroups wait for each other and never
+// for the Q workgroups, which follow the chain one exchanged S_k at a time and
+// hold nothing back but a buffer (the exchanged S_k live in a ring of kRsRing
+// buffers; a slot is written again only after every Q workgroup has read what
+// it held).
+//
+// Products on the vector ALUs.  Lane l of wave w owns the column pair
+// c0 = 32 w + 2 (l >> 2), c0 + 1 and the contraction quarter q = l & 3,
+// k in [q r/4, (q+1) r/4).  Each exchange a workgroup copies S_k into LDS
+// (coalesced 16-byte device-coherent loads, row pitch r + 4) and every thread
+// then keeps its r/4 x 2 entries in registers for the exchange's products, so
+// a product reads only its left row from LDS (16-byte reads, one address per
+// lane quad) and adds the four quarters across the quad (two DPP steps; every
+// lane of the quad ends with the same sum).  One row per workgroup keeps the
+// chain of products between exchanges short: a product is 2 r^2 / (4 r) fused
+// multiply-adds per thread, where 4 rows on v_mfma_f32_4x4x1_16b_f32 (half the
+// matrix core's rate) took as long as 4 rows on the vector ALUs.
 //
 // Exchange.  Each workgroup owns a progress counter: an S workgroup's is the
 // number of S_k whose rows it has stored, a Q workgroup's the number of S_k it
@@ -328,40 +347,27 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
 // has seen every counter it needs.  A wait that exceeds its bound (a second or
 // two) sets the timeout word, and the Q workgroups then write NaN: a wrong
 // result is never silent and no wait is endless.  The launch is ordinary; its
-// few workgroups (at most 64) are resident together on an otherwise idle
-// device.
+// workgroups (at most 256, with a few KB of LDS each) are resident together on
+// an otherwise idle device.
 //
-// Matrix cores (fp32), v_mfma_f32_4x4x1_16b_f32: 16 blocks of 4 x 4; lane l
-// is row l % 4 of block l / 4 in A, column l % 4 of block l / 4 in B and D
-// (register v: row v).  With A the same in every block and block b of column
-// group g taking columns 64 g + 4 b .. + 3, lane l of group g accumulates
-// column 64 g + l of the 4 output rows.  The 4 waves split K and add their
-// partial rows in LDS in wave order.
-constexpr int kRsS = 4;  // rows of S_k or Q_k per workgroup
 // each spin is a sleep and an uncached load: 2^20 spins take about 1-2 s.  The
 // environment variable MAPL_SPEL_SPIN_LIMIT lowers the bound, for tests of the
 // timeout path.
 constexpr unsigned kRsSpinLimit = 1u << 20;
 
-__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 __device__ __forceinline__ f32x4 mfma_f32_4x4x1(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
 }
 
 constexpr int kRsRing = 4;  // S_k buffers
 
-// Device-coherent (sc1) 16-byte accesses through a buffer resource: the
-// compiler tracks them like its own loads and stores.  Offsets in bytes.
+// Device-coherent (sc1) accesses through a buffer resource: the compiler
+// tracks them like its own loads and stores.  Offsets in bytes.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rs_rsrc(const float* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), 0, 0x7fffffff, 0x00020000);
 }
 __device__ __forceinline__ f32x4 rs_ld(__amdgpu_buffer_rsrc_t rs, int off) {
   return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16));
-}
-__device__ __forceinline__ void rs_st(__amdgpu_buffer_rsrc_t rs, int off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 16);
 }
 
 // Move this workgroup's progress counter to `val` once every wave's stores are
@@ -369,7 +375,7 @@ __device__ __forceinline__ void rs_st(__amdgpu_buffer_rsrc_t rs, int off, f32x4 
 __device__ __forceinline__ void rs_publish(unsigned* flags, int idx, unsigned val) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flags + idx, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(flags + kRsFlagStride * idx, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wait (one wave polls) until counters [0, ns) are >= sneed and counters
@@ -383,7 +389,7 @@ __device__ bool rs_wait(unsigned* flags, int ns, unsigned sneed, int nq, unsigne
     for (;;) {
       bool done = true;
       for (int i = l; i < ns + nq; i += 64) {
-        const unsigned v = __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned v = __hip_atomic_load(flags + kRsFlagStride * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         done = done && v >= (i < ns ? sneed : qneed);
       }
       if (__all(done)) break;
@@ -405,160 +411,148 @@ __device__ bool rs_wait(unsigned* flags, int ns, unsigned sneed, int nq, unsigne
   return ok;
 }
 
-// S [R][R] (ring slot, row-major) -> LDS rows of pitch R + 4, every thread's
+// LDS position of row i of a staged S_k: pitch R + 4, and 8 more floats
+// between row quarters, so that the four lanes of a quad (rows R/4 apart, the
+// same columns) read different banks
+template <int R>
+__device__ __forceinline__ int rs_row(int i) {
+  return i * (R + 4) + (i / (R / 4)) * 8;
+}
+template <int R>
+constexpr int kRsStageFloats = R * (R + 4) + 32;
+
+// S [R][R] (ring slot, row-major) -> LDS rows at rs_row, every thread's
 // 16-byte loads issued before the first is stored (consecutive threads read
 // consecutive 16 bytes)
-template <int R>
+template <int R, int NT>
 __device__ __forceinline__ void rs_stage(__amdgpu_buffer_rsrc_t rs, int base, float* __restrict__ sh) {
-  constexpr int U = R / 4, TOTAL = R * U, PER = (TOTAL + 255) / 256;
+  constexpr int U = R / 4, TOTAL = R * U, PER = (TOTAL + NT - 1) / NT;
   f32x4 v[PER];
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const int u = threadIdx.x + 256 * p;
+    const int u = threadIdx.x + NT * p;
     if (u < TOTAL) v[p] = rs_ld(rs, base + 16 * u);
   }
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const int u = threadIdx.x + 256 * p;
-    if (u < TOTAL) st4(sh + (u / U) * (R + 4) + 4 * (u % U), v[p]);
+    const int u = threadIdx.x + NT * p;
+    if (u < TOTAL) st4(sh + rs_row<R>(u / U) + 4 * (u % U), v[p]);
   }
 }
 
-// S workgroup product: out = L S for the 4 rows L (LDS, stride R + 4).  Wave w
-// takes k in [w R/4, (w+1) R/4); its partial rows go to red, and thread t then
-// adds the 4 waves' parts for elements e = t + 256 p (row e / R, column e % R).
-template <int R>
-struct RsRows {
-  static constexpr int NG = (R + 63) / 64, KW = R / 4, KU = KW / 4, NE = (4 * R + 255) / 256;
-  f32x4 b[NG][KU];  // b[g][u] = S[64 g + l][w KW + 4 u .. + 3]
-  __device__ __forceinline__ void load(const float* __restrict__ Ssh, int w, int l) {  // S_k staged in LDS
-#pragma unroll
-    for (int g = 0; g < NG; ++g)
-#pragma unroll
-      for (int u = 0; u < KU; ++u)
-        b[g][u] = (64 * g + l < R) ? ld4(Ssh + (64 * g + l) * (R + 4) + w * KW + 4 * u) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  __device__ __forceinline__ void product(const float* __restrict__ Lsh, float* __restrict__ red, int w, int l,
-                                          float (&out)[NE]) const {
-    f32x4 a[KU];
-#pragma unroll
-    for (int u = 0; u < KU; ++u) a[u] = ld4(Lsh + (l & 3) * (R + 4) + w * KW + 4 * u);
-    f32x4 h[NG][2];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) h[g][0] = h[g][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < KU; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int g = 0; g < NG; ++g) h[g][e & 1] = mfma_f32_4x4x1(a[u][e], b[g][u][e], h[g][e & 1]);
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const f32x4 p = h[g][0] + h[g][1];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) red[((w * NG + g) * 4 + v) * 64 + l] = p[v];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int p = 0; p < NE; ++p) {
-      const int e = threadIdx.x + 256 * p;
-      const int i = e / R, j = e % R, g = j >> 6, jl = j & 63;
-      float sum = 0.f;
-      if (e < 4 * R) {
-        sum = red[((0 * NG + g) * 4 + i) * 64 + jl];
-#pragma unroll
-        for (int q = 1; q < 4; ++q) sum += red[((q * NG + g) * 4 + i) * 64 + jl];
-      }
-      out[p] = sum;
-    }
-  }
-};
+// sum over the lane quad (lanes 4 j .. 4 j + 3), the same in all four lanes
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ void rs_st2(__amdgpu_buffer_rsrc_t rs, int off, f32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, 16);
+}
+__device__ __forceinline__ f32x2 ld2(const float* p) { return *reinterpret_cast<const f32x2*>(p); }
 
 // part: G Gram pieces [R][R] of X0 (their sum is X0^T X0); nparts: the nnp
 // partial sums of ||X0||_F^2 (s = 1/||X0||_F, 0 for X0 = 0) or null (s = 1);
 // Sring: kRsRing R x R floats; flags: kRsSyncWords words cleared by the launch
-// before; M: s Q_iters [R][R]; limit: polls per wait before it gives up.
-template <int R>
-__global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part, int G,
-                                                 const float* __restrict__ nparts, int nnp, int iters,
-                                                 float* __restrict__ Sring, unsigned* __restrict__ flags,
-                                                 float* __restrict__ M, unsigned limit) {
-  constexpr int RP = R + 4, NS = R / kRsS, NE = RsRows<R>::NE, NG = RsRows<R>::NG, U4 = R / 4;
-  constexpr int SLOT = R * R * 4;  // bytes per ring slot
+// before; M: s Q_iters [R][R]; limit: polls per wait before it gives up.  RHO
+// rows per workgroup (the launch uses 1).
+template <int R, int RHO>
+__global__ __launch_bounds__(2 * R) void k_spel_rsv(const float* __restrict__ part, int G,
+                                                    const float* __restrict__ nparts, int nnp, int iters,
+                                                    float* __restrict__ Sring, unsigned* __restrict__ flags,
+                                                    float* __restrict__ M, unsigned limit) {
+  constexpr int KQ = R / 4, LP = 4 * (KQ + 4), NS = R / RHO, SLOT = R * R * 4;
+  static_assert(R % 32 == 0 && R <= 128 && R % RHO == 0, "shape");
   static_assert(2 * NS <= kRsFlagWords, "one progress counter per workgroup");
-  extern __shared__ __align__(16) float Ssh[];     // the exchanged S_k [R][RP], staged
-  __shared__ __align__(16) float Xsh[kRsS * RP];  // left operand rows of the next product
-  __shared__ float red[4 * NG * 4 * 64];
+  __shared__ __align__(16) float Lb[2][RHO][LP];  // left rows of a product, double-buffered
+  extern __shared__ __align__(16) float Ssh[];     // S_k, staged (rows at rs_row)
   __shared__ float scs;
   __shared__ int slot;
   const int lane = threadIdx.x & 63, w = wave_id();
+  const int q = lane & 3, c0 = 32 * w + 2 * (lane >> 2);
+  const int lo = (c0 / KQ) * (KQ + 4) + c0 % KQ;  // position of column c0 in an LDS row
   const bool isS = blockIdx.x < NS;
-  const int J = isS ? blockIdx.x : blockIdx.x - NS, r0 = J * kRsS;
+  const int J = isS ? blockIdx.x : blockIdx.x - NS, r0 = J * RHO;
   const float sx = nparts ? block_inv_norm(nparts, nnp, &scs) : 1.f;
   const __amdgpu_buffer_rsrc_t rs = rs_rsrc(Sring);
-  RsRows<R> B;  // right factor: the staged S_k, this wave's K range
-  // element e = threadIdx.x + 256 p of the 4 rows: row e / R, column e % R
-  auto put = [&](const float (&v)[NE]) {  // v -> Xsh, visible to every wave
+  f32x2 b[KQ];  // S_k[q KQ + t][c0 .. c0 + 1]
+  auto load = [&](int x) {  // S_{2x} -> LDS -> b
+    rs_stage<R, 2 * R>(rs, (x % kRsRing) * SLOT, Ssh);
+    __syncthreads();
 #pragma unroll
-    for (int p = 0; p < NE; ++p) {
-      const int e = threadIdx.x + 256 * p;
-      if (e < 4 * R) Xsh[(e / R) * RP + e % R] = v[p];
+    for (int t = 0; t < KQ; ++t) b[t] = ld2(Ssh + rs_row<R>(q * KQ + t) + c0);
+  };
+  int buf = 0;
+  auto put = [&](const f32x2 (&v)[RHO]) {  // v -> the next left rows, visible to every wave
+    buf ^= 1;
+    if (q == 0) {
+#pragma unroll
+      for (int i = 0; i < RHO; ++i) *reinterpret_cast<f32x2*>(&Lb[buf][i][lo]) = v[i];
     }
     __syncthreads();
   };
-  auto mul = [&](float (&out)[NE]) { B.product(Xsh, red, w, lane, out); };  // out = Xsh S_k
-  // rows times h(S_k) = 2.25 S - 1.5 S^2 + 0.25 S^3 (the rows are in Xsh)
-  auto mul_h = [&](float (&out)[NE]) {
-    float a1[NE], a2[NE], a3[NE];
+  auto mul = [&](f32x2 (&out)[RHO]) {  // out = (left rows) S_k
+#pragma unroll
+    for (int i = 0; i < RHO; ++i) {
+      float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+      for (int t = 0; t < KQ; t += 4) {
+        const f32x4 l4 = ld4(&Lb[buf][i][q * (KQ + 4) + t]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          a0 = fmaf(l4[e], b[t + e][0], a0);
+          a1 = fmaf(l4[e], b[t + e][1], a1);
+        }
+      }
+      out[i] = f32x2{quad_sum(a0), quad_sum(a1)};
+    }
+  };
+  // (left rows) h(S_k), h(x) = 2.25 x - 1.5 x^2 + 0.25 x^3
+  auto mul_h = [&](f32x2 (&out)[RHO]) {
+    f32x2 a1[RHO], a2[RHO], a3[RHO];
     mul(a1);
     put(a1);
     mul(a2);
     put(a2);
     mul(a3);
 #pragma unroll
-    for (int p = 0; p < NE; ++p) out[p] = (2.25f * a1[p] - 1.5f * a2[p]) + 0.25f * a3[p];
+    for (int i = 0; i < RHO; ++i) out[i] = (2.25f * a1[i] - 1.5f * a2[i]) + 0.25f * a3[i];
   };
   const int nx = (iters - 1) / 2;  // exchanges after S_0: S_2, S_4, .., S_{2 nx}
 
   if (isS) {
     // S_0 rows: s^2 times the pieces' sum, in piece order
     const float s2 = sx * sx;
-    if (threadIdx.x < kRsS * U4) {
-      const size_t o = size_t(r0 + threadIdx.x / U4) * R + 4 * (threadIdx.x % U4);
-      f32x4 v = ld4(part + o);
-      for (int q = 1; q < G; ++q) v += ld4(part + size_t(q) * R * R + o);
-      rs_st(rs, int(o) * 4, v * s2);
+    f32x2 s0[RHO];
+#pragma unroll
+    for (int i = 0; i < RHO; ++i) {
+      const size_t o = size_t(r0 + i) * R + c0;
+      f32x2 v = ld2(part + o);
+      for (int g = 1; g < G; ++g) v += ld2(part + size_t(g) * R * R + o);
+      s0[i] = v * s2;
+      if (q == 0) rs_st2(rs, int(o) * 4, s0[i]);
     }
     rs_publish(flags, J, 1u);
     for (int x = 0; x < nx; ++x) {  // S_{2x} -> S_{2x+2}
-      // S_{2x} complete, and slot (x + 1) mod kRsRing read by every Q workgroup (S_{2(x+1-kRsRing)})
+      // S_{2x} complete and, once the ring wraps, slot (x + 1) mod kRsRing (S_{2(x+1-kRsRing)})
+      // read by every Q workgroup
       const int qneed = x + 2 - kRsRing;
       if (!rs_wait(flags, NS, unsigned(x + 1), qneed > 0 ? NS : 0, unsigned(max(qneed, 0)), limit, &slot)) return;
-      rs_stage<R>(rs, (x % kRsRing) * SLOT, Ssh);
-      __syncthreads();
-      B.load(Ssh, w, lane);
-      float s0[NE], t1[NE], t2[NE], u[NE], wv[NE], y[NE];
-#pragma unroll
-      for (int p = 0; p < NE; ++p) {
-        const int e = min(int(threadIdx.x) + 256 * p, 4 * R - 1);
-        s0[p] = Ssh[(r0 + e / R) * RP + e % R];
-      }
+      load(x);
+      f32x2 t1[RHO], t2[RHO], u[RHO], wv[RHO], y[RHO];
       put(s0);
       mul(t1);  // rows of S^2
       put(t1);
       mul(t2);  // rows of S^3
 #pragma unroll
-      for (int p = 0; p < NE; ++p) u[p] = (2.25f * s0[p] - 1.5f * t1[p]) + 0.25f * t2[p];  // rows of S_{k+1}
+      for (int i = 0; i < RHO; ++i) u[i] = (2.25f * s0[i] - 1.5f * t1[i]) + 0.25f * t2[i];  // rows of S_{k+1}
       put(u);
       mul_h(wv);  // rows of S_{k+1}^2
       put(wv);
       mul_h(y);  // rows of S_{k+1}^3
 #pragma unroll
-      for (int p = 0; p < NE; ++p) y[p] = (2.25f * u[p] - 1.5f * wv[p]) + 0.25f * y[p];  // rows of S_{k+2}
-      put(y);
-      if (threadIdx.x < kRsS * U4) {
-        const int i = threadIdx.x / U4, j = 4 * (threadIdx.x % U4);
-        rs_st(rs, ((x + 1) % kRsRing) * SLOT + ((r0 + i) * R + j) * 4, ld4(Xsh + i * RP + j));
+      for (int i = 0; i < RHO; ++i) {
+        s0[i] = (2.25f * u[i] - 1.5f * wv[i]) + 0.25f * y[i];  // rows of S_{k+2}
+        if (q == 0) rs_st2(rs, ((x + 1) % kRsRing) * SLOT + ((r0 + i) * R + c0) * 4, s0[i]);
       }
       rs_publish(flags, J, unsigned(x + 2));
     }
@@ -568,54 +562,55 @@ __global__ __launch_bounds__(256) void k_spel_rs(const float* __restrict__ part,
   // Q workgroup: Q_{k+2} = B (1.5 I - 0.5 h(S_k)), B = Q_k T_k, for k = 0, 2, ..; an odd
   // step count ends with Q_n = Q_{n-1} T_{n-1}
   bool ok = true;
-  float q[NE] = {};
+  f32x2 qv[RHO];
   for (int x = 0; 2 * x < iters; ++x) {
     if (!rs_wait(flags, NS, unsigned(x + 1), 0, 0u, limit, &slot)) {
       ok = false;
       break;
     }
-    rs_stage<R>(rs, (x % kRsRing) * SLOT, Ssh);
-    rs_publish(flags, NS + J, unsigned(x + 1));  // S_{2x} read (its loads are complete)
-    B.load(Ssh, w, lane);
-    float b[NE];
-    if (x == 0) {  // B = T_0
+    load(x);
+    f32x2 bq[RHO];
+    if (x == 0) {  // B = T_0, from this workgroup's rows of S_0
 #pragma unroll
-      for (int p = 0; p < NE; ++p) {
-        const int e = min(int(threadIdx.x) + 256 * p, 4 * R - 1), i = r0 + e / R, j = e % R;
-        b[p] = (i == j ? 1.5f : 0.f) - 0.5f * Ssh[i * RP + j];
+      for (int i = 0; i < RHO; ++i) {
+        const f32x2 srow = ld2(Ssh + rs_row<R>(r0 + i) + c0);
+        bq[i] = f32x2{r0 + i == c0 ? 1.5f : 0.f, r0 + i == c0 + 1 ? 1.5f : 0.f} - 0.5f * srow;
       }
-    } else {
-      put(q);
-      float t[NE];
+    }
+    // the slot is rewritten only after every Q workgroup has read it, where an S
+    // workgroup still has to write it (x + kRsRing <= nx)
+    if (x + kRsRing <= nx) rs_publish(flags, NS + J, unsigned(x + 1));
+    if (x > 0) {
+      f32x2 t[RHO];
+      put(qv);
       mul(t);
 #pragma unroll
-      for (int p = 0; p < NE; ++p) b[p] = 1.5f * q[p] - 0.5f * t[p];
+      for (int i = 0; i < RHO; ++i) bq[i] = 1.5f * qv[i] - 0.5f * t[i];
     }
     if (2 * x + 1 == iters) {  // the last, single step
 #pragma unroll
-      for (int p = 0; p < NE; ++p) q[p] = b[p];
+      for (int i = 0; i < RHO; ++i) qv[i] = bq[i];
       break;
     }
-    put(b);
-    float bh[NE];
+    f32x2 bh[RHO];
+    put(bq);
     mul_h(bh);
 #pragma unroll
-    for (int p = 0; p < NE; ++p) q[p] = 1.5f * b[p] - 0.5f * bh[p];
-    __syncthreads();  // every wave is done with the staged S_k before the next is staged
+    for (int i = 0; i < RHO; ++i) qv[i] = 1.5f * bq[i] - 0.5f * bh[i];
   }
   if (threadIdx.x == 0) slot = int(__hip_atomic_load(flags + kRsTimeoutWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   __syncthreads();
   if (slot != 0) ok = false;
   const float nan = __builtin_nanf("");
-  put(q);
-  if (threadIdx.x < kRsS * U4) {
-    const int i = threadIdx.x / U4, j = 4 * (threadIdx.x % U4);
-    st4(M + size_t(r0 + i) * R + j, ok ? ld4(Xsh + i * RP + j) * sx : f32x4{nan, nan, nan, nan});
+  if (q == 0) {
+#pragma unroll
+    for (int i = 0; i < RHO; ++i)
+      *reinterpret_cast<f32x2*>(M + size_t(r0 + i) * R + c0) = ok ? qv[i] * sx : f32x2{nan, nan};
   }
 }
 
 // Gram-space Newton-Schulz for 128 < r <= 256, one launch per half step.
-// The same recurrence as k_spel_rs (X_k = X Q_k, S_k = X_k^T X_k, T_k =
+// The same recurrence as k_spel_rsv (X_k = X Q_k, S_k = X_k^T X_k, T_k =
 // 1.5 I - 0.5 S_k, Q_{k+1} = Q_k T_k, S_{k+1} = T_k S_k T_k), but r x r no
 // longer fits one workgroup's LDS, so the kernel boundary is the exchange:
 //   RS_UQ   (step k < n)  U = S_{k-1} T_{k-1} and Q_k = Q_{k-1} T_{k-1}
@@ -878,25 +873,25 @@ unsigned rs_spin_limit() {
   return v < kRsSpinLimit ? unsigned(v) : kRsSpinLimit;
 }
 
+// rows per workgroup of the vector-ALU Gram-space iteration
+constexpr int kRsvRows = 1;
+
 template <int R>
-void launch_rs(const float* part, int G, const float* nparts, int nnp, int iters, float* Sbuf, unsigned* sync,
-               float* M, hipStream_t s) {
-  constexpr int lds = R * (R + 4) * int(sizeof(float));  // the staged S_k
-  // with the kernel's static arrays (own Q and S^2 rows, the wave partials)
-  static_assert(lds + kRsS * (R + 4) * 4 + 4 * RsRows<R>::NG * 4 * 64 * 4 + 64 <= kMaxLdsBytes,
-                "Gram-space iteration LDS");
-  (void)LdsLimit<k_spel_rs<R>, lds>::bytes();
-  hipLaunchKernelGGL(k_spel_rs<R>, dim3(2 * (R / kRsS)), dim3(256), lds, s, part, G, nparts, nnp, iters, Sbuf,
-                     sync, M, rs_spin_limit());
+void launch_rsv(const float* part, int G, const float* nparts, int nnp, int iters, float* Sbuf, unsigned* sync,
+                float* M, hipStream_t s) {
+  constexpr int lds = kRsStageFloats<R> * int(sizeof(float));  // the staged S_k
+  (void)LdsLimit<k_spel_rsv<R, kRsvRows>, lds>::bytes();
+  hipLaunchKernelGGL((k_spel_rsv<R, kRsvRows>), dim3(2 * (R / kRsvRows)), dim3(2 * R), lds, s, part, G, nparts, nnp,
+                     iters, Sbuf, sync, M, rs_spin_limit());
 }
 
 // M = s Q_iters of the Gram-space iteration inside one launch (r <= 128)
 void launch_rs_any(int r, const float* part, int G, const float* nparts, int nnp, int iters, float* Sbuf,
                    unsigned* sync, float* M, hipStream_t s) {
-  if (r == 32) launch_rs<32>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
-  else if (r == 64) launch_rs<64>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
-  else if (r == 96) launch_rs<96>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
-  else launch_rs<128>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
+  if (r == 32) launch_rsv<32>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
+  else if (r == 64) launch_rsv<64>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
+  else if (r == 96) launch_rsv<96>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
+  else launch_rsv<128>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
 }
 
 // M = s Q_iters by the one-launch-per-half-step Gram-space iteration (128 < r <= 256).
