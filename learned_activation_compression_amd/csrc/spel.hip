@@ -440,75 +440,102 @@ __device__ __forceinline__ void rs_stage(__amdgpu_buffer_rsrc_t rs, int base, fl
   }
 }
 
-// sum over the lane quad (lanes 4 j .. 4 j + 3), the same in all four lanes
-__device__ __forceinline__ float quad_sum(float v) {
+// sum over the KS lanes 4 j .. 4 j + KS - 1 (KS = 4: the lane quad; KS = 8:
+// both quads of a half row, added by a half-row mirror), the same in all of them
+template <int KS>
+__device__ __forceinline__ float ksum(float v) {
+  static_assert(KS == 4 || KS == 8, "lane group");
   v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+  if (KS == 8) v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));
+  return v;
 }
-__device__ __forceinline__ void rs_st2(__amdgpu_buffer_rsrc_t rs, int off, f32x2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, 16);
+
+template <int N> struct FVec;
+template <> struct FVec<2> { typedef f32x2 T; };
+template <> struct FVec<4> { typedef f32x4 T; };
+template <int N>
+__device__ __forceinline__ typename FVec<N>::T rs_ldv(__amdgpu_buffer_rsrc_t rs, int off) {
+  if constexpr (N == 2) return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 16));
+  else return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 16));
 }
-__device__ __forceinline__ f32x2 ld2(const float* p) { return *reinterpret_cast<const f32x2*>(p); }
+template <int N>
+__device__ __forceinline__ void rs_stv(__amdgpu_buffer_rsrc_t rs, int off, typename FVec<N>::T v) {
+  if constexpr (N == 2) __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, 16);
+  else __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 16);
+}
 
 // part: G Gram pieces [R][R] of X0 (their sum is X0^T X0); nparts: the nnp
 // partial sums of ||X0||_F^2 (s = 1/||X0||_F, 0 for X0 = 0) or null (s = 1);
 // Sring: kRsRing R x R floats; flags: kRsSyncWords words cleared by the launch
-// before; M: s Q_iters [R][R]; limit: polls per wait before it gives up.  RHO
-// rows per workgroup (the launch uses 1).
-template <int R, int RHO>
+// before; M: s Q_iters [R][R]; limit: polls per wait before it gives up.
+// RHO rows per workgroup; lane l of wave w owns the CPT columns from
+// c0 = 32 w + CPT (l / KS) and the contraction part l % KS (R / KS values of
+// k); STAGE: S_k is copied to LDS first (r <= 128), else every thread loads
+// its entries itself.
+template <int R, int RHO, int KS, int CPT, bool STAGE>
 __global__ __launch_bounds__(2 * R) void k_spel_rsv(const float* __restrict__ part, int G,
                                                     const float* __restrict__ nparts, int nnp, int iters,
                                                     float* __restrict__ Sring, unsigned* __restrict__ flags,
                                                     float* __restrict__ M, unsigned limit) {
-  constexpr int KQ = R / 4, LP = 4 * (KQ + 4), NS = R / RHO, SLOT = R * R * 4;
-  static_assert(R % 32 == 0 && R <= 128 && R % RHO == 0, "shape");
+  typedef typename FVec<CPT>::T V;
+  constexpr int KQ = R / KS, LP = KS * (KQ + 4), NS = R / RHO, SLOT = R * R * 4;
+  static_assert(R % 32 == 0 && R % RHO == 0 && (64 / KS) * CPT == 32 && KQ % 4 == 0, "shape");
+  static_assert(!STAGE || KS == 4, "the staged layout is padded for lane quads");
   static_assert(2 * NS <= kRsFlagWords, "one progress counter per workgroup");
   __shared__ __align__(16) float Lb[2][RHO][LP];  // left rows of a product, double-buffered
   extern __shared__ __align__(16) float Ssh[];     // S_k, staged (rows at rs_row)
   __shared__ float scs;
   __shared__ int slot;
   const int lane = threadIdx.x & 63, w = wave_id();
-  const int q = lane & 3, c0 = 32 * w + 2 * (lane >> 2);
+  const int q = lane % KS, c0 = 32 * w + CPT * (lane / KS);
   const int lo = (c0 / KQ) * (KQ + 4) + c0 % KQ;  // position of column c0 in an LDS row
   const bool isS = blockIdx.x < NS;
   const int J = isS ? blockIdx.x : blockIdx.x - NS, r0 = J * RHO;
   const float sx = nparts ? block_inv_norm(nparts, nnp, &scs) : 1.f;
   const __amdgpu_buffer_rsrc_t rs = rs_rsrc(Sring);
-  f32x2 b[KQ];  // S_k[q KQ + t][c0 .. c0 + 1]
-  auto load = [&](int x) {  // S_{2x} -> LDS -> b
-    rs_stage<R, 2 * R>(rs, (x % kRsRing) * SLOT, Ssh);
-    __syncthreads();
+  V b[KQ];  // S_k[q KQ + t][c0 .. c0 + CPT - 1]
+  auto load = [&](int x) {  // S_{2x} -> b
+    if constexpr (STAGE) {
+      rs_stage<R, 2 * R>(rs, (x % kRsRing) * SLOT, Ssh);
+      __syncthreads();
 #pragma unroll
-    for (int t = 0; t < KQ; ++t) b[t] = ld2(Ssh + rs_row<R>(q * KQ + t) + c0);
+      for (int t = 0; t < KQ; ++t) b[t] = *reinterpret_cast<const V*>(Ssh + rs_row<R>(q * KQ + t) + c0);
+    } else {
+      const int base = (x % kRsRing) * SLOT + (q * KQ * R + c0) * 4;
+#pragma unroll
+      for (int t = 0; t < KQ; ++t) b[t] = rs_ldv<CPT>(rs, base + t * R * 4);
+      __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first use
+    }
   };
   int buf = 0;
-  auto put = [&](const f32x2 (&v)[RHO]) {  // v -> the next left rows, visible to every wave
+  auto put = [&](const V (&v)[RHO]) {  // v -> the next left rows, visible to every wave
     buf ^= 1;
     if (q == 0) {
 #pragma unroll
-      for (int i = 0; i < RHO; ++i) *reinterpret_cast<f32x2*>(&Lb[buf][i][lo]) = v[i];
+      for (int i = 0; i < RHO; ++i) *reinterpret_cast<V*>(&Lb[buf][i][lo]) = v[i];
     }
     __syncthreads();
   };
-  auto mul = [&](f32x2 (&out)[RHO]) {  // out = (left rows) S_k
+  auto mul = [&](V (&out)[RHO]) {  // out = (left rows) S_k
 #pragma unroll
     for (int i = 0; i < RHO; ++i) {
-      float a0 = 0.f, a1 = 0.f;
+      float a[CPT] = {};
 #pragma unroll
       for (int t = 0; t < KQ; t += 4) {
         const f32x4 l4 = ld4(&Lb[buf][i][q * (KQ + 4) + t]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a0 = fmaf(l4[e], b[t + e][0], a0);
-          a1 = fmaf(l4[e], b[t + e][1], a1);
-        }
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int c = 0; c < CPT; ++c) a[c] = fmaf(l4[e], b[t + e][c], a[c]);
       }
-      out[i] = f32x2{quad_sum(a0), quad_sum(a1)};
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) out[i][c] = ksum<KS>(a[c]);
     }
   };
   // (left rows) h(S_k), h(x) = 2.25 x - 1.5 x^2 + 0.25 x^3
-  auto mul_h = [&](f32x2 (&out)[RHO]) {
-    f32x2 a1[RHO], a2[RHO], a3[RHO];
+  auto mul_h = [&](V (&out)[RHO]) {
+    V a1[RHO], a2[RHO], a3[RHO];
     mul(a1);
     put(a1);
     mul(a2);
@@ -522,14 +549,14 @@ __global__ __launch_bounds__(2 * R) void k_spel_rsv(const float* __restrict__ pa
   if (isS) {
     // S_0 rows: s^2 times the pieces' sum, in piece order
     const float s2 = sx * sx;
-    f32x2 s0[RHO];
+    V s0[RHO];
 #pragma unroll
     for (int i = 0; i < RHO; ++i) {
       const size_t o = size_t(r0 + i) * R + c0;
-      f32x2 v = ld2(part + o);
-      for (int g = 1; g < G; ++g) v += ld2(part + size_t(g) * R * R + o);
+      V v = *reinterpret_cast<const V*>(part + o);
+      for (int g = 1; g < G; ++g) v += *reinterpret_cast<const V*>(part + size_t(g) * R * R + o);
       s0[i] = v * s2;
-      if (q == 0) rs_st2(rs, int(o) * 4, s0[i]);
+      if (q == 0) rs_stv<CPT>(rs, int(o) * 4, s0[i]);
     }
     rs_publish(flags, J, 1u);
     for (int x = 0; x < nx; ++x) {  // S_{2x} -> S_{2x+2}
@@ -538,7 +565,7 @@ __global__ __launch_bounds__(2 * R) void k_spel_rsv(const float* __restrict__ pa
       const int qneed = x + 2 - kRsRing;
       if (!rs_wait(flags, NS, unsigned(x + 1), qneed > 0 ? NS : 0, unsigned(max(qneed, 0)), limit, &slot)) return;
       load(x);
-      f32x2 t1[RHO], t2[RHO], u[RHO], wv[RHO], y[RHO];
+      V t1[RHO], t2[RHO], u[RHO], wv[RHO], y[RHO];
       put(s0);
       mul(t1);  // rows of S^2
       put(t1);
@@ -552,7 +579,7 @@ __global__ __launch_bounds__(2 * R) void k_spel_rsv(const float* __restrict__ pa
 #pragma unroll
       for (int i = 0; i < RHO; ++i) {
         s0[i] = (2.25f * u[i] - 1.5f * wv[i]) + 0.25f * y[i];  // rows of S_{k+2}
-        if (q == 0) rs_st2(rs, ((x + 1) % kRsRing) * SLOT + ((r0 + i) * R + c0) * 4, s0[i]);
+        if (q == 0) rs_stv<CPT>(rs, ((x + 1) % kRsRing) * SLOT + ((r0 + i) * R + c0) * 4, s0[i]);
       }
       rs_publish(flags, J, unsigned(x + 2));
     }
@@ -562,26 +589,36 @@ __global__ __launch_bounds__(2 * R) void k_spel_rsv(const float* __restrict__ pa
   // Q workgroup: Q_{k+2} = B (1.5 I - 0.5 h(S_k)), B = Q_k T_k, for k = 0, 2, ..; an odd
   // step count ends with Q_n = Q_{n-1} T_{n-1}
   bool ok = true;
-  f32x2 qv[RHO];
+  V qv[RHO];
   for (int x = 0; 2 * x < iters; ++x) {
     if (!rs_wait(flags, NS, unsigned(x + 1), 0, 0u, limit, &slot)) {
       ok = false;
       break;
     }
-    load(x);
-    f32x2 bq[RHO];
+    V bq[RHO];
     if (x == 0) {  // B = T_0, from this workgroup's rows of S_0
 #pragma unroll
       for (int i = 0; i < RHO; ++i) {
-        const f32x2 srow = ld2(Ssh + rs_row<R>(r0 + i) + c0);
-        bq[i] = f32x2{r0 + i == c0 ? 1.5f : 0.f, r0 + i == c0 + 1 ? 1.5f : 0.f} - 0.5f * srow;
+        V srow;
+        if constexpr (STAGE) srow = V{};
+        else srow = rs_ldv<CPT>(rs, ((r0 + i) * R + c0) * 4);
+        bq[i] = srow;
+      }
+    }
+    load(x);
+    if (x == 0) {
+#pragma unroll
+      for (int i = 0; i < RHO; ++i) {
+        if constexpr (STAGE) bq[i] = *reinterpret_cast<const V*>(Ssh + rs_row<R>(r0 + i) + c0);
+#pragma unroll
+        for (int c = 0; c < CPT; ++c) bq[i][c] = (r0 + i == c0 + c ? 1.5f : 0.f) - 0.5f * bq[i][c];
       }
     }
     // the slot is rewritten only after every Q workgroup has read it, where an S
     // workgroup still has to write it (x + kRsRing <= nx)
     if (x + kRsRing <= nx) rs_publish(flags, NS + J, unsigned(x + 1));
     if (x > 0) {
-      f32x2 t[RHO];
+      V t[RHO];
       put(qv);
       mul(t);
 #pragma unroll
@@ -592,7 +629,7 @@ __global__ __launch_bounds__(2 * R) void k_spel_rsv(const float* __restrict__ pa
       for (int i = 0; i < RHO; ++i) qv[i] = bq[i];
       break;
     }
-    f32x2 bh[RHO];
+    V bh[RHO];
     put(bq);
     mul_h(bh);
 #pragma unroll
@@ -601,11 +638,13 @@ __global__ __launch_bounds__(2 * R) void k_spel_rsv(const float* __restrict__ pa
   if (threadIdx.x == 0) slot = int(__hip_atomic_load(flags + kRsTimeoutWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
   __syncthreads();
   if (slot != 0) ok = false;
-  const float nan = __builtin_nanf("");
   if (q == 0) {
 #pragma unroll
-    for (int i = 0; i < RHO; ++i)
-      *reinterpret_cast<f32x2*>(M + size_t(r0 + i) * R + c0) = ok ? qv[i] * sx : f32x2{nan, nan};
+    for (int i = 0; i < RHO; ++i) {
+      V o = qv[i] * sx;
+      if (!ok) o = V{} + __builtin_nanf("");
+      *reinterpret_cast<V*>(M + size_t(r0 + i) * R + c0) = o;
+    }
   }
 }
 
@@ -873,25 +912,45 @@ unsigned rs_spin_limit() {
   return v < kRsSpinLimit ? unsigned(v) : kRsSpinLimit;
 }
 
-// rows per workgroup of the vector-ALU Gram-space iteration
-constexpr int kRsvRows = 1;
-
+// The vector-ALU Gram-space iteration inside one launch: r <= 128 one row per
+// workgroup, lane quads, S_k staged in LDS; 128 < r <= 256 two rows per
+// workgroup, lane octets, S_k read straight into registers (r x r no longer
+// fits LDS).  Either way 2 r / RHO workgroups that must all be resident.
 template <int R>
 void launch_rsv(const float* part, int G, const float* nparts, int nnp, int iters, float* Sbuf, unsigned* sync,
                 float* M, hipStream_t s) {
-  constexpr int lds = kRsStageFloats<R> * int(sizeof(float));  // the staged S_k
-  (void)LdsLimit<k_spel_rsv<R, kRsvRows>, lds>::bytes();
-  hipLaunchKernelGGL((k_spel_rsv<R, kRsvRows>), dim3(2 * (R / kRsvRows)), dim3(2 * R), lds, s, part, G, nparts, nnp,
-                     iters, Sbuf, sync, M, rs_spin_limit());
+  if constexpr (R <= 128) {
+    constexpr int lds = kRsStageFloats<R> * int(sizeof(float));  // the staged S_k
+    (void)LdsLimit<k_spel_rsv<R, 1, 4, 2, true>, lds>::bytes();
+    hipLaunchKernelGGL((k_spel_rsv<R, 1, 4, 2, true>), dim3(2 * R), dim3(2 * R), lds, s, part, G, nparts, nnp, iters,
+                       Sbuf, sync, M, rs_spin_limit());
+  } else {
+    hipLaunchKernelGGL((k_spel_rsv<R, 2, 8, 4, false>), dim3(R), dim3(2 * R), 0, s, part, G, nparts, nnp, iters, Sbuf,
+                       sync, M, rs_spin_limit());
+  }
 }
 
-// M = s Q_iters of the Gram-space iteration inside one launch (r <= 128)
+// M = s Q_iters of the Gram-space iteration inside one launch (r <= 256)
 void launch_rs_any(int r, const float* part, int G, const float* nparts, int nnp, int iters, float* Sbuf,
                    unsigned* sync, float* M, hipStream_t s) {
-  if (r == 32) launch_rsv<32>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
-  else if (r == 64) launch_rsv<64>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
-  else if (r == 96) launch_rsv<96>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
-  else launch_rsv<128>(part, G, nparts, nnp, iters, Sbuf, sync, M, s);
+  switch (r) {
+    case 32: launch_rsv<32>(part, G, nparts, nnp, iters, Sbuf, sync, M, s); break;
+    case 64: launch_rsv<64>(part, G, nparts, nnp, iters, Sbuf, sync, M, s); break;
+    case 96: launch_rsv<96>(part, G, nparts, nnp, iters, Sbuf, sync, M, s); break;
+    case 128: launch_rsv<128>(part, G, nparts, nnp, iters, Sbuf, sync, M, s); break;
+    case 160: launch_rsv<160>(part, G, nparts, nnp, iters, Sbuf, sync, M, s); break;
+    case 192: launch_rsv<192>(part, G, nparts, nnp, iters, Sbuf, sync, M, s); break;
+    case 224: launch_rsv<224>(part, G, nparts, nnp, iters, Sbuf, sync, M, s); break;
+    default: launch_rsv<256>(part, G, nparts, nnp, iters, Sbuf, sync, M, s); break;
+  }
+}
+
+// Compute units of the current device (0 if it cannot be read).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return n;
 }
 
 // M = s Q_iters by the one-launch-per-half-step Gram-space iteration (128 < r <= 256).
@@ -989,9 +1048,10 @@ void launch_spel(float* A, const float* g, float* m, float alpha, float beta, in
   launch_xm<false>(G, xgrid, s, A, nullptr, part, w.Xm, d, r, int(XM_TANGENT), g, m, beta, w.nparts, nullptr, 0.f,
                    nullptr, nullptr);
 
-  if (r <= 128) {
-    // Gram-space iteration: S_0 from the pieces of Xm^T Xm, M = s Q_n, then D = Xm M and
-    // Y0 = A - alpha D (Eq. (6)); the same for Y0 (unscaled) and A = Y0 M (Eq. (7))
+  if (r <= 128 || (r <= 256 && device_cus() >= r)) {
+    // Gram-space iteration in one launch: S_0 from the pieces of Xm^T Xm, M = s Q_n, then
+    // D = Xm M and Y0 = A - alpha D (Eq. (6)); the same for Y0 (unscaled) and A = Y0 M
+    // (Eq. (7)).  Above r = 128 its r workgroups take a compute unit each.
     const int npn = (d / 32) * (r / 32);
     hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, w.Xm, w.Xm, part, d, r, G, w.sync, kRsStickyWord);
     launch_rs_any(r, part, G, w.nparts, npn, ns_iters, w.Sbuf, w.sync, w.Mb, s);
@@ -1005,8 +1065,8 @@ void launch_spel(float* A, const float* g, float* m, float alpha, float beta, in
   }
 
   if (r <= 256) {
-    // the same Gram-space iteration with one launch per half step (r x r no longer fits a
-    // workgroup): S_k, S_{k-1} T_{k-1} and Q_k live in the rs ring and Xa
+    // the same Gram-space iteration with one launch per half step (a device with fewer
+    // than r compute units): S_k, S_{k-1} T_{k-1} and Q_k live in the rs ring and Xa
     const int npn = (d / 32) * (r / 32);
     const size_t rr = size_t(r) * r;
     float *Sb0 = w.Sbuf, *Sb1 = w.Sbuf + rr, *U = w.Sbuf + 2 * rr, *Q0 = w.Sbuf + 3 * rr, *Q1 = w.Xa;

@@ -93,23 +93,25 @@ def test_spel_repeat_is_bitwise_deterministic():
         assert torch.equal(x, y)
 
 
-def test_spel_repeat_is_bitwise_deterministic_at_r128():
-    # r <= 128 runs the r x r (Gram-space) form of the iteration, whose workgroups meet at a counter
-    inp = synth.spel_inputs(34, 1024, 128, 1e-3)
-    m0 = torch.from_numpy(synth.gaussian(synth.stream(8, 1024, 128), (1024, 128), 1e-4).astype(np.float32))
+@pytest.mark.parametrize("d,r", [(1024, 128), (2048, 256)])
+def test_spel_repeat_is_bitwise_deterministic_in_gram_space(d, r):
+    # r <= 256 runs the r x r (Gram-space) form of the iteration, whose workgroups meet at counters
+    inp = synth.spel_inputs(34, d, r, 1e-3)
+    m0 = torch.from_numpy(synth.gaussian(synth.stream(8, d, r), (d, r), 1e-4).astype(np.float32))
     a = run(inp["A"], inp["g"], m0, 1e-3, 0.9, 8)
     b = run(inp["A"], inp["g"], m0, 1e-3, 0.9, 8)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
 
 
-def test_spel_wait_timeout_leaves_the_state_unchanged_then_recovers(monkeypatch):
+@pytest.mark.parametrize("d,r", [(1024, 128), (2048, 256)])
+def test_spel_wait_timeout_leaves_the_state_unchanged_then_recovers(monkeypatch, d, r):
     # the r x r iteration's workgroups wait for one another with a bounded wait; a test hook
     # lowers the bound to zero, so the first wait gives up and every kernel still exits: the
     # step must then be abandoned -- A and m bit-for-bit as they were, status 1 -- and the next
     # call with the normal bound must be correct again
-    inp = synth.spel_inputs(35, 1024, 128, 1e-3)
-    m0 = torch.from_numpy(synth.gaussian(synth.stream(11, 1024, 128), (1024, 128), 1e-4).astype(np.float32))
+    inp = synth.spel_inputs(35, d, r, 1e-3)
+    m0 = torch.from_numpy(synth.gaussian(synth.stream(11, d, r), (d, r), 1e-4).astype(np.float32))
     monkeypatch.setenv("MAPL_SPEL_SPIN_LIMIT", "0")
     Ad, md, D = run(inp["A"], inp["g"], m0, 1e-3, 0.9, 8, expect_status=1)
     assert torch.equal(Ad.cpu(), inp["A"]) and torch.equal(md.cpu(), m0)
