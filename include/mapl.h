@@ -293,12 +293,14 @@ int rvq_stream_decode(float* C, int64_t C_round_stride, int64_t R_c, const int32
  * may share it, calls that overlap in time may not.
  * For r <= 256 both polar maps run as iterations on r x r matrices (every
  * iterate is the input times a polynomial in its Gram matrix, so the result is
- * the same up to rounding).  For r <= 128 each map is one launch of r/2
+ * the same up to rounding): each map is one launch of 2r (r <= 128) or r
  * workgroups that wait for one another through counters in the workspace.
- * They need to be resident together, which an otherwise idle device always
- * allows; should a wait last beyond about a second (a device kept full by
- * other work), the step is abandoned rather than the call hanging.  For
- * 128 < r <= 256 every half step is its own launch, with no such wait.
+ * They need to be resident together; the library checks once per device that
+ * the device can hold them all (an MI355X can), and otherwise -- or for
+ * r > 256, or with the environment variable MAPL_SPEL_GRAM_SPACE=0 -- runs
+ * every Newton-Schulz step on the d x r iterate, with no waits.  Should a wait
+ * last beyond about a second (a device kept full by other work), the step is
+ * abandoned rather than the call hanging.
  * The step is transactional: the new m and A are formed in the workspace and
  * the last launch writes both only if no wait timed out; an abandoned step
  * leaves A and m exactly as they were (D_out, if given, is then unspecified).

@@ -317,25 +317,27 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
 // (4 products), and an odd step count ends with one plain step on the last
 // even S_k.
 //
-// One launch of 2 r workgroups of 2 r threads, each owning one row: S
-// workgroup J < r row J of the even S_k, Q workgroup J row J of the Q_k.  Only
-// the S_k chain is sequential: the S workgroups wait for each other and never
-// for the Q workgroups, which follow the chain one exchanged S_k at a time and
-// hold nothing back but a buffer (the exchanged S_k live in a ring of kRsRing
-// buffers; a slot is written again only after every Q workgroup has read what
-// it held).
+// One launch of workgroups of 2 r threads, each owning RHO rows (one for
+// r <= 128, two above): S workgroup J rows J RHO .. of the even S_k, Q
+// workgroup J the same rows of the Q_k.  Only the S_k chain is sequential: the
+// S workgroups wait for each other and never for the Q workgroups, which follow
+// the chain one exchanged S_k at a time and hold nothing back but a buffer
+// (the exchanged S_k live in a ring of kRsRing buffers; a slot is written
+// again only after every Q workgroup has read what it held).
 //
-// Products on the vector ALUs.  Lane l of wave w owns the column pair
-// c0 = 32 w + 2 (l >> 2), c0 + 1 and the contraction quarter q = l & 3,
-// k in [q r/4, (q+1) r/4).  Each exchange a workgroup copies S_k into LDS
-// (coalesced 16-byte device-coherent loads, row pitch r + 4) and every thread
-// then keeps its r/4 x 2 entries in registers for the exchange's products, so
-// a product reads only its left row from LDS (16-byte reads, one address per
-// lane quad) and adds the four quarters across the quad (two DPP steps; every
-// lane of the quad ends with the same sum).  One row per workgroup keeps the
-// chain of products between exchanges short: a product is 2 r^2 / (4 r) fused
-// multiply-adds per thread, where 4 rows on v_mfma_f32_4x4x1_16b_f32 (half the
-// matrix core's rate) took as long as 4 rows on the vector ALUs.
+// Products on the vector ALUs.  Lane l of wave w owns CPT columns from
+// c0 = 32 w + CPT (l / KS) and the contraction part q = l % KS, k in
+// [q r/KS, (q+1) r/KS): r <= 128 two columns and lane quads (KS = 4), above
+// four columns and lane octets (KS = 8).  Every thread keeps its entries of the
+// exchanged S_k in registers for the exchange's products (r <= 128: copied
+// into LDS first with coalesced 16-byte device-coherent loads; above, r x r no
+// longer fits LDS and each thread loads its own), so a product reads only its
+// left rows from LDS (16-byte reads, one address per lane group) and adds the
+// contraction parts across the group with DPP (every lane of the group ends
+// with the same sum).  Few rows per workgroup keep the chain of products
+// between exchanges short: at r = 128 a product is 64 fused multiply-adds per
+// thread, where 4 rows on v_mfma_f32_4x4x1_16b_f32 (half the matrix core's
+// rate) took as long as 4 rows on the vector ALUs.
 //
 // Exchange.  Each workgroup owns a progress counter: an S workgroup's is the
 // number of S_k whose rows it has stored, a Q workgroup's the number of S_k it
@@ -347,17 +349,14 @@ __global__ __launch_bounds__(256) void k_spel_xm(const float* __restrict__ X, co
 // has seen every counter it needs.  A wait that exceeds its bound (a second or
 // two) sets the timeout word, and the Q workgroups then write NaN: a wrong
 // result is never silent and no wait is endless.  The launch is ordinary; its
-// workgroups (at most 256, with a few KB of LDS each) are resident together on
-// an otherwise idle device.
+// workgroups (256 at r = 128 and r = 256) must be resident together, which the
+// host checks against the device's compute units and the kernel's occupancy
+// before it takes this form.
 //
 // each spin is a sleep and an uncached load: 2^20 spins take about 1-2 s.  The
 // environment variable MAPL_SPEL_SPIN_LIMIT lowers the bound, for tests of the
 // timeout path.
 constexpr unsigned kRsSpinLimit = 1u << 20;
-
-__device__ __forceinline__ f32x4 mfma_f32_4x4x1(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, c, 0, 0, 0);
-}
 
 constexpr int kRsRing = 4;  // S_k buffers
 
@@ -648,143 +647,6 @@ __global__ __launch_bounds__(2 * R) void k_spel_rsv(const float* __restrict__ pa
   }
 }
 
-// Gram-space Newton-Schulz for 128 < r <= 256, one launch per half step.
-// The same recurrence as k_spel_rsv (X_k = X Q_k, S_k = X_k^T X_k, T_k =
-// 1.5 I - 0.5 S_k, Q_{k+1} = Q_k T_k, S_{k+1} = T_k S_k T_k), but r x r no
-// longer fits one workgroup's LDS, so the kernel boundary is the exchange:
-//   RS_UQ   (step k < n)  U = S_{k-1} T_{k-1} and Q_k = Q_{k-1} T_{k-1}
-//   RS_S    (step k < n)  S_k = U T_{k-1}
-//   RS_LAST (step n)      M = s Q_n = s Q_{n-1} T_{n-1}
-// (Q_1 = T_0, so step 1 has no Q product).  S_0 = s^2 times the sum of the G
-// Gram pieces (added in order), s = 1/||X||_F from per-block partial sums or 1.
-// One block: 4 rows x 64 columns of the output.  The right factor's 64
-// columns are staged in LDS as 64 rows (T is symmetric up to rounding, so
-// column c is read as row c: coalesced loads, 16-byte operand reads); the left
-// operand's 4 rows likewise.  v_mfma_f32_4x4x1_16b_f32 (four rows against 64
-// columns per instruction), the contraction split over the 4 waves and added in
-// LDS in wave order.
-enum { RS_UQ = 0, RS_S = 1, RS_LAST = 2 };
-
-template <int R, bool FIRST>
-__global__ __launch_bounds__(256) void k_spel_rstep(const float* __restrict__ Sprev, const float* __restrict__ part,
-                                                    int G, const float* __restrict__ nparts, int nnp,
-                                                    const float* __restrict__ Lrows, const float* __restrict__ Qprev,
-                                                    float* __restrict__ out1, float* __restrict__ out2, int mode) {
-  constexpr bool first = FIRST;
-  constexpr int RP = R + 4, KW = R / 4, KU = KW / 4, U4 = R / 4, NPT = 64 * U4 / 256;
-  extern __shared__ __align__(16) float rs_lds[];
-  float* Bsh = rs_lds;            // [64][RP]: row c = column c0 + c of T
-  float* Lsh = Bsh + 64 * RP;     // [4][RP]: left operand rows
-  float* Qsh = Lsh + 4 * RP;      // [4][RP]: Q_{k-1} rows
-  float* red = Qsh + 4 * RP;      // [4 waves][4][64]
-  __shared__ float scs;
-  const int lane = threadIdx.x & 63, w = wave_id();
-  const int r0 = blockIdx.x * 4, c0 = blockIdx.y * 64;
-  const float sx = (nparts && (first || mode == RS_LAST)) ? block_inv_norm(nparts, nnp, &scs) : 1.f;
-  const float s2 = sx * sx;
-  const size_t rr = size_t(R) * R;
-  // 16 bytes of row i of S_{k-1} (S_0 = s^2 times the pieces' sum)
-  auto srow4 = [&](int i, int j) {
-    const size_t o = size_t(i) * R + j;
-    if (!first) return ld4(Sprev + o);
-    f32x4 v = ld4(part + o);
-    for (int q = 1; q < G; ++q) v += ld4(part + size_t(q) * rr + o);
-    return v * s2;
-  };
-  auto t4 = [&](int i, int j, f32x4 sv) {  // T = 1.5 I - 0.5 S on 16 bytes of row i at column j
-    f32x4 t;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) t[e] = ((i == j + e) ? 1.5f : 0.f) - 0.5f * sv[e];
-    return t;
-  };
-  // stage the 64 rows of T (zeros past R): every load of the thread is issued before the
-  // first is used (the pieces of S_0 one piece at a time), then the rows are stored
-  {
-    f32x4 v[NPT];
-    const float* src = FIRST ? part : Sprev;
-#pragma unroll
-    for (int q = 0; q < NPT; ++q) {
-      const int e = threadIdx.x + 256 * q, i = min(c0 + e / U4, R - 1), j = 4 * (e % U4);
-      v[q] = ld4(src + size_t(i) * R + j);
-    }
-    if (FIRST) {
-      for (int g = 1; g < G; ++g) {
-        f32x4 t[NPT];
-#pragma unroll
-        for (int q = 0; q < NPT; ++q) {
-          const int e = threadIdx.x + 256 * q, i = min(c0 + e / U4, R - 1), j = 4 * (e % U4);
-          t[q] = ld4(part + size_t(g) * rr + size_t(i) * R + j);
-        }
-#pragma unroll
-        for (int q = 0; q < NPT; ++q) v[q] += t[q];
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < NPT; ++q) {
-      const int e = threadIdx.x + 256 * q, c = e / U4, j = 4 * (e % U4), i = c0 + c;
-      st4(Bsh + c * RP + j, i < R ? t4(i, j, FIRST ? v[q] * s2 : v[q]) : f32x4{0.f, 0.f, 0.f, 0.f});
-    }
-  }
-  const bool needQ = mode != RS_S && !first;
-  for (int e = threadIdx.x; e < 4 * U4; e += 256) {
-    const int i = e / U4, j = 4 * (e % U4), row = r0 + i;
-    if (mode == RS_UQ) st4(Lsh + i * RP + j, srow4(row, j));
-    else if (mode == RS_S) st4(Lsh + i * RP + j, ld4(Lrows + size_t(row) * R + j));
-    if (needQ) st4(Qsh + i * RP + j, ld4(Qprev + size_t(row) * R + j));
-  }
-  __syncthreads();
-  f32x4 b[KU];
-#pragma unroll
-  for (int u = 0; u < KU; ++u) b[u] = ld4(Bsh + lane * RP + w * KW + 4 * u);
-  // rows (4 x R in LDS) times the staged columns: element (i, c0 + lane) for i = threadIdx.x / 64
-  auto product = [&](const float* rows) {
-    f32x4 h0 = f32x4{0.f, 0.f, 0.f, 0.f}, h1 = h0;
-#pragma unroll
-    for (int u = 0; u < KU; ++u) {
-      const f32x4 a = ld4(rows + (lane & 3) * RP + w * KW + 4 * u);
-      h0 = mfma_f32_4x4x1(a[0], b[u][0], h0);
-      h1 = mfma_f32_4x4x1(a[1], b[u][1], h1);
-      h0 = mfma_f32_4x4x1(a[2], b[u][2], h0);
-      h1 = mfma_f32_4x4x1(a[3], b[u][3], h1);
-    }
-    const f32x4 pv = h0 + h1;
-#pragma unroll
-    for (int v = 0; v < 4; ++v) red[(w * 4 + v) * 64 + lane] = pv[v];
-    __syncthreads();
-    const int i = threadIdx.x >> 6;
-    const float sum = ((red[(0 * 4 + i) * 64 + lane] + red[(1 * 4 + i) * 64 + lane]) + red[(2 * 4 + i) * 64 + lane]) +
-                      red[(3 * 4 + i) * 64 + lane];
-    __syncthreads();  // red is free again
-    return sum;
-  };
-  const int i = threadIdx.x >> 6, col = c0 + lane, row = r0 + i;
-  const bool inside = col < R;
-  const size_t o = size_t(row) * R + col;
-  // T_{k-1}[row][col] (for Q_1 = T_0): from the staged rows of the left operand or directly
-  auto t_at = [&]() {
-    const float sv = first ? [&]() {
-      float v = part[size_t(row) * R + col];
-      for (int q = 1; q < G; ++q) v += part[size_t(q) * rr + size_t(row) * R + col];
-      return v * s2;
-    }() : Sprev[o];
-    return ((row == col) ? 1.5f : 0.f) - 0.5f * sv;
-  };
-  if (mode == RS_UQ) {
-    const float u = product(Lsh);
-    const float q = first ? (inside ? t_at() : 0.f) : product(Qsh);
-    if (inside) {
-      out1[o] = u;
-      out2[o] = q;
-    }
-  } else if (mode == RS_S) {
-    const float sk = product(Lsh);
-    if (inside) out1[o] = sk;
-  } else {
-    const float q = first ? (inside ? t_at() : 0.f) : product(Qsh);
-    if (inside) out1[o] = q * sx;
-  }
-}
-
 // Polar Express step matrix M = s (a I + b s^2 S + c s^4 S^2) [r][r], S the
 // sum of the G Gram pieces, s = 1 / ||X||_F from per-block partial sums (the
 // first step) or 1.  One block per 32 x 32 tile (bi, bj); S^2's tile is
@@ -945,49 +807,55 @@ void launch_rs_any(int r, const float* part, int G, const float* nparts, int nnp
   }
 }
 
-// Compute units of the current device (0 if it cannot be read).
-int device_cus() {
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return 0;
-  return n;
-}
-
-// M = s Q_iters by the one-launch-per-half-step Gram-space iteration (128 < r <= 256).
-// Sb0/Sb1 and Q0/Q1 alternate between steps; U holds S_{k-1} T_{k-1}.
+// Whether every workgroup of the one-launch iteration for this r can be resident
+// at once on the current device (its workgroups wait for each other), from the
+// device's compute units and the kernel's occupancy; cached per device.  The
+// environment variable MAPL_SPEL_GRAM_SPACE=0 answers no, for tests of the
+// other form.
 template <int R>
-void launch_rsteps_r(const float* part, int G, const float* nparts, int nnp, int iters, float* Sb0, float* Sb1,
-                     float* U, float* Q0, float* Q1, float* M, hipStream_t s) {
-  constexpr int lds = (64 * (R + 4) + 8 * (R + 4) + 4 * 4 * 64) * int(sizeof(float));
-  (void)LdsLimit<k_spel_rstep<R, true>, lds>::bytes();
-  (void)LdsLimit<k_spel_rstep<R, false>, lds>::bytes();
-  const dim3 grid(R / 4, (R + 63) / 64), blk(256);
-  float* Sb[2] = {Sb0, Sb1};
-  float* Qb[2] = {Q0, Q1};
-  const float* Sprev = nullptr;
-  const float* Qprev = nullptr;
-  for (int k = 1; k <= iters; ++k) {
-    auto k_step = k == 1 ? k_spel_rstep<R, true> : k_spel_rstep<R, false>;
-    if (k < iters) {
-      float* Qk = Qb[k & 1];
-      float* Sk = Sb[k & 1];
-      hipLaunchKernelGGL(k_step, grid, blk, lds, s, Sprev, part, G, nparts, nnp, nullptr, Qprev, U, Qk, int(RS_UQ));
-      hipLaunchKernelGGL(k_step, grid, blk, lds, s, Sprev, part, G, nparts, nnp, U, nullptr, Sk, nullptr, int(RS_S));
-      Sprev = Sk;
-      Qprev = Qk;
-    } else {
-      hipLaunchKernelGGL(k_step, grid, blk, lds, s, Sprev, part, G, nparts, nnp, nullptr, Qprev, M, nullptr,
-                         int(RS_LAST));
-    }
+bool rsv_fits_now() {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return false;
+  hipError_t e;
+  int grid;
+  if constexpr (R <= 128) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_spel_rsv<R, 1, 4, 2, true>),
+                                                     2 * R, kRsStageFloats<R> * sizeof(float));
+    grid = 2 * R;
+  } else {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(k_spel_rsv<R, 2, 8, 4, false>),
+                                                     2 * R, 0);
+    grid = R;
   }
+  return e == hipSuccess && int64_t(per_cu) * cus >= grid;
 }
 
-void launch_rsteps(int r, const float* part, int G, const float* nparts, int nnp, int iters, float* Sb0, float* Sb1,
-                   float* U, float* Q0, float* Q1, float* M, hipStream_t s) {
-  if (r == 160) launch_rsteps_r<160>(part, G, nparts, nnp, iters, Sb0, Sb1, U, Q0, Q1, M, s);
-  else if (r == 192) launch_rsteps_r<192>(part, G, nparts, nnp, iters, Sb0, Sb1, U, Q0, Q1, M, s);
-  else if (r == 224) launch_rsteps_r<224>(part, G, nparts, nnp, iters, Sb0, Sb1, U, Q0, Q1, M, s);
-  else launch_rsteps_r<256>(part, G, nparts, nnp, iters, Sb0, Sb1, U, Q0, Q1, M, s);
+bool rsv_fits(int r) {
+  const char* e = std::getenv("MAPL_SPEL_GRAM_SPACE");
+  if (e != nullptr && e[0] == '0' && e[1] == 0) return false;
+  if (r > 256 || r % 32 != 0) return false;
+  static std::atomic<int8_t> cache[64][8];  // 0 not known yet, 1 no, 2 yes
+  int dev = 0;
+  const bool cacheable = hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64;
+  const int k = r / 32 - 1;
+  if (cacheable) {
+    const int8_t v = cache[dev][k].load(std::memory_order_relaxed);
+    if (v != 0) return v == 2;
+  }
+  bool fits = false;
+  switch (r) {
+    case 32: fits = rsv_fits_now<32>(); break;
+    case 64: fits = rsv_fits_now<64>(); break;
+    case 96: fits = rsv_fits_now<96>(); break;
+    case 128: fits = rsv_fits_now<128>(); break;
+    case 160: fits = rsv_fits_now<160>(); break;
+    case 192: fits = rsv_fits_now<192>(); break;
+    case 224: fits = rsv_fits_now<224>(); break;
+    default: fits = rsv_fits_now<256>(); break;
+  }
+  if (cacheable) cache[dev][k].store(fits ? 2 : 1, std::memory_order_relaxed);
+  return fits;
 }
 
 }  // namespace
@@ -1048,10 +916,10 @@ void launch_spel(float* A, const float* g, float* m, float alpha, float beta, in
   launch_xm<false>(G, xgrid, s, A, nullptr, part, w.Xm, d, r, int(XM_TANGENT), g, m, beta, w.nparts, nullptr, 0.f,
                    nullptr, nullptr);
 
-  if (r <= 128 || (r <= 256 && device_cus() >= r)) {
-    // Gram-space iteration in one launch: S_0 from the pieces of Xm^T Xm, M = s Q_n, then
-    // D = Xm M and Y0 = A - alpha D (Eq. (6)); the same for Y0 (unscaled) and A = Y0 M
-    // (Eq. (7)).  Above r = 128 its r workgroups take a compute unit each.
+  if (rsv_fits(r)) {
+    // Gram-space iteration in one launch (r <= 256, and all its workgroups resident at
+    // once): S_0 from the pieces of Xm^T Xm, M = s Q_n, then D = Xm M and Y0 = A - alpha D
+    // (Eq. (6)); the same for Y0 (unscaled) and A = Y0 M (Eq. (7)).
     const int npn = (d / 32) * (r / 32);
     hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, w.Xm, w.Xm, part, d, r, G, w.sync, kRsStickyWord);
     launch_rs_any(r, part, G, w.nparts, npn, ns_iters, w.Sbuf, w.sync, w.Mb, s);
@@ -1059,23 +927,6 @@ void launch_spel(float* A, const float* g, float* m, float alpha, float beta, in
                      nullptr, A, alpha, D_out, w.Xc);
     hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, w.Xc, w.Xc, part, d, r, G, w.sync, kRsStickyWord);
     launch_rs_any(r, part, G, nullptr, 0, ns_iters, w.Sbuf, w.sync, w.Mb, s);
-    launch_xm<false>(1, xgrid, s, w.Xc, nullptr, w.Mb, A, d, r, int(XM_NS_LAST_RET), nullptr, nullptr, 0.f, nullptr,
-                     nullptr, 0.f, nullptr, nullptr, cm);
-    return;
-  }
-
-  if (r <= 256) {
-    // the same Gram-space iteration with one launch per half step (a device with fewer
-    // than r compute units): S_k, S_{k-1} T_{k-1} and Q_k live in the rs ring and Xa
-    const int npn = (d / 32) * (r / 32);
-    const size_t rr = size_t(r) * r;
-    float *Sb0 = w.Sbuf, *Sb1 = w.Sbuf + rr, *U = w.Sbuf + 2 * rr, *Q0 = w.Sbuf + 3 * rr, *Q1 = w.Xa;
-    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, w.Xm, w.Xm, part, d, r, G, nullptr, 0);
-    launch_rsteps(r, part, G, w.nparts, npn, ns_iters, Sb0, Sb1, U, Q0, Q1, w.Mb, s);
-    launch_xm<false>(1, xgrid, s, w.Xm, nullptr, w.Mb, nullptr, d, r, int(XM_NS_LAST_LMO), nullptr, nullptr, 0.f,
-                     nullptr, A, alpha, D_out, w.Xc);
-    hipLaunchKernelGGL(k_spel_gram<0>, ggrid, blk, 0, s, w.Xc, w.Xc, part, d, r, G, nullptr, 0);
-    launch_rsteps(r, part, G, nullptr, 0, ns_iters, Sb0, Sb1, U, Q0, Q1, w.Mb, s);
     launch_xm<false>(1, xgrid, s, w.Xc, nullptr, w.Mb, A, d, r, int(XM_NS_LAST_RET), nullptr, nullptr, 0.f, nullptr,
                      nullptr, 0.f, nullptr, nullptr, cm);
     return;

@@ -120,6 +120,18 @@ def test_spel_wait_timeout_leaves_the_state_unchanged_then_recovers(monkeypatch,
     check(inp["A"], inp["g"], m0, 1e-3, 0.9, 8, Ad, md, D)
 
 
+@pytest.mark.parametrize("d,r", [(1024, 128), (2048, 256), (640, 96)])
+def test_spel_dxr_form_below_r256(monkeypatch, d, r):
+    # a device that cannot hold every workgroup of the one-launch Gram-space iteration runs
+    # each Newton-Schulz step on the d x r iterate; a test hook selects that form here
+    inp = synth.spel_inputs(500 + d + r, d, r, 1e-3)
+    m0 = torch.from_numpy(synth.gaussian(synth.stream(13, d, r), (d, r), 1e-4).astype(np.float32))
+    monkeypatch.setenv("MAPL_SPEL_GRAM_SPACE", "0")
+    Ad, md, D = run(inp["A"], inp["g"], m0, 1e-3, 0.9, 8)
+    monkeypatch.delenv("MAPL_SPEL_GRAM_SPACE")
+    check(inp["A"], inp["g"], m0, 1e-3, 0.9, 8, Ad, md, D)
+
+
 @pytest.mark.parametrize("d,r,cond", [(1024, 128, 1e2), (1024, 128, 1e4), (256, 32, 1e4), (640, 96, 1e3),
                                       (2048, 256, 1e2), (2048, 256, 1e4), (1056, 160, 1e4)])
 def test_spel_ill_conditioned_momentum(d, r, cond):
