@@ -939,6 +939,9 @@ __global__ __launch_bounds__(256) void k_sub_ptm(const bf16_t* __restrict__ P, c
   const int i0 = blockIdx.x * 32, j0 = blockIdx.y * 32;
   const int kq = ra >> 2;  // ra % 32 == 0: a multiple of 8
   const int kb = wave * kq, ke = kb + kq;
+  const int i = threadIdx.x >> 3, j = (threadIdx.x & 7) * 4;
+  f32x4* o = reinterpret_cast<f32x4*>(gA + size_t(i0 + i) * r + j0 + j);
+  const f32x4 g0 = *o;  // issued with the operands' loads, not after the products
   f32x16 acc = f32x16{};
   // 32 values of k per batch, all loads issued before the batch's multiplies
   for (int kc = kb; kc < ke; kc += 32) {
@@ -957,12 +960,10 @@ __global__ __launch_bounds__(256) void k_sub_ptm(const bf16_t* __restrict__ P, c
 #pragma unroll
   for (int v = 0; v < 16; ++v) red[wave * 1024 + v * 64 + lane] = acc[v];
   __syncthreads();
-  const int i = threadIdx.x >> 3, j = (threadIdx.x & 7) * 4;
   const int fi = ((((i >> 3) << 2) | (i & 3)) << 6) + (((i >> 2) & 1) << 5) + j;
   const f32x4* r4 = reinterpret_cast<const f32x4*>(red);
   const f32x4 sum = (r4[fi / 4] + r4[(1024 + fi) / 4]) + (r4[(2048 + fi) / 4] + r4[(3072 + fi) / 4]);
-  f32x4* o = reinterpret_cast<f32x4*>(gA + size_t(i0 + i) * r + j0 + j);
-  *o = *o - sum;
+  *o = g0 - sum;
 }
 
 // gA -= M elementwise (the identity anchor projector), 4 values per thread
