@@ -581,6 +581,7 @@ __global__ __launch_bounds__(256) void k_rvq_decode(const uint8_t* __restrict__ 
 // Narrow groups (W = 2 or 4, r % 8 == 0): a thread owns 8 consecutive outputs,
 // i.e. 8 / W whole groups; per round it reads their codes with one load and
 // each codeword as one W-float vector.
+constexpr int kDecRounds = 4;
 template <typename OT, int W>
 __global__ __launch_bounds__(256) void k_rvq_decode_narrow(const uint8_t* __restrict__ codes,
                                                            const float* __restrict__ C, int64_t stride,
@@ -594,24 +595,44 @@ __global__ __launch_bounds__(256) void k_rvq_decode_narrow(const uint8_t* __rest
   float acc[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) acc[q] = 0.f;
-  for (int rho = 0; rho < R; ++rho) {
-    const uint8_t* cp = codes + (size_t(n) * R + rho) * G + g0;
-    uint32_t kk;
-    if (NG == 4) kk = *reinterpret_cast<const uint32_t*>(cp);
-    else kk = *reinterpret_cast<const uint16_t*>(cp);
+  // rounds in batches of kDecRounds: the batch's codes are loaded together, then
+  // its codewords, so a thread waits for two loads per batch, not two per round
+  for (int r0 = 0; r0 < R; r0 += kDecRounds) {
+    uint32_t kk[kDecRounds];
 #pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int k = int((kk >> (8 * i)) & 0xffu);
-      if (k >= K) continue;  // a code >= K (corrupt input) adds nothing
-      const float* cw = C + rho * stride + (size_t(g0 + i) * K + k) * W;
-      if (W == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(cw);
-        acc[2 * i] += v.x;
-        acc[2 * i + 1] += v.y;
-      } else {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(cw);
+    for (int u = 0; u < kDecRounds; ++u) {
+      const uint8_t* cp = codes + (size_t(n) * R + min(r0 + u, R - 1)) * G + g0;
+      if (NG == 4) kk[u] = *reinterpret_cast<const uint32_t*>(cp);
+      else kk[u] = *reinterpret_cast<const uint16_t*>(cp);
+    }
+    float v[kDecRounds][8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[4 * i + q] += v[q];
+    for (int u = 0; u < kDecRounds; ++u) {
+      const int rho = min(r0 + u, R - 1);
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        int k = int((kk[u] >> (8 * i)) & 0xffu);
+        k = k < K ? k : 0;
+        const float* cw = C + rho * stride + (size_t(g0 + i) * K + k) * W;
+        if (W == 2) {
+          const float2 t2 = *reinterpret_cast<const float2*>(cw);
+          v[u][2 * i] = t2.x;
+          v[u][2 * i + 1] = t2.y;
+        } else {
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(cw);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[u][4 * i + q] = t4[q];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kDecRounds; ++u) {
+      if (r0 + u >= R) break;
+#pragma unroll
+      for (int i = 0; i < NG; ++i) {
+        if (int((kk[u] >> (8 * i)) & 0xffu) >= K) continue;  // a code >= K (corrupt input) adds nothing
+#pragma unroll
+        for (int q = 0; q < W; ++q) acc[W * i + q] += v[u][W * i + q];
       }
     }
   }
