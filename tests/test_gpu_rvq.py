@@ -143,6 +143,27 @@ def test_rvq_decode_of_unaligned_codes(w):
     assert_close(np64(a), rvq.decode(codes.cpu().numpy(), np64(C), G, K, R), F32_TOL, "decode")
 
 
+@pytest.mark.parametrize("w,R,R_c", [(2, 6, 1), (4, 5, 5), (2, 4, 4), (8, 6, 6), (32, 5, 1)])
+def test_rvq_decode_many_rounds_and_codes_out_of_range(w, R, R_c):
+    """More rounds than the narrow decode reads in one batch (four), so a partial
+    second batch, and codes >= K, which add nothing: the expected rows are the
+    oracle's sums with each such code pointed at an appended zero codeword."""
+    G, K, N = 8, 37, 611
+    r = G * w
+    rng = np.random.default_rng(w * 10 + R)
+    C = torch.from_numpy((rng.standard_normal((R_c, G, K, w)) / math.sqrt(w)).astype(np.float32)).to(DEV)
+    codes_np = rng.integers(0, K, size=(N, R, G)).astype(np.uint8)
+    bad = rng.random((N, R, G)) < 0.05
+    codes_np[bad] = rng.integers(K, 256, size=int(bad.sum())).astype(np.uint8)
+    codes = torch.from_numpy(codes_np).to(DEV)
+    stride = 0 if R_c == 1 else r * K
+    Zq = lac.rvq_decode(codes, C, G, K, R, r, round_stride=stride)
+    torch.cuda.synchronize()
+    C_ext = np.concatenate([np64(C), np.zeros((R_c, G, 1, w))], axis=2)
+    want = rvq.decode(np.minimum(codes_np, K), C_ext, G, K + 1, R)
+    assert_close(np64(Zq), want, F32_TOL, "decode")
+
+
 def test_rvq_codeword_inputs_come_back_exactly():
     rng = np.random.default_rng(5)
     N, G, K, w = 1000, 8, 256, 32
