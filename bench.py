@@ -473,10 +473,15 @@ def run_cases(lac, dev, flush):
         N * r * R, "hbm", tokens=N, peak_tf=F32_PEAK_TFLOPS)
     del g, Z, Cb, codes, Zq, gZ, C2, codes2
 
-    # one spel_step on the fp32 2048 x 256 projector (the d x r iteration) and on the 1024 x 128 one (the r x r
-    # iteration of r <= 128: per polar map a Gram and X M, 2 d r^2 each, and 6 r^3 per step after the first)
+    # one spel_step on the fp32 2048 x 256 and 1024 x 128 projectors, flops executed.  r <= 256 (the r x r
+    # iteration): the tangent projection's Gram and product and, per polar map, a Gram and X M, 2 d r^2 each
+    # (12 d r^2); per polar map 8 row products (2 r^2 flops per row) for each exchanged S_k after S_0,
+    # floor((n - 1) / 2) of them, and about 4 for each of the ceil(n / 2) Q steps.  r > 256 (the d x r
+    # iteration): 4 d r^2 per step and the projection's.
     def ns_flops(d, r, n):
-        return 12 * d * r * r + 12 * r ** 3 * (n - 1) if r <= 128 else 4 * d * r * r * (1 + 2 * n)
+        if r <= 256:
+            return 12 * d * r * r + 4 * r ** 3 * (8 * ((n - 1) // 2) + 4 * ((n + 1) // 2))
+        return 4 * d * r * r * (1 + 2 * n)
     c = C["1b"]
     d, r, sp = c["d"], c["r"], c["spel"]
     si = synth.spel_inputs(c["seed"], d, r, sp["g_var"])

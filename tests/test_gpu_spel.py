@@ -136,13 +136,25 @@ def test_spel_dxr_form_below_r256(monkeypatch, d, r):
                                       (2048, 256, 1e2), (2048, 256, 1e4), (1056, 160, 1e4)])
 def test_spel_ill_conditioned_momentum(d, r, cond):
     """The LMO's input spread over a wide spectrum (condition number 1e2 to
-    1e4), in both forms of the iteration: the r x r Gram-space one (r <= 128)
-    and the d x r one.  g = 0 leaves m = beta m0, so the prescribed spectrum
-    reaches the polar map unchanged."""
+    1e4) through the r x r Gram-space iteration (every r <= 256 here).  g = 0
+    leaves m = beta m0, so the prescribed spectrum reaches the polar map
+    unchanged."""
     inp = synth.spel_inputs(400 + d + r, d, r, 1e-3)
     m0 = spectrum_matrix(int(cond) + d + r, d, r, cond)
     z = torch.zeros_like(inp["g"])
     Ad, md, D = run(inp["A"], z, m0, 0.05, 0.9, 8)
+    check(inp["A"], z, m0, 0.05, 0.9, 8, Ad, md, D)
+
+
+@pytest.mark.parametrize("d,r,cond", [(1024, 128, 1e4), (2048, 256, 1e2), (640, 96, 1e3)])
+def test_spel_ill_conditioned_momentum_dxr_form(monkeypatch, d, r, cond):
+    """The same spectra through the d x r iteration (selected by the test hook)."""
+    inp = synth.spel_inputs(400 + d + r, d, r, 1e-3)
+    m0 = spectrum_matrix(int(cond) + d + r, d, r, cond)
+    z = torch.zeros_like(inp["g"])
+    monkeypatch.setenv("MAPL_SPEL_GRAM_SPACE", "0")
+    Ad, md, D = run(inp["A"], z, m0, 0.05, 0.9, 8)
+    monkeypatch.delenv("MAPL_SPEL_GRAM_SPACE")
     check(inp["A"], z, m0, 0.05, 0.9, 8, Ad, md, D)
 
 

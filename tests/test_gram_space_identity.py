@@ -1,5 +1,5 @@
 """The algebra behind the r x r (Gram-space) form of the cubic Newton-Schulz
-polar map that spel_step uses for r <= 128: with S_k = X_k^T X_k,
+polar map that spel_step uses for r <= 256: with S_k = X_k^T X_k,
 T_k = 1.5 I - 0.5 S_k,
     X_k = X_0 Q_k,  Q_{k+1} = Q_k T_k,  S_{k+1} = 2.25 S_k - 1.5 S_k^2 + 0.25 S_k^3,
 so n steps of X <- X (1.5 I - 0.5 X^T X) equal X_0 Q_n.  Checked here in fp64
