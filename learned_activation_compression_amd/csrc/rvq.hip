@@ -86,9 +86,12 @@ __device__ __forceinline__ float rvq_norm2(const double (&res)[H]) {
 // added (fp addition commutes, so both lanes get the same value).  Exact ties
 // keep the lower index; codewords past K (padding) are skipped; NaN never
 // wins.  With no candidate (all scores NaN) the code is 0.
-// Every pass takes each lane's next candidate, wherever it sits in the eight
-// mask words, so the wave makes as many passes as its busiest token has
-// candidates (not one per mask word that any token uses).
+// Every pass takes each lane's next two candidates, wherever they sit in the
+// eight mask words (picked with selects, no branches), and scores both with
+// their loads and arithmetic side by side, so the wave makes
+// ceil(c / 2) passes for its busiest token's candidate count c.  The order in
+// which candidates are scored does not change the result: the winner is the
+// smallest distance, the lowest index among equal ones.
 template <typename PartFn>
 __device__ __forceinline__ int rvq_rescore(const uint32_t (&mine)[4], int h, int K, PartFn part) {
   uint32_t mm[8];  // words 0-3: candidates of half 0, 4-7: of half 1 (the same in both lanes)
@@ -104,29 +107,37 @@ __device__ __forceinline__ int rvq_rescore(const uint32_t (&mine)[4], int h, int
     for (int q = 0; q < 8; ++q) a |= mm[q];
     return a != 0u;
   };
+  // the first set bit in word order, taken out of its word; -1 when none is left
+  auto pop = [&]() {
+    int qi = 8;
+    uint32_t wv = 0u;
+#pragma unroll
+    for (int q = 7; q >= 0; --q) {
+      const bool nz = mm[q] != 0u;
+      qi = nz ? q : qi;
+      wv = nz ? mm[q] : wv;
+    }
+    const int bit = __builtin_ctz(wv | 0x80000000u);
+    const uint32_t rest = wv & (wv - 1u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) mm[q] = (q == qi) ? rest : mm[q];
+    return qi < 8 ? 64 * (qi & 3) + 32 * (bit >> 4) + mfma32_row(bit & 15, qi >> 2) : -1;
+  };
   double best = __builtin_inf();
   int bk = 0;
-  while (__any(left())) {
-    if (left()) {  // the same in both lanes of the token, so both take the exchange below
-      // the first set bit in word order, taken out of its word
-      int k = 0;
-      bool found = false;
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        if (!found && mm[q] != 0u) {
-          const int bit = __builtin_ctz(mm[q]);
-          mm[q] &= mm[q] - 1u;
-          k = 64 * (q & 3) + 32 * (bit >> 4) + mfma32_row(bit & 15, q >> 2);
-          found = true;
-        }
-      }
-      const double p = part(k);
-      const double dk = p + __shfl_xor(p, 32);
-      if (k < K && (dk < best || (dk == best && k < bk))) {
-        best = dk;
-        bk = k;
-      }
+  auto offer = [&](int k, double p) {
+    const double dk = p + __shfl_xor(p, 32);
+    if (k >= 0 && k < K && (dk < best || (dk == best && k < bk))) {
+      best = dk;
+      bk = k;
     }
+  };
+  while (__any(left())) {
+    // both lanes of a token pop the same candidates, so both take the exchanges in offer()
+    const int k1 = pop(), k2 = pop();
+    const double p1 = part(k1 < 0 ? 0 : k1), p2 = part(k2 < 0 ? 0 : k2);
+    offer(k1, p1);
+    offer(k2, p2);
   }
   return bk;
 }
@@ -305,23 +316,32 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode(const ZT* __restr
 // ---------------------------------------------- encode, bf16-scored (w >= 16) --
 // The scan over the K codewords runs on bf16 matrix cores.  For token n the
 // bf16 score of codeword k is
-//   a_k = <bf16(-2 res), bf16(c_k)> + hi_k + lo_k    (products exact, fp32 sums)
-// with hi_k + lo_k the two-part bf16 split of ||c_k||^2 (fed to the matrix
-// core as two more dimensions against a constant 1).  Each bf16 rounding is a
-// relative 2^-9 at most (2^-9 + 2^-24 for -2 res, rounded from fp64 through
-// fp32), so against the exact s_k = ||c_k||^2 - 2 <res, c_k>
-//   |a_k - s_k| <= 2^-7 (1 + 2^-8) ||res|| ||c_k|| + 2^-17 ||c_k||^2 + (fp32 sums)
-// (Cauchy-Schwarz); taken twice over and uniformly in k,
-//   delta = 2^-6 ||res|| max_k ||c_k|| + 2^-14 max_k ||c_k||^2 + 1e-30.
+//   a_k = nrm_k + <bf16(-2 res), bf16(c_k)>    (products exact, fp32 sums)
+// with nrm_k the fp32 ||c_k||^2, which starts the matrix-core accumulator.
+// With u = 2^-8 the
+// bf16 unit roundoff (8 significant bits): bf16(fp32(-2 res_j)) is
+// -2 res_j (1 + e1), |e1| <= u (1 + 2^-15), and bf16(c_kj) is c_kj (1 + e2),
+// |e2| <= u, so each product is off by at most 2^-7 (1 + 2^-8) |2 res_j c_kj|
+// and their sum by 2^-6 (1 + 2^-8) ||res|| ||c_k|| (Cauchy-Schwarz).  The
+// fp32 norm is within W 2^-24 of ||c_k||^2, and the fp32 sums of nrm_k and
+// the W exact products add at most 2^-17 of the sum of their magnitudes.
+// Together, against the exact
+// s_k = ||c_k||^2 - 2 <res, c_k>,
+//   |a_k - s_k| <= 2^-6 (1 + 2^-7) ||res|| ||c_k|| + 2^-15 ||c_k||^2,
+// and the kernel takes, uniformly in k and with room for the fp32 rounding of
+// its own norms and square roots,
+//   delta = 2^-6 (1 + 2^-6) ||res|| max_k ||c_k|| + 2^-14 max_k ||c_k||^2 + 1e-30.
 // A first scan finds min_j a_j, a second (the same instructions, so the same
 // a_k) marks every codeword with a_k <= min_j a_j + 2 delta in a 128-bit mask
 // per lane, and those are rescored exactly in fp64 (rvq_rescore): about 1.3
 // codewords per token at the step's workload.
 //
 // The bf16 MFMA takes 8 dims per lane per K-step: at step t < W/16 lane half
-// h supplies dims h W/2 + 8 t .. + 7 of codeword and residual alike; step
-// W/16 carries (hi_k, lo_k) against (1, 1) in half 0 and zeros in half 1.
-// Padding codewords (k >= K) have zero dims and hi = +inf, so their score is
+// h supplies dims h W/2 + 8 t .. + 7 of codeword and residual alike.  The
+// accumulator of a block of 32 codewords starts at their norms, kept in LDS in
+// the accumulator's order (lane half h, register v holds codeword row
+// mfma32_row(v, h)), so every lane of a half reads the same 64 bytes.
+// Padding codewords (k >= K) have zero dims and norm +inf, so their score is
 // +inf.
 template <int W, typename ZT>
 __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __restrict__ Z,
@@ -329,11 +349,13 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
                                                                   uint8_t* __restrict__ codes, int N, int r, int G,
                                                                   int K, int R) {
   constexpr int H = W / 2, T = W / 16, FP = W + 4, WB = W + 16;  // dims per lane, K-steps, fp32 / bf16 row pitch
+  constexpr float inf = __builtin_inff();
   extern __shared__ __attribute__((aligned(16))) float sh[];
   float* cbF = sh;                   // [256][FP] fp32 codewords
   float* nrm = cbF + kRvqMaxK * FP;  // [256] ||c_k||^2
   float* bnd = nrm + kRvqMaxK;       // [4]: max ||c_k||^2 (the block's reduction)
-  bf16_t* cbB = reinterpret_cast<bf16_t*>(bnd + 4);  // [256][WB] bf16 codewords, then hi_k, lo_k, zeros
+  float* nrmv = bnd + 4;             // [256] ||c_k||^2 in accumulator order: [32-codeword block][h][v]
+  bf16_t* cbB = reinterpret_cast<bf16_t*>(nrmv + kRvqMaxK);  // [256][WB] bf16 codewords (W used)
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int h = lane >> 5, l32 = lane & 31;
   const int g = blockIdx.x;
@@ -374,10 +396,9 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
         for (int off = 1; off < W / 4; off <<= 1) s2 += __shfl_xor(s2, off);
         if (j0 == 0) {
           nrm[k] = s2;
-          const float hi = k < K ? bf2f(f2bf(s2)) : __builtin_inff();
-          const float lo = k < K ? s2 - hi : 0.f;
-          *reinterpret_cast<u32x4*>(cbB + k * WB + W) = u32x4{pack2bf(hi, lo), 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(cbB + k * WB + W + 8) = u32x4{0u, 0u, 0u, 0u};
+          // codeword row rho of block k / 32 sits in lane half (rho >> 2) & 1, register 4 (rho >> 3) + (rho & 3)
+          const int rho = k & 31;
+          nrmv[(2 * (k >> 5) + ((rho >> 2) & 1)) * 16 + 4 * (rho >> 3) + (rho & 3)] = k < K ? s2 : inf;
         }
       }
       __syncthreads();
@@ -390,9 +411,9 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
       }
       __syncthreads();
     }
-    // the residual's bf16 operand (pre-scaled by -2; the norm step's (1, 1) in half 0),
+    // the residual's bf16 operand (pre-scaled by -2),
     // its norm and the per-token bound
-    bf16x8 bB[T + 1];
+    bf16x8 bB[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
       u32x4 u;
@@ -401,17 +422,22 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
         u[e] = pack2bf(float(-2.0 * res[8 * t + 2 * e]), float(-2.0 * res[8 * t + 2 * e + 1]));
       bB[t] = __builtin_bit_cast(bf16x8, u);
     }
-    bB[T] = __builtin_bit_cast(bf16x8, u32x4{h == 0 ? pack2bf(1.f, 1.f) : 0u, 0u, 0u, 0u});
     const float rn2 = rvq_norm2<H>(res);
     const float nmax = bnd[0];
-    const float delta = fmaf(0x1p-6f * sqrtf(rn2), sqrtf(nmax), fmaf(0x1p-14f, nmax, 1e-30f));
+    const float delta = fmaf(0x1.04p-6f * sqrtf(rn2), sqrtf(nmax), fmaf(0x1p-14f, nmax, 1e-30f));
 
     auto scan = [&](int b) {  // bf16 scores of codewords 32 b .. 32 b + 31 (rows of the accumulator)
       const bf16_t* row = cbB + (32 * b + l32) * WB;
-      f32x16 acc = f32x16{};
+      const f32x4* nv = reinterpret_cast<const f32x4*>(nrmv + (2 * b + h) * 16);
+      f32x16 acc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 n4 = nv[q];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * q + e] = n4[e];
+      }
 #pragma unroll
       for (int t = 0; t < T; ++t) acc = mfma_bf16_32x32x16(ld_bf16x8(row + H * h + 8 * t), bB[t], acc);
-      acc = mfma_bf16_32x32x16(ld_bf16x8(row + W + 8 * h), bB[T], acc);
       return acc;
     };
     // scan 1: the smallest bf16 score (NaN drops out of fminf)
@@ -457,10 +483,11 @@ __global__ __launch_bounds__(64 * kRvqWaves) void k_rvq_encode_bf(const ZT* __re
   }
 }
 
-// LDS of the bf16-scored encode: fp32 codewords [256][W+4], norms [256], bound [4], bf16 rows [256][W+16]
+// LDS of the bf16-scored encode: fp32 codewords [256][W+4], norms [256], bound [4], norms in accumulator
+// order [256], bf16 rows [256][W+16]
 template <int W>
 constexpr size_t rvq_bf_lds() {
-  return (size_t(kRvqMaxK) * (W + 4) + kRvqMaxK + 4) * sizeof(float) + size_t(kRvqMaxK) * (W + 16) * sizeof(bf16_t);
+  return (size_t(kRvqMaxK) * (W + 4) + 2 * kRvqMaxK + 4) * sizeof(float) + size_t(kRvqMaxK) * (W + 16) * sizeof(bf16_t);
 }
 // LDS of the fp32-scored encode: transposed codebook [W][Kp+2], norms [Kp], bound
 inline size_t rvq_f32_lds(int W, int K) {

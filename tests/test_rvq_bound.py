@@ -2,12 +2,14 @@
 checked on the CPU.  Both kernels score codeword k approximately, a_k ~ s_k =
 ||c_k||^2 - 2 <res, c_k> (res kept in fp64), and rescore exactly every k with
 a_k <= min_j a_j + 2 delta; that finds the exact argmin (Section 3.5's nearest
-codeword) if |a_k - s_k| <= delta.  The kernels' delta is twice a proven
-bound, so here the emulated error must stay under half of it.
+codeword) if |a_k - s_k| <= delta.  Each kernel's delta is a proven bound
+(derived beside the kernel); the worst case needs every rounding error to
+line up with the operands' signs, so on these inputs the emulated error stays
+under half of it, and an error above that would point at a mistake in the
+emulation or the derivation.
 
-* w >= 16: a_k = <bf16(fp32(-2 res)), bf16(c_k)> + hi_k + lo_k (bf16 products
-  exact, fp32 sums; hi_k + lo_k the two-part bf16 split of the fp32
-  ||c_k||^2), delta = 2^-6 ||res|| max ||c|| + 2^-14 max ||c||^2 + 1e-30.
+* w >= 16: a_k = nrm_k + <bf16(fp32(-2 res)), bf16(c_k)> (nrm_k the fp32
+  ||c_k||^2; bf16 products exact, fp32 sums), delta = 2^-6 (1 + 2^-6) ||res|| max ||c|| + 2^-14 max ||c||^2 + 1e-30.
 * w < 16: a_k = fp32 sums starting at nrm_k (the fp32 ||c_k||^2) of the fp32
   products fp32(-2 res_j) c_kj, delta = (2 w + 4) 2^-23 (max ||c||^2 +
   2 ||res|| max ||c||) + 1e-30; a token whose second-smallest score exceeds
@@ -37,16 +39,15 @@ def norms_f32(C):
 
 
 def emulate_bf16(res, C, reverse=False):
-    """bf16 scores a [n][K] as the w >= 16 kernel forms them (fp32 sums, in dim order or reversed)."""
+    """bf16 scores a [n][K] as the w >= 16 kernel forms them: the accumulator starts at nrm_k
+    (the fp32 ||c_k||^2) and adds the exact bf16 products in fp32 (dims in order or reversed)."""
     nrm = norms_f32(C)
-    hi = bf16(nrm)
-    lo = bf16(nrm - hi)
     rb, cb = bf16(f32(-2.0 * res)), bf16(C)
-    a = np.zeros((res.shape[0], C.shape[0]), np.float32)
+    a = np.broadcast_to(nrm[None, :], (res.shape[0], C.shape[0])).astype(np.float32)
     dims = range(C.shape[1] - 1, -1, -1) if reverse else range(C.shape[1])
     for j in dims:
         a = np.float32(a + np.outer(rb[:, j], cb[:, j]).astype(np.float32))
-    return np.float32(np.float32(a + hi[None, :]) + lo[None, :]), nrm
+    return a, nrm
 
 
 def emulate_f32(res, C, reverse=False):
@@ -68,7 +69,7 @@ def exact_scores(res, C):
 def delta_bf16(res, nrm):
     rn = np.sqrt(np.float32((res ** 2).sum(1)))
     nmax = np.float32(nrm.max())
-    return np.float32(2.0 ** -6) * rn * np.sqrt(nmax) + np.float32(2.0 ** -14) * nmax + np.float32(1e-30)
+    return np.float32(2.0 ** -6 * (1 + 2.0 ** -6)) * rn * np.sqrt(nmax) + np.float32(2.0 ** -14) * nmax + np.float32(1e-30)
 
 
 def delta_f32(res, nrm, w):
