@@ -452,11 +452,11 @@ def run_cases(lac, dev, flush):
     Zq = torch.empty((N, r), dtype=torch.float32, device=dev)
     enc = lambda: lac.rvq_encode(Z, Cb, G, K, R, codes=codes)
     dec = lambda: lac.rvq_decode(codes, Cb, G, K, R, r, Zq=Zq)
-    # w = 32 >= 16: two bf16 matrix-core scans of the K codewords (w + 16 dims each: the norm rides along) and
-    # a few exact fp32 scores; the executed flops are the scans', against the bf16 peak (2 r K R = 262144
-    # flops per token would be the fp32-equivalent count)
+    # w = 32 >= 16: two bf16 matrix-core scans of the K codewords (w dims each; the norm starts the
+    # accumulator) and a few exact fp64 distances; the executed flops are the scans', 4 r K R per token,
+    # against the bf16 peak (the method's count is 2 r K R = 262144 flops per token)
     add("rvq r256 G8 K256 R2 encode (bf16 scan)", _timed(enc, flush), N * (2 * r + R * G) + Cb.numel() * 4,
-        N * G * R * 2 * 2 * (r // G + 16) * K, "alu", tokens=N, peak_tf=BF16_PEAK_TFLOPS)
+        N * G * R * 2 * 2 * (r // G) * K, "alu", tokens=N, peak_tf=BF16_PEAK_TFLOPS)
     add("rvq r256 G8 K256 R2 decode (fp32)", _timed(dec, flush), N * (R * G + 4 * r) + Cb.numel() * 4,
         N * r * R, "hbm", tokens=N, peak_tf=F32_PEAK_TFLOPS)
     # the backward gradient gZ = gXhat A in the paper's grouping: 128 groups of width 2, K = 256, R = 2
