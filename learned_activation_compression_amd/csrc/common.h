@@ -73,11 +73,15 @@ __device__ __forceinline__ bf16x8 mask_bf16x8(bf16x8 v, uint32_t m) {
 // (hi = 1) or lower half-wave, for the 32x32 MFMA output layout.
 __device__ __forceinline__ int mfma32_row(int v, int hi) { return 8 * (v >> 2) + 4 * hi + (v & 3); }
 
-// Spread consecutive workgroup ids over the 8 XCDs so that each XCD receives a
-// contiguous range of tiles (tiles that share operands then share an L2).
+// Workgroups are dispatched to the 8 XCDs round-robin (id i to XCD i % 8).
+// Renumber them so that each XCD receives a contiguous range of tiles (tiles
+// that share operands then share an L2): XCD x holds the ids i = x + 8 j, and
+// takes tiles start_x + j, where the first total % 8 XCDs hold one id more
+// than the others.  A bijection of [0, total) for any total; only locality,
+// never a result, depends on the dispatch order.
 __device__ __forceinline__ int xcd_swizzle(int bid, int total) {
-  if ((total & 7) != 0) return bid;
-  return (bid & 7) * (total >> 3) + (bid >> 3);
+  const int x = bid & 7, j = bid >> 3, q = total >> 3, rem = total & 7;
+  return (x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q) + j;
 }
 
 // Lane l copies 16 bytes from g to LDS byte address (l_base + 16 l); l_base is
